@@ -1,0 +1,317 @@
+"""Pins of the CPU oracle to things other than itself (CPU only).
+
+Each test names the passage or the mathematical fact it checks.  Together they
+are meant to fail on any plausible slip in the oracle: a wrong softmax scale
+or causal diagonal (SDPA pins, P5), a wrong tie-break (P2, P7, P8), a wrong
+own-block count (P2, P6, golden example), a transposed gate (P6, P10), a
+wrong GQA head map (GQA pin), a wrong pooling axis (block-mean pins) or a
+wrong query alignment (decode pin).
+"""
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import moba_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _case(seed, L, H=1, Hkv=1, D=8, B=4, offset=0.5):
+    rng = np.random.default_rng(seed)
+    nb = -(-L // B)
+    off = rng.standard_normal((nb, Hkv, D)) * offset
+    q = rng.standard_normal((L, H, D))
+    k = rng.standard_normal((L, Hkv, D)) + off[np.arange(L) // B]
+    v = rng.standard_normal((L, Hkv, D))
+    return q, k, v
+
+
+def _sdpa(q, k, v, mask=None, causal=False):
+    """torch CPU float64 scaled_dot_product_attention, KV heads repeated."""
+    H, Hkv = q.shape[1], k.shape[1]
+    qt = torch.from_numpy(q).permute(1, 0, 2)[None]
+    kt = torch.from_numpy(k).permute(1, 0, 2).repeat_interleave(H // Hkv, 0)[None]
+    vt = torch.from_numpy(v).permute(1, 0, 2).repeat_interleave(H // Hkv, 0)[None]
+    m = None if mask is None else torch.from_numpy(mask)[None]
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=m,
+                                                         is_causal=causal)
+    return o[0].permute(1, 0, 2).numpy()
+
+
+# ---------------------------------------------------------------- golden ---
+def test_golden_hand_worked_example():
+    """Hand-derived closed forms for a 6-token case (tests/golden/)."""
+    g = json.load(open(os.path.join(GOLDEN, "hand_worked_6tok.json")))
+    L = g["seq_len"]
+    q = np.array(g["q"], float).reshape(L, 1, 1)
+    k = np.array(g["k"], float).reshape(L, 1, 1)
+    v = np.array(g["v"], float).reshape(L, 1, 1)
+    out, sel, gap = O.moba_reference(q, k, v, g["block_size"], g["topk"])
+    env = {"e": math.e, "exp": math.exp}
+    want = np.array([eval(x, {}, env) for x in g["out_closed_form"]])
+    np.testing.assert_allclose(out[:, 0, 0], want, rtol=0, atol=1e-14)
+    assert sel[0].tolist() == g["sel"]
+    assert [float(x) for x in g["gap"]] == gap[0].tolist()
+
+
+# ------------------------------------------------------------- pooling -----
+def test_block_mean_ramp_and_partial_block():
+    """Mean of a ramp K[t] = t is the block midpoint; a partial last block is
+    averaged over the keys it holds (reading R11)."""
+    B, L = 8, 29
+    k = np.broadcast_to(np.arange(L, dtype=float)[:, None, None], (L, 2, 3)).copy()
+    k[:, 1] *= -2.0
+    kb = O.block_mean(k, B)
+    assert kb.shape == (2, 4, 3)
+    for j in range(4):
+        lo, hi = j * B, min(L, (j + 1) * B)
+        mid = (lo + hi - 1) / 2.0
+        np.testing.assert_allclose(kb[0, j], mid, atol=1e-13)
+        np.testing.assert_allclose(kb[1, j], -2 * mid, atol=1e-13)
+
+
+def test_block_mean_block_size_one_is_identity():
+    q, k, v = _case(3, 17, Hkv=2, D=5, B=1)
+    np.testing.assert_array_equal(O.block_mean(k, 1), k.transpose(1, 0, 2))
+
+
+# ------------------------------------------------------- P1 invariants -----
+@pytest.mark.parametrize("seed,L,B,topk", [(0, 64, 8, 3), (1, 100, 16, 5), (2, 33, 4, 1),
+                                           (3, 48, 8, 20), (4, 128, 32, 2)])
+def test_p1_selection_invariants(seed, L, B, topk):
+    """Own block present, it is the largest index, nothing from the future,
+    size min(k, b+1), ascending and unique, -1 padding last (causality design
+    of the AiBoss page; readings R2, R3)."""
+    q, k, v = _case(seed, L, H=2, Hkv=1, D=6, B=B)
+    sel, gap = O.select_all(q, O.block_mean(k, B), B, topk)
+    for h in range(2):
+        for i in range(L):
+            b = i // B
+            row = sel[h, i].tolist()
+            valid = [x for x in row if x >= 0]
+            assert row == valid + [-1] * (topk - len(valid))
+            assert b in valid and max(valid) == b
+            assert len(valid) == min(topk, b + 1)
+            assert valid == sorted(set(valid))
+
+
+# ------------------------------------------------------ P2 brute force -----
+@pytest.mark.parametrize("B", [1, 2, 4, 8])
+def test_p2_brute_force_selection(B):
+    """Exhaustive subset enumeration on tiny inputs, with integer-valued data
+    so that exact ties are common (reading R4: lowest index wins)."""
+    rng = np.random.default_rng(10 + B)
+    L, D = {1: 14, 2: 28, 4: 48, 8: 64}[B], 3
+    q = rng.integers(-1, 2, size=(L, 1, D)).astype(float)
+    k = rng.integers(-2, 3, size=(L, 1, D)).astype(float)
+    kb = O.block_mean(k, B)
+    nb = kb.shape[1]
+    for topk in range(1, min(nb, 6) + 2):
+        sel, _ = O.select_all(q, kb, B, topk)
+        for i in range(L):
+            b = i // B
+            s = O.gate_scores(q[i, 0], kb[0], b)
+            want = O.brute_force_select(s, b, topk)
+            assert tuple(sel[0, i].tolist()) == want, (topk, i)
+            assert O.select_blocks(s, b, topk)[0] == want
+
+
+# ---------------------------------------------- P3 sparse -> full switch ----
+@pytest.mark.parametrize("H,Hkv", [(1, 1), (4, 2), (4, 1)])
+def test_p3_topk_all_equals_full_causal_attention(H, Hkv):
+    """topk >= number of blocks is full causal attention (seamless full/sparse
+    switching: MoBA card 'How It Works', AiBoss '主な機能'); checked against
+    torch's float64 SDPA with is_causal (its default scale is 1/sqrt(D))."""
+    L, B, D = 40, 8, 16
+    q, k, v = _case(21, L, H, Hkv, D, B)
+    nb = L // B
+    for topk in (nb, nb + 3):
+        out, sel, _ = O.moba_reference(q, k, v, B, topk)
+        np.testing.assert_allclose(out, _sdpa(q, k, v, causal=True), atol=1e-12, rtol=0)
+    np.testing.assert_allclose(O.full_reference(q, k, v), _sdpa(q, k, v, causal=True),
+                               atol=1e-12, rtol=0)
+
+
+# ------------------------------------------------ P4 mask form vs gather ----
+@pytest.mark.parametrize("seed,L,B,topk,H,Hkv", [(31, 64, 8, 3, 1, 1), (32, 72, 8, 4, 4, 2),
+                                                 (33, 50, 16, 2, 2, 2)])
+def test_p4_gather_equals_mask_form_equals_sdpa(seed, L, B, topk, H, Hkv):
+    """The naive mask version and the gathered version compute the same thing
+    (Dev Tutorial step 1; MoBA card 'Limitations & Caveats'), and both equal
+    torch SDPA with the boolean mask built from the selection."""
+    q, k, v = _case(seed, L, H, Hkv, 16, B)
+    out, sel, _ = O.moba_reference(q, k, v, B, topk)
+    naive = O.naive_mask_reference(q, k, v, B, topk)
+    np.testing.assert_allclose(out, naive, atol=1e-12, rtol=0)
+    t = np.arange(L)
+    mask = np.zeros((H, L, L), dtype=bool)
+    for h in range(H):
+        for i in range(L):
+            chosen = [j for j in sel[h, i] if j >= 0]
+            mask[h, i] = np.isin(t // B, chosen) & (t <= i)
+    np.testing.assert_allclose(out, _sdpa(q, k, v, mask=mask), atol=1e-12, rtol=0)
+
+
+# -------------------------------------------------- P5 local attention -----
+def test_p5_topk_one_is_block_diagonal_causal():
+    """k = 1 keeps only the own block with its causal mask: block-diagonal
+    causal attention; a query at a block start sees only itself."""
+    L, B = 48, 8
+    q, k, v = _case(41, L, 2, 1, 8, B)
+    out, sel, _ = O.moba_reference(q, k, v, B, 1)
+    t = np.arange(L)
+    mask = (t[None, :] <= t[:, None]) & (t[None, :] // B == t[:, None] // B)
+    mask = np.broadcast_to(mask, (2, L, L)).copy()
+    np.testing.assert_allclose(out, _sdpa(q, k, v, mask=mask), atol=1e-12, rtol=0)
+    for i in range(0, L, B):
+        np.testing.assert_allclose(out[i, :, :], np.repeat(v[i, 0][None], 2, 0), atol=1e-14)
+    out3, _, _ = O.moba_reference(q, k, v, B, 3)
+    np.testing.assert_allclose(out3[0], np.repeat(v[0, 0][None], 2, 0), atol=1e-14)
+
+
+# --------------------------------------------- P6 token-level top-k --------
+def test_p6_block_size_one_is_token_topk():
+    """B = 1 makes every key its own block: Sel = {i} plus the k-1 earlier
+    tokens with the largest q.k_t (ties to the lower index)."""
+    L, topk = 30, 4
+    q, k, v = _case(51, L, 1, 1, 5, 1)
+    sel, _ = O.select_all(q, O.block_mean(k, 1), 1, topk)
+    for i in range(L):
+        s = k[:i, 0] @ q[i, 0]
+        order = np.lexsort((np.arange(i), -s))[: topk - 1]
+        want = sorted(order.tolist() + [i])
+        want += [-1] * (topk - len(want))
+        assert sel[0, i].tolist() == want
+
+
+# --------------------------------------------- P7 zero query closed form ---
+def test_p7_zero_query_closed_form():
+    """q = 0 makes every gate score 0: the lowest-index past blocks win, and
+    every attended key gets the same weight, so out is the plain mean of V
+    over the attended keys."""
+    L, B, topk = 64, 8, 3
+    q, k, v = _case(61, L, 1, 1, 8, B)
+    q[:] = 0.0
+    out, sel, _ = O.moba_reference(q, k, v, B, topk)
+    for i in range(L):
+        b = i // B
+        past = list(range(min(topk - 1, b)))
+        assert [x for x in sel[0, i] if x >= 0] == past + [b]
+        keys = [t for j in past for t in range(j * B, (j + 1) * B)] + list(range(b * B, i + 1))
+        np.testing.assert_allclose(out[i, 0], v[keys, 0].mean(axis=0), atol=1e-13)
+
+
+# ---------------------------------------------- P8 duplicate-block tie -----
+def test_p8_duplicate_block_exact_tie_goes_to_lower_index():
+    L, B, D = 64, 8, 8
+    rng = np.random.default_rng(71)
+    q = rng.standard_normal((L, 1, D))
+    k = rng.standard_normal((L, 1, D)) * 0.1
+    u = q[-1, 0] / np.linalg.norm(q[-1, 0])
+    k[2 * B:3 * B, 0] = u * 5.0 + k[2 * B:3 * B, 0] * 0.01
+    k[5 * B:6 * B] = k[2 * B:3 * B]                       # block 5 == block 2
+    sel, gap = O.select_all(q, O.block_mean(k, B), B, 2)
+    assert sel[0, L - 1].tolist() == [2, 7]
+    assert gap[0, L - 1] == 0.0
+
+
+# ------------------------------------------------- P9 softmax weights -----
+def test_p9_one_hot_values_expose_the_weights():
+    """With V[t] = e_t the output row is the attention weight vector: it sums
+    to one, is zero off the key set, and equals exp-normalised logits."""
+    L, B, topk = 24, 4, 3
+    q, k, _ = _case(81, L, 1, 1, 6, B)
+    v = np.eye(L)[:, None, :]
+    out, sel, _ = O.moba_reference(q, k, v, B, topk)
+    for i in range(L):
+        keys = O.key_set(sel[0, i], i, B, L)
+        w = out[i, 0]
+        np.testing.assert_allclose(w.sum(), 1.0, atol=1e-14)
+        off = np.setdiff1d(np.arange(L), keys)
+        assert np.all(w[off] == 0.0)
+        z = k[keys, 0] @ q[i, 0] / math.sqrt(6)
+        ref = torch.softmax(torch.from_numpy(z), 0).numpy()
+        np.testing.assert_allclose(w[keys], ref, atol=1e-14)
+    vc = np.ones((L, 1, 5)) * np.array([1.5, -2.0, 0.0, 3.25, 7.0])
+    outc, _, _ = O.moba_reference(q, k, vc, B, topk)
+    np.testing.assert_allclose(outc[:, 0], np.broadcast_to(vc[0, 0], (L, 5)), atol=1e-13)
+
+
+# ---------------------------------------- P10 scaling / head permutation ---
+def test_p10_power_of_two_query_scaling_and_head_permutation():
+    L, B, topk = 64, 8, 4
+    q, k, v = _case(91, L, 4, 2, 8, B)
+    kb = O.block_mean(k, B)
+    sel, _ = O.select_all(q, kb, B, topk)
+    for m in (-3, 5):
+        sel2, _ = O.select_all(q * 2.0 ** m, kb, B, topk)
+        np.testing.assert_array_equal(sel, sel2)
+    out, _, _ = O.moba_reference(q, k, v, B, topk)
+    perm = [1, 0, 3, 2]                                   # swap heads inside each group
+    outp, selp, _ = O.moba_reference(q[:, perm], k, v, B, topk)
+    np.testing.assert_allclose(outp, out[:, perm], atol=1e-14)
+    np.testing.assert_array_equal(selp, sel[perm])
+
+
+def test_gqa_head_map_uses_h_div_group():
+    """Query head h reads KV head h // (H/Hkv) (reading R8): changing KV head 1
+    leaves heads 0 and 1 untouched and changes heads 2 and 3."""
+    L, B, topk = 48, 8, 3
+    q, k, v = _case(101, L, 4, 2, 8, B)
+    out, _, _ = O.moba_reference(q, k, v, B, topk)
+    k2, v2 = k.copy(), v.copy()
+    k2[:, 1] += 1.0
+    v2[:, 1] *= -1.0
+    out2, _, _ = O.moba_reference(q, k2, v2, B, topk)
+    np.testing.assert_array_equal(out2[:, :2], out[:, :2])
+    assert np.abs(out2[:, 2:] - out[:, 2:]).max() > 1e-3
+
+
+# ------------------------------------------------ decode alignment pin -----
+def test_decode_rows_equal_prefill_tail():
+    """Queries given on their own against the full cache (q_len < kv_len) sit
+    at the end of the cache (reading R10) and reproduce the prefill's last
+    rows, selection included."""
+    L, B, topk, lq = 64, 8, 3, 5
+    q, k, v = _case(111, L, 4, 2, 8, B)
+    out, sel, gap = O.moba_reference(q, k, v, B, topk)
+    outd, seld, gapd = O.moba_reference(q[-lq:], k, v, B, topk)
+    np.testing.assert_allclose(outd, out[-lq:], atol=1e-14)
+    np.testing.assert_array_equal(seld, sel[:, -lq:])
+    outb, selb, _ = O.moba_decode_reference(np.stack([q[-lq:], q[-lq:] * 0.5]),
+                                            np.stack([k, k]), np.stack([v, v]), B, topk)
+    np.testing.assert_allclose(outb[0], out[-lq:], atol=1e-14)
+
+
+# --------------------------------------------------------- routing view ----
+def test_routing_table_partitions_every_routed_pair():
+    """Every (query, selected past block) pair lands exactly once in the bucket
+    of (sequence, KV head, block), in ascending slot order; recounted by a
+    direct loop."""
+    L, B, topk, H, Hkv = 40, 8, 3, 4, 2
+    q, k, v = _case(121, L, H, Hkv, 8, B)
+    sel, _ = O.select_all(q, O.block_mean(k, B), B, topk)
+    sel2 = np.stack([sel, sel[::-1]])                       # batch of 2
+    nb = L // B
+    counts, offsets, entries = O.routing_table(sel2, Hkv, nb, B, 0)
+    buckets = {}
+    kp = topk - 1
+    for s in range(2):
+        for h in range(H):
+            for r in range(L):
+                for slot in range(min(kp, r // B)):
+                    j = int(sel2[s, h, r, slot])
+                    assert 0 <= j < r // B
+                    key = (s * Hkv + h // (H // Hkv)) * nb + j
+                    buckets.setdefault(key, []).append(((s * H + h) * L + r) * kp + slot)
+    for key in range(2 * Hkv * nb):
+        got = entries[offsets[key]:offsets[key + 1]].tolist()
+        assert got == buckets.get(key, []), key
+        assert counts[key] == len(got)
+    assert offsets[-1] == entries.size == sum(len(x) for x in buckets.values())
