@@ -133,14 +133,15 @@ def brute_force_select(scores_past: np.ndarray, own_block: int, topk: int):
     return tuple(sel + [-1] * (topk - len(sel)))
 
 
-def select_all(q, kbar, block_size, topk, q_offset=0, rows=None):
+def select_all(q, kbar, block_size, topk, q_offset=0, rows=None, positions=None):
     """Selection for many queries at once (same rule as ``select_blocks``).
 
     ``q`` is ``[Lq, H, D]``, ``kbar`` ``[Hkv, nb, D]``.  Uses a matmul for the
     scores and a stable argsort of the negated scores for the ranking (stable
     keeps the lower index first among equal scores, R4).  ``rows`` restricts
     the work to a subset of query rows; ``q_offset`` is the position of query
-    row 0 (``kv_len - q_len``, R10).  Returns ``sel [H, R, topk]`` (int64)
+    row 0 (``kv_len - q_len``, R10).  ``positions`` instead gives the position
+    of every row of ``q`` explicitly (for a sample of rows).  Returns ``sel [H, R, topk]`` (int64)
     and ``gap [H, R]``.
     """
     q = np.asarray(q, dtype=np.float64)
@@ -148,7 +149,7 @@ def select_all(q, kbar, block_size, topk, q_offset=0, rows=None):
     hkv, nb, _ = kbar.shape
     group = h_n // hkv
     rows = np.arange(lq) if rows is None else np.asarray(rows)
-    pos = q_offset + rows
+    pos = q_offset + rows if positions is None else np.asarray(positions)[rows]
     own = pos // block_size
     n_keep = np.minimum(topk - 1, own)
     sel = np.full((h_n, rows.size, topk), -1, dtype=np.int64)

@@ -315,3 +315,16 @@ def test_routing_table_partitions_every_routed_pair():
         assert got == buckets.get(key, []), key
         assert counts[key] == len(got)
     assert offsets[-1] == entries.size == sum(len(x) for x in buckets.values())
+
+
+def test_select_all_explicit_positions_match_offsets():
+    """Sampled rows given with explicit positions select exactly what the
+    same rows select in the full query array."""
+    L, B, topk = 96, 8, 4
+    q, k, v = _case(131, L, 2, 1, 8, B)
+    kb = O.block_mean(k, B)
+    sel, gap = O.select_all(q, kb, B, topk)
+    rows = np.array([0, 7, 8, 50, 95])
+    sel2, gap2 = O.select_all(q[rows], kb, B, topk, positions=rows)
+    np.testing.assert_array_equal(sel2, sel[:, rows])
+    np.testing.assert_array_equal(gap2, gap[:, rows])
