@@ -1,0 +1,276 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoBA forward on one MI355X (gfx950).
+
+One step = one moba_forward_ex call over one batch of resident synthetic
+inputs: block means, gate + top-k, routing, routed attention and the own-block
+attention with the merge.  The workspace is allocated once, outside the timed
+region.  Prints one JSON line.
+
+  value        effective TFLOP/s of the MoBA forward on the 32K single-head
+               shape (block 2048, top-k 3): only selected-block FLOPs count,
+               F = 4 D sum_{h,i} (B |past blocks kept| + keys of the own block
+               up to i).
+  speedup      time of the library's own full causal attention at the same
+               shape / time of the MoBA forward.
+  also         the same figures at the 1M-token prefill (32/8 heads, block
+               4096, top-k 12).
+  roofline     the dominant kernel (routed attention): its algorithmic FLOPs
+               per launch / its average launch time from HIP events recorded
+               on the launch stream, against the 2.5 PFLOP/s bf16 dense MFMA
+               peak.
+  cpu_baseline the float64 CPU oracle on a bounded sample of the same
+               workload, in the same unit.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoBA fwd effective TFLOP/s & speedup vs full attn at 32K and 1M tokens (1 GPU)"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------- work accounting
+def prefill_flops(w):
+    """(effective, routed, own, full) FLOPs of a prefill workload.
+
+    Per query i of a head: the routed part attends B keys for each of its
+    min(k-1, b(i)) kept past blocks; the own part attends i - b(i) B + 1 keys;
+    2 FLOPs per multiply-add in Q K^T and in P V: 4 D per (query, key)."""
+    N, B, k, D, H, S = w.q_len, w.block_size, w.topk, w.head_dim, w.n_heads, w.batch
+    q_off = w.kv_len - w.q_len
+    routed_keys = 0
+    own_keys = 0
+    full_keys = 0
+    # closed form per block of positions
+    for b in range((q_off + N - 1) // B + 1):
+        lo = max(b * B, q_off)
+        hi = min((b + 1) * B, q_off + N)
+        if hi <= lo:
+            continue
+        cnt = hi - lo
+        routed_keys += cnt * B * min(k - 1, b)
+        # sum over positions p in [lo, hi) of (p - bB + 1)
+        own_keys += (lo - b * B + 1 + hi - b * B) * cnt // 2
+        full_keys += (lo + 1 + hi) * cnt // 2
+    f = 4 * D * H * S
+    return f * (routed_keys + own_keys), f * routed_keys, f * own_keys, f * full_keys
+
+
+# ---------------------------------------------------------------- timing
+def time_region(fn, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(st)
+    for _ in range(steps):
+        fn()
+    e1.record(st)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    return e0.elapsed_time(e1) / steps, wall * 1e3
+
+
+def kernel_breakdown(moba, fn, steps):
+    """Per-kernel average launch time (ms) from the library's HIP events."""
+    import torch
+    torch.cuda.synchronize()
+    moba.moba_profile_reset()
+    moba.moba_profile_enable(True)
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    moba.moba_profile_enable(False)
+    out = {}
+    for name in moba.KERNEL_NAMES:
+        ms, n = moba.moba_profile_read(name)
+        if n:
+            out[name] = {"avg_ms": ms / n, "launches": n}
+    moba.moba_profile_reset()
+    return out
+
+
+def run_prefill(moba, w, steps, warmup, full_steps, full_warmup, with_full=True):
+    import torch
+    import moba_inputs
+    log(f"[bench] {w.name}: generating inputs")
+    q, k, v = moba_inputs.make_inputs(w, device="cuda:0")
+    out = torch.empty_like(q)
+    ws_bytes = moba.moba_workspace_size(q, k, v, w.block_size, w.topk)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    fwd = lambda: moba.moba_forward_ex(q, k, v, w.block_size, w.topk, out=out, workspace=ws)
+    log(f"[bench] {w.name}: workspace {ws_bytes / 2**30:.2f} GiB; timing MoBA forward")
+    ms, wall_ms = time_region(fwd, steps, warmup)
+    kern = kernel_breakdown(moba, fwd, steps)
+    eff, routed, own, full = prefill_flops(w)
+    res = {
+        "workload": w.name, "ms": ms, "wall_ms": wall_ms,
+        "effective_tflops": eff / (ms * 1e-3) / 1e12,
+        "frac_of_bf16_peak": eff / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "effective_flop": eff, "routed_flop": routed, "own_flop": own,
+        "kernels_ms": {k_: round(v_["avg_ms"], 4) for k_, v_ in kern.items()},
+    }
+    if "attn_routed" in kern:
+        t = kern["attn_routed"]["avg_ms"] * 1e-3
+        res["attn_routed_tflops"] = routed / t / 1e12
+    if "attn_own_merge" in kern:
+        t = kern["attn_own_merge"]["avg_ms"] * 1e-3
+        res["attn_own_merge_tflops"] = own / t / 1e12
+    if with_full:
+        fout = torch.empty_like(q)
+        fws = torch.empty(max(moba.moba_full_workspace_size(q, k, v), 1), dtype=torch.uint8,
+                          device=q.device)
+        ffn = lambda: moba.moba_full_attention_ex(q, k, v, out=fout, workspace=fws)
+        log(f"[bench] {w.name}: timing full attention")
+        fms, _ = time_region(ffn, full_steps, full_warmup)
+        fk = kernel_breakdown(moba, ffn, 1)
+        res["full_ms"] = fms
+        res["full_tflops"] = full / (fms * 1e-3) / 1e12
+        res["full_frac_of_bf16_peak"] = res["full_tflops"] / PEAK_BF16_TFLOPS
+        res["speedup_vs_full"] = fms / ms
+        res["full_kernels_ms"] = {k_: round(v_["avg_ms"], 4) for k_, v_ in fk.items()}
+        del fout, fws
+    res["_roofline_src"] = kern
+    del q, k, v, out, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def roofline(res):
+    kern = res["_roofline_src"]
+    if "attn_routed" not in kern:
+        return None
+    t = kern["attn_routed"]["avg_ms"] * 1e-3
+    achieved = res["routed_flop"] / t / 1e12
+    return {"bound": "mfma", "kernel": "attn_routed", "achieved": achieved,
+            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+            "traffic": None, "avg_launch_ms": kern["attn_routed"]["avg_ms"]}
+
+
+# ------------------------------------------------------------ CPU baseline
+def cpu_baseline(w, budget_s):
+    """The float64 oracle on a bounded sample of the workload: the gate and
+    top-k for every query (one matmul + stable argsort per head) and the
+    attention of uniformly drawn queries until ~budget_s of CPU time."""
+    import numpy as np
+    import torch
+    import moba_inputs
+    from oracle import moba_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    q, k, v = moba_inputs.make_inputs(w, device="cuda:0")
+    qh, kh, vh = (t.float().cpu().numpy().astype(np.float64) for t in (q, k, v))
+    del q, k, v
+    torch.cuda.empty_cache()
+    N, D, B = qh.shape[0], qh.shape[2], w.block_size
+    rng = np.random.default_rng(0)
+    t0 = time.perf_counter()
+    kbar = O.block_mean(kh, B)
+    sel, _ = O.select_all(qh, kbar, B, w.topk)
+    t_sel = time.perf_counter() - t0
+    flop = 0
+    nq = 0
+    t1 = time.perf_counter()
+    scale = 1.0 / math.sqrt(D)
+    while time.perf_counter() - t1 < budget_s:
+        r = int(rng.integers(0, N))
+        h = int(rng.integers(0, qh.shape[1]))
+        g = h // (qh.shape[1] // kh.shape[1])
+        keys = O.key_set(sel[h, r], r, B, N)
+        O.attend(qh[r, h], kh[:, g, :], vh[:, g, :], keys, scale)
+        flop += 4 * D * keys.size
+        nq += 1
+    t_att = time.perf_counter() - t1
+    # selection time attributed to the sampled queries pro rata
+    t_total = t_att + t_sel * nq / (N * qh.shape[1])
+    return {"value": flop / t_total / 1e12, "unit": "TFLOP/s", "cores": blas_threads,
+            "kind": "oracle",
+            "sample": (f"{nq} uniformly drawn (head, query) rows of {w.name} in {t_att:.1f} s "
+                       f"(float64 NumPy attention over each row's selected keys) plus their "
+                       f"share of the full-workload gate/top-k pass ({t_sel:.1f} s for all "
+                       f"{N * qh.shape[1]} rows)"),
+            "host_cpus": os.cpu_count(),
+            "affinity_cpus": len(os.sched_getaffinity(0))}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--skip-1m", action="store_true", help="skip the 1M-token prefill")
+    ap.add_argument("--skip-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(this build runs on a single MI355X)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_sparse_attention_gate_amd as moba
+    import moba_inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    w = moba_inputs.WORKLOADS["micro_32k"]
+    main_res = run_prefill(moba, w, args.steps, args.warmup, full_steps=args.steps,
+                           full_warmup=args.warmup)
+    also = {}
+    if not args.skip_1m:
+        w1 = moba_inputs.WORKLOADS["prefill_1m"]
+        r1 = run_prefill(moba, w1, min(args.steps, 3), min(args.warmup, 1), full_steps=1,
+                         full_warmup=0)
+        r1["roofline"] = roofline(r1)
+        r1.pop("_roofline_src")
+        also["prefill_1m"] = r1
+    rl = roofline(main_res)
+    main_res.pop("_roofline_src")
+    cpu = None if args.skip_cpu else cpu_baseline(w, args.cpu_budget)
+    line = {
+        "metric": METRIC,
+        "value": main_res["effective_tflops"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_res["ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "seq_len": w.q_len,
+                   "n_heads": w.n_heads, "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
+                   "block_size": w.block_size, "topk": w.topk, "parallelism": "single GPU"},
+        "speedup_vs_full": main_res.get("speedup_vs_full"),
+        "detail": main_res,
+        "roofline": rl,
+        "cpu_baseline": cpu,
+        "also": also,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

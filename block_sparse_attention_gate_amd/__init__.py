@@ -1,0 +1,321 @@
+"""Python binding of libmoba.so, the MI355X (gfx950) MoBA forward library.
+
+Argument marshalling only: every step of the forward runs in the HIP kernels
+behind the C ABI declared in ``include/moba.h``.  PyTorch supplies device
+memory (tensors, the workspace) and the current HIP stream.  There is no
+fallback: if ``libmoba.so`` has not been built, importing this package fails.
+
+Layouts (contiguous, head_dim innermost):
+  prefill  q, out [L, H, D]        k, v [L, Hkv, D]
+  general  q, out [S, Lq, H, D]    k, v [S, L, Hkv, D]
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoba.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()')")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+MOBA_DTYPE_F32 = 0
+MOBA_DTYPE_BF16 = 1
+MOBA_OK = 0
+MOBA_ERR_INVALID_ARGUMENT = 1
+MOBA_ERR_UNSUPPORTED = 2
+MOBA_ERR_OUT_OF_MEMORY = 3
+MOBA_ERR_HIP = 4
+
+
+class MobaArgs(ctypes.Structure):
+    """Mirror of ``moba_args`` in include/moba.h."""
+
+    _fields_ = [
+        ("struct_size", ctypes.c_size_t),
+        ("q", ctypes.c_void_p),
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("out", ctypes.c_void_p),
+        ("k_block_mean", ctypes.c_void_p),
+        ("sel_out", ctypes.c_void_p),
+        ("batch", ctypes.c_int32),
+        ("n_heads", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("topk", ctypes.c_int32),
+        ("q_len", ctypes.c_int64),
+        ("kv_len", ctypes.c_int64),
+        ("dtype", ctypes.c_int),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+        ("stream", ctypes.c_void_p),
+    ]
+
+
+_P = ctypes.c_void_p
+_I32, _I64 = ctypes.c_int32, ctypes.c_int64
+_ST = ctypes.c_int
+
+_SIGNATURES = {
+    "moba_forward": (_ST, [_P, _P, _P, _I64, _I32, _I32, _I32, _I32, _I32, _P, ctypes.c_int, _P]),
+    "moba_full_attention": (_ST, [_P, _P, _P, _I64, _I32, _I32, _I32, _P, ctypes.c_int, _P]),
+    "moba_forward_ex": (_ST, [ctypes.POINTER(MobaArgs)]),
+    "moba_full_attention_ex": (_ST, [ctypes.POINTER(MobaArgs)]),
+    "moba_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(MobaArgs)]),
+    "moba_full_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(MobaArgs)]),
+    "moba_block_mean": (_ST, [_P, _I32, _I64, _I32, _I32, _I32, _P, ctypes.c_int, _P]),
+    "moba_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "moba_last_error": (ctypes.c_char_p, []),
+    "moba_abi_version": (_I32, []),
+    "moba_profile_enable": (_ST, [_I32]),
+    "moba_profile_reset": (_ST, []),
+    "moba_profile_read": (_ST, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
+                                ctypes.POINTER(ctypes.c_int64)]),
+}
+for _name, (_res, _args) in _SIGNATURES.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+EXPORTED = tuple(_SIGNATURES)
+
+
+class MobaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+def _check(status: int, what: str):
+    if status == MOBA_OK:
+        return
+    msg = f"{what}: {_lib.moba_status_string(status).decode()}: {_lib.moba_last_error().decode()}"
+    if status in (MOBA_ERR_INVALID_ARGUMENT, MOBA_ERR_UNSUPPORTED):
+        err = ValueError(msg)
+        err.status = status
+        raise err
+    if status == MOBA_ERR_OUT_OF_MEMORY:
+        raise MemoryError(msg)
+    raise MobaError(status, msg)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return MOBA_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return MOBA_DTYPE_F32
+    raise ValueError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _dev_tensor(t, name, dtype=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+def _stream_ptr(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _shape4(q, k, v):
+    """Return (S, Lq, H, D, L, Hkv) for prefill (3-D) or general (4-D) tensors."""
+    if q.dim() == 3:
+        if k.dim() != 3 or v.dim() != 3:
+            raise ValueError("q, k, v must all be 3-D (prefill) or 4-D (batched)")
+        L, H, D = q.shape
+        Lk, Hkv, Dk = k.shape
+        if Lk != L:
+            raise ValueError("3-D form needs q_len == kv_len")
+        S, Lq = 1, L
+    elif q.dim() == 4:
+        S, Lq, H, D = q.shape
+        Sk, Lk, Hkv, Dk = k.shape
+        if Sk != S:
+            raise ValueError("batch of q and k differ")
+    else:
+        raise ValueError("q must be 3-D or 4-D")
+    if tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k and v shapes differ")
+    if Dk != D:
+        raise ValueError("head_dim of q and k differ")
+    return S, Lq, H, D, Lk, Hkv
+
+
+def _args(q, k, v, out, block_size=64, topk=1, k_block_mean=None, sel_out=None) -> MobaArgs:
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        _dev_tensor(t, name, q.dtype)
+    S, Lq, H, D, L, Hkv = _shape4(q, k, v)
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError("out must have the shape of q")
+    a = MobaArgs()
+    a.struct_size = ctypes.sizeof(MobaArgs)
+    a.q, a.k, a.v, a.out = q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr()
+    if k_block_mean is not None:
+        _dev_tensor(k_block_mean, "k_block_mean", torch.float32)
+        a.k_block_mean = k_block_mean.data_ptr()
+    if sel_out is not None:
+        _dev_tensor(sel_out, "sel_out", torch.int32)
+        if tuple(sel_out.shape) != (S, H, Lq, topk):
+            raise ValueError(f"sel_out must be int32 [{S}, {H}, {Lq}, {topk}]")
+        a.sel_out = sel_out.data_ptr()
+    a.batch, a.n_heads, a.n_kv_heads, a.head_dim = S, H, Hkv, D
+    a.block_size, a.topk = int(block_size), int(topk)
+    a.q_len, a.kv_len = Lq, L
+    a.dtype = _dtype_code(q)
+    a.stream = _stream_ptr(q.device)
+    return a
+
+
+def moba_forward(q, k, v, block_size, topk, out=None):
+    """MoBA prefill forward (C ``moba_forward``; the library allocates its
+    workspace stream-ordered).  q [L, H, D], k, v [L, Hkv, D]."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _dev_tensor(t, name, q.dtype)
+    if q.dim() != 3:
+        raise ValueError("moba_forward takes 3-D prefill tensors; use moba_forward_ex")
+    S, Lq, H, D, L, Hkv = _shape4(q, k, v)
+    out = torch.empty_like(q) if out is None else _dev_tensor(out, "out", q.dtype)
+    st = _lib.moba_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), L, H, Hkv, D,
+                           int(block_size), int(topk), out.data_ptr(), _dtype_code(q),
+                           _stream_ptr(q.device))
+    _check(st, "moba_forward")
+    return out
+
+
+def moba_full_attention(q, k, v, out=None):
+    """Full causal attention (C ``moba_full_attention``), prefill layout."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _dev_tensor(t, name, q.dtype)
+    if q.dim() != 3:
+        raise ValueError("moba_full_attention takes 3-D prefill tensors; use the _ex form")
+    S, Lq, H, D, L, Hkv = _shape4(q, k, v)
+    out = torch.empty_like(q) if out is None else _dev_tensor(out, "out", q.dtype)
+    st = _lib.moba_full_attention(q.data_ptr(), k.data_ptr(), v.data_ptr(), L, H, Hkv, D,
+                                  out.data_ptr(), _dtype_code(q), _stream_ptr(q.device))
+    _check(st, "moba_full_attention")
+    return out
+
+
+def moba_workspace_size(q, k, v, block_size, topk, k_block_mean=None, sel_out=None) -> int:
+    """Workspace bytes moba_forward_ex needs (C ``moba_workspace_size``)."""
+    a = _args(q, k, v, q, block_size, topk, k_block_mean, sel_out)
+    n = int(_lib.moba_workspace_size(ctypes.byref(a)))
+    if n == 0 and _lib.moba_last_error():
+        raise ValueError(f"moba_workspace_size: {_lib.moba_last_error().decode()}")
+    return n
+
+
+def moba_full_workspace_size(q, k, v) -> int:
+    """Workspace bytes moba_full_attention_ex needs (C ``moba_full_workspace_size``)."""
+    a = _args(q, k, v, q)
+    n = int(_lib.moba_full_workspace_size(ctypes.byref(a)))
+    if n == 0 and _lib.moba_last_error():
+        raise ValueError(f"moba_full_workspace_size: {_lib.moba_last_error().decode()}")
+    return n
+
+
+def _workspace_tensor(nbytes: int, device, workspace):
+    if nbytes == 0:
+        return None
+    if workspace is not None:
+        # the library checks the size and rejects a short workspace
+        return _dev_tensor(workspace, "workspace")
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def moba_forward_ex(q, k, v, block_size, topk, *, out=None, k_block_mean=None, sel_out=None,
+                    return_selection=False, workspace=None):
+    """General MoBA forward (C ``moba_forward_ex``): batches, q_len <= kv_len,
+    optional precomputed block means, optional selection output.  The
+    workspace is a torch allocation (or the given uint8 tensor)."""
+    out = torch.empty_like(q) if out is None else out
+    if return_selection and sel_out is None:
+        S, Lq, H, D, L, Hkv = _shape4(q, k, v)
+        sel_out = torch.empty((S, H, Lq, int(topk)), dtype=torch.int32, device=q.device)
+    a = _args(q, k, v, out, block_size, topk, k_block_mean, sel_out)
+    need = int(_lib.moba_workspace_size(ctypes.byref(a)))
+    if need == 0 and _lib.moba_last_error():
+        _check(_lib.moba_forward_ex(ctypes.byref(a)), "moba_forward_ex")  # raises the error
+    ws = _workspace_tensor(need, q.device, workspace)
+    if ws is not None:
+        a.workspace = ws.data_ptr()
+        a.workspace_bytes = ws.numel() * ws.element_size()
+    _check(_lib.moba_forward_ex(ctypes.byref(a)), "moba_forward_ex")
+    if return_selection:
+        return out, (sel_out[0] if q.dim() == 3 else sel_out)
+    return out
+
+
+def moba_full_attention_ex(q, k, v, *, out=None, workspace=None):
+    out = torch.empty_like(q) if out is None else out
+    a = _args(q, k, v, out)
+    need = int(_lib.moba_full_workspace_size(ctypes.byref(a)))
+    if need == 0 and _lib.moba_last_error():
+        _check(_lib.moba_full_attention_ex(ctypes.byref(a)), "moba_full_attention_ex")
+    ws = _workspace_tensor(need, q.device, workspace)
+    if ws is not None:
+        a.workspace = ws.data_ptr()
+        a.workspace_bytes = ws.numel() * ws.element_size()
+    _check(_lib.moba_full_attention_ex(ctypes.byref(a)), "moba_full_attention_ex")
+    return out
+
+
+def moba_block_mean(k, block_size, out=None):
+    """Block-mean keys: k [S, L, Hkv, D] (or [L, Hkv, D]) -> fp32 [S, Hkv, nb, D]."""
+    _dev_tensor(k, "k")
+    k4 = k if k.dim() == 4 else k.unsqueeze(0)
+    S, L, Hkv, D = k4.shape
+    nb = L // int(block_size) if block_size > 0 else 0
+    out = torch.empty((S, Hkv, max(nb, 1), D), dtype=torch.float32, device=k.device) \
+        if out is None else _dev_tensor(out, "out", torch.float32)
+    st = _lib.moba_block_mean(k4.data_ptr(), S, L, Hkv, D, int(block_size), out.data_ptr(),
+                              _dtype_code(k4), _stream_ptr(k.device))
+    _check(st, "moba_block_mean")
+    return out
+
+
+def moba_status_string(status: int) -> str:
+    return _lib.moba_status_string(int(status)).decode()
+
+
+def moba_last_error() -> str:
+    return _lib.moba_last_error().decode()
+
+
+def moba_abi_version() -> int:
+    return int(_lib.moba_abi_version())
+
+
+def moba_profile_enable(on: bool = True):
+    _check(_lib.moba_profile_enable(1 if on else 0), "moba_profile_enable")
+
+
+def moba_profile_reset():
+    _check(_lib.moba_profile_reset(), "moba_profile_reset")
+
+
+def moba_profile_read(name: str):
+    """Return (total_ms, launches) recorded for kernel `name` since the last reset."""
+    ms = ctypes.c_double(0.0)
+    n = ctypes.c_int64(0)
+    _check(_lib.moba_profile_read(name.encode(), ctypes.byref(ms), ctypes.byref(n)),
+           "moba_profile_read")
+    return ms.value, n.value
+
+
+KERNEL_NAMES = ("block_mean", "transpose_v", "gate_topk", "route_count", "route_scan_rows",
+                "route_scan_buckets", "route_scatter", "attn_routed", "attn_own_merge",
+                "attn_full", "decode_gate", "decode_attn", "decode_merge")

@@ -1,0 +1,512 @@
+// C ABI of libmoba.so: argument checks, workspace layout and the launch
+// sequence of the MoBA forward.  Every entry point checks all arguments
+// before it enqueues anything and never lets a C++ exception cross the ABI.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+#include "moba.h"
+
+using moba::Dims;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+moba_status fail(moba_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+// ---------------------------------------------------------------- profiling
+enum KernelId {
+  K_BLOCK_MEAN, K_TRANSPOSE_V, K_GATE, K_RCOUNT, K_RSCAN_ROWS, K_RSCAN_BUCKETS, K_RSCATTER,
+  K_ATTN_ROUTED, K_ATTN_OWN, K_ATTN_FULL, K_DEC_GATE, K_DEC_ATTN, K_DEC_MERGE, K_COUNT
+};
+const char* const kKernelNames[K_COUNT] = {
+    "block_mean", "transpose_v", "gate_topk", "route_count", "route_scan_rows",
+    "route_scan_buckets", "route_scatter", "attn_routed", "attn_own_merge", "attn_full",
+    "decode_gate", "decode_attn", "decode_merge"};
+
+struct ProfRecord {
+  int id;
+  hipEvent_t a, b;
+};
+
+struct Profiler {
+  std::mutex mu;
+  bool on = false;
+  std::vector<ProfRecord> recs;
+  double total_ms[K_COUNT] = {};
+  int64_t launches[K_COUNT] = {};
+};
+Profiler g_prof;
+
+struct Launch {
+  hipStream_t st;
+  hipError_t err = hipSuccess;
+  const char* what = nullptr;
+  template <class F>
+  void run(int id, F&& f) {
+    if (err != hipSuccess) return;
+    hipEvent_t a = nullptr, b = nullptr;
+    bool prof = false;
+    {
+      std::lock_guard<std::mutex> g(g_prof.mu);
+      prof = g_prof.on;
+    }
+    if (prof) {
+      if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess ||
+          hipEventRecord(a, st) != hipSuccess) {
+        err = hipErrorUnknown;
+        what = "profiling event";
+        return;
+      }
+    }
+    err = f();
+    if (err != hipSuccess) {
+      what = kKernelNames[id];
+      return;
+    }
+    if (prof) {
+      (void)hipEventRecord(b, st);
+      std::lock_guard<std::mutex> g(g_prof.mu);
+      g_prof.recs.push_back({id, a, b});
+    }
+  }
+};
+
+// ------------------------------------------------------------------ checks
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  if (a < 0 || b < 0) return false;
+  if (a != 0 && b > INT64_MAX / a) return false;
+  *out = a * b;
+  return true;
+}
+
+size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct Plan {
+  Dims d;
+  bool need_kbar = false, need_vt = false, need_sel = false, routed = false;
+  size_t off_kbar = 0, off_vt = 0, off_sel = 0, off_counts = 0, off_btotal = 0, off_boff = 0,
+         off_toff = 0, off_list = 0, off_po = 0, off_plse = 0, total = 0;
+};
+
+moba_status check_common(const moba_args* a, bool full, Plan* p) {
+  if (!a) return fail(MOBA_ERR_INVALID_ARGUMENT, "args is NULL");
+  if (a->struct_size != sizeof(moba_args))
+    return fail(MOBA_ERR_INVALID_ARGUMENT, "struct_size %zu != sizeof(moba_args) %zu",
+                a->struct_size, sizeof(moba_args));
+  if (!a->q || !a->k || !a->v || !a->out)
+    return fail(MOBA_ERR_INVALID_ARGUMENT, "q, k, v and out must be non-NULL");
+  if (a->batch < 1 || a->n_heads < 1 || a->n_kv_heads < 1 || a->head_dim < 1 || a->q_len < 1 ||
+      a->kv_len < 1)
+    return fail(MOBA_ERR_INVALID_ARGUMENT, "sizes must be >= 1");
+  if (!full && (a->block_size < 1 || a->topk < 1))
+    return fail(MOBA_ERR_INVALID_ARGUMENT, "block_size and topk must be >= 1");
+  if (a->n_heads % a->n_kv_heads != 0)
+    return fail(MOBA_ERR_INVALID_ARGUMENT, "n_heads %% n_kv_heads != 0");
+  if (a->q_len > a->kv_len) return fail(MOBA_ERR_INVALID_ARGUMENT, "q_len > kv_len");
+  if (a->dtype != MOBA_DTYPE_F32 && a->dtype != MOBA_DTYPE_BF16)
+    return fail(MOBA_ERR_UNSUPPORTED, "unknown dtype %d", (int)a->dtype);
+  if (a->head_dim != 64 && a->head_dim != 128)
+    return fail(MOBA_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", a->head_dim);
+  const uintptr_t align = (uintptr_t)a->q | (uintptr_t)a->k | (uintptr_t)a->v |
+                          (uintptr_t)a->out | (uintptr_t)a->k_block_mean |
+                          (uintptr_t)a->workspace;
+  if (align & 15) return fail(MOBA_ERR_INVALID_ARGUMENT, "pointers must be 16-byte aligned");
+  if (a->sel_out && ((uintptr_t)a->sel_out & 3))
+    return fail(MOBA_ERR_INVALID_ARGUMENT, "sel_out must be 4-byte aligned");
+
+  Dims& d = p->d;
+  d.S = a->batch; d.H = a->n_heads; d.Hkv = a->n_kv_heads; d.G = d.H / d.Hkv; d.D = a->head_dim;
+  d.Lq = a->q_len; d.L = a->kv_len; d.q_off = d.L - d.Lq; d.bf16 = a->dtype == MOBA_DTYPE_BF16;
+  int64_t t = 0;
+  if (!mul_ok(d.S, d.Lq, &t) || !mul_ok(t, d.H, &t) || !mul_ok(t, d.D, &t) ||
+      !mul_ok(d.S, d.L, &t) || !mul_ok(t, d.Hkv, &t) || !mul_ok(t, d.D, &t) ||
+      !mul_ok(t, 4, &t))
+    return fail(MOBA_ERR_INVALID_ARGUMENT, "tensor size overflows int64");
+  if ((int64_t)d.S * d.H > 65535)
+    return fail(MOBA_ERR_UNSUPPORTED, "batch * n_heads > 65535");
+  if (d.L >= ((int64_t)1 << 31)) return fail(MOBA_ERR_UNSUPPORTED, "kv_len >= 2^31");
+  return MOBA_OK;
+}
+
+moba_status plan_forward(const moba_args* a, Plan* p) {
+  moba_status st = check_common(a, false, p);
+  if (st != MOBA_OK) return st;
+  Dims& d = p->d;
+  if (a->block_size % 64 != 0)
+    return fail(MOBA_ERR_UNSUPPORTED, "block_size %d is not a multiple of 64", a->block_size);
+  if (d.L % a->block_size != 0)
+    return fail(MOBA_ERR_UNSUPPORTED, "kv_len is not a multiple of block_size");
+  if (a->topk > moba::kMaxTopk)
+    return fail(MOBA_ERR_UNSUPPORTED, "topk %d > %d", a->topk, moba::kMaxTopk);
+  const int64_t nb = d.L / a->block_size;
+  if (nb > moba::kMaxBlocks) return fail(MOBA_ERR_UNSUPPORTED, "more than %d blocks", moba::kMaxBlocks);
+  d.B = a->block_size;
+  d.topk = a->topk;
+  d.kp = d.topk - 1;
+  d.nb = (int)nb;
+  d.nchunk_r = (int)((d.Lq + moba::kRouteChunkRows - 1) / moba::kRouteChunkRows);
+  d.ncols = d.G * d.nchunk_r;
+  d.nrows = d.S * d.Hkv * d.nb;
+  int64_t slots = 0;
+  if (!mul_ok((int64_t)d.S * d.H, d.Lq, &slots) || !mul_ok(slots, d.kp, &slots))
+    return fail(MOBA_ERR_INVALID_ARGUMENT, "slot count overflows");
+  if (slots >= ((int64_t)1 << 32))
+    return fail(MOBA_ERR_UNSUPPORTED, "more than 2^32 routed slots");
+  d.slots = slots;
+  if ((int64_t)d.S * d.H * d.nchunk_r >= ((int64_t)1 << 31))
+    return fail(MOBA_ERR_UNSUPPORTED, "too many routing chunks");
+  const int64_t esz = d.bf16 ? 2 : 4;
+  p->need_kbar = a->k_block_mean == nullptr;
+  p->need_vt = d.bf16;
+  p->need_sel = a->sel_out == nullptr;
+  p->routed = d.kp > 0 && d.nb > 1;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  if (p->need_kbar) p->off_kbar = take((size_t)d.S * d.Hkv * d.nb * d.D * 4);
+  if (p->need_vt) p->off_vt = take((size_t)d.S * d.Hkv * d.D * d.L * 2);
+  if (p->need_sel) p->off_sel = take((size_t)d.S * d.H * d.Lq * d.topk * 4);
+  if (p->routed) {
+    p->off_counts = take((size_t)d.nrows * d.ncols * 4);
+    p->off_btotal = take((size_t)d.nrows * 4);
+    p->off_boff = take((size_t)(d.nrows + 1) * 4);
+    p->off_toff = take((size_t)(d.nrows + 1) * 4);
+    p->off_list = take((size_t)d.slots * 4);
+    p->off_po = take((size_t)d.slots * d.D * esz);
+    p->off_plse = take((size_t)d.slots * 4);
+  }
+  p->total = off;
+  if (a->workspace && a->workspace_bytes < p->total)
+    return fail(MOBA_ERR_INVALID_ARGUMENT, "workspace too small: %zu < %zu bytes",
+                a->workspace_bytes, p->total);
+  return MOBA_OK;
+}
+
+moba_status plan_full(const moba_args* a, Plan* p) {
+  moba_status st = check_common(a, true, p);
+  if (st != MOBA_OK) return st;
+  Dims& d = p->d;
+  if (d.L % 64 != 0) return fail(MOBA_ERR_UNSUPPORTED, "kv_len is not a multiple of 64");
+  d.B = 64;
+  d.topk = 1;
+  d.kp = 0;
+  d.nb = (int)(d.L / 64);
+  p->need_vt = d.bf16;
+  size_t off = 0;
+  if (p->need_vt) {
+    p->off_vt = 0;
+    off = align_up((size_t)d.S * d.Hkv * d.D * d.L * 2);
+  }
+  p->total = off;
+  if (a->workspace && a->workspace_bytes < p->total)
+    return fail(MOBA_ERR_INVALID_ARGUMENT, "workspace too small: %zu < %zu bytes",
+                a->workspace_bytes, p->total);
+  return MOBA_OK;
+}
+
+struct Workspace {
+  char* base = nullptr;
+  bool owned = false;
+  hipStream_t st = nullptr;
+  ~Workspace() {
+    if (owned && base) (void)hipFreeAsync(base, st);
+  }
+};
+
+moba_status get_workspace(const moba_args* a, const Plan& p, Workspace* ws) {
+  ws->st = (hipStream_t)a->stream;
+  if (p.total == 0) return MOBA_OK;
+  if (a->workspace) {
+    ws->base = (char*)a->workspace;
+    return MOBA_OK;
+  }
+  void* ptr = nullptr;
+  const hipError_t e = hipMallocAsync(&ptr, p.total, ws->st);
+  if (e != hipSuccess || !ptr) {
+    (void)hipGetLastError();
+    return fail(MOBA_ERR_OUT_OF_MEMORY, "hipMallocAsync(%zu bytes) failed: %s", p.total,
+                hipGetErrorString(e));
+  }
+  ws->base = (char*)ptr;
+  ws->owned = true;
+  return MOBA_OK;
+}
+
+moba_status hip_fail(const Launch& l) {
+  return fail(MOBA_ERR_HIP, "launch of %s failed: %s", l.what ? l.what : "?",
+              hipGetErrorString(l.err));
+}
+
+moba_status forward_impl(const moba_args* a) {
+  Plan p;
+  moba_status st = plan_forward(a, &p);
+  if (st != MOBA_OK) return st;
+  Workspace ws;
+  st = get_workspace(a, p, &ws);
+  if (st != MOBA_OK) return st;
+  const Dims& d = p.d;
+  char* w = ws.base;
+  float* kbar = p.need_kbar ? (float*)(w + p.off_kbar) : const_cast<float*>(a->k_block_mean);
+  void* vt = p.need_vt ? (void*)(w + p.off_vt) : nullptr;
+  int32_t* sel = p.need_sel ? (int32_t*)(w + p.off_sel) : a->sel_out;
+  uint32_t* counts = (uint32_t*)(w + p.off_counts);
+  uint32_t* btotal = (uint32_t*)(w + p.off_btotal);
+  uint32_t* boff = (uint32_t*)(w + p.off_boff);
+  uint32_t* toff = (uint32_t*)(w + p.off_toff);
+  uint32_t* list = (uint32_t*)(w + p.off_list);
+  void* po = (void*)(w + p.off_po);
+  float* plse = (float*)(w + p.off_plse);
+
+  Launch l{(hipStream_t)a->stream};
+  if (p.need_kbar)
+    l.run(K_BLOCK_MEAN, [&] { return moba::launch_block_mean(a->k, kbar, d, l.st); });
+  l.run(K_GATE, [&] { return moba::launch_gate_topk(a->q, kbar, sel, d, l.st); });
+  if (p.need_vt) l.run(K_TRANSPOSE_V, [&] { return moba::launch_transpose_v(a->v, vt, d, l.st); });
+  if (p.routed) {
+    l.run(K_RCOUNT, [&] { return moba::launch_route_count(sel, counts, d, l.st); });
+    l.run(K_RSCAN_ROWS, [&] { return moba::launch_route_scan_rows(counts, btotal, d, l.st); });
+    l.run(K_RSCAN_BUCKETS,
+          [&] { return moba::launch_route_scan_buckets(btotal, boff, toff, d, l.st); });
+    l.run(K_RSCATTER,
+          [&] { return moba::launch_route_scatter(sel, counts, boff, list, d, l.st); });
+    l.run(K_ATTN_ROUTED, [&] {
+      return d.bf16 ? moba::launch_attn_routed_bf16(a->q, a->k, vt, list, boff, toff, po, plse,
+                                                    d, l.st)
+                    : moba::launch_attn_routed_f32(a->q, a->k, a->v, list, boff, toff, po, plse,
+                                                   d, l.st);
+    });
+  }
+  Dims dq = d;
+  if (!p.routed) dq.kp = 0;  // nothing to merge
+  l.run(K_ATTN_OWN, [&] {
+    return d.bf16 ? moba::launch_attn_query_bf16(a->q, a->k, vt, po, plse, a->out, 0, dq, l.st)
+                  : moba::launch_attn_query_f32(a->q, a->k, a->v, po, plse, a->out, 0, dq,
+                                                l.st);
+  });
+  if (l.err != hipSuccess) return hip_fail(l);
+  return MOBA_OK;
+}
+
+moba_status full_impl(const moba_args* a) {
+  Plan p;
+  moba_status st = plan_full(a, &p);
+  if (st != MOBA_OK) return st;
+  Workspace ws;
+  st = get_workspace(a, p, &ws);
+  if (st != MOBA_OK) return st;
+  const Dims& d = p.d;
+  void* vt = p.need_vt ? (void*)(ws.base + p.off_vt) : nullptr;
+  Launch l{(hipStream_t)a->stream};
+  if (p.need_vt) l.run(K_TRANSPOSE_V, [&] { return moba::launch_transpose_v(a->v, vt, d, l.st); });
+  l.run(K_ATTN_FULL, [&] {
+    return d.bf16 ? moba::launch_attn_query_bf16(a->q, a->k, vt, nullptr, nullptr, a->out, 1, d,
+                                                 l.st)
+                  : moba::launch_attn_query_f32(a->q, a->k, a->v, nullptr, nullptr, a->out, 1,
+                                                d, l.st);
+  });
+  if (l.err != hipSuccess) return hip_fail(l);
+  return MOBA_OK;
+}
+
+moba_args simple_args(const void* q, const void* k, const void* v, int64_t seq_len,
+                      int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, int32_t block_size,
+                      int32_t topk, void* out, moba_dtype dtype, void* stream) {
+  moba_args a;
+  std::memset(&a, 0, sizeof(a));
+  a.struct_size = sizeof(moba_args);
+  a.q = q; a.k = k; a.v = v; a.out = out;
+  a.batch = 1; a.n_heads = n_heads; a.n_kv_heads = n_kv_heads; a.head_dim = head_dim;
+  a.block_size = block_size; a.topk = topk; a.q_len = seq_len; a.kv_len = seq_len;
+  a.dtype = dtype; a.stream = stream;
+  return a;
+}
+
+template <class F>
+moba_status guarded(F&& f) {
+  g_last_error.clear();
+  try {
+    return f();
+  } catch (const std::exception& e) {
+    return fail(MOBA_ERR_HIP, "internal error: %s", e.what());
+  } catch (...) {
+    return fail(MOBA_ERR_HIP, "internal error");
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+moba_status moba_forward(const void* q, const void* k, const void* v, int64_t seq_len,
+                         int32_t n_heads, int32_t n_kv_heads, int32_t head_dim,
+                         int32_t block_size, int32_t topk, void* out, moba_dtype dtype,
+                         void* stream) {
+  return guarded([&] {
+    const moba_args a = simple_args(q, k, v, seq_len, n_heads, n_kv_heads, head_dim, block_size,
+                                    topk, out, dtype, stream);
+    return forward_impl(&a);
+  });
+}
+
+moba_status moba_full_attention(const void* q, const void* k, const void* v, int64_t seq_len,
+                                int32_t n_heads, int32_t n_kv_heads, int32_t head_dim,
+                                void* out, moba_dtype dtype, void* stream) {
+  return guarded([&] {
+    const moba_args a =
+        simple_args(q, k, v, seq_len, n_heads, n_kv_heads, head_dim, 64, 1, out, dtype, stream);
+    return full_impl(&a);
+  });
+}
+
+moba_status moba_forward_ex(const moba_args* a) {
+  return guarded([&] { return forward_impl(a); });
+}
+
+moba_status moba_full_attention_ex(const moba_args* a) {
+  return guarded([&] { return full_impl(a); });
+}
+
+size_t moba_workspace_size(const moba_args* a) {
+  g_last_error.clear();
+  try {
+    if (!a) {
+      fail(MOBA_ERR_INVALID_ARGUMENT, "args is NULL");
+      return 0;
+    }
+    moba_args b = *a;
+    b.workspace = nullptr;
+    b.workspace_bytes = 0;
+    Plan p;
+    if (plan_forward(&b, &p) != MOBA_OK) return 0;
+    return p.total;
+  } catch (...) {
+    return 0;
+  }
+}
+
+size_t moba_full_workspace_size(const moba_args* a) {
+  g_last_error.clear();
+  try {
+    if (!a) {
+      fail(MOBA_ERR_INVALID_ARGUMENT, "args is NULL");
+      return 0;
+    }
+    moba_args b = *a;
+    b.workspace = nullptr;
+    b.workspace_bytes = 0;
+    Plan p;
+    if (plan_full(&b, &p) != MOBA_OK) return 0;
+    return p.total;
+  } catch (...) {
+    return 0;
+  }
+}
+
+moba_status moba_block_mean(const void* k, int32_t batch, int64_t kv_len, int32_t n_kv_heads,
+                            int32_t head_dim, int32_t block_size, float* k_block_mean,
+                            moba_dtype dtype, void* stream) {
+  return guarded([&]() -> moba_status {
+    if (!k || !k_block_mean)
+      return fail(MOBA_ERR_INVALID_ARGUMENT, "k and k_block_mean must be non-NULL");
+    if (batch < 1 || kv_len < 1 || n_kv_heads < 1 || head_dim < 1 || block_size < 1)
+      return fail(MOBA_ERR_INVALID_ARGUMENT, "sizes must be >= 1");
+    if (((uintptr_t)k | (uintptr_t)k_block_mean) & 15)
+      return fail(MOBA_ERR_INVALID_ARGUMENT, "pointers must be 16-byte aligned");
+    if (dtype != MOBA_DTYPE_F32 && dtype != MOBA_DTYPE_BF16)
+      return fail(MOBA_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
+    if (head_dim != 64 && head_dim != 128)
+      return fail(MOBA_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", head_dim);
+    if (block_size % 64 != 0)
+      return fail(MOBA_ERR_UNSUPPORTED, "block_size is not a multiple of 64");
+    if (kv_len % block_size != 0)
+      return fail(MOBA_ERR_UNSUPPORTED, "kv_len is not a multiple of block_size");
+    if (kv_len / block_size > moba::kMaxBlocks || batch > 65535)
+      return fail(MOBA_ERR_UNSUPPORTED, "too many blocks or sequences");
+    Dims d;
+    d.S = batch; d.L = kv_len; d.Hkv = n_kv_heads; d.D = head_dim; d.B = block_size;
+    d.nb = (int)(kv_len / block_size); d.bf16 = dtype == MOBA_DTYPE_BF16;
+    Launch l{(hipStream_t)stream};
+    l.run(K_BLOCK_MEAN, [&] { return moba::launch_block_mean(k, k_block_mean, d, l.st); });
+    if (l.err != hipSuccess) return hip_fail(l);
+    return MOBA_OK;
+  });
+}
+
+const char* moba_status_string(moba_status s) {
+  switch (s) {
+    case MOBA_OK: return "MOBA_OK";
+    case MOBA_ERR_INVALID_ARGUMENT: return "MOBA_ERR_INVALID_ARGUMENT";
+    case MOBA_ERR_UNSUPPORTED: return "MOBA_ERR_UNSUPPORTED";
+    case MOBA_ERR_OUT_OF_MEMORY: return "MOBA_ERR_OUT_OF_MEMORY";
+    case MOBA_ERR_HIP: return "MOBA_ERR_HIP";
+  }
+  return "MOBA_STATUS_UNKNOWN";
+}
+
+const char* moba_last_error(void) { return g_last_error.c_str(); }
+
+int32_t moba_abi_version(void) { return MOBA_ABI_VERSION; }
+
+moba_status moba_profile_enable(int32_t on) {
+  std::lock_guard<std::mutex> g(g_prof.mu);
+  g_prof.on = on != 0;
+  return MOBA_OK;
+}
+
+static void drain_locked() {
+  for (const ProfRecord& r : g_prof.recs) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.b) == hipSuccess && hipEventElapsedTime(&ms, r.a, r.b) == hipSuccess) {
+      g_prof.total_ms[r.id] += ms;
+      g_prof.launches[r.id] += 1;
+    }
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
+  }
+  g_prof.recs.clear();
+}
+
+moba_status moba_profile_reset(void) {
+  std::lock_guard<std::mutex> g(g_prof.mu);
+  drain_locked();
+  for (int i = 0; i < K_COUNT; ++i) {
+    g_prof.total_ms[i] = 0.0;
+    g_prof.launches[i] = 0;
+  }
+  return MOBA_OK;
+}
+
+moba_status moba_profile_read(const char* name, double* total_ms, int64_t* launches) {
+  if (!name || !total_ms || !launches)
+    return fail(MOBA_ERR_INVALID_ARGUMENT, "name, total_ms and launches must be non-NULL");
+  int id = -1;
+  for (int i = 0; i < K_COUNT; ++i)
+    if (std::strcmp(name, kKernelNames[i]) == 0) id = i;
+  if (id < 0) return fail(MOBA_ERR_INVALID_ARGUMENT, "unknown kernel name '%s'", name);
+  std::lock_guard<std::mutex> g(g_prof.mu);
+  drain_locked();
+  *total_ms = g_prof.total_ms[id];
+  *launches = g_prof.launches[id];
+  return MOBA_OK;
+}
+
+}  // extern "C"

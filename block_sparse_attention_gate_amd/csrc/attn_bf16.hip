@@ -1,0 +1,401 @@
+// Flash-style attention on MFMA (bf16 inputs, fp32 accumulation).
+//
+// Two kernels share one inner step:
+//   k_attn_routed: one tile = up to 128 routed entries of one (sequence, KV
+//     head, block) bucket; the block is a selected PAST block, so all of its
+//     keys are visible (no mask).  Writes, per entry, the normalised partial
+//     output (bf16) and its log2-sum-exp (fp32) to the entry's slot.
+//   k_attn_query: query-centric causal attention.  Mode 0 (own block): keys
+//     from the start of the query's block up to and including the query
+//     (causal mask inside the current block, AiBoss MoBA article,
+//     "MoBAの技術的原則"), then merges the routed partials of that query by
+//     their log-sum-exp, which gives one softmax over the union of the
+//     selected keys.  Mode 1: full causal attention (the topk = all case of
+//     the full/sparse switch, "MoBA" project card, "How It Works").
+//
+// Wave tile: 32 queries (lane l owns query l%32) x 64 keys per step.
+//   S^T = K Q^T on 32x32x16 MFMA (K rows in the kperm order, see common.h),
+//   online softmax in fp32 (base-2, scale folded into one FMA),
+//   O^T += V^T P^T on 32x32x16 MFMA; V^T rows come from the transposed V.
+// Workgroup: 4 waves sharing double-buffered LDS tiles of K [64][D] and
+// V^T [D][64] (rows padded by 16 bytes against bank conflicts).
+#include "common.h"
+#include "kernels.h"
+
+namespace moba {
+
+template <int D>
+struct Tiles {
+  static constexpr int KS = D + 8;   // K tile row stride (elements)
+  static constexpr int VS = 64 + 8;  // V^T tile row stride (elements)
+  static constexpr int KE = 64 * KS;
+  static constexpr int VE = D * VS;
+  static constexpr int BUF = KE + VE;
+  static constexpr int KCH = 64 * (D / 8) / 256;  // 16-byte K chunks per thread
+  static constexpr int VCH = D * 8 / 256;         // 16-byte V^T chunks per thread
+};
+
+// Global -> register staging of one 64-key tile (all 256 threads).
+template <int D>
+struct TileRegs {
+  u32x4 kr[Tiles<D>::KCH];
+  u32x4 vr[Tiles<D>::VCH];
+
+  __device__ __forceinline__ void load(const bf16_t* kbase, int64_t krow_stride,
+                                       const bf16_t* vtbase, int64_t L, int64_t key0, int tid) {
+#pragma unroll
+    for (int i = 0; i < Tiles<D>::KCH; ++i) {
+      const int c = tid + 256 * i;
+      const int row = c / (D / 8), cc = c % (D / 8);
+      kr[i] = *reinterpret_cast<const u32x4*>(kbase + (key0 + row) * krow_stride + cc * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < Tiles<D>::VCH; ++i) {
+      const int c = tid + 256 * i;
+      const int dd = c / 8, kc = c % 8;
+      vr[i] = *reinterpret_cast<const u32x4*>(vtbase + (int64_t)dd * L + key0 + kc * 8);
+    }
+  }
+  __device__ __forceinline__ void store(bf16_t* buf, int tid) const {
+#pragma unroll
+    for (int i = 0; i < Tiles<D>::KCH; ++i) {
+      const int c = tid + 256 * i;
+      const int row = c / (D / 8), cc = c % (D / 8);
+      *reinterpret_cast<u32x4*>(buf + row * Tiles<D>::KS + cc * 8) = kr[i];
+    }
+#pragma unroll
+    for (int i = 0; i < Tiles<D>::VCH; ++i) {
+      const int c = tid + 256 * i;
+      const int dd = c / 8, kc = c % 8;
+      *reinterpret_cast<u32x4*>(buf + Tiles<D>::KE + dd * Tiles<D>::VS + kc * 8) = vr[i];
+    }
+  }
+};
+
+template <int D>
+struct FlashAcc {
+  f32x16 o[D / 32];
+  float m;  // running max of the scaled logits (base 2)
+  float l;  // running sum of this lane half's probabilities
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) o[dt] = f32x16{};
+    m = -__builtin_inff();
+    l = 0.f;
+  }
+};
+
+// One 64-key step of one wave.  MASK: drop keys outside [klo, qpos].
+template <int D, bool MASK>
+__device__ __forceinline__ void flash_step(const bf16_t* buf, const bf16x8 (&qf)[D / 16],
+                                           FlashAcc<D>& acc, int n, int hh, float sl2,
+                                           int64_t key0, int64_t klo, int64_t qpos) {
+  using T = Tiles<D>;
+  f32x16 s[2];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    s[kt] = f32x16{};
+    const bf16_t* krow = buf + (32 * kt + kperm(n)) * T::KS + 8 * hh;
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) s[kt] = mfma32(ld_bf16x8(krow + 16 * t), qf[t], s[kt]);
+  }
+  if (MASK) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int reg = 0; reg < 16; ++reg) {
+        const int64_t key = key0 + 32 * kt + acc_key(reg, hh);
+        if (key > qpos || key < klo) s[kt][reg] = -__builtin_inff();
+      }
+  }
+  float mx = s[0][0];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int reg = 0; reg < 16; ++reg) mx = fmaxf(mx, s[kt][reg]);
+  mx = fmaxf(mx, half_swap(mx));
+  const float mnew = fmaxf(acc.m, mx * sl2);
+  const float mref = (mnew == -__builtin_inff()) ? 0.f : mnew;
+  const float alpha = __builtin_amdgcn_exp2f(acc.m - mref);
+  float psum = 0.f;
+  bf16x8 pb[2][2];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][8 * c + r], sl2, -mref));
+        psum += p;
+        pb[kt][c][r] = static_cast<__bf16>(p);
+      }
+  acc.l = fmaf(acc.l, alpha, psum);
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int reg = 0; reg < 16; ++reg) acc.o[dt][reg] *= alpha;
+  acc.m = mnew;
+  const bf16_t* vbase = buf + T::KE + 8 * hh;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+    const bf16_t* vrow = vbase + (32 * dt + n) * T::VS;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+        acc.o[dt] = mfma32(ld_bf16x8(vrow + 32 * kt + 16 * c), pb[kt][c], acc.o[dt]);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void load_q(const bf16_t* qrow, bool valid, int hh,
+                                       bf16x8 (&qf)[D / 16]) {
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) {
+    qf[t] = ld_bf16x8(qrow + 16 * t + 8 * hh);
+    if (!valid) qf[t] = bf16x8{};
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Routed tiles.  grid = upper bound of the tile count; workgroups past the
+// device-side tile count exit.  The tile order is XCD-aware: workgroup b runs
+// on XCD b % 8, and XCD x takes the contiguous tile range
+// [x*per, (x+1)*per), so the tiles of one bucket (same K/V block) share an L2.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256, 2) void k_attn_routed(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ vt,
+    const uint32_t* __restrict__ list, const uint32_t* __restrict__ bucket_off,
+    const uint32_t* __restrict__ tile_off, bf16_t* __restrict__ po, float* __restrict__ plse,
+    int64_t Lq, int64_t L, int H, int Hkv, int kp, int B, int nb, int nrows, float sl2,
+    uint32_t nslots) {
+  using T = Tiles<D>;
+  __shared__ __attribute__((aligned(16))) bf16_t lds[2 * T::BUF];
+  const uint32_t ntiles = tile_off[nrows];
+  const uint32_t per = (ntiles + 7) / 8;
+  const uint32_t bid = blockIdx.x;
+  if (bid / 8 >= per) return;
+  const uint32_t tile = (bid % 8) * per + bid / 8;
+  if (tile >= ntiles) return;
+  int lo = 0, hi = nrows;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (tile_off[mid] <= tile) lo = mid; else hi = mid;
+  }
+  const int row = lo;
+  const uint32_t start = (tile - tile_off[row]) * kRoutedTileM;
+  const uint32_t avail = bucket_off[row + 1] - bucket_off[row] - start;
+  const int cnt = avail < (uint32_t)kRoutedTileM ? (int)avail : kRoutedTileM;
+  const int j = row % nb;
+  const int sg = row / nb, g = sg % Hkv, s = sg / Hkv;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int n = lane & 31, hh = lane >> 5;
+  const int e = 32 * w + n;
+  const bool wave_on = 32 * w < cnt;
+  const uint32_t slot_raw = (e < cnt) ? list[bucket_off[row] + start + e] : 0u;
+  const bool valid = e < cnt && slot_raw < nslots;  // never write outside the partials
+  const uint32_t slot = valid ? slot_raw : 0u;
+  const uint32_t qh = slot / (uint32_t)kp;
+  const int64_t r = qh % Lq;
+  const int h = (int)((qh / Lq) % H);
+  bf16x8 qf[D / 16];
+  load_q<D>(q + (((int64_t)s * Lq + r) * H + h) * D, valid, hh, qf);
+
+  const bf16_t* kbase = k + ((int64_t)s * L * Hkv + g) * D;
+  const bf16_t* vtbase = vt + ((int64_t)s * Hkv + g) * D * L;
+  const int64_t kstart = (int64_t)j * B;
+  const int nsteps = B / 64;
+  FlashAcc<D> acc;
+  acc.init();
+  TileRegs<D> tr;
+  tr.load(kbase, (int64_t)Hkv * D, vtbase, L, kstart, tid);
+  tr.store(lds, tid);
+  __syncthreads();
+  for (int it = 0; it < nsteps; ++it) {
+    const bool more = it + 1 < nsteps;
+    if (more) tr.load(kbase, (int64_t)Hkv * D, vtbase, L, kstart + 64 * (it + 1), tid);
+    if (wave_on)
+      flash_step<D, false>(lds + (it & 1) * T::BUF, qf, acc, n, hh, sl2, 0, 0, 0);
+    if (more) tr.store(lds + ((it + 1) & 1) * T::BUF, tid);
+    __syncthreads();
+  }
+  if (!valid) return;
+  const float ltot = acc.l + half_swap(acc.l);
+  const float inv = 1.0f / ltot;
+  bf16_t* orow = po + (int64_t)slot * D;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int d0 = 32 * dt + 8 * i + 4 * hh;
+      const uint32_t w0 = (uint32_t)f32_to_bf16(acc.o[dt][4 * i] * inv) |
+                          ((uint32_t)f32_to_bf16(acc.o[dt][4 * i + 1] * inv) << 16);
+      const uint32_t w1 = (uint32_t)f32_to_bf16(acc.o[dt][4 * i + 2] * inv) |
+                          ((uint32_t)f32_to_bf16(acc.o[dt][4 * i + 3] * inv) << 16);
+      *reinterpret_cast<uint2*>(orow + d0) = make_uint2(w0, w1);
+    }
+  if (hh == 0) plse[slot] = acc.m + __log2f(ltot);
+}
+
+// ---------------------------------------------------------------------------
+// Query-centric causal attention (own block + merge, or full).
+// A workgroup covers HW heads of one KV group x RW query rows (HW*RW = 128);
+// wave w takes head h0 + w % HW and rows [r0 + 32*(w / HW), +32).
+// grid (ceil(Lq / RW), S * H / HW).
+// ---------------------------------------------------------------------------
+template <int D, int MODE>
+__global__ __launch_bounds__(256, 2) void k_attn_query(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ vt,
+    const bf16_t* __restrict__ po, const float* __restrict__ plse, bf16_t* __restrict__ out,
+    int Lq, int L, int q_off, int H, int Hkv, int kp, int B, int HW, float sl2) {
+  using T = Tiles<D>;
+  __shared__ __attribute__((aligned(16))) bf16_t lds[2 * T::BUF];
+  const int RW = 128 / HW;
+  const int rt = (MODE == 1) ? (int)(gridDim.x - 1 - blockIdx.x) : (int)blockIdx.x;
+  const int hgroups = H / HW;
+  const int s = blockIdx.y / hgroups;
+  const int h0 = (blockIdx.y % hgroups) * HW;
+  const int g = h0 / (H / Hkv);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int n = lane & 31, hh = lane >> 5;
+  const int h = h0 + w % HW;
+  const int rw0 = rt * RW;                 // first row of the workgroup
+  const int r0 = rw0 + 32 * (w / HW);      // first row of this wave
+  const int r = r0 + n;
+  const bool valid = r < Lq;
+  const bool wave_on = r0 < Lq;
+  const int pos = q_off + r;
+  // key windows [klo, khi)
+  const int wlast = (r0 + 31 < Lq ? r0 + 31 : Lq - 1);
+  const int klo_w = (MODE == 0) ? ((q_off + r0) / B) * B : 0;
+  const int khi_w = wave_on ? q_off + wlast + 1 : 0;
+  const int wglast = (rw0 + RW - 1 < Lq ? rw0 + RW - 1 : Lq - 1);
+  const int klo_g = (MODE == 0) ? ((q_off + rw0) / B) * B : 0;
+  const int khi_g = q_off + wglast + 1;
+  const int t0 = klo_g / 64, t1 = (khi_g + 63) / 64;
+  const int klo_l = (MODE == 0) ? (pos / B) * B : 0;
+
+  bf16x8 qf[D / 16];
+  load_q<D>(q + (((int64_t)s * Lq + (valid ? r : 0)) * H + h) * D, valid, hh, qf);
+  const bf16_t* kbase = k + ((int64_t)s * L * Hkv + g) * D;
+  const bf16_t* vtbase = vt + ((int64_t)s * Hkv + g) * D * L;
+  const int pos_first = q_off + r0;        // smallest query position of the wave
+  FlashAcc<D> acc;
+  acc.init();
+  TileRegs<D> tr;
+  tr.load(kbase, (int64_t)Hkv * D, vtbase, L, (int64_t)t0 * 64, tid);
+  tr.store(lds, tid);
+  __syncthreads();
+  for (int it = t0; it < t1; ++it) {
+    const bool more = it + 1 < t1;
+    if (more) tr.load(kbase, (int64_t)Hkv * D, vtbase, L, (int64_t)(it + 1) * 64, tid);
+    const int key0 = it * 64;
+    const bf16_t* buf = lds + ((it - t0) & 1) * T::BUF;
+    if (wave_on && key0 < khi_w && key0 + 64 > klo_w) {
+      if ((key0 + 63 > pos_first) || (key0 < klo_w))
+        flash_step<D, true>(buf, qf, acc, n, hh, sl2, key0, klo_l, pos);
+      else
+        flash_step<D, false>(buf, qf, acc, n, hh, sl2, key0, 0, 0);
+    }
+    if (more) tr.store(lds + ((it + 1 - t0) & 1) * T::BUF, tid);
+    __syncthreads();
+  }
+  if (!valid) return;
+  const float ltot = acc.l + half_swap(acc.l);
+  bf16_t* orow = out + (((int64_t)s * Lq + r) * H + h) * D;
+  float inv = 1.0f / ltot;
+  if (MODE == 0 && kp > 0) {
+    // Merge: out = sum_x 2^(lse_x - M) o_x / sum_x 2^(lse_x - M) over the own
+    // partial and the routed partials of this query.
+    const int own = pos / B;
+    const int npast = kp < own ? kp : own;
+    const float lse_own = acc.m + __log2f(ltot);
+    float M = lse_own;
+    const int64_t sbase = (((int64_t)s * H + h) * Lq + r) * kp;
+    for (int t = 0; t < npast; ++t) M = fmaxf(M, plse[sbase + t]);
+    const float w_own = __builtin_amdgcn_exp2f(lse_own - M);
+    float wsum = w_own;
+    const float sc = w_own / ltot;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int reg = 0; reg < 16; ++reg) acc.o[dt][reg] *= sc;
+    for (int t = 0; t < npast; ++t) {
+      const float wt = __builtin_amdgcn_exp2f(plse[sbase + t] - M);
+      wsum += wt;
+      const bf16_t* prow = po + (sbase + t) * D;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint2 raw = *reinterpret_cast<const uint2*>(prow + 32 * dt + 8 * i + 4 * hh);
+          acc.o[dt][4 * i] = fmaf(wt, __uint_as_float(raw.x << 16), acc.o[dt][4 * i]);
+          acc.o[dt][4 * i + 1] =
+              fmaf(wt, __uint_as_float(raw.x & 0xffff0000u), acc.o[dt][4 * i + 1]);
+          acc.o[dt][4 * i + 2] = fmaf(wt, __uint_as_float(raw.y << 16), acc.o[dt][4 * i + 2]);
+          acc.o[dt][4 * i + 3] =
+              fmaf(wt, __uint_as_float(raw.y & 0xffff0000u), acc.o[dt][4 * i + 3]);
+        }
+    }
+    inv = 1.0f / wsum;
+  }
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int d0 = 32 * dt + 8 * i + 4 * hh;
+      const uint32_t w0 = (uint32_t)f32_to_bf16(acc.o[dt][4 * i] * inv) |
+                          ((uint32_t)f32_to_bf16(acc.o[dt][4 * i + 1] * inv) << 16);
+      const uint32_t w1 = (uint32_t)f32_to_bf16(acc.o[dt][4 * i + 2] * inv) |
+                          ((uint32_t)f32_to_bf16(acc.o[dt][4 * i + 3] * inv) << 16);
+      *reinterpret_cast<uint2*>(orow + d0) = make_uint2(w0, w1);
+    }
+}
+
+static int gcd_int(int a, int b) {
+  while (b) { const int t = a % b; a = b; b = t; }
+  return a;
+}
+
+hipError_t launch_attn_routed_bf16(const void* q, const void* k, const void* vt,
+                                   const uint32_t* list, const uint32_t* bucket_off,
+                                   const uint32_t* tile_off, void* part_o, float* part_lse,
+                                   const Dims& d, hipStream_t st) {
+  const int64_t grid = routed_tile_bound(d);
+  const float sl2 = kLog2e / sqrtf((float)d.D);
+#define MOBA_ROUTED(DV)                                                                      \
+  hipLaunchKernelGGL(k_attn_routed<DV>, dim3((unsigned)grid), dim3(256), 0, st,              \
+                     static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),           \
+                     static_cast<const bf16_t*>(vt), list, bucket_off, tile_off,             \
+                     static_cast<bf16_t*>(part_o), part_lse, d.Lq, d.L, d.H, d.Hkv, d.kp,    \
+                     d.B, d.nb, d.nrows, sl2, (uint32_t)d.slots)
+  if (d.D == 128) MOBA_ROUTED(128); else MOBA_ROUTED(64);
+#undef MOBA_ROUTED
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_query_bf16(const void* q, const void* k, const void* vt,
+                                  const void* part_o, const float* part_lse, void* out, int mode,
+                                  const Dims& d, hipStream_t st) {
+  const int HW = gcd_int(d.G, 4);
+  const int RW = 128 / HW;
+  dim3 grid((unsigned)((d.Lq + RW - 1) / RW), d.S * d.H / HW);
+  const float sl2 = kLog2e / sqrtf((float)d.D);
+#define MOBA_QUERY(DV, MV)                                                                   \
+  hipLaunchKernelGGL((k_attn_query<DV, MV>), grid, dim3(256), 0, st,                         \
+                     static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),           \
+                     static_cast<const bf16_t*>(vt), static_cast<const bf16_t*>(part_o),     \
+                     part_lse, static_cast<bf16_t*>(out), (int)d.Lq, (int)d.L, (int)d.q_off, \
+                     d.H, d.Hkv, d.kp, d.B, HW, sl2)
+  if (d.D == 128) {
+    if (mode == 0) MOBA_QUERY(128, 0); else MOBA_QUERY(128, 1);
+  } else {
+    if (mode == 0) MOBA_QUERY(64, 0); else MOBA_QUERY(64, 1);
+  }
+#undef MOBA_QUERY
+  return hipGetLastError();
+}
+
+}  // namespace moba

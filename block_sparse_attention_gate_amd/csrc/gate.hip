@@ -1,0 +1,191 @@
+// Gate and top-k selection.
+//
+// For every query token the gate scores each PAST block by the dot product
+// of the query with the block's mean key; it is parameter-less and picks the
+// best blocks per query token ("MoBA" project card, "How It Works").  A query
+// never selects a future block and always keeps its own block, which is then
+// causally masked (AiBoss MoBA article, "MoBAの技術的原則", causality design).
+// The own block counts as one of the k; the best k-1 past blocks are kept,
+// ties going to the lower block index.  Output: sel[s, h, r, 0..k) ascending,
+// -1 padded.
+#include "common.h"
+#include "kernels.h"
+
+namespace moba {
+
+// bf16 queries: scores on MFMA.  S^T[block][query] = kbar . q with kbar split
+// into three bf16 terms (hi + mid + lo reproduce the fp32 mean exactly up to
+// fp32 rounding), so the scores carry fp32 accuracy.  Lane l owns query
+// column l%32 and sees 16 of every 32 blocks; the two lane halves keep their
+// own top list and merge at the end.  grid (ceil(Lq/128), S*H), 256 threads.
+template <int D, int KM>
+__global__ __launch_bounds__(256) void k_gate_topk_bf16(
+    const bf16_t* __restrict__ q, const float* __restrict__ kbar, int32_t* __restrict__ sel,
+    int64_t Lq, int64_t q_off, int H, int Hkv, int B, int nb, int topk) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int n = lane & 31, hh = lane >> 5;
+  const int sh = blockIdx.y, s = sh / H, h = sh % H, g = h / (H / Hkv);
+  const int64_t rbase = (int64_t)blockIdx.x * 128 + w * 32;
+  if (rbase >= Lq) return;
+  const int64_t r = rbase + n;
+  const bool valid = r < Lq;
+  const int b = valid ? (int)((q_off + r) / B) : 0;
+  const int kp = topk - 1;
+  const int nkeep = kp < b ? kp : b;
+
+  bf16x8 qf[D / 16];
+  const bf16_t* qrow = q + (((int64_t)s * Lq + (valid ? r : 0)) * H + h) * D;
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) {
+    qf[t] = ld_bf16x8(qrow + 16 * t + 8 * hh);
+    if (!valid) qf[t] = bf16x8{};
+  }
+  const int64_t rlast = (rbase + 31 < Lq ? rbase + 31 : Lq - 1);
+  const int bmax = (int)((q_off + rlast) / B);
+
+  TopList<KM> top;
+  top.init();
+  const float* kb = kbar + ((int64_t)s * Hkv + g) * nb * D;
+  if (kp > 0) {
+    for (int jt = 0; jt * 32 < bmax; ++jt) {
+      const int jrow = (jt * 32 + n < nb) ? jt * 32 + n : nb - 1;
+      const float* arow = kb + (int64_t)jrow * D + 8 * hh;
+      f32x16 acc = {};
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t) {
+        const float4 x0 = *reinterpret_cast<const float4*>(arow + 16 * t);
+        const float4 x1 = *reinterpret_cast<const float4*>(arow + 16 * t + 4);
+        const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+        bf16x8 a0, a1, a2;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const __bf16 hi = static_cast<__bf16>(xs[e]);
+          const float r1 = xs[e] - static_cast<float>(hi);
+          const __bf16 mid = static_cast<__bf16>(r1);
+          const float r2 = r1 - static_cast<float>(mid);
+          a0[e] = hi;
+          a1[e] = mid;
+          a2[e] = static_cast<__bf16>(r2);
+        }
+        acc = mfma32(a0, qf[t], acc);
+        acc = mfma32(a1, qf[t], acc);
+        acc = mfma32(a2, qf[t], acc);
+      }
+#pragma unroll
+      for (int reg = 0; reg < 16; ++reg) {
+        const int j = jt * 32 + 8 * (reg >> 2) + 4 * hh + (reg & 3);
+        if (j < b) top.insert_ascending(acc[reg], j);
+      }
+    }
+    // Merge the other lane half's list: snapshot it first, since both halves
+    // rewrite their own lists while merging.
+    float os[KM];
+    int oi[KM];
+#pragma unroll
+    for (int t = 0; t < KM; ++t) {
+      os[t] = half_swap(top.s[t]);
+      oi[t] = __shfl_xor(top.i[t], 32);
+    }
+#pragma unroll
+    for (int t = 0; t < KM; ++t) top.insert_any(os[t], oi[t]);
+    top.truncate(kp);
+    top.sort_indices();
+  }
+  if (!valid || hh != 0) return;
+  int32_t* out = sel + (((int64_t)s * H + h) * Lq + r) * topk;
+#pragma unroll
+  for (int t = 0; t < KM + 1; ++t) {
+    if (t < topk) {
+      const int kept = (t < KM) ? top.i[t < KM ? t : 0] : 0;
+      out[t] = t < nkeep ? kept : (t == nkeep ? b : -1);
+    }
+  }
+  for (int t = KM + 1; t < topk; ++t) out[t] = -1;
+}
+
+// fp32 queries: one thread per query, fp32 FMA dot products.
+// grid (ceil(Lq/256), S*H), 256 threads.
+template <int D, int KM>
+__global__ __launch_bounds__(256) void k_gate_topk_f32(
+    const float* __restrict__ q, const float* __restrict__ kbar, int32_t* __restrict__ sel,
+    int64_t Lq, int64_t q_off, int H, int Hkv, int B, int nb, int topk) {
+  const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (r >= Lq) return;
+  const int sh = blockIdx.y, s = sh / H, h = sh % H, g = h / (H / Hkv);
+  const int b = (int)((q_off + r) / B);
+  const int kp = topk - 1;
+  const int nkeep = kp < b ? kp : b;
+  TopList<KM> top;
+  top.init();
+  if (kp > 0) {
+    const float* qrow = q + (((int64_t)s * Lq + r) * H + h) * D;
+    float qr[D];
+#pragma unroll
+    for (int dd = 0; dd < D; dd += 4) {
+      const float4 x = *reinterpret_cast<const float4*>(qrow + dd);
+      qr[dd] = x.x; qr[dd + 1] = x.y; qr[dd + 2] = x.z; qr[dd + 3] = x.w;
+    }
+    const float* kb = kbar + ((int64_t)s * Hkv + g) * nb * D;
+    for (int j = 0; j < b; ++j) {
+      const float* kr = kb + (int64_t)j * D;
+      float acc = 0.f;
+#pragma unroll
+      for (int dd = 0; dd < D; dd += 4) {
+        const float4 x = *reinterpret_cast<const float4*>(kr + dd);
+        acc = fmaf(qr[dd], x.x, acc);
+        acc = fmaf(qr[dd + 1], x.y, acc);
+        acc = fmaf(qr[dd + 2], x.z, acc);
+        acc = fmaf(qr[dd + 3], x.w, acc);
+      }
+      top.insert_ascending(acc, j);
+    }
+    top.truncate(kp);
+    top.sort_indices();
+  }
+  int32_t* out = sel + (((int64_t)s * H + h) * Lq + r) * topk;
+#pragma unroll
+  for (int t = 0; t < KM + 1; ++t) {
+    if (t < topk) {
+      const int kept = (t < KM) ? top.i[t < KM ? t : 0] : 0;
+      out[t] = t < nkeep ? kept : (t == nkeep ? b : -1);
+    }
+  }
+  for (int t = KM + 1; t < topk; ++t) out[t] = -1;
+}
+
+template <int D>
+static hipError_t gate_dispatch_d(const void* q, const float* kbar, int32_t* sel, const Dims& d,
+                                  hipStream_t st) {
+  const int kp = d.topk - 1;
+#define MOBA_GATE_CASE(KMV)                                                                  \
+  if (kp <= KMV) {                                                                           \
+    if (d.bf16) {                                                                            \
+      dim3 grid((unsigned)((d.Lq + 127) / 128), d.S * d.H);                                  \
+      hipLaunchKernelGGL((k_gate_topk_bf16<D, KMV>), grid, dim3(256), 0, st,                 \
+                         static_cast<const bf16_t*>(q), kbar, sel, d.Lq, d.q_off, d.H, d.Hkv, \
+                         d.B, d.nb, d.topk);                                                 \
+    } else {                                                                                 \
+      dim3 grid((unsigned)((d.Lq + 255) / 256), d.S * d.H);                                  \
+      hipLaunchKernelGGL((k_gate_topk_f32<D, KMV>), grid, dim3(256), 0, st,                  \
+                         static_cast<const float*>(q), kbar, sel, d.Lq, d.q_off, d.H, d.Hkv,  \
+                         d.B, d.nb, d.topk);                                                 \
+    }                                                                                        \
+    return hipGetLastError();                                                                \
+  }
+  MOBA_GATE_CASE(1)
+  MOBA_GATE_CASE(2)
+  MOBA_GATE_CASE(4)
+  MOBA_GATE_CASE(8)
+  MOBA_GATE_CASE(12)
+  MOBA_GATE_CASE(16)
+#undef MOBA_GATE_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gate_topk(const void* q, const float* kbar, int32_t* sel, const Dims& d,
+                            hipStream_t st) {
+  if (d.D == 128) return gate_dispatch_d<128>(q, kbar, sel, d, st);
+  return gate_dispatch_d<64>(q, kbar, sel, d, st);
+}
+
+}  // namespace moba

@@ -1,0 +1,68 @@
+// Host-side launch interface of the MoBA kernels (internal to libmoba.so).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moba {
+
+constexpr int kRouteChunkRows = 256;   // query rows per routing chunk (one head)
+constexpr int kRoutedTileM = 128;      // routed entries per attention workgroup
+constexpr int kMaxBlocks = 8192;       // largest supported number of KV blocks
+constexpr int kMaxTopk = 17;           // largest supported topk (16 routed blocks + own)
+
+// Problem dimensions shared by every launch of one call.
+struct Dims {
+  int S = 1;          // batch (sequences)
+  int H = 1;          // query heads
+  int Hkv = 1;        // KV heads
+  int G = 1;          // H / Hkv
+  int D = 128;        // head dim
+  int B = 64;         // block size
+  int topk = 1;       // blocks per query, own block included
+  int kp = 0;         // topk - 1: routed (past) blocks per query at most
+  int nb = 1;         // number of KV blocks
+  int64_t Lq = 1;     // queries per sequence
+  int64_t L = 1;      // keys per sequence
+  int64_t q_off = 0;  // position of query row 0 (L - Lq)
+  bool bf16 = true;   // element type of q, k, v, out
+  // routing
+  int nchunk_r = 1;   // routing chunks per (sequence, head)
+  int ncols = 1;      // G * nchunk_r: columns of the per-bucket count rows
+  int nrows = 1;      // S * Hkv * nb buckets
+  int64_t slots = 0;  // S * H * Lq * kp routed slots
+};
+
+hipError_t launch_block_mean(const void* k, float* kbar, const Dims& d, hipStream_t st);
+hipError_t launch_transpose_v(const void* v, void* vt, const Dims& d, hipStream_t st);
+hipError_t launch_gate_topk(const void* q, const float* kbar, int32_t* sel, const Dims& d,
+                            hipStream_t st);
+hipError_t launch_route_count(const int32_t* sel, uint32_t* counts, const Dims& d,
+                              hipStream_t st);
+hipError_t launch_route_scan_rows(uint32_t* counts, uint32_t* bucket_total, const Dims& d,
+                                  hipStream_t st);
+hipError_t launch_route_scan_buckets(const uint32_t* bucket_total, uint32_t* bucket_off,
+                                     uint32_t* tile_off, const Dims& d, hipStream_t st);
+hipError_t launch_route_scatter(const int32_t* sel, const uint32_t* counts,
+                                const uint32_t* bucket_off, uint32_t* list, const Dims& d,
+                                hipStream_t st);
+// Upper bound of the number of routed tiles (grid size of the routed kernel).
+int64_t routed_tile_bound(const Dims& d);
+hipError_t launch_attn_routed_bf16(const void* q, const void* k, const void* vt,
+                                   const uint32_t* list, const uint32_t* bucket_off,
+                                   const uint32_t* tile_off, void* part_o, float* part_lse,
+                                   const Dims& d, hipStream_t st);
+hipError_t launch_attn_routed_f32(const void* q, const void* k, const void* v,
+                                  const uint32_t* list, const uint32_t* bucket_off,
+                                  const uint32_t* tile_off, void* part_o, float* part_lse,
+                                  const Dims& d, hipStream_t st);
+// mode 0: own block + merge of the routed partials; mode 1: full causal attention.
+// The bf16 form reads V^T [S, Hkv, D, L]; the fp32 form reads V as given.
+hipError_t launch_attn_query_bf16(const void* q, const void* k, const void* vt,
+                                  const void* part_o, const float* part_lse, void* out, int mode,
+                                  const Dims& d, hipStream_t st);
+hipError_t launch_attn_query_f32(const void* q, const void* k, const void* v, const void* part_o,
+                                 const float* part_lse, void* out, int mode, const Dims& d,
+                                 hipStream_t st);
+
+}  // namespace moba

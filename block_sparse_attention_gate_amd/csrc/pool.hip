@@ -1,0 +1,116 @@
+// Block-mean pooling of K and the V layout transform.
+//
+// Block means feed the gate: the MoBA pages divide the context into blocks
+// and gate every query against every block ("MoBA" project card, "How It
+// Works"); the affinity is read here as the dot product with the block's
+// mean key.  The V transform writes V^T [batch, Hkv, D, L] so that the P.V
+// product of the attention kernels reads 8 consecutive keys per lane.
+#include "common.h"
+#include "kernels.h"
+
+namespace moba {
+
+// grid (nb, S, column groups); 256 threads.  Each thread accumulates VEC
+// columns over a strided subset of the block's rows in fp32, then the row
+// slices are summed in a fixed order (deterministic).
+template <typename T>
+__global__ __launch_bounds__(256) void k_block_mean(const T* __restrict__ k,
+                                                    float* __restrict__ kbar, int Hkv, int D,
+                                                    int64_t L, int B, int nb) {
+  constexpr int VEC = 16 / sizeof(T);
+  __shared__ float red[256 * VEC];
+  const int cols = Hkv * D;
+  const int tpr = cols / VEC;
+  const int cw = tpr < 256 ? tpr : 256;  // threads across columns
+  const int RS = 256 / cw;               // row slices
+  const int tid = threadIdx.x;
+  const int ct = tid % cw, rs = tid / cw;
+  const int s = blockIdx.y, j = blockIdx.x;
+  const int col = (blockIdx.z * cw + ct) * VEC;
+  float acc[VEC];
+#pragma unroll
+  for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
+  if (rs < RS && col < cols) {
+    const T* base = k + ((int64_t)s * L + (int64_t)j * B) * cols + col;
+    for (int r = rs; r < B; r += RS) {
+      const u32x4 raw = *reinterpret_cast<const u32x4*>(base + (int64_t)r * cols);
+      const T* e = reinterpret_cast<const T*>(&raw);
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) acc[v] += load_as_f32(e + v);
+    }
+  }
+  const int width = cw * VEC;
+  if (rs < RS) {
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) red[rs * width + ct * VEC + v] = acc[v];
+  }
+  __syncthreads();
+  const float inv = 1.0f / (float)B;
+  for (int e = tid; e < width; e += 256) {
+    const int c = blockIdx.z * width + e;
+    if (c >= cols) continue;
+    float sum = 0.f;
+    for (int r = 0; r < RS; ++r) sum += red[r * width + e];
+    const int g = c / D, dd = c % D;
+    kbar[(((int64_t)s * Hkv + g) * nb + j) * D + dd] = sum * inv;
+  }
+}
+
+hipError_t launch_block_mean(const void* k, float* kbar, const Dims& d, hipStream_t st) {
+  const int cols = d.Hkv * d.D;
+  const int vec = d.bf16 ? 8 : 4;
+  const int tpr = cols / vec;
+  dim3 grid(d.nb, d.S, (tpr + 255) / 256);
+  if (d.bf16)
+    hipLaunchKernelGGL(k_block_mean<bf16_t>, grid, dim3(256), 0, st,
+                       static_cast<const bf16_t*>(k), kbar, d.Hkv, d.D, d.L, d.B, d.nb);
+  else
+    hipLaunchKernelGGL(k_block_mean<float>, grid, dim3(256), 0, st,
+                       static_cast<const float*>(k), kbar, d.Hkv, d.D, d.L, d.B, d.nb);
+  return hipGetLastError();
+}
+
+// V [S, L, Hkv, D] -> V^T [S, Hkv, D, L] (bf16).  grid (L/64, Hkv, S).
+template <int D>
+__global__ __launch_bounds__(256) void k_transpose_v(const bf16_t* __restrict__ v,
+                                                     bf16_t* __restrict__ vt, int Hkv,
+                                                     int64_t L) {
+  constexpr int LD = D + 8;
+  __shared__ bf16_t tile[64 * LD];
+  const int64_t key0 = (int64_t)blockIdx.x * 64;
+  const int g = blockIdx.y, s = blockIdx.z;
+  const int tid = threadIdx.x;
+  constexpr int CPR = D / 8;  // 16-byte chunks per key row
+  for (int c = tid; c < 64 * CPR; c += 256) {
+    const int row = c / CPR, cc = c % CPR;
+    const u32x4 val = *reinterpret_cast<const u32x4*>(
+        v + (((int64_t)s * L + key0 + row) * Hkv + g) * D + cc * 8);
+    *reinterpret_cast<u32x4*>(&tile[row * LD + cc * 8]) = val;
+  }
+  __syncthreads();
+  for (int c = tid; c < D * 8; c += 256) {
+    const int dd = c / 8, kc = c % 8;
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t lo = tile[(kc * 8 + 2 * e) * LD + dd];
+      const uint32_t hi = tile[(kc * 8 + 2 * e + 1) * LD + dd];
+      w[e] = lo | (hi << 16);
+    }
+    *reinterpret_cast<u32x4*>(vt + (((int64_t)s * Hkv + g) * D + dd) * L + key0 + kc * 8) =
+        u32x4{w[0], w[1], w[2], w[3]};
+  }
+}
+
+hipError_t launch_transpose_v(const void* v, void* vt, const Dims& d, hipStream_t st) {
+  dim3 grid((unsigned)(d.L / 64), d.Hkv, d.S);
+  if (d.D == 128)
+    hipLaunchKernelGGL(k_transpose_v<128>, grid, dim3(256), 0, st,
+                       static_cast<const bf16_t*>(v), static_cast<bf16_t*>(vt), d.Hkv, d.L);
+  else
+    hipLaunchKernelGGL(k_transpose_v<64>, grid, dim3(256), 0, st,
+                       static_cast<const bf16_t*>(v), static_cast<bf16_t*>(vt), d.Hkv, d.L);
+  return hipGetLastError();
+}
+
+}  // namespace moba

@@ -1,0 +1,235 @@
+// Query -> KV-block dispatch.
+//
+// The pages liken the gate to an MoE router with the blocks as experts
+// ("MoBA" project card, "How It Works"; AiBoss MoBA article,
+// "MoBAの主な機能": FlashAttention combined with MoE optimisation).  Here
+// every (query, selected PAST block) pair is a routed entry and is regrouped
+// into the bucket of (sequence, KV head, block), so that one attention tile
+// reads one block's K/V for up to 128 routed queries.
+//
+// Entry slot id: ((s*H + h)*Lq + r)*kp + t for the t-th past block of query
+// row r of head h (kp = topk - 1).  Buckets are ordered (s, g, j); inside a
+// bucket entries are in ascending slot id (stable counting sort):
+//   1. route_count: per routing chunk (one head, 256 query rows) an LDS
+//      histogram over the blocks, written to counts[bucket][column];
+//   2. route_scan_rows: exclusive scan of each bucket's columns (LDS scan);
+//   3. route_scan_buckets: exclusive scan over buckets -> bucket offsets and
+//      attention-tile offsets;
+//   4. route_scatter: each chunk replays its entries in order; a wave ranks
+//      equal buckets among its lanes with ballots and writes the slot ids.
+#include "common.h"
+#include "kernels.h"
+
+namespace moba {
+
+struct RouteArgs {
+  int64_t Lq, q_off;
+  int H, Hkv, G, B, nb, topk, kp, nchunk_r, ncols, nchunks, nbits;
+};
+
+static RouteArgs route_args(const Dims& d) {
+  RouteArgs a;
+  a.Lq = d.Lq; a.q_off = d.q_off; a.H = d.H; a.Hkv = d.Hkv; a.G = d.G; a.B = d.B;
+  a.nb = d.nb; a.topk = d.topk; a.kp = d.kp; a.nchunk_r = d.nchunk_r; a.ncols = d.ncols;
+  a.nchunks = d.S * d.H * d.nchunk_r;
+  int bits = 0;
+  while ((1 << bits) < d.nb) ++bits;
+  a.nbits = bits;
+  return a;
+}
+
+// Chunk ci -> (s, h, c); one wave per chunk, 4 waves per workgroup.
+__device__ __forceinline__ void chunk_coords(const RouteArgs& a, int ci, int& s, int& h, int& c) {
+  c = ci % a.nchunk_r;
+  const int sh = ci / a.nchunk_r;
+  h = sh % a.H;
+  s = sh / a.H;
+}
+
+__global__ __launch_bounds__(256) void k_route_count(const int32_t* __restrict__ sel,
+                                                     uint32_t* __restrict__ counts, RouteArgs a) {
+  extern __shared__ uint32_t lds_hist[];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int ci = blockIdx.x * 4 + w;
+  if (ci >= a.nchunks) return;
+  uint32_t* hist = lds_hist + w * a.nb;
+  for (int j = lane; j < a.nb; j += 64) hist[j] = 0;
+  int s, h, c;
+  chunk_coords(a, ci, s, h, c);
+  const int64_t r0 = (int64_t)c * kRouteChunkRows;
+  const int64_t rows = (a.Lq - r0 < kRouteChunkRows) ? a.Lq - r0 : kRouteChunkRows;
+  const int total = (int)rows * a.kp;
+  const int32_t* selh = sel + ((int64_t)s * a.H + h) * a.Lq * a.topk;
+  for (int e = lane; e < total; e += 64) {
+    const int64_t r = r0 + e / a.kp;
+    const int t = e % a.kp;
+    const int own = (int)((a.q_off + r) / a.B);
+    if (t < own) {  // t < min(kp, own) since t < kp
+      const int j = selh[r * a.topk + t];
+      if (j >= 0 && j < own) atomicAdd(&hist[j], 1u);  // same predicate as the scatter
+    }
+  }
+  const int g = h / a.G;
+  const int col = (h - g * a.G) * a.nchunk_r + c;
+  for (int j = lane; j < a.nb; j += 64) {
+    const int64_t row = ((int64_t)s * a.Hkv + g) * a.nb + j;
+    counts[row * a.ncols + col] = hist[j];
+  }
+}
+
+// Workgroup-wide exclusive scan of one value per thread (256 threads).
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, uint32_t& total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  uint32_t incl = v;
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) wsum[w] = incl;
+  __syncthreads();
+  uint32_t before = 0;
+  for (int i = 0; i < w; ++i) before += wsum[i];
+  total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+  __syncthreads();
+  return before + incl - v;
+}
+
+__global__ __launch_bounds__(256) void k_route_scan_rows(uint32_t* __restrict__ counts,
+                                                         uint32_t* __restrict__ bucket_total,
+                                                         int ncols) {
+  __shared__ uint32_t wsum[4];
+  uint32_t* p = counts + (int64_t)blockIdx.x * ncols;
+  uint32_t carry = 0;
+  for (int base = 0; base < ncols; base += 1024) {
+    const int i0 = base + threadIdx.x * 4;
+    uint32_t v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = (i0 + e < ncols) ? p[i0 + e] : 0u;
+    const uint32_t tsum = v[0] + v[1] + v[2] + v[3];
+    uint32_t seg;
+    const uint32_t ex = block_excl_scan(tsum, wsum, seg);
+    uint32_t run = carry + ex;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (i0 + e < ncols) p[i0 + e] = run;
+      run += v[e];
+    }
+    carry += seg;
+  }
+  if (threadIdx.x == 0) bucket_total[blockIdx.x] = carry;
+}
+
+__global__ __launch_bounds__(256) void k_route_scan_buckets(const uint32_t* __restrict__ total,
+                                                            uint32_t* __restrict__ bucket_off,
+                                                            uint32_t* __restrict__ tile_off,
+                                                            int nrows, int tile_m) {
+  __shared__ uint32_t wsum[4];
+  uint32_t carry_e = 0, carry_t = 0;
+  for (int base = 0; base < nrows; base += 256) {
+    const int i = base + threadIdx.x;
+    const uint32_t e = i < nrows ? total[i] : 0u;
+    const uint32_t t = (e + tile_m - 1) / tile_m;
+    uint32_t seg_e, seg_t;
+    const uint32_t ex_e = block_excl_scan(e, wsum, seg_e);
+    const uint32_t ex_t = block_excl_scan(t, wsum, seg_t);
+    if (i < nrows) {
+      bucket_off[i] = carry_e + ex_e;
+      tile_off[i] = carry_t + ex_t;
+    }
+    carry_e += seg_e;
+    carry_t += seg_t;
+  }
+  if (threadIdx.x == 0) {
+    bucket_off[nrows] = carry_e;
+    tile_off[nrows] = carry_t;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_route_scatter(const int32_t* __restrict__ sel,
+                                                       const uint32_t* __restrict__ counts,
+                                                       const uint32_t* __restrict__ bucket_off,
+                                                       uint32_t* __restrict__ list, RouteArgs a) {
+  extern __shared__ uint32_t lds_cur[];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int ci = blockIdx.x * 4 + w;
+  if (ci >= a.nchunks) return;
+  uint32_t* cur = lds_cur + w * a.nb;
+  int s, h, c;
+  chunk_coords(a, ci, s, h, c);
+  const int g = h / a.G;
+  const int col = (h - g * a.G) * a.nchunk_r + c;
+  for (int j = lane; j < a.nb; j += 64) {
+    const int64_t row = ((int64_t)s * a.Hkv + g) * a.nb + j;
+    cur[j] = bucket_off[row] + counts[row * a.ncols + col];
+  }
+  const int64_t r0 = (int64_t)c * kRouteChunkRows;
+  const int64_t rows = (a.Lq - r0 < kRouteChunkRows) ? a.Lq - r0 : kRouteChunkRows;
+  const int total = (int)rows * a.kp;
+  const int32_t* selh = sel + ((int64_t)s * a.H + h) * a.Lq * a.topk;
+  const uint64_t slot_base = (((uint64_t)s * a.H + h) * a.Lq + r0) * a.kp;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
+  for (int base = 0; base < total; base += 64) {
+    const int e = base + lane;
+    bool valid = e < total;
+    int j = 0;
+    if (valid) {
+      const int64_t r = r0 + e / a.kp;
+      const int t = e % a.kp;
+      const int own = (int)((a.q_off + r) / a.B);
+      valid = t < own;
+      if (valid) j = selh[r * a.topk + t];
+      valid = valid && j >= 0 && j < own;  // same predicate as the count
+      if (!valid) j = 0;
+    }
+    uint64_t peers = __ballot(valid);
+    for (int bit = 0; bit < a.nbits; ++bit) {
+      const bool set = (j >> bit) & 1;
+      const uint64_t bb = __ballot(valid && set);
+      peers &= set ? bb : ~bb;
+    }
+    const uint32_t rank = (uint32_t)__popcll(peers & lt_mask);
+    if (valid) list[cur[j] + rank] = (uint32_t)(slot_base + (uint64_t)e);
+    __asm__ volatile("" ::: "memory");
+    if (valid && rank == 0) cur[j] += (uint32_t)__popcll(peers);
+    __asm__ volatile("" ::: "memory");
+  }
+}
+
+hipError_t launch_route_count(const int32_t* sel, uint32_t* counts, const Dims& d,
+                              hipStream_t st) {
+  const RouteArgs a = route_args(d);
+  const unsigned grid = (unsigned)((a.nchunks + 3) / 4);
+  hipLaunchKernelGGL(k_route_count, dim3(grid), dim3(256), 4 * d.nb * sizeof(uint32_t), st, sel,
+                     counts, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_scan_rows(uint32_t* counts, uint32_t* bucket_total, const Dims& d,
+                                  hipStream_t st) {
+  hipLaunchKernelGGL(k_route_scan_rows, dim3(d.nrows), dim3(256), 0, st, counts, bucket_total,
+                     d.ncols);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_scan_buckets(const uint32_t* bucket_total, uint32_t* bucket_off,
+                                     uint32_t* tile_off, const Dims& d, hipStream_t st) {
+  hipLaunchKernelGGL(k_route_scan_buckets, dim3(1), dim3(256), 0, st, bucket_total, bucket_off,
+                     tile_off, d.nrows, kRoutedTileM);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_scatter(const int32_t* sel, const uint32_t* counts,
+                                const uint32_t* bucket_off, uint32_t* list, const Dims& d,
+                                hipStream_t st) {
+  const RouteArgs a = route_args(d);
+  const unsigned grid = (unsigned)((a.nchunks + 3) / 4);
+  hipLaunchKernelGGL(k_route_scatter, dim3(grid), dim3(256), 4 * d.nb * sizeof(uint32_t), st,
+                     sel, counts, bucket_off, list, a);
+  return hipGetLastError();
+}
+
+int64_t routed_tile_bound(const Dims& d) {
+  return (d.slots + kRoutedTileM - 1) / kRoutedTileM + d.nrows;
+}
+
+}  // namespace moba

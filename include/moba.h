@@ -1,0 +1,155 @@
+/*
+ * moba.h -- C ABI of the MI355X (gfx950) MoBA forward library (libmoba.so).
+ *
+ * MoBA (Mixture of Block Attention) splits the keys and values into blocks of
+ * a fixed size, scores every query against every block with a parameter-less
+ * gate, keeps the top-k blocks per query token and runs softmax attention over
+ * the kept blocks only ("MoBA" project card, sourcepulse, "How It Works" and
+ * "Highlighted Details": the two knobs "MoBA Block" and "MoBA Topk").  A query
+ * never reads a future block and its own block is causally masked ("MoBA -
+ * Moonshot AIが提案した新しいアテンションメカニズム", aiboss88, section
+ * "MoBAの技術的原則", causality design).  The gate's affinity and the other
+ * points the pages leave open are fixed as follows:
+ *
+ *   - score(query q, block j) = q . mean of the block's keys (unscaled);
+ *   - the query's own block always counts as one of the k selected blocks;
+ *     the other k-1 are its best past blocks, ties to the lower index;
+ *   - the output is one softmax over the union of the selected keys, scale
+ *     1/sqrt(head_dim), causal diagonal inclusive;
+ *   - GQA: query head h reads KV head h / (n_heads / n_kv_heads); each query
+ *     head gates on its own;
+ *   - query row r of a sequence sits at position kv_len - q_len + r.
+ *   - topk >= number of blocks is full causal attention.
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers, contiguous, 16-byte aligned.
+ *     Layouts are row-major with head_dim innermost:
+ *       q, out   [batch, q_len, n_heads, head_dim]
+ *       k, v     [batch, kv_len, n_kv_heads, head_dim]
+ *     (batch 1 with q_len == kv_len == seq_len for the plain calls.)
+ *   - Element type is given by `dtype`; out has the input type (bf16 output
+ *     is rounded to nearest even from fp32).  Accumulation is fp32.
+ *   - The caller owns every buffer.  Inputs are read only; `out` (and
+ *     `sel_out` when given) are fully overwritten.  The library keeps no
+ *     pointer after the queued work completes.
+ *   - Every call only enqueues work on `stream` (a hipStream_t; NULL is the
+ *     default stream) and returns; there is no host synchronisation inside.
+ *   - All argument checks run before anything is enqueued: a call that
+ *     returns an error has enqueued nothing and written nothing.
+ *     MOBA_ERR_INVALID_ARGUMENT: null required pointer, size < 1,
+ *       n_heads % n_kv_heads != 0, q_len > kv_len, size overflow, workspace
+ *       too small.
+ *     MOBA_ERR_UNSUPPORTED: head_dim not 64 or 128, block_size not a multiple
+ *       of 64, kv_len not a multiple of block_size, topk > 17, more than 8192
+ *       blocks, or more than 2^32 routed slots.
+ *     MOBA_ERR_OUT_OF_MEMORY: the internal workspace could not be allocated.
+ *     MOBA_ERR_HIP: a HIP launch or runtime call failed.  Faults inside the
+ *       kernels surface at the caller's next synchronisation.
+ *   - moba_last_error() returns a thread-local text for the last failure.
+ *   - Concurrent calls on different streams are safe; the profiling switch
+ *     below is process-wide and not meant for concurrent use.
+ */
+#ifndef MOBA_H_
+#define MOBA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOBA_ABI_VERSION 1
+
+typedef enum { MOBA_DTYPE_F32 = 0, MOBA_DTYPE_BF16 = 1 } moba_dtype;
+
+typedef enum {
+  MOBA_OK = 0,
+  MOBA_ERR_INVALID_ARGUMENT = 1,
+  MOBA_ERR_UNSUPPORTED = 2,
+  MOBA_ERR_OUT_OF_MEMORY = 3,
+  MOBA_ERR_HIP = 4
+} moba_status;
+
+/*
+ * MoBA prefill forward for one sequence (batch 1, q_len == kv_len == seq_len):
+ * out[i, h, :] = softmax over the selected keys of query i, head h.
+ * Allocates its workspace stream-ordered (hipMallocAsync / hipFreeAsync).
+ */
+moba_status moba_forward(const void* q, const void* k, const void* v, int64_t seq_len,
+                         int32_t n_heads, int32_t n_kv_heads, int32_t head_dim,
+                         int32_t block_size, int32_t topk, void* out, moba_dtype dtype,
+                         void* stream);
+
+/*
+ * Full causal attention (every key t <= position), the topk = all comparator
+ * of the sparse/full switch.  No workspace for bf16 beyond a transposed copy
+ * of V, allocated stream-ordered.
+ */
+moba_status moba_full_attention(const void* q, const void* k, const void* v, int64_t seq_len,
+                                int32_t n_heads, int32_t n_kv_heads, int32_t head_dim,
+                                void* out, moba_dtype dtype, void* stream);
+
+/* General form: batches, q_len <= kv_len (decode q_len = 1), precomputed block
+ * means, the selection as an output, and a caller workspace. */
+typedef struct moba_args {
+  size_t struct_size;          /* = sizeof(moba_args) */
+  const void* q;               /* [batch, q_len, n_heads, head_dim] */
+  const void* k;               /* [batch, kv_len, n_kv_heads, head_dim] */
+  const void* v;               /* [batch, kv_len, n_kv_heads, head_dim] */
+  void* out;                   /* [batch, q_len, n_heads, head_dim] */
+  const float* k_block_mean;   /* nullable: fp32 [batch, n_kv_heads, nb, head_dim]
+                                  from moba_block_mean; computed when NULL */
+  int32_t* sel_out;            /* nullable: int32 [batch, n_heads, q_len, topk];
+                                  selected blocks ascending, -1 padded */
+  int32_t batch;
+  int32_t n_heads, n_kv_heads, head_dim, block_size, topk;
+  int64_t q_len, kv_len;
+  moba_dtype dtype;
+  void* workspace;             /* nullable: device scratch of at least
+                                  moba_workspace_size(args) bytes; when NULL the
+                                  library allocates it stream-ordered */
+  size_t workspace_bytes;
+  void* stream;                /* hipStream_t, NULL = default stream */
+} moba_args;
+
+moba_status moba_forward_ex(const moba_args* a);
+/* Full attention in the general form; block_size, topk, k_block_mean and
+ * sel_out are ignored. */
+moba_status moba_full_attention_ex(const moba_args* a);
+
+/* Workspace bytes moba_forward_ex / moba_full_attention_ex need for `a`
+ * (0 for an invalid argument set; read moba_last_error()). */
+size_t moba_workspace_size(const moba_args* a);
+size_t moba_full_workspace_size(const moba_args* a);
+
+/* Block-mean keys: k_block_mean[s, g, j, :] = mean of k[s, t, g, :] over the
+ * block_size keys of block j (fp32 accumulation).  The decode path reuses it
+ * across calls on the same cache. */
+moba_status moba_block_mean(const void* k, int32_t batch, int64_t kv_len, int32_t n_kv_heads,
+                            int32_t head_dim, int32_t block_size, float* k_block_mean,
+                            moba_dtype dtype, void* stream);
+
+const char* moba_status_string(moba_status s);
+const char* moba_last_error(void);
+int32_t moba_abi_version(void);
+
+/*
+ * Per-kernel timing for measurement.  While enabled, every kernel the library
+ * launches is bracketed by HIP events on the launch stream.  moba_profile_read
+ * waits for the recorded events and returns, for the kernel named `name`, the
+ * summed duration in milliseconds and the number of launches since the last
+ * reset.  Names: "block_mean", "transpose_v", "gate_topk", "route_count",
+ * "route_scan_rows", "route_scan_buckets", "route_scatter", "attn_routed",
+ * "attn_own_merge", "attn_full", "decode_gate", "decode_attn",
+ * "decode_merge".  Unknown names give MOBA_ERR_INVALID_ARGUMENT.
+ */
+moba_status moba_profile_enable(int32_t on);
+moba_status moba_profile_reset(void);
+moba_status moba_profile_read(const char* name, double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOBA_H_ */

@@ -1,0 +1,115 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/moba.h declares, and rejects bad arguments before touching HIP."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "block_sparse_attention_gate_amd", "libmoba.so")
+HEADER = os.path.join(ROOT, "include", "moba.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libmoba.so not built")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(moba_[a-z0-9_]+)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(LIB)
+    names = _declared_functions()
+    assert len(names) >= 13, names
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in moba.h but not exported"
+
+
+def test_binding_covers_the_header():
+    import block_sparse_attention_gate_amd as moba
+    assert set(_declared_functions()) <= set(moba.EXPORTED)
+    for n in _declared_functions():
+        assert hasattr(moba, n), n
+
+
+def test_version_and_status_strings():
+    import block_sparse_attention_gate_amd as moba
+    assert moba.moba_abi_version() == 1
+    assert moba.moba_status_string(0) == "MOBA_OK"
+    assert moba.moba_status_string(2) == "MOBA_ERR_UNSUPPORTED"
+    assert moba.moba_status_string(99) == "MOBA_STATUS_UNKNOWN"
+
+
+def _args(**kw):
+    import block_sparse_attention_gate_amd as moba
+    a = moba.MobaArgs()
+    a.struct_size = ctypes.sizeof(moba.MobaArgs)
+    fake = 1 << 40   # never dereferenced: every case fails validation first
+    a.q = a.k = a.v = a.out = fake
+    a.batch, a.n_heads, a.n_kv_heads, a.head_dim = 1, 32, 8, 128
+    a.block_size, a.topk = 4096, 12
+    a.q_len = a.kv_len = 1 << 20
+    a.dtype = moba.MOBA_DTYPE_BF16
+    for k_, v_ in kw.items():
+        setattr(a, k_, v_)
+    return a
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("q", 0, 1), ("head_dim", 96, 2), ("block_size", 100, 2), ("block_size", 0, 1),
+    ("topk", 0, 1), ("topk", 18, 2), ("n_kv_heads", 5, 1), ("q_len", 0, 1),
+    ("dtype", 7, 2), ("kv_len", (1 << 20) + 64, 1), ("struct_size", 8, 1),
+])
+def test_validation_rejects_before_any_launch(field, value, status):
+    import block_sparse_attention_gate_amd as moba
+    a = _args(**{field: value})
+    if field == "kv_len":      # q_len > kv_len is invalid; also not a block multiple
+        a.q_len = value + 64
+    st = moba._lib.moba_forward_ex(ctypes.byref(a))
+    assert st == status, (field, value, st, moba.moba_last_error())
+    assert moba.moba_last_error()
+
+
+def test_workspace_size_of_the_1m_prefill():
+    """Workspace for 1M tokens, 32/8 heads, block 4096, top-k 12: V^T, block
+    means, selection, routing tables and the routed partials (bf16 o + fp32
+    lse per slot) -- about 100 GB, within one GPU's 288 GB."""
+    import block_sparse_attention_gate_amd as moba
+    a = _args()
+    n = moba._lib.moba_workspace_size(ctypes.byref(a))
+    slots = 32 * (1 << 20) * 11
+    expect_min = (1 << 20) * 8 * 128 * 2 + slots * (128 * 2 + 4 + 4)
+    assert expect_min <= n <= expect_min * 1.1, n
+    bad = _args(head_dim=96)
+    assert moba._lib.moba_workspace_size(ctypes.byref(bad)) == 0
+    assert "head_dim" in moba.moba_last_error()
+
+
+def test_too_small_workspace_is_rejected():
+    import block_sparse_attention_gate_amd as moba
+    a = _args()
+    a.workspace = 1 << 41
+    a.workspace_bytes = 1024
+    assert moba._lib.moba_forward_ex(ctypes.byref(a)) == moba.MOBA_ERR_INVALID_ARGUMENT
+    assert "workspace too small" in moba.moba_last_error()
+
+
+def test_python_binding_rejects_host_tensors():
+    import torch
+    import block_sparse_attention_gate_amd as moba
+    q = torch.zeros(128, 1, 64)
+    with pytest.raises(ValueError):
+        moba.moba_forward(q, q, q, 64, 2)
+
+
+def test_profile_names():
+    import block_sparse_attention_gate_amd as moba
+    for n in moba.KERNEL_NAMES:
+        assert moba.moba_profile_read(n) == (0.0, 0)
+    with pytest.raises(ValueError):
+        moba.moba_profile_read("nope")

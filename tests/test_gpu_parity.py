@@ -1,0 +1,220 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import moba_inputs
+from oracle import moba_oracle as O
+from tests.parity import (check_outputs, check_selection, device_fetch, host_fetch,
+                          sample_rows, to64)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _moba():
+    import block_sparse_attention_gate_amd as moba
+    return moba
+
+
+def _run_case(w, n_uniform=None, seed=0):
+    """Parity run of one workload: every row when n_uniform is None, else a
+    sample of rows (block edges + n_uniform uniform rows) for outputs."""
+    moba = _moba()
+    print(f"case {w}", flush=True)
+    q, k, v = moba_inputs.make_inputs(w, device=DEV)
+    out, sel = moba.moba_forward_ex(q, k, v, w.block_size, w.topk, return_selection=True)
+    torch.cuda.synchronize()
+    batched = q.dim() == 4
+    qs = [q] if not batched else list(q)
+    ks = [k] if not batched else list(k)
+    vs = [v] if not batched else list(v)
+    outs = [out] if not batched else list(out)
+    sels = [sel] if not batched else list(sel)
+    rng = np.random.default_rng(seed)
+    for s in range(len(qs)):
+        qh, kh, vh = to64(qs[s]), to64(ks[s]), to64(vs[s])
+        Lq, H = qh.shape[0], qh.shape[1]
+        q_off = kh.shape[0] - Lq
+        positions = q_off + np.arange(Lq)
+        kbar = O.block_mean(kh, w.block_size)
+        sel_np = sels[s].cpu().numpy()
+        ntie, _ = check_selection(qh, positions, kbar, sel_np, w.block_size, w.topk)
+        rows = np.arange(Lq) if n_uniform is None else sample_rows(Lq, w.block_size, q_off,
+                                                                   n_uniform, rng)
+        pairs = [(h, r) for h in range(H) for r in rows]
+        emax, emean = check_outputs(to64(outs[s]), qh, positions, sel_np, w.block_size,
+                                    kh.shape[0], w.dtype, pairs, host_fetch(kh, vh),
+                                    kh.shape[1])
+        print(f"  seq {s}: tie-window {ntie}, max|err| {emax:.2e} mean|err| {emean:.2e}")
+    return q, k, v, out, sel
+
+
+def _run_large(w, n_sel_rows, n_out_rows, heads_out, n_edge_rows=32, seed=0):
+    """Full-size workload in the launch configuration the benchmark times:
+    selection checked on a row sample for every head, outputs on block-edge
+    and uniform rows of a few heads; K and V rows are fetched per query."""
+    moba = _moba()
+    print(f"case {w}", flush=True)
+    q, k, v = moba_inputs.make_inputs(w, device=DEV)
+    out, sel = moba.moba_forward_ex(q, k, v, w.block_size, w.topk, return_selection=True)
+    torch.cuda.synchronize()
+    print("  forward done", flush=True)
+    rng = np.random.default_rng(seed)
+    L = k.shape[0]
+    kbar = O.block_mean(to64(k), w.block_size)
+    print("  oracle block means done", flush=True)
+    edges = sample_rows(L, w.block_size, 0, 0, rng)
+    out_pick = np.unique(np.concatenate([
+        rng.choice(edges, size=min(n_edge_rows, edges.size), replace=False),
+        rng.integers(0, L, size=n_out_rows), [L - 1]]))
+    rows = np.unique(np.concatenate([edges, out_pick, rng.integers(0, L, size=n_sel_rows)]))
+    idx = torch.from_numpy(rows).to(DEV)
+    q_rows = to64(q.index_select(0, idx))
+    sel_rows = sel.index_select(1, idx).cpu().numpy()
+    ntie, gap = check_selection(q_rows, rows, kbar, sel_rows, w.block_size, w.topk)
+    print(f"  selection ok on {rows.size} rows x {q.shape[1]} heads, tie-window {ntie}",
+          flush=True)
+    out_rows = to64(out.index_select(0, idx))
+    where = np.searchsorted(rows, out_pick)
+    pairs = [(h, int(n)) for h in heads_out for n in where]
+    emax, emean = check_outputs(out_rows, q_rows, rows, sel_rows, w.block_size, L, w.dtype,
+                                pairs, device_fetch(k, v), k.shape[1])
+    print(f"  outputs ok on {len(pairs)} pairs: max|err| {emax:.2e} mean|err| {emean:.2e}")
+
+
+SMALL = [
+    moba_inputs.custom("h1_1k", "bf16", 1, 1024, None, 1, 1, 128, 64, 3, 21),
+    moba_inputs.custom("gqa_ragged", "bf16", 1, 960, None, 4, 2, 128, 64, 4, 22),
+    moba_inputs.custom("d64", "bf16", 1, 512, None, 2, 2, 64, 128, 2, 23),
+    moba_inputs.custom("local_k1", "bf16", 1, 640, None, 2, 1, 128, 64, 1, 24),
+    moba_inputs.custom("g8", "bf16", 1, 1024, None, 8, 1, 128, 128, 5, 25),
+    moba_inputs.custom("k12_nb32", "bf16", 1, 2048, None, 4, 1, 128, 64, 12, 26),
+    moba_inputs.custom("f32_d128", "f32", 1, 512, None, 2, 1, 128, 64, 3, 27),
+    moba_inputs.custom("f32_gqa", "f32", 1, 768, None, 4, 2, 64, 64, 4, 28),
+    moba_inputs.WORKLOADS["tiny_f32_1k"],
+]
+
+
+@pytest.mark.parametrize("w", SMALL, ids=[w.name for w in SMALL])
+def test_small_parity(w):
+    _run_case(w)
+
+
+def test_chunked_and_batched_queries():
+    """q_len < kv_len (queries at the end of the cache), batch 2, ragged q_len."""
+    w = moba_inputs.custom("batch2_q100", "bf16", 2, 100, 1024, 4, 2, 128, 64, 3, 31)
+    _run_case(w)
+    w1 = moba_inputs.custom("decode_q1", "bf16", 3, 1, 2048, 4, 1, 128, 128, 4, 32)
+    _run_case(w1)
+
+
+def test_topk_all_equals_full_attention():
+    """topk >= number of blocks is full causal attention, on the GPU too."""
+    moba = _moba()
+    w = moba_inputs.custom("full_switch", "bf16", 1, 1024, None, 2, 1, 128, 64, 17, 33)
+    q, k, v, out, sel = _run_case(w, n_uniform=64)
+    full = moba.moba_full_attention(q, k, v)
+    torch.cuda.synchronize()
+    d = (out.float() - full.float()).abs()
+    assert d.max().item() <= 2e-2 and d.mean().item() <= 2e-3
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_full_attention_parity(dtype):
+    moba = _moba()
+    w = moba_inputs.custom("full_" + dtype, dtype, 1, 1024 if dtype == "bf16" else 512, None,
+                           4, 2, 128, 64, 1, 34)
+    q, k, v = moba_inputs.make_inputs(w, device=DEV)
+    out = moba.moba_full_attention(q, k, v)
+    torch.cuda.synchronize()
+    qh, kh, vh = to64(q), to64(k), to64(v)
+    ref = O.full_reference(qh, kh, vh)
+    err = np.abs(to64(out) - ref)
+    tmax, tmean = {"bf16": (2e-2, 2e-3), "f32": (1e-4, 1e-4)}[dtype]
+    print(f"full {dtype}: max {err.max():.2e} mean {err.mean():.2e}")
+    assert err.max() <= tmax and err.mean() <= tmean
+
+
+def test_duplicate_block_tie_goes_to_lower_index():
+    """An exact copy of block 2 in block 5 ties exactly in the gate; the GPU
+    computes identical scores for both and must keep block 2."""
+    moba = _moba()
+    L, B, D = 512, 64, 128
+    g = torch.Generator(device="cpu").manual_seed(41)
+    q = torch.randn(L, 1, D, generator=g)
+    k = torch.randn(L, 1, D, generator=g) * 0.1
+    u = q[-1, 0] / q[-1, 0].norm()
+    k[2 * B:3 * B, 0] = u * 5.0 + k[2 * B:3 * B, 0] * 0.01
+    k[5 * B:6 * B] = k[2 * B:3 * B]
+    v = torch.randn(L, 1, D, generator=g)
+    qb, kb, vb = (t.to(torch.bfloat16).to(DEV) for t in (q, k, v))
+    out, sel = moba.moba_forward_ex(qb, kb, vb, B, 2, return_selection=True)
+    torch.cuda.synchronize()
+    assert sel[0, L - 1].tolist() == [2, 7]
+
+
+def test_run_to_run_bitwise_determinism():
+    moba = _moba()
+    w = moba_inputs.custom("det", "bf16", 1, 2048, None, 4, 2, 128, 128, 4, 35)
+    q, k, v = moba_inputs.make_inputs(w, device=DEV)
+    o1, s1 = moba.moba_forward_ex(q, k, v, w.block_size, w.topk, return_selection=True)
+    o2, s2 = moba.moba_forward_ex(q, k, v, w.block_size, w.topk, return_selection=True)
+    o3 = moba.moba_forward(q, k, v, w.block_size, w.topk)
+    torch.cuda.synchronize()
+    assert torch.equal(s1, s2)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(o1.view(torch.int16), o3.view(torch.int16))
+
+
+def test_micro_32k_parity():
+    """The 32K single-head shape (block 2048, top-k 3): every selection, and
+    outputs for block-edge and uniform rows."""
+    _run_case(moba_inputs.WORKLOADS["micro_32k"], n_uniform=2048)
+
+
+def test_error_paths_enqueue_nothing():
+    moba = _moba()
+    q = torch.zeros(256, 2, 96, dtype=torch.bfloat16, device=DEV)
+    k = torch.zeros(256, 1, 96, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(ValueError, match="UNSUPPORTED"):
+        moba.moba_forward(q, k, k, 64, 3)
+    q = torch.zeros(256, 2, 128, dtype=torch.bfloat16, device=DEV)
+    k = torch.zeros(256, 1, 128, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(ValueError, match="UNSUPPORTED"):
+        moba.moba_forward(q, k, k, 96, 3)
+    with pytest.raises(ValueError, match="workspace too small"):
+        moba.moba_forward_ex(q, k, k, 64, 3,
+                             workspace=torch.empty(16, dtype=torch.uint8, device=DEV))
+
+
+def test_llama8b_128k_parity_sampled():
+    """Llama-3.1-8B layer shape at 128K (32/8 heads, block 4096, top-k 12)."""
+    _run_large(moba_inputs.WORKLOADS["llama8b_128k"], n_sel_rows=8192, n_out_rows=32,
+               heads_out=(0, 5, 31), n_edge_rows=32)
+
+
+def test_prefill_1m_parity_sampled():
+    """The 1M-token prefill (32/8 heads, block 4096, top-k 12), sampled."""
+    _run_large(moba_inputs.WORKLOADS["prefill_1m"], n_sel_rows=4096, n_out_rows=24,
+               heads_out=(0, 17), n_edge_rows=24)
+
+
+def test_full_attention_32k_sampled():
+    """Full causal attention at the 32K single-head shape, sampled rows."""
+    moba = _moba()
+    w = moba_inputs.WORKLOADS["micro_32k"]
+    q, k, v = moba_inputs.make_inputs(w, device=DEV)
+    out = moba.moba_full_attention(q, k, v)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    rows = sample_rows(q.shape[0], 4096, 0, 48, rng)
+    idx = torch.from_numpy(rows).to(DEV)
+    q_rows = to64(q.index_select(0, idx))
+    out_rows = to64(out.index_select(0, idx))
+    pairs = [(0, n) for n in range(rows.size)]
+    emax, emean = check_outputs(out_rows, q_rows, rows, None, w.block_size, q.shape[0],
+                                "bf16", pairs, device_fetch(k, v), 1, full=True)
+    print(f"full 32K: max {emax:.2e} mean {emean:.2e}")
