@@ -222,6 +222,12 @@ def main():
     ap.add_argument("--skip-1m", action="store_true", help="skip the 1M-token prefill")
     ap.add_argument("--skip-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--workload", default=None,
+                    help="time only this prefill workload's MoBA forward (profiling runs)")
+    ap.add_argument("--no-full", action="store_true", help="with --workload: skip full attention")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="with --workload: also run a plain device copy of this many MiB "
+                         "(reference for the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -233,6 +239,24 @@ def main():
     import moba_inputs
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.workload:
+        if args.calib_copy_mib:
+            n = args.calib_copy_mib << 20
+            src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+            dst = torch.empty_like(src)
+            for _ in range(2):
+                dst.copy_(src)
+            torch.cuda.synchronize()
+            log(f"[bench] calibration copy of {args.calib_copy_mib} MiB done")
+            del src, dst
+        w = moba_inputs.WORKLOADS[args.workload]
+        r = run_prefill(moba, w, args.steps, args.warmup, full_steps=1, full_warmup=0,
+                        with_full=not args.no_full)
+        r["roofline"] = roofline(r)
+        r.pop("_roofline_src")
+        print(json.dumps({"workload": w.name, "steps": args.steps, "warmup": args.warmup,
+                          "detail": r}), flush=True)
+        return
     w = moba_inputs.WORKLOADS["micro_32k"]
     main_res = run_prefill(moba, w, args.steps, args.warmup, full_steps=args.steps,
                            full_warmup=args.warmup)

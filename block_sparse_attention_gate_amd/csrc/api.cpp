@@ -32,12 +32,12 @@ moba_status fail(moba_status s, const char* fmt, ...) {
 // ---------------------------------------------------------------- profiling
 enum KernelId {
   K_BLOCK_MEAN, K_TRANSPOSE_V, K_GATE, K_RCOUNT, K_RSCAN_ROWS, K_RSCAN_BUCKETS, K_RSCATTER,
-  K_ATTN_ROUTED, K_ATTN_OWN, K_ATTN_FULL, K_DEC_GATE, K_DEC_ATTN, K_DEC_MERGE, K_COUNT
+  K_ATTN_ROUTED, K_ATTN_OWN, K_ATTN_FULL, K_DEC_PLAN, K_DEC_ATTN, K_DEC_MERGE, K_COUNT
 };
 const char* const kKernelNames[K_COUNT] = {
     "block_mean", "transpose_v", "gate_topk", "route_count", "route_scan_rows",
     "route_scan_buckets", "route_scatter", "attn_routed", "attn_own_merge", "attn_full",
-    "decode_gate", "decode_attn", "decode_merge"};
+    "decode_plan", "decode_attn", "decode_merge"};
 
 struct ProfRecord {
   int id;
@@ -99,9 +99,10 @@ size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct Plan {
   Dims d;
-  bool need_kbar = false, need_vt = false, need_sel = false, routed = false;
+  bool need_kbar = false, need_vt = false, need_sel = false, routed = false, decode = false;
   size_t off_kbar = 0, off_vt = 0, off_sel = 0, off_counts = 0, off_btotal = 0, off_boff = 0,
          off_toff = 0, off_list = 0, off_po = 0, off_plse = 0, total = 0;
+  size_t off_ublk = 0, off_umask = 0, off_ucount = 0, off_part = 0, off_bmpart = 0;
 };
 
 moba_status check_common(const moba_args* a, bool full, Plan* p) {
@@ -173,16 +174,27 @@ moba_status plan_forward(const moba_args* a, Plan* p) {
     return fail(MOBA_ERR_UNSUPPORTED, "too many routing chunks");
   const int64_t esz = d.bf16 ? 2 : 4;
   p->need_kbar = a->k_block_mean == nullptr;
-  p->need_vt = d.bf16;
   p->need_sel = a->sel_out == nullptr;
-  p->routed = d.kp > 0 && d.nb > 1;
+  p->decode = moba::decode_supported(d);
+  p->need_vt = d.bf16 && !p->decode;
+  p->routed = !p->decode && d.kp > 0 && d.nb > 1;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
     off = align_up(off + bytes);
     return o;
   };
-  if (p->need_kbar) p->off_kbar = take((size_t)d.S * d.Hkv * d.nb * d.D * 4);
+  if (p->need_kbar) {
+    p->off_kbar = take((size_t)d.S * d.Hkv * d.nb * d.D * 4);
+    p->off_bmpart = take(moba::block_mean_partial_floats(d) * 4);
+  }
+  if (p->decode) {
+    const size_t nu = (size_t)d.S * d.Hkv * moba::decode_umax(d);
+    p->off_ublk = take(nu * 4);
+    p->off_umask = take(nu * 4);
+    p->off_ucount = take((size_t)d.S * d.Hkv * 4);
+    p->off_part = take(moba::decode_part_floats(d) * 4);
+  }
   if (p->need_vt) p->off_vt = take((size_t)d.S * d.Hkv * d.D * d.L * 2);
   if (p->need_sel) p->off_sel = take((size_t)d.S * d.H * d.Lq * d.topk * 4);
   if (p->routed) {
@@ -206,15 +218,33 @@ moba_status plan_full(const moba_args* a, Plan* p) {
   if (st != MOBA_OK) return st;
   Dims& d = p->d;
   if (d.L % 64 != 0) return fail(MOBA_ERR_UNSUPPORTED, "kv_len is not a multiple of 64");
-  d.B = 64;
-  d.topk = 1;
-  d.kp = 0;
-  d.nb = (int)(d.L / 64);
-  p->need_vt = d.bf16;
   size_t off = 0;
-  if (p->need_vt) {
-    p->off_vt = 0;
-    off = align_up((size_t)d.S * d.Hkv * d.D * d.L * 2);
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  // q_len 1: split-K over 512-key chunks with every chunk kept by every head
+  Dims dd = d;
+  dd.B = moba::decode_chunk();
+  dd.nb = (int)(d.L / dd.B);
+  dd.topk = dd.nb;
+  if (d.L % dd.B == 0 && dd.nb <= moba::kMaxBlocks && moba::decode_supported(dd)) {
+    d = dd;
+    d.kp = 0;
+    p->decode = true;
+    const size_t nu = (size_t)d.S * d.Hkv * moba::decode_umax(d);
+    p->off_ublk = take(nu * 4);
+    p->off_umask = take(nu * 4);
+    p->off_ucount = take((size_t)d.S * d.Hkv * 4);
+    p->off_part = take(moba::decode_part_floats(d) * 4);
+  } else {
+    d.B = 64;
+    d.topk = 1;
+    d.kp = 0;
+    d.nb = (int)(d.L / 64);
+    p->need_vt = d.bf16;
+    if (p->need_vt) p->off_vt = take((size_t)d.S * d.Hkv * d.D * d.L * 2);
   }
   p->total = off;
   if (a->workspace && a->workspace_bytes < p->total)
@@ -278,8 +308,26 @@ moba_status forward_impl(const moba_args* a) {
 
   Launch l{(hipStream_t)a->stream};
   if (p.need_kbar)
-    l.run(K_BLOCK_MEAN, [&] { return moba::launch_block_mean(a->k, kbar, d, l.st); });
+    l.run(K_BLOCK_MEAN, [&] {
+      return moba::launch_block_mean(a->k, kbar, (float*)(w + p.off_bmpart), d, l.st);
+    });
   l.run(K_GATE, [&] { return moba::launch_gate_topk(a->q, kbar, sel, d, l.st); });
+  if (p.decode) {
+    int32_t* ublk = (int32_t*)(w + p.off_ublk);
+    uint32_t* umask = (uint32_t*)(w + p.off_umask);
+    int32_t* ucount = (int32_t*)(w + p.off_ucount);
+    float* part = (float*)(w + p.off_part);
+    l.run(K_DEC_PLAN,
+          [&] { return moba::launch_decode_plan(sel, ublk, umask, ucount, false, d, l.st); });
+    l.run(K_DEC_ATTN, [&] {
+      return moba::launch_decode_attn(a->q, a->k, a->v, ublk, umask, ucount, part, d, l.st);
+    });
+    l.run(K_DEC_MERGE, [&] {
+      return moba::launch_decode_merge(part, ublk, umask, ucount, a->out, d, l.st);
+    });
+    if (l.err != hipSuccess) return hip_fail(l);
+    return MOBA_OK;
+  }
   if (p.need_vt) l.run(K_TRANSPOSE_V, [&] { return moba::launch_transpose_v(a->v, vt, d, l.st); });
   if (p.routed) {
     l.run(K_RCOUNT, [&] { return moba::launch_route_count(sel, counts, d, l.st); });
@@ -316,6 +364,23 @@ moba_status full_impl(const moba_args* a) {
   const Dims& d = p.d;
   void* vt = p.need_vt ? (void*)(ws.base + p.off_vt) : nullptr;
   Launch l{(hipStream_t)a->stream};
+  if (p.decode) {
+    char* w = ws.base;
+    int32_t* ublk = (int32_t*)(w + p.off_ublk);
+    uint32_t* umask = (uint32_t*)(w + p.off_umask);
+    int32_t* ucount = (int32_t*)(w + p.off_ucount);
+    float* part = (float*)(w + p.off_part);
+    l.run(K_DEC_PLAN,
+          [&] { return moba::launch_decode_plan(nullptr, ublk, umask, ucount, true, d, l.st); });
+    l.run(K_DEC_ATTN, [&] {
+      return moba::launch_decode_attn(a->q, a->k, a->v, ublk, umask, ucount, part, d, l.st);
+    });
+    l.run(K_DEC_MERGE, [&] {
+      return moba::launch_decode_merge(part, ublk, umask, ucount, a->out, d, l.st);
+    });
+    if (l.err != hipSuccess) return hip_fail(l);
+    return MOBA_OK;
+  }
   if (p.need_vt) l.run(K_TRANSPOSE_V, [&] { return moba::launch_transpose_v(a->v, vt, d, l.st); });
   l.run(K_ATTN_FULL, [&] {
     return d.bf16 ? moba::launch_attn_query_bf16(a->q, a->k, vt, nullptr, nullptr, a->out, 1, d,
@@ -445,7 +510,19 @@ moba_status moba_block_mean(const void* k, int32_t batch, int64_t kv_len, int32_
     d.S = batch; d.L = kv_len; d.Hkv = n_kv_heads; d.D = head_dim; d.B = block_size;
     d.nb = (int)(kv_len / block_size); d.bf16 = dtype == MOBA_DTYPE_BF16;
     Launch l{(hipStream_t)stream};
-    l.run(K_BLOCK_MEAN, [&] { return moba::launch_block_mean(k, k_block_mean, d, l.st); });
+    const size_t pbytes = moba::block_mean_partial_floats(d) * 4;
+    void* partial = nullptr;
+    if (pbytes) {
+      const hipError_t e = hipMallocAsync(&partial, pbytes, l.st);
+      if (e != hipSuccess || !partial) {
+        (void)hipGetLastError();
+        return fail(MOBA_ERR_OUT_OF_MEMORY, "hipMallocAsync(%zu bytes) failed", pbytes);
+      }
+    }
+    l.run(K_BLOCK_MEAN, [&] {
+      return moba::launch_block_mean(k, k_block_mean, (float*)partial, d, l.st);
+    });
+    if (partial) (void)hipFreeAsync(partial, l.st);
     if (l.err != hipSuccess) return hip_fail(l);
     return MOBA_OK;
   });

@@ -35,40 +35,48 @@ struct Tiles {
   static constexpr int VCH = D * 8 / 256;         // 16-byte V^T chunks per thread
 };
 
-// Global -> register staging of one 64-key tile (all 256 threads).
+// Global -> register staging of one 64-key tile (all 256 threads).  The
+// per-thread offsets inside a tile are fixed; only the tile base (uniform)
+// moves, so the loop does no per-thread 64-bit address arithmetic.
 template <int D>
 struct TileRegs {
   u32x4 kr[Tiles<D>::KCH];
   u32x4 vr[Tiles<D>::VCH];
+  int koff[Tiles<D>::KCH];   // element offsets inside a K tile (global)
+  int voff[Tiles<D>::VCH];   // element offsets inside a V^T tile (global)
+  int kls[Tiles<D>::KCH];    // LDS element offsets
+  int vls[Tiles<D>::VCH];
 
-  __device__ __forceinline__ void load(const bf16_t* kbase, int64_t krow_stride,
-                                       const bf16_t* vtbase, int64_t L, int64_t key0, int tid) {
+  __device__ __forceinline__ void setup(int krow_stride, int L, int tid) {
 #pragma unroll
     for (int i = 0; i < Tiles<D>::KCH; ++i) {
       const int c = tid + 256 * i;
       const int row = c / (D / 8), cc = c % (D / 8);
-      kr[i] = *reinterpret_cast<const u32x4*>(kbase + (key0 + row) * krow_stride + cc * 8);
+      koff[i] = row * krow_stride + cc * 8;
+      kls[i] = row * Tiles<D>::KS + cc * 8;
     }
 #pragma unroll
     for (int i = 0; i < Tiles<D>::VCH; ++i) {
       const int c = tid + 256 * i;
       const int dd = c / 8, kc = c % 8;
-      vr[i] = *reinterpret_cast<const u32x4*>(vtbase + (int64_t)dd * L + key0 + kc * 8);
+      voff[i] = dd * L + kc * 8;
+      vls[i] = Tiles<D>::KE + dd * Tiles<D>::VS + kc * 8;
     }
   }
-  __device__ __forceinline__ void store(bf16_t* buf, int tid) const {
+  // ktile / vttile: K row `key0` and V^T column `key0` of the tile (uniform).
+  __device__ __forceinline__ void load(const bf16_t* ktile, const bf16_t* vttile) {
 #pragma unroll
-    for (int i = 0; i < Tiles<D>::KCH; ++i) {
-      const int c = tid + 256 * i;
-      const int row = c / (D / 8), cc = c % (D / 8);
-      *reinterpret_cast<u32x4*>(buf + row * Tiles<D>::KS + cc * 8) = kr[i];
-    }
+    for (int i = 0; i < Tiles<D>::KCH; ++i)
+      kr[i] = *reinterpret_cast<const u32x4*>(ktile + koff[i]);
 #pragma unroll
-    for (int i = 0; i < Tiles<D>::VCH; ++i) {
-      const int c = tid + 256 * i;
-      const int dd = c / 8, kc = c % 8;
-      *reinterpret_cast<u32x4*>(buf + Tiles<D>::KE + dd * Tiles<D>::VS + kc * 8) = vr[i];
-    }
+    for (int i = 0; i < Tiles<D>::VCH; ++i)
+      vr[i] = *reinterpret_cast<const u32x4*>(vttile + voff[i]);
+  }
+  __device__ __forceinline__ void store(bf16_t* buf) const {
+#pragma unroll
+    for (int i = 0; i < Tiles<D>::KCH; ++i) *reinterpret_cast<u32x4*>(buf + kls[i]) = kr[i];
+#pragma unroll
+    for (int i = 0; i < Tiles<D>::VCH; ++i) *reinterpret_cast<u32x4*>(buf + vls[i]) = vr[i];
   }
 };
 
@@ -89,22 +97,29 @@ struct FlashAcc {
 template <int D, bool MASK>
 __device__ __forceinline__ void flash_step(const bf16_t* buf, const bf16x8 (&qf)[D / 16],
                                            FlashAcc<D>& acc, int n, int hh, float sl2,
-                                           int64_t key0, int64_t klo, int64_t qpos) {
+                                           int key0, int klo, int qpos) {
   using T = Tiles<D>;
-  f32x16 s[2];
+  // S^T = K Q^T for two 32-key subtiles; all K fragments are read first so
+  // the LDS latency overlaps, and the two accumulation chains interleave.
+  bf16x8 ka[D / 16], kb[D / 16];
+  const bf16_t* krow0 = buf + kperm(n) * T::KS + 8 * hh;
+  const bf16_t* krow1 = krow0 + 32 * T::KS;
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
-    s[kt] = f32x16{};
-    const bf16_t* krow = buf + (32 * kt + kperm(n)) * T::KS + 8 * hh;
+  for (int t = 0; t < D / 16; ++t) ka[t] = ld_bf16x8(krow0 + 16 * t);
 #pragma unroll
-    for (int t = 0; t < D / 16; ++t) s[kt] = mfma32(ld_bf16x8(krow + 16 * t), qf[t], s[kt]);
+  for (int t = 0; t < D / 16; ++t) kb[t] = ld_bf16x8(krow1 + 16 * t);
+  f32x16 s[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) {
+    s[0] = mfma32(ka[t], qf[t], s[0]);
+    s[1] = mfma32(kb[t], qf[t], s[1]);
   }
   if (MASK) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int reg = 0; reg < 16; ++reg) {
-        const int64_t key = key0 + 32 * kt + acc_key(reg, hh);
+        const int key = key0 + 32 * kt + acc_key(reg, hh);
         if (key > qpos || key < klo) s[kt][reg] = -__builtin_inff();
       }
   }
@@ -116,7 +131,6 @@ __device__ __forceinline__ void flash_step(const bf16_t* buf, const bf16x8 (&qf)
   mx = fmaxf(mx, half_swap(mx));
   const float mnew = fmaxf(acc.m, mx * sl2);
   const float mref = (mnew == -__builtin_inff()) ? 0.f : mnew;
-  const float alpha = __builtin_amdgcn_exp2f(acc.m - mref);
   float psum = 0.f;
   bf16x8 pb[2][2];
 #pragma unroll
@@ -129,21 +143,26 @@ __device__ __forceinline__ void flash_step(const bf16_t* buf, const bf16x8 (&qf)
         psum += p;
         pb[kt][c][r] = static_cast<__bf16>(p);
       }
-  acc.l = fmaf(acc.l, alpha, psum);
+  // Rescale only when some row's max moved (exact: otherwise alpha == 1).
+  if (__any(mnew > acc.m)) {
+    const float alpha = __builtin_amdgcn_exp2f(acc.m - mref);
+    acc.l *= alpha;
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt)
+    for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-    for (int reg = 0; reg < 16; ++reg) acc.o[dt][reg] *= alpha;
+      for (int reg = 0; reg < 16; ++reg) acc.o[dt][reg] *= alpha;
+  }
+  acc.l += psum;
   acc.m = mnew;
   const bf16_t* vbase = buf + T::KE + 8 * hh;
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) {
     const bf16_t* vrow = vbase + (32 * dt + n) * T::VS;
+    bf16x8 va[4];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int kc = 0; kc < 4; ++kc) va[kc] = ld_bf16x8(vrow + 16 * kc);
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
-        acc.o[dt] = mfma32(ld_bf16x8(vrow + 32 * kt + 16 * c), pb[kt][c], acc.o[dt]);
+    for (int kc = 0; kc < 4; ++kc) acc.o[dt] = mfma32(va[kc], pb[kc >> 1][kc & 1], acc.o[dt]);
   }
 }
 
@@ -210,16 +229,34 @@ __global__ __launch_bounds__(256, 2) void k_attn_routed(
   FlashAcc<D> acc;
   acc.init();
   TileRegs<D> tr;
-  tr.load(kbase, (int64_t)Hkv * D, vtbase, L, kstart, tid);
-  tr.store(lds, tid);
+  tr.setup(Hkv * D, (int)L, tid);
+  const int64_t ktile_step = (int64_t)64 * Hkv * D;
+  const bf16_t* ktile = kbase + kstart * Hkv * D;
+  const bf16_t* vttile = vtbase + kstart;
+  tr.load(ktile, vttile);
+  tr.store(lds);
   __syncthreads();
-  for (int it = 0; it < nsteps; ++it) {
-    const bool more = it + 1 < nsteps;
-    if (more) tr.load(kbase, (int64_t)Hkv * D, vtbase, L, kstart + 64 * (it + 1), tid);
-    if (wave_on)
+  // Every wave runs the same loads, stores and barriers; the waves holding
+  // entries also compute (two loops keep the accumulators out of a branch).
+  if (wave_on) {
+    for (int it = 0; it < nsteps; ++it) {
+      const bool more = it + 1 < nsteps;
+      ktile += ktile_step;
+      vttile += 64;
+      if (more) tr.load(ktile, vttile);
       flash_step<D, false>(lds + (it & 1) * T::BUF, qf, acc, n, hh, sl2, 0, 0, 0);
-    if (more) tr.store(lds + ((it + 1) & 1) * T::BUF, tid);
-    __syncthreads();
+      if (more) tr.store(lds + ((it + 1) & 1) * T::BUF);
+      __syncthreads();
+    }
+  } else {
+    for (int it = 0; it < nsteps; ++it) {
+      const bool more = it + 1 < nsteps;
+      ktile += ktile_step;
+      vttile += 64;
+      if (more) tr.load(ktile, vttile);
+      if (more) tr.store(lds + ((it + 1) & 1) * T::BUF);
+      __syncthreads();
+    }
   }
   if (!valid) return;
   const float ltot = acc.l + half_swap(acc.l);
@@ -285,21 +322,56 @@ __global__ __launch_bounds__(256, 2) void k_attn_query(
   FlashAcc<D> acc;
   acc.init();
   TileRegs<D> tr;
-  tr.load(kbase, (int64_t)Hkv * D, vtbase, L, (int64_t)t0 * 64, tid);
-  tr.store(lds, tid);
+  tr.setup(Hkv * D, L, tid);
+  const int64_t ktile_step = (int64_t)64 * Hkv * D;
+  const bf16_t* ktile = kbase + (int64_t)t0 * ktile_step;
+  const bf16_t* vttile = vtbase + (int64_t)t0 * 64;
+  tr.load(ktile, vttile);
+  tr.store(lds);
   __syncthreads();
-  for (int it = t0; it < t1; ++it) {
-    const bool more = it + 1 < t1;
-    if (more) tr.load(kbase, (int64_t)Hkv * D, vtbase, L, (int64_t)(it + 1) * 64, tid);
-    const int key0 = it * 64;
-    const bf16_t* buf = lds + ((it - t0) & 1) * T::BUF;
-    if (wave_on && key0 < khi_w && key0 + 64 > klo_w) {
-      if ((key0 + 63 > pos_first) || (key0 < klo_w))
-        flash_step<D, true>(buf, qf, acc, n, hh, sl2, key0, klo_l, pos);
-      else
-        flash_step<D, false>(buf, qf, acc, n, hh, sl2, key0, 0, 0);
-    }
-    if (more) tr.store(lds + ((it + 1 - t0) & 1) * T::BUF, tid);
+  // Per wave the workgroup's tiles [t0, t1) split into: idle before the
+  // wave's window, full tiles, tiles that need the mask (diagonal or the
+  // block start), idle after.  Each phase is its own loop; every iteration of
+  // every loop does the same loads, stores and one barrier.
+  int ws_ = t1, wd_ = t1, we_ = t1;
+  if (wave_on) {
+    ws_ = klo_w / 64;                                  // first tile of the window
+    we_ = (khi_w + 63) / 64;                           // one past the last
+    // first tile that needs the mask: its last key passes the wave's first
+    // query (key0 + 63 > pos_first)
+    const int d_ = (pos_first + 1) / 64;
+    wd_ = d_ < ws_ ? ws_ : (d_ > we_ ? we_ : d_);
+    if (klo_w % 64 != 0) wd_ = ws_;                    // window start not tile-aligned
+  }
+  int it = t0;
+  auto advance = [&](int i) {
+    const bool more = i + 1 < t1;
+    ktile += ktile_step;
+    vttile += 64;
+    if (more) tr.load(ktile, vttile);
+    return more;
+  };
+  for (; it < ws_; ++it) {
+    const bool more = advance(it);
+    if (more) tr.store(lds + ((it + 1 - t0) & 1) * T::BUF);
+    __syncthreads();
+  }
+  for (; it < wd_; ++it) {
+    const bool more = advance(it);
+    flash_step<D, false>(lds + ((it - t0) & 1) * T::BUF, qf, acc, n, hh, sl2, 0, 0, 0);
+    if (more) tr.store(lds + ((it + 1 - t0) & 1) * T::BUF);
+    __syncthreads();
+  }
+  for (; it < we_; ++it) {
+    const bool more = advance(it);
+    flash_step<D, true>(lds + ((it - t0) & 1) * T::BUF, qf, acc, n, hh, sl2, it * 64, klo_l,
+                        pos);
+    if (more) tr.store(lds + ((it + 1 - t0) & 1) * T::BUF);
+    __syncthreads();
+  }
+  for (; it < t1; ++it) {
+    const bool more = advance(it);
+    if (more) tr.store(lds + ((it + 1 - t0) & 1) * T::BUF);
     __syncthreads();
   }
   if (!valid) return;

@@ -1,0 +1,336 @@
+// Decode: one new query per sequence against a long K/V cache.
+//
+// Same method as the prefill (gate on block means, top-k with the own block,
+// one softmax over the kept keys), but the work is dominated by reading the
+// kept K/V blocks from HBM, so the kernels are organised around reading each
+// kept block once:
+//   k_decode_plan:  per (sequence, KV head): the union of the blocks kept by
+//                   the group's query heads, each with the mask of heads that
+//                   kept it (a block kept by several heads is read once).
+//   k_decode_attn:  per (union block, key chunk): scores of the chunk for the
+//                   heads in the mask, a chunk-local softmax and P.V, written
+//                   as an unnormalised partial (max, sum, o).
+//   k_decode_merge: per (sequence, head): log-sum-exp merge of the partials
+//                   of the head's kept blocks -> out.
+// With q_len = 1 the query sits at the last cache position, so every kept
+// block, its own block included, is fully visible (no mask).
+#include "common.h"
+#include "kernels.h"
+
+namespace moba {
+
+constexpr int kDecChunk = 512;  // keys per decode work item
+
+// grid S*Hkv, 64 threads.
+// all_blocks = 1 selects every block for every head (split-K full attention).
+__global__ __launch_bounds__(64) void k_decode_plan(const int32_t* __restrict__ sel,
+                                                    int32_t* __restrict__ ublk,
+                                                    uint32_t* __restrict__ umask,
+                                                    int32_t* __restrict__ ucount, int H,
+                                                    int Hkv, int nb, int topk, int umax,
+                                                    int all_blocks) {
+  extern __shared__ uint32_t lds_mask[];  // [nb]
+  const int sg = blockIdx.x, s = sg / Hkv, g = sg % Hkv, G = H / Hkv;
+  const int lane = threadIdx.x;
+  const uint32_t all = (G >= 32) ? 0xffffffffu : ((1u << G) - 1u);
+  for (int j = lane; j < nb; j += 64) lds_mask[j] = all_blocks ? all : 0u;
+  __syncthreads();
+  for (int e = lane; !all_blocks && e < G * topk; e += 64) {
+    const int hl = e / topk, t = e % topk;
+    const int j = sel[((int64_t)s * H + g * G + hl) * topk + t];  // q_len = 1
+    if (j >= 0 && j < nb) atomicOr(&lds_mask[j], 1u << hl);
+  }
+  __syncthreads();
+  int base = 0;
+  const uint64_t lt = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
+  for (int j0 = 0; j0 < nb; j0 += 64) {
+    const int j = j0 + lane;
+    const uint32_t m = j < nb ? lds_mask[j] : 0u;
+    const uint64_t bal = __ballot(m != 0u);
+    if (m != 0u) {
+      const int idx = base + __popcll(bal & lt);
+      if (idx < umax) {
+        ublk[(int64_t)sg * umax + idx] = j;
+        umask[(int64_t)sg * umax + idx] = m;
+      }
+    }
+    base += __popcll(bal);
+  }
+  if (lane == 0) ucount[sg] = base < umax ? base : umax;
+}
+
+// grid (chunks per block, umax, S*Hkv), 256 threads.  GM = max heads per group.
+template <typename T, int D, int GM>
+__global__ __launch_bounds__(256) void k_decode_attn(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const int32_t* __restrict__ ublk, const uint32_t* __restrict__ umask,
+    const int32_t* __restrict__ ucount, float* __restrict__ part, int64_t L, int H, int Hkv,
+    int B, int umax, float scale_log2) {
+  constexpr int VEC = 16 / sizeof(T);   // elements per 16-byte load
+  constexpr int KPT = kDecChunk / 256;  // keys per thread in the score phase
+  constexpr int DG = D / 8;             // d-groups of 8 in the P.V phase
+  constexpr int KG = 256 / DG;          // key groups in the P.V phase
+  __shared__ float qs[GM][D];
+  __shared__ float ps[GM][kDecChunk];
+  __shared__ float red[KG][D];
+  __shared__ float stat[GM][2];
+  __shared__ float wred[4];
+
+  const int sg = blockIdx.z, u = blockIdx.y, c = blockIdx.x;
+  if (u >= ucount[sg]) return;
+  const int s = sg / Hkv, g = sg % Hkv, G = H / Hkv;
+  const int j = ublk[(int64_t)sg * umax + u];
+  const uint32_t mask = umask[(int64_t)sg * umax + u];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t key0 = (int64_t)j * B + (int64_t)c * kDecChunk;
+
+  for (int e = tid; e < G * D; e += 256) {
+    const int hl = e / D, dd = e % D;
+    qs[hl][dd] = load_as_f32(q + ((int64_t)s * H + g * G + hl) * D + dd) * scale_log2;
+  }
+  __syncthreads();
+
+  // scores (base 2, scale folded into q)
+  const T* kb = k + (((int64_t)s * L + key0) * Hkv + g) * D;
+  for (int kk = 0; kk < KPT; ++kk) {
+    const int key = tid + 256 * kk;
+    const T* krow = kb + (int64_t)key * Hkv * D;
+    float acc[GM];
+#pragma unroll
+    for (int hl = 0; hl < GM; ++hl) acc[hl] = 0.f;
+#pragma unroll 4
+    for (int d0 = 0; d0 < D; d0 += VEC) {
+      const u32x4 raw = *reinterpret_cast<const u32x4*>(krow + d0);
+      const T* e = reinterpret_cast<const T*>(&raw);
+      float x[VEC];
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) x[i] = load_as_f32(e + i);
+#pragma unroll
+      for (int hl = 0; hl < GM; ++hl) {
+        if (hl < G && ((mask >> hl) & 1u)) {
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) acc[hl] = fmaf(x[i], qs[hl][d0 + i], acc[hl]);
+        }
+      }
+    }
+#pragma unroll
+    for (int hl = 0; hl < GM; ++hl)
+      if (hl < G && ((mask >> hl) & 1u)) ps[hl][key] = acc[hl];
+  }
+  __syncthreads();
+
+  // chunk-local softmax statistics per selected head
+  for (int hl = 0; hl < G && hl < GM; ++hl) {
+    if (!((mask >> hl) & 1u)) continue;
+    float mx = -__builtin_inff();
+    for (int key = tid; key < kDecChunk; key += 256) mx = fmaxf(mx, ps[hl][key]);
+    mx = wave_max(mx);
+    if (lane == 0) wred[w] = mx;
+    __syncthreads();
+    mx = fmaxf(fmaxf(wred[0], wred[1]), fmaxf(wred[2], wred[3]));
+    __syncthreads();
+    float sum = 0.f;
+    for (int key = tid; key < kDecChunk; key += 256) {
+      const float p = __builtin_amdgcn_exp2f(ps[hl][key] - mx);
+      ps[hl][key] = p;
+      sum += p;
+    }
+    for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
+    if (lane == 0) wred[w] = sum;
+    __syncthreads();
+    if (tid == 0) {
+      stat[hl][0] = mx;
+      stat[hl][1] = wred[0] + wred[1] + wred[2] + wred[3];
+    }
+    __syncthreads();
+  }
+
+  // P.V: thread (key group kg, d group dg)
+  const int dg = tid % DG, kg = tid / DG;
+  const T* vb = v + (((int64_t)s * L + key0) * Hkv + g) * D + dg * 8;
+  float o[GM][8];
+#pragma unroll
+  for (int hl = 0; hl < GM; ++hl)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[hl][i] = 0.f;
+  for (int key = kg; key < kDecChunk; key += KG) {
+    const T* vrow = vb + (int64_t)key * Hkv * D;
+    float x[8];
+    if (sizeof(T) == 2) {
+      const u32x4 raw = *reinterpret_cast<const u32x4*>(vrow);
+      const T* e = reinterpret_cast<const T*>(&raw);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = load_as_f32(e + i);
+    } else {
+      const u32x4 r0 = *reinterpret_cast<const u32x4*>(vrow);
+      const u32x4 r1 = *reinterpret_cast<const u32x4*>(vrow + 4);
+      const T* e0 = reinterpret_cast<const T*>(&r0);
+      const T* e1 = reinterpret_cast<const T*>(&r1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[i] = load_as_f32(e0 + i);
+        x[4 + i] = load_as_f32(e1 + i);
+      }
+    }
+#pragma unroll
+    for (int hl = 0; hl < GM; ++hl) {
+      if (hl < G && ((mask >> hl) & 1u)) {
+        const float p = ps[hl][key];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[hl][i] = fmaf(p, x[i], o[hl][i]);
+      }
+    }
+  }
+  // reduce over key groups, one head at a time; write (max, sum, o)
+  const int64_t item = ((int64_t)sg * umax + u) * (B / kDecChunk) + c;
+#pragma unroll
+  for (int hl = 0; hl < GM; ++hl) {
+    if (!(hl < G && ((mask >> hl) & 1u))) continue;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) red[kg][dg * 8 + i] = o[hl][i];
+    __syncthreads();
+    float* prow = part + (item * GM + hl) * (D + 2);
+    for (int dd = tid; dd < D; dd += 256) {
+      float acc = 0.f;
+      for (int r = 0; r < KG; ++r) acc += red[r][dd];
+      prow[2 + dd] = acc;
+    }
+    if (tid == 0) {
+      prow[0] = stat[hl][0];
+      prow[1] = stat[hl][1];
+    }
+  }
+}
+
+// grid S*H, D threads.
+template <typename T, int D, int GM>
+__global__ __launch_bounds__(D) void k_decode_merge(const float* __restrict__ part,
+                                                    const int32_t* __restrict__ ublk,
+                                                    const uint32_t* __restrict__ umask,
+                                                    const int32_t* __restrict__ ucount,
+                                                    T* __restrict__ out, int H, int Hkv, int B,
+                                                    int umax) {
+  const int sh = blockIdx.x, s = sh / H, h = sh % H, G = H / Hkv, g = h / G, hl = h % G;
+  const int sg = s * Hkv + g;
+  const int dd = threadIdx.x;
+  const int cpb = B / kDecChunk;
+  const int n = ucount[sg];
+  float M = -__builtin_inff();
+  for (int u = 0; u < n; ++u) {
+    if (!((umask[(int64_t)sg * umax + u] >> hl) & 1u)) continue;
+    for (int c = 0; c < cpb; ++c) {
+      const int64_t item = ((int64_t)sg * umax + u) * cpb + c;
+      M = fmaxf(M, part[(item * GM + hl) * (D + 2)]);
+    }
+  }
+  float lsum = 0.f, acc = 0.f;
+  for (int u = 0; u < n; ++u) {
+    if (!((umask[(int64_t)sg * umax + u] >> hl) & 1u)) continue;
+    for (int c = 0; c < cpb; ++c) {
+      const int64_t item = ((int64_t)sg * umax + u) * cpb + c;
+      const float* prow = part + (item * GM + hl) * (D + 2);
+      const float wgt = __builtin_amdgcn_exp2f(prow[0] - M);
+      lsum = fmaf(wgt, prow[1], lsum);
+      acc = fmaf(wgt, prow[2 + dd], acc);
+    }
+  }
+  const float r = acc / lsum;
+  T* orow = out + ((int64_t)s * H + h) * D;
+  if (sizeof(T) == 2)
+    reinterpret_cast<bf16_t*>(orow)[dd] = f32_to_bf16(r);
+  else
+    reinterpret_cast<float*>(orow)[dd] = r;
+}
+
+int decode_umax(const Dims& d) {
+  const int u = d.G * d.topk;
+  return u < d.nb ? u : d.nb;
+}
+
+int decode_chunk() { return kDecChunk; }
+
+int decode_gm(const Dims& d) {
+  return d.G <= 1 ? 1 : d.G <= 2 ? 2 : d.G <= 4 ? 4 : 8;
+}
+
+size_t decode_part_floats(const Dims& d) {
+  return (size_t)d.S * d.Hkv * decode_umax(d) * (d.B / kDecChunk) * decode_gm(d) * (d.D + 2);
+}
+
+bool decode_supported(const Dims& d) {
+  return d.Lq == 1 && d.G <= 8 && d.B % kDecChunk == 0;
+}
+
+hipError_t launch_decode_plan(const int32_t* sel, int32_t* ublk, uint32_t* umask,
+                              int32_t* ucount, bool all_blocks, const Dims& d, hipStream_t st) {
+  hipLaunchKernelGGL(k_decode_plan, dim3(d.S * d.Hkv), dim3(64), d.nb * sizeof(uint32_t), st, sel,
+                     ublk, umask, ucount, d.H, d.Hkv, d.nb, d.topk, decode_umax(d),
+                     all_blocks ? 1 : 0);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t decode_attn_gm(const void* q, const void* k, const void* v,
+                                 const int32_t* ublk, const uint32_t* umask,
+                                 const int32_t* ucount, float* part, const Dims& d,
+                                 hipStream_t st) {
+  const int umax = decode_umax(d);
+  dim3 grid(d.B / kDecChunk, umax, d.S * d.Hkv);
+  const float sl2 = kLog2e / sqrtf((float)d.D);
+#define MOBA_DEC(GMV)                                                                      \
+  hipLaunchKernelGGL((k_decode_attn<T, D, GMV>), grid, dim3(256), 0, st,                   \
+                     static_cast<const T*>(q), static_cast<const T*>(k),                   \
+                     static_cast<const T*>(v), ublk, umask, ucount, part, d.L, d.H, d.Hkv, \
+                     d.B, umax, sl2)
+  switch (decode_gm(d)) {
+    case 1: MOBA_DEC(1); break;
+    case 2: MOBA_DEC(2); break;
+    case 4: MOBA_DEC(4); break;
+    default: MOBA_DEC(8); break;
+  }
+#undef MOBA_DEC
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_attn(const void* q, const void* k, const void* v, const int32_t* ublk,
+                              const uint32_t* umask, const int32_t* ucount, float* part,
+                              const Dims& d, hipStream_t st) {
+  if (d.bf16) {
+    if (d.D == 128) return decode_attn_gm<bf16_t, 128>(q, k, v, ublk, umask, ucount, part, d, st);
+    return decode_attn_gm<bf16_t, 64>(q, k, v, ublk, umask, ucount, part, d, st);
+  }
+  if (d.D == 128) return decode_attn_gm<float, 128>(q, k, v, ublk, umask, ucount, part, d, st);
+  return decode_attn_gm<float, 64>(q, k, v, ublk, umask, ucount, part, d, st);
+}
+
+template <typename T, int D>
+static hipError_t decode_merge_gm(const float* part, const int32_t* ublk, const uint32_t* umask,
+                                  const int32_t* ucount, void* out, const Dims& d,
+                                  hipStream_t st) {
+  const int umax = decode_umax(d);
+#define MOBA_DM(GMV)                                                                         \
+  hipLaunchKernelGGL((k_decode_merge<T, D, GMV>), dim3(d.S * d.H), dim3(D), 0, st, part, ublk, \
+                     umask, ucount, static_cast<T*>(out), d.H, d.Hkv, d.B, umax)
+  switch (decode_gm(d)) {
+    case 1: MOBA_DM(1); break;
+    case 2: MOBA_DM(2); break;
+    case 4: MOBA_DM(4); break;
+    default: MOBA_DM(8); break;
+  }
+#undef MOBA_DM
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_merge(const float* part, const int32_t* ublk, const uint32_t* umask,
+                               const int32_t* ucount, void* out, const Dims& d,
+                               hipStream_t st) {
+  if (d.bf16) {
+    if (d.D == 128) return decode_merge_gm<bf16_t, 128>(part, ublk, umask, ucount, out, d, st);
+    return decode_merge_gm<bf16_t, 64>(part, ublk, umask, ucount, out, d, st);
+  }
+  if (d.D == 128) return decode_merge_gm<float, 128>(part, ublk, umask, ucount, out, d, st);
+  return decode_merge_gm<float, 64>(part, ublk, umask, ucount, out, d, st);
+}
+
+}  // namespace moba

@@ -33,7 +33,11 @@ struct Dims {
   int64_t slots = 0;  // S * H * Lq * kp routed slots
 };
 
-hipError_t launch_block_mean(const void* k, float* kbar, const Dims& d, hipStream_t st);
+// Block means; `partial` holds block_mean_partial_floats(d) floats (may be
+// NULL when that is 0).
+size_t block_mean_partial_floats(const Dims& d);
+hipError_t launch_block_mean(const void* k, float* kbar, float* partial, const Dims& d,
+                             hipStream_t st);
 hipError_t launch_transpose_v(const void* v, void* vt, const Dims& d, hipStream_t st);
 hipError_t launch_gate_topk(const void* q, const float* kbar, int32_t* sel, const Dims& d,
                             hipStream_t st);
@@ -64,5 +68,19 @@ hipError_t launch_attn_query_bf16(const void* q, const void* k, const void* vt,
 hipError_t launch_attn_query_f32(const void* q, const void* k, const void* v, const void* part_o,
                                  const float* part_lse, void* out, int mode, const Dims& d,
                                  hipStream_t st);
+
+// Decode (q_len == 1): union of kept blocks per (sequence, KV head), split-K
+// attention over 512-key chunks, log-sum-exp merge.
+bool decode_supported(const Dims& d);   // q_len 1, G <= 8, block_size % 512 == 0
+int decode_chunk();
+int decode_umax(const Dims& d);
+size_t decode_part_floats(const Dims& d);
+hipError_t launch_decode_plan(const int32_t* sel, int32_t* ublk, uint32_t* umask,
+                              int32_t* ucount, bool all_blocks, const Dims& d, hipStream_t st);
+hipError_t launch_decode_attn(const void* q, const void* k, const void* v, const int32_t* ublk,
+                              const uint32_t* umask, const int32_t* ucount, float* part,
+                              const Dims& d, hipStream_t st);
+hipError_t launch_decode_merge(const float* part, const int32_t* ublk, const uint32_t* umask,
+                               const int32_t* ucount, void* out, const Dims& d, hipStream_t st);
 
 }  // namespace moba

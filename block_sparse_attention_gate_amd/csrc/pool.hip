@@ -10,13 +10,17 @@
 
 namespace moba {
 
-// grid (nb, S, column groups); 256 threads.  Each thread accumulates VEC
-// columns over a strided subset of the block's rows in fp32, then the row
-// slices are summed in a fixed order (deterministic).
+// grid (nb * splits, S, column groups); 256 threads.  Workgroup (j, split)
+// accumulates VEC columns over rows [split*rows, (split+1)*rows) of block j in
+// fp32; the row slices inside the workgroup are summed in a fixed order.
+// splits == 1 writes the mean directly; otherwise the per-split sums go to
+// `partial` [S, nb, splits, Hkv*D] and k_block_mean_finalize adds them in
+// split order (deterministic, no atomics).
 template <typename T>
 __global__ __launch_bounds__(256) void k_block_mean(const T* __restrict__ k,
-                                                    float* __restrict__ kbar, int Hkv, int D,
-                                                    int64_t L, int B, int nb) {
+                                                    float* __restrict__ kbar,
+                                                    float* __restrict__ partial, int Hkv, int D,
+                                                    int64_t L, int B, int nb, int splits) {
   constexpr int VEC = 16 / sizeof(T);
   __shared__ float red[256 * VEC];
   const int cols = Hkv * D;
@@ -25,14 +29,15 @@ __global__ __launch_bounds__(256) void k_block_mean(const T* __restrict__ k,
   const int RS = 256 / cw;               // row slices
   const int tid = threadIdx.x;
   const int ct = tid % cw, rs = tid / cw;
-  const int s = blockIdx.y, j = blockIdx.x;
+  const int s = blockIdx.y, j = blockIdx.x / splits, sp = blockIdx.x % splits;
+  const int rows = B / splits;
   const int col = (blockIdx.z * cw + ct) * VEC;
   float acc[VEC];
 #pragma unroll
   for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
   if (rs < RS && col < cols) {
-    const T* base = k + ((int64_t)s * L + (int64_t)j * B) * cols + col;
-    for (int r = rs; r < B; r += RS) {
+    const T* base = k + ((int64_t)s * L + (int64_t)j * B + (int64_t)sp * rows) * cols + col;
+    for (int r = rs; r < rows; r += RS) {
       const u32x4 raw = *reinterpret_cast<const u32x4*>(base + (int64_t)r * cols);
       const T* e = reinterpret_cast<const T*>(&raw);
 #pragma unroll
@@ -51,22 +56,61 @@ __global__ __launch_bounds__(256) void k_block_mean(const T* __restrict__ k,
     if (c >= cols) continue;
     float sum = 0.f;
     for (int r = 0; r < RS; ++r) sum += red[r * width + e];
+    if (splits == 1) {
+      const int g = c / D, dd = c % D;
+      kbar[(((int64_t)s * Hkv + g) * nb + j) * D + dd] = sum * inv;
+    } else {
+      partial[(((int64_t)s * nb + j) * splits + sp) * cols + c] = sum;
+    }
+  }
+}
+
+// grid (nb, S); 256 threads.
+__global__ __launch_bounds__(256) void k_block_mean_finalize(const float* __restrict__ partial,
+                                                             float* __restrict__ kbar, int Hkv,
+                                                             int D, int B, int nb, int splits) {
+  const int s = blockIdx.y, j = blockIdx.x, cols = Hkv * D;
+  const float inv = 1.0f / (float)B;
+  for (int c = threadIdx.x; c < cols; c += 256) {
+    const float* p = partial + ((int64_t)s * nb + j) * splits * cols + c;
+    float sum = 0.f;
+    for (int sp = 0; sp < splits; ++sp) sum += p[(int64_t)sp * cols];
     const int g = c / D, dd = c % D;
     kbar[(((int64_t)s * Hkv + g) * nb + j) * D + dd] = sum * inv;
   }
 }
 
-hipError_t launch_block_mean(const void* k, float* kbar, const Dims& d, hipStream_t st) {
+int block_mean_splits(const Dims& d) {
+  // enough workgroups to cover the chip (>= 1024), at least 64 rows each
+  int splits = 1;
+  const int64_t wgs = (int64_t)d.nb * d.S;
+  while (wgs * splits < 1024 && d.B % (splits * 2) == 0 && d.B / (splits * 2) >= 64) splits *= 2;
+  return splits;
+}
+
+size_t block_mean_partial_floats(const Dims& d) {
+  const int sp = block_mean_splits(d);
+  return sp > 1 ? (size_t)d.S * d.nb * sp * d.Hkv * d.D : 0;
+}
+
+hipError_t launch_block_mean(const void* k, float* kbar, float* partial, const Dims& d,
+                             hipStream_t st) {
   const int cols = d.Hkv * d.D;
   const int vec = d.bf16 ? 8 : 4;
   const int tpr = cols / vec;
-  dim3 grid(d.nb, d.S, (tpr + 255) / 256);
+  const int splits = block_mean_splits(d);
+  dim3 grid(d.nb * splits, d.S, (tpr + 255) / 256);
   if (d.bf16)
     hipLaunchKernelGGL(k_block_mean<bf16_t>, grid, dim3(256), 0, st,
-                       static_cast<const bf16_t*>(k), kbar, d.Hkv, d.D, d.L, d.B, d.nb);
+                       static_cast<const bf16_t*>(k), kbar, partial, d.Hkv, d.D, d.L, d.B, d.nb,
+                       splits);
   else
     hipLaunchKernelGGL(k_block_mean<float>, grid, dim3(256), 0, st,
-                       static_cast<const float*>(k), kbar, d.Hkv, d.D, d.L, d.B, d.nb);
+                       static_cast<const float*>(k), kbar, partial, d.Hkv, d.D, d.L, d.B, d.nb,
+                       splits);
+  if (splits > 1)
+    hipLaunchKernelGGL(k_block_mean_finalize, dim3(d.nb, d.S), dim3(256), 0, st, partial, kbar,
+                       d.Hkv, d.D, d.B, d.nb, splits);
   return hipGetLastError();
 }
 

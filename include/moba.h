@@ -141,7 +141,7 @@ int32_t moba_abi_version(void);
  * summed duration in milliseconds and the number of launches since the last
  * reset.  Names: "block_mean", "transpose_v", "gate_topk", "route_count",
  * "route_scan_rows", "route_scan_buckets", "route_scatter", "attn_routed",
- * "attn_own_merge", "attn_full", "decode_gate", "decode_attn",
+ * "attn_own_merge", "attn_full", "decode_plan", "decode_attn",
  * "decode_merge".  Unknown names give MOBA_ERR_INVALID_ARGUMENT.
  */
 moba_status moba_profile_enable(int32_t on);

@@ -218,3 +218,82 @@ def test_full_attention_32k_sampled():
     emax, emean = check_outputs(out_rows, q_rows, rows, None, w.block_size, q.shape[0],
                                 "bf16", pairs, device_fetch(k, v), 1, full=True)
     print(f"full 32K: max {emax:.2e} mean {emean:.2e}")
+
+
+DECODE = [
+    moba_inputs.custom("dec_b512_g4", "bf16", 3, 1, 8192, 8, 2, 128, 512, 5, 41),
+    moba_inputs.custom("dec_b1024_g1", "bf16", 2, 1, 16384, 2, 2, 64, 1024, 4, 42),
+    moba_inputs.custom("dec_g8_k1", "bf16", 2, 1, 4096, 8, 1, 128, 512, 1, 43),
+    moba_inputs.custom("dec_f32", "f32", 2, 1, 4096, 4, 1, 128, 512, 3, 44),
+]
+
+
+@pytest.mark.parametrize("w", DECODE, ids=[w.name for w in DECODE])
+def test_decode_kernels_parity(w):
+    """q_len = 1 with blocks that are multiples of 512 keys runs the decode
+    kernels (union of kept blocks per KV head, split-K, merge); the block
+    means come from moba_block_mean, as a decode loop over a fixed cache would."""
+    moba = _moba()
+    print(f"case {w}", flush=True)
+    q, k, v = moba_inputs.make_inputs(w, device=DEV)
+    kbar = moba.moba_block_mean(k, w.block_size)
+    out, sel = moba.moba_forward_ex(q, k, v, w.block_size, w.topk, k_block_mean=kbar,
+                                    return_selection=True)
+    out2 = moba.moba_forward_ex(q, k, v, w.block_size, w.topk)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+    for s in range(q.shape[0]):
+        qh, kh, vh = to64(q[s]), to64(k[s]), to64(v[s])
+        positions = np.array([kh.shape[0] - 1])
+        kb = O.block_mean(kh, w.block_size)
+        np.testing.assert_allclose(kbar[s].double().cpu().numpy(), kb, rtol=0, atol=1e-5)
+        sel_np = sel[s].cpu().numpy()
+        ntie, _ = check_selection(qh, positions, kb, sel_np, w.block_size, w.topk)
+        pairs = [(h, 0) for h in range(qh.shape[1])]
+        emax, emean = check_outputs(to64(out[s]), qh, positions, sel_np, w.block_size,
+                                    kh.shape[0], w.dtype, pairs, host_fetch(kh, vh),
+                                    kh.shape[1])
+        print(f"  seq {s}: tie {ntie} max|err| {emax:.2e} mean|err| {emean:.2e}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_full_attention_decode_parity(dtype):
+    """Full causal attention with q_len = 1 (split-K over the whole cache)."""
+    moba = _moba()
+    w = moba_inputs.custom("full_dec_" + dtype, dtype, 2, 1, 8192, 8, 2, 128, 512, 1, 45)
+    q, k, v = moba_inputs.make_inputs(w, device=DEV)
+    out = moba.moba_full_attention_ex(q, k, v)
+    torch.cuda.synchronize()
+    for s in range(q.shape[0]):
+        ref = O.full_reference(to64(q[s]), to64(k[s]), to64(v[s]))
+        err = np.abs(to64(out[s]) - ref)
+        tmax, tmean = {"bf16": (2e-2, 2e-3), "f32": (1e-4, 1e-4)}[dtype]
+        assert err.max() <= tmax and err.mean() <= tmean, (err.max(), err.mean())
+
+
+def test_decode_1m_parity():
+    """8 sequences x 1 query against a 1M-token cache (32/8 heads, block
+    4096, top-k 12), block means precomputed: every selection, and the
+    outputs of 64 (sequence, head) pairs."""
+    moba = _moba()
+    w = moba_inputs.WORKLOADS["decode_1m"]
+    print(f"case {w}", flush=True)
+    q, k, v = moba_inputs.make_inputs(w, device=DEV)
+    kbar = moba.moba_block_mean(k, w.block_size)
+    out, sel = moba.moba_forward_ex(q, k, v, w.block_size, w.topk, k_block_mean=kbar,
+                                    return_selection=True)
+    torch.cuda.synchronize()
+    print("  forward done", flush=True)
+    rng = np.random.default_rng(9)
+    L = k.shape[1]
+    for s in range(q.shape[0]):
+        kb = O.block_mean(to64(k[s]), w.block_size)
+        qh = to64(q[s])
+        positions = np.array([L - 1])
+        sel_np = sel[s].cpu().numpy()
+        ntie, _ = check_selection(qh, positions, kb, sel_np, w.block_size, w.topk)
+        heads = rng.choice(q.shape[2], size=8, replace=False)
+        pairs = [(int(h), 0) for h in heads]
+        emax, emean = check_outputs(to64(out[s]), qh, positions, sel_np, w.block_size, L,
+                                    w.dtype, pairs, device_fetch(k[s], v[s]), k.shape[2])
+        print(f"  seq {s}: tie {ntie} max|err| {emax:.2e} mean|err| {emean:.2e}", flush=True)
