@@ -13,7 +13,8 @@ region.  Prints one JSON line.
   speedup      time of the library's own full causal attention at the same
                shape / time of the MoBA forward.
   also         the same figures at the 1M-token prefill (32/8 heads, block
-               4096, top-k 12).
+               4096, top-k 12), and the batch-8 decode against a 1M-token
+               cache in GB/s of algorithmic bytes against the HBM peak.
   roofline     the dominant kernel (routed attention): its algorithmic FLOPs
                per launch / its average launch time from HIP events recorded
                on the launch stream, against the 2.5 PFLOP/s bf16 dense MFMA
@@ -154,6 +155,65 @@ def run_prefill(moba, w, steps, warmup, full_steps, full_warmup, with_full=True)
     return res
 
 
+def run_decode(moba, w, steps, warmup):
+    """Decode against a long cache: one moba_forward_ex call with the block
+    means precomputed (untimed, as a decode loop reuses them).  Algorithmic
+    bytes = every kept K/V block read once per (sequence, KV head) -- the
+    union over the group's heads -- plus the block means, q and out."""
+    import numpy as np
+    import torch
+    import moba_inputs
+    log(f"[bench] {w.name}: generating the cache")
+    q, k, v = moba_inputs.make_inputs(w, device="cuda:0")
+    kbar = moba.moba_block_mean(k, w.block_size)
+    S, Lq, H, D = q.shape
+    L, Hkv = k.shape[1], k.shape[2]
+    nb = L // w.block_size
+    out = torch.empty_like(q)
+    sel = torch.empty((S, H, Lq, w.topk), dtype=torch.int32, device=q.device)
+    ws = torch.empty(max(moba.moba_workspace_size(q, k, v, w.block_size, w.topk, kbar, sel), 1),
+                     dtype=torch.uint8, device=q.device)
+    fwd = lambda: moba.moba_forward_ex(q, k, v, w.block_size, w.topk, out=out,
+                                       k_block_mean=kbar, sel_out=sel, workspace=ws)
+    log(f"[bench] {w.name}: timing MoBA decode")
+    ms, wall_ms = time_region(fwd, steps, warmup)
+    kern = kernel_breakdown(moba, fwd, steps)
+    selh = sel.cpu().numpy()
+    G = H // Hkv
+    union = 0
+    for s_ in range(S):
+        for g in range(Hkv):
+            blocks = selh[s_, g * G:(g + 1) * G, 0, :].ravel()
+            union += np.unique(blocks[blocks >= 0]).size
+    esz = q.element_size()
+    kv_bytes = union * w.block_size * D * esz * 2
+    alg = kv_bytes + S * Hkv * nb * D * 4 + 2 * q.numel() * esz
+    res = {"workload": w.name, "ms": ms, "wall_ms": wall_ms, "algorithmic_bytes": alg,
+           "union_blocks_per_seq_kvhead": union / (S * Hkv),
+           "gbs": alg / (ms * 1e-3) / 1e9, "frac_of_hbm_peak": alg / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+           "kernels_ms": {k_: round(v_["avg_ms"], 4) for k_, v_ in kern.items()}}
+    if "decode_attn" in kern:
+        t = kern["decode_attn"]["avg_ms"] * 1e-3
+        res["roofline"] = {"bound": "hbm", "kernel": "decode_attn", "achieved": kv_bytes / t / 1e9,
+                           "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                           "frac": kv_bytes / t / 1e9 / PEAK_HBM_GBS, "traffic": None,
+                           "avg_launch_ms": kern["decode_attn"]["avg_ms"]}
+    fout = torch.empty_like(q)
+    fws = torch.empty(max(moba.moba_full_workspace_size(q, k, v), 1), dtype=torch.uint8,
+                      device=q.device)
+    ffn = lambda: moba.moba_full_attention_ex(q, k, v, out=fout, workspace=fws)
+    log(f"[bench] {w.name}: timing full-attention decode")
+    fms, _ = time_region(ffn, max(1, steps // 2), max(1, warmup // 2))
+    full_bytes = S * L * Hkv * D * esz * 2 + 2 * q.numel() * esz
+    res["full_ms"] = fms
+    res["full_gbs"] = full_bytes / (fms * 1e-3) / 1e9
+    res["full_frac_of_hbm_peak"] = res["full_gbs"] / PEAK_HBM_GBS
+    res["speedup_vs_full"] = fms / ms
+    del q, k, v, out, ws, fout, fws, kbar
+    torch.cuda.empty_cache()
+    return res
+
+
 def roofline(res):
     kern = res["_roofline_src"]
     if "attn_routed" not in kern:
@@ -220,6 +280,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--skip-1m", action="store_true", help="skip the 1M-token prefill")
+    ap.add_argument("--skip-decode", action="store_true", help="skip the 1M-cache decode")
     ap.add_argument("--skip-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--workload", default=None,
@@ -268,6 +329,9 @@ def main():
         r1["roofline"] = roofline(r1)
         r1.pop("_roofline_src")
         also["prefill_1m"] = r1
+    if not args.skip_decode:
+        also["decode_1m"] = run_decode(moba, moba_inputs.WORKLOADS["decode_1m"], args.steps,
+                                       args.warmup)
     rl = roofline(main_res)
     main_res.pop("_roofline_src")
     cpu = None if args.skip_cpu else cpu_baseline(w, args.cpu_budget)

@@ -32,12 +32,13 @@ moba_status fail(moba_status s, const char* fmt, ...) {
 // ---------------------------------------------------------------- profiling
 enum KernelId {
   K_BLOCK_MEAN, K_TRANSPOSE_V, K_GATE, K_RCOUNT, K_RSCAN_ROWS, K_RSCAN_BUCKETS, K_RSCATTER,
-  K_ATTN_ROUTED, K_ATTN_OWN, K_ATTN_FULL, K_DEC_PLAN, K_DEC_ATTN, K_DEC_MERGE, K_COUNT
+  K_ATTN_ROUTED, K_ATTN_OWN, K_ATTN_FULL, K_DEC_PLAN, K_DEC_ATTN, K_DEC_MERGE, K_MERGE,
+  K_COUNT
 };
 const char* const kKernelNames[K_COUNT] = {
     "block_mean", "transpose_v", "gate_topk", "route_count", "route_scan_rows",
     "route_scan_buckets", "route_scatter", "attn_routed", "attn_own_merge", "attn_full",
-    "decode_plan", "decode_attn", "decode_merge"};
+    "decode_plan", "decode_attn", "decode_merge", "merge_partials"};
 
 struct ProfRecord {
   int id;
@@ -87,6 +88,31 @@ struct Launch {
   }
 };
 
+// ------------------------------------------------------------ side stream
+// One non-blocking stream per device (default priority), created on first use
+// and kept for the life of the process.  The own-block attention runs on it
+// concurrently with the gate and routing; fork/join events are per call.
+constexpr int kMaxDevices = 64;
+std::mutex g_side_mu;
+hipStream_t g_side[kMaxDevices] = {};
+
+hipError_t side_stream(hipStream_t* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> g(g_side_mu);
+  if (!g_side[dev]) {
+    e = hipStreamCreateWithFlags(&g_side[dev], hipStreamNonBlocking);
+    if (e != hipSuccess) {
+      g_side[dev] = nullptr;
+      return e;
+    }
+  }
+  *out = g_side[dev];
+  return hipSuccess;
+}
+
 // ------------------------------------------------------------------ checks
 bool mul_ok(int64_t a, int64_t b, int64_t* out) {
   if (a < 0 || b < 0) return false;
@@ -103,6 +129,8 @@ struct Plan {
   size_t off_kbar = 0, off_vt = 0, off_sel = 0, off_counts = 0, off_btotal = 0, off_boff = 0,
          off_toff = 0, off_list = 0, off_po = 0, off_plse = 0, total = 0;
   size_t off_ublk = 0, off_umask = 0, off_ucount = 0, off_part = 0, off_bmpart = 0;
+  size_t off_own_o = 0, off_own_lse = 0;
+  bool split_own = false;  // own block on the side stream + separate merge
 };
 
 moba_status check_common(const moba_args* a, bool full, Plan* p) {
@@ -170,6 +198,10 @@ moba_status plan_forward(const moba_args* a, Plan* p) {
   if (slots >= ((int64_t)1 << 32))
     return fail(MOBA_ERR_UNSUPPORTED, "more than 2^32 routed slots");
   d.slots = slots;
+  // Routed tiles of 256 entries (8-wave workgroups) once there are enough of
+  // them to fill the chip several times over; 128 otherwise.  The fp32 path
+  // always uses 128.
+  d.tile_m = (d.bf16 && slots / 256 >= 8192) ? 256 : 128;
   if ((int64_t)d.S * d.H * d.nchunk_r >= ((int64_t)1 << 31))
     return fail(MOBA_ERR_UNSUPPORTED, "too many routing chunks");
   const int64_t esz = d.bf16 ? 2 : 4;
@@ -205,6 +237,15 @@ moba_status plan_forward(const moba_args* a, Plan* p) {
     p->off_list = take((size_t)d.slots * 4);
     p->off_po = take((size_t)d.slots * d.D * esz);
     p->off_plse = take((size_t)d.slots * 4);
+    // Small problems: run the own block concurrently with the routing (its
+    // workgroups alone do not fill the chip).  Large ones fill the chip with
+    // the routed attention already, and the fused own-block + merge is cheaper.
+    if (d.bf16 && (int64_t)d.S * d.H * d.Lq <= ((int64_t)1 << 20)) {
+      p->split_own = true;
+      const size_t nqh = (size_t)d.S * d.H * d.Lq;
+      p->off_own_o = take(nqh * d.D * 2);
+      p->off_own_lse = take(nqh * 4);
+    }
   }
   p->total = off;
   if (a->workspace && a->workspace_bytes < p->total)
@@ -307,11 +348,56 @@ moba_status forward_impl(const moba_args* a) {
   float* plse = (float*)(w + p.off_plse);
 
   Launch l{(hipStream_t)a->stream};
+  float* bm_partial = (float*)(w + p.off_bmpart);
+  // the V transpose finishes the block means when both run (one launch less)
+  const bool fold_mean = p.need_kbar && p.need_vt && moba::block_mean_partial_floats(d) > 0;
   if (p.need_kbar)
     l.run(K_BLOCK_MEAN, [&] {
-      return moba::launch_block_mean(a->k, kbar, (float*)(w + p.off_bmpart), d, l.st);
+      return moba::launch_block_mean(a->k, kbar, bm_partial, d, l.st, fold_mean);
     });
-  l.run(K_GATE, [&] { return moba::launch_gate_topk(a->q, kbar, sel, d, l.st); });
+  if (p.need_vt)
+    l.run(K_TRANSPOSE_V, [&] {
+      return moba::launch_transpose_v(a->v, vt, d, l.st, fold_mean ? bm_partial : nullptr,
+                                      fold_mean ? kbar : nullptr);
+    });
+  if (l.err != hipSuccess) return hip_fail(l);
+
+  // Small bf16 problems: the own-block attention (needs only V^T) runs on the
+  // side stream while the gate, routing and routed attention run here.
+  void* own_o = (void*)(w + p.off_own_o);
+  float* own_lse = (float*)(w + p.off_own_lse);
+  hipStream_t side = nullptr;
+  hipEvent_t join = nullptr;
+  Launch ls{nullptr};
+  if (p.split_own) {
+    hipEvent_t fork = nullptr;
+    hipError_t e = side_stream(&side);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&fork, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&join, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventRecord(fork, l.st);
+    if (e == hipSuccess) e = hipStreamWaitEvent(side, fork, 0);
+    if (fork) (void)hipEventDestroy(fork);
+    if (e != hipSuccess) {
+      if (join) (void)hipEventDestroy(join);
+      return fail(MOBA_ERR_HIP, "side stream setup failed: %s", hipGetErrorString(e));
+    }
+    ls.st = side;
+    ls.run(K_ATTN_OWN, [&] {
+      return moba::launch_attn_query_bf16(a->q, a->k, vt, own_o, own_lse, nullptr, 2, d, side);
+    });
+    const hipError_t ej = hipEventRecord(join, side);
+    if (ls.err != hipSuccess || ej != hipSuccess) {
+      (void)hipEventDestroy(join);
+      if (ls.err != hipSuccess) return hip_fail(ls);
+      return fail(MOBA_ERR_HIP, "side stream join failed: %s", hipGetErrorString(ej));
+    }
+  }
+
+  // the gate writes the routing histogram itself when it can
+  const bool gate_counts = p.routed && moba::gate_writes_counts(d);
+  l.run(K_GATE, [&] {
+    return moba::launch_gate_topk(a->q, kbar, sel, d, l.st, gate_counts ? counts : nullptr);
+  });
   if (p.decode) {
     int32_t* ublk = (int32_t*)(w + p.off_ublk);
     uint32_t* umask = (uint32_t*)(w + p.off_umask);
@@ -328,9 +414,9 @@ moba_status forward_impl(const moba_args* a) {
     if (l.err != hipSuccess) return hip_fail(l);
     return MOBA_OK;
   }
-  if (p.need_vt) l.run(K_TRANSPOSE_V, [&] { return moba::launch_transpose_v(a->v, vt, d, l.st); });
   if (p.routed) {
-    l.run(K_RCOUNT, [&] { return moba::launch_route_count(sel, counts, d, l.st); });
+    if (!gate_counts)
+      l.run(K_RCOUNT, [&] { return moba::launch_route_count(sel, counts, d, l.st); });
     l.run(K_RSCAN_ROWS, [&] { return moba::launch_route_scan_rows(counts, btotal, d, l.st); });
     l.run(K_RSCAN_BUCKETS,
           [&] { return moba::launch_route_scan_buckets(btotal, boff, toff, d, l.st); });
@@ -342,6 +428,17 @@ moba_status forward_impl(const moba_args* a) {
                     : moba::launch_attn_routed_f32(a->q, a->k, a->v, list, boff, toff, po, plse,
                                                    d, l.st);
     });
+  }
+  if (p.split_own) {
+    const hipError_t ew = hipStreamWaitEvent(l.st, join, 0);
+    (void)hipEventDestroy(join);
+    if (ew != hipSuccess)
+      return fail(MOBA_ERR_HIP, "side stream join failed: %s", hipGetErrorString(ew));
+    l.run(K_MERGE, [&] {
+      return moba::launch_merge_partials_bf16(own_o, own_lse, po, plse, a->out, d, l.st);
+    });
+    if (l.err != hipSuccess) return hip_fail(l);
+    return MOBA_OK;
   }
   Dims dq = d;
   if (!p.routed) dq.kp = 0;  // nothing to merge

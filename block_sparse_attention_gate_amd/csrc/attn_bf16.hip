@@ -11,7 +11,9 @@
 //     "MoBAの技術的原則"), then merges the routed partials of that query by
 //     their log-sum-exp, which gives one softmax over the union of the
 //     selected keys.  Mode 1: full causal attention (the topk = all case of
-//     the full/sparse switch, "MoBA" project card, "How It Works").
+//     the full/sparse switch, "MoBA" project card, "How It Works").  Mode 2:
+//     the own block only, written as a partial (o, log-sum-exp) for
+//     k_merge_partials, so that it can run concurrently with the routing.
 //
 // Wave tile: 32 queries (lane l owns query l%32) x 64 keys per step.
 //   S^T = K Q^T on 32x32x16 MFMA (K rows in the kperm order, see common.h),
@@ -24,59 +26,59 @@
 
 namespace moba {
 
-template <int D>
+template <int D, int NW = 4>
 struct Tiles {
+  static constexpr int NT = 64 * NW;  // threads per workgroup
   static constexpr int KS = D + 8;   // K tile row stride (elements)
   static constexpr int VS = 64 + 8;  // V^T tile row stride (elements)
   static constexpr int KE = 64 * KS;
   static constexpr int VE = D * VS;
   static constexpr int BUF = KE + VE;
-  static constexpr int KCH = 64 * (D / 8) / 256;  // 16-byte K chunks per thread
-  static constexpr int VCH = D * 8 / 256;         // 16-byte V^T chunks per thread
+  static constexpr int KCH = 64 * (D / 8) / NT;  // 16-byte K chunks per thread
+  static constexpr int VCH = D * 8 / NT;         // 16-byte V^T chunks per thread
 };
 
-// Global -> register staging of one 64-key tile (all 256 threads).  The
+// Global -> register staging of one 64-key tile (all threads).  The
 // per-thread offsets inside a tile are fixed; only the tile base (uniform)
 // moves, so the loop does no per-thread 64-bit address arithmetic.
-template <int D>
+template <int D, int NW>
 struct TileRegs {
-  u32x4 kr[Tiles<D>::KCH];
-  u32x4 vr[Tiles<D>::VCH];
-  int koff[Tiles<D>::KCH];   // element offsets inside a K tile (global)
-  int voff[Tiles<D>::VCH];   // element offsets inside a V^T tile (global)
-  int kls[Tiles<D>::KCH];    // LDS element offsets
-  int vls[Tiles<D>::VCH];
+  using T = Tiles<D, NW>;
+  u32x4 kr[T::KCH];
+  u32x4 vr[T::VCH];
+  int koff[T::KCH];   // element offsets inside a K tile (global)
+  int voff[T::VCH];   // element offsets inside a V^T tile (global)
+  int kls[T::KCH];    // LDS element offsets
+  int vls[T::VCH];
 
   __device__ __forceinline__ void setup(int krow_stride, int L, int tid) {
 #pragma unroll
-    for (int i = 0; i < Tiles<D>::KCH; ++i) {
-      const int c = tid + 256 * i;
+    for (int i = 0; i < T::KCH; ++i) {
+      const int c = tid + T::NT * i;
       const int row = c / (D / 8), cc = c % (D / 8);
       koff[i] = row * krow_stride + cc * 8;
-      kls[i] = row * Tiles<D>::KS + cc * 8;
+      kls[i] = row * T::KS + cc * 8;
     }
 #pragma unroll
-    for (int i = 0; i < Tiles<D>::VCH; ++i) {
-      const int c = tid + 256 * i;
+    for (int i = 0; i < T::VCH; ++i) {
+      const int c = tid + T::NT * i;
       const int dd = c / 8, kc = c % 8;
       voff[i] = dd * L + kc * 8;
-      vls[i] = Tiles<D>::KE + dd * Tiles<D>::VS + kc * 8;
+      vls[i] = T::KE + dd * T::VS + kc * 8;
     }
   }
   // ktile / vttile: K row `key0` and V^T column `key0` of the tile (uniform).
   __device__ __forceinline__ void load(const bf16_t* ktile, const bf16_t* vttile) {
 #pragma unroll
-    for (int i = 0; i < Tiles<D>::KCH; ++i)
-      kr[i] = *reinterpret_cast<const u32x4*>(ktile + koff[i]);
+    for (int i = 0; i < T::KCH; ++i) kr[i] = *reinterpret_cast<const u32x4*>(ktile + koff[i]);
 #pragma unroll
-    for (int i = 0; i < Tiles<D>::VCH; ++i)
-      vr[i] = *reinterpret_cast<const u32x4*>(vttile + voff[i]);
+    for (int i = 0; i < T::VCH; ++i) vr[i] = *reinterpret_cast<const u32x4*>(vttile + voff[i]);
   }
   __device__ __forceinline__ void store(bf16_t* buf) const {
 #pragma unroll
-    for (int i = 0; i < Tiles<D>::KCH; ++i) *reinterpret_cast<u32x4*>(buf + kls[i]) = kr[i];
+    for (int i = 0; i < T::KCH; ++i) *reinterpret_cast<u32x4*>(buf + kls[i]) = kr[i];
 #pragma unroll
-    for (int i = 0; i < Tiles<D>::VCH; ++i) *reinterpret_cast<u32x4*>(buf + vls[i]) = vr[i];
+    for (int i = 0; i < T::VCH; ++i) *reinterpret_cast<u32x4*>(buf + vls[i]) = vr[i];
   }
 };
 
@@ -154,16 +156,18 @@ __device__ __forceinline__ void flash_step(const bf16_t* buf, const bf16x8 (&qf)
   }
   acc.l += psum;
   acc.m = mnew;
-  const bf16_t* vbase = buf + T::KE + 8 * hh;
+  // O^T += V^T P^T: the D/32 accumulators are independent; interleave them.
+  const bf16_t* vbase = buf + T::KE + 8 * hh + n * T::VS;
+  bf16x8 va[D / 32][4];
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) {
-    const bf16_t* vrow = vbase + (32 * dt + n) * T::VS;
-    bf16x8 va[4];
+  for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) va[kc] = ld_bf16x8(vrow + 16 * kc);
+    for (int kc = 0; kc < 4; ++kc) va[dt][kc] = ld_bf16x8(vbase + 32 * dt * T::VS + 16 * kc);
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) acc.o[dt] = mfma32(va[kc], pb[kc >> 1][kc & 1], acc.o[dt]);
-  }
+  for (int kc = 0; kc < 4; ++kc)
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+      acc.o[dt] = mfma32(va[dt][kc], pb[kc >> 1][kc & 1], acc.o[dt]);
 }
 
 template <int D>
@@ -182,14 +186,15 @@ __device__ __forceinline__ void load_q(const bf16_t* qrow, bool valid, int hh,
 // on XCD b % 8, and XCD x takes the contiguous tile range
 // [x*per, (x+1)*per), so the tiles of one bucket (same K/V block) share an L2.
 // ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(256, 2) void k_attn_routed(
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_routed(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ vt,
     const uint32_t* __restrict__ list, const uint32_t* __restrict__ bucket_off,
     const uint32_t* __restrict__ tile_off, bf16_t* __restrict__ po, float* __restrict__ plse,
     int64_t Lq, int64_t L, int H, int Hkv, int kp, int B, int nb, int nrows, float sl2,
     uint32_t nslots) {
-  using T = Tiles<D>;
+  using T = Tiles<D, NW>;
+  constexpr int TM = 32 * NW;  // routed entries per tile
   __shared__ __attribute__((aligned(16))) bf16_t lds[2 * T::BUF];
   const uint32_t ntiles = tile_off[nrows];
   const uint32_t per = (ntiles + 7) / 8;
@@ -203,9 +208,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_routed(
     if (tile_off[mid] <= tile) lo = mid; else hi = mid;
   }
   const int row = lo;
-  const uint32_t start = (tile - tile_off[row]) * kRoutedTileM;
+  const uint32_t start = (tile - tile_off[row]) * TM;
   const uint32_t avail = bucket_off[row + 1] - bucket_off[row] - start;
-  const int cnt = avail < (uint32_t)kRoutedTileM ? (int)avail : kRoutedTileM;
+  const int cnt = avail < (uint32_t)TM ? (int)avail : TM;
   const int j = row % nb;
   const int sg = row / nb, g = sg % Hkv, s = sg / Hkv;
 
@@ -228,7 +233,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_routed(
   const int nsteps = B / 64;
   FlashAcc<D> acc;
   acc.init();
-  TileRegs<D> tr;
+  TileRegs<D, NW> tr;
   tr.setup(Hkv * D, (int)L, tid);
   const int64_t ktile_step = (int64_t)64 * Hkv * D;
   const bf16_t* ktile = kbase + kstart * Hkv * D;
@@ -282,14 +287,14 @@ __global__ __launch_bounds__(256, 2) void k_attn_routed(
 // wave w takes head h0 + w % HW and rows [r0 + 32*(w / HW), +32).
 // grid (ceil(Lq / RW), S * H / HW).
 // ---------------------------------------------------------------------------
-template <int D, int MODE>
-__global__ __launch_bounds__(256, 2) void k_attn_query(
+template <int D, int MODE, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_query(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ vt,
     const bf16_t* __restrict__ po, const float* __restrict__ plse, bf16_t* __restrict__ out,
     int Lq, int L, int q_off, int H, int Hkv, int kp, int B, int HW, float sl2) {
-  using T = Tiles<D>;
+  using T = Tiles<D, NW>;
   __shared__ __attribute__((aligned(16))) bf16_t lds[2 * T::BUF];
-  const int RW = 128 / HW;
+  const int RW = 32 * NW / HW;
   const int rt = (MODE == 1) ? (int)(gridDim.x - 1 - blockIdx.x) : (int)blockIdx.x;
   const int hgroups = H / HW;
   const int s = blockIdx.y / hgroups;
@@ -306,13 +311,13 @@ __global__ __launch_bounds__(256, 2) void k_attn_query(
   const int pos = q_off + r;
   // key windows [klo, khi)
   const int wlast = (r0 + 31 < Lq ? r0 + 31 : Lq - 1);
-  const int klo_w = (MODE == 0) ? ((q_off + r0) / B) * B : 0;
+  const int klo_w = (MODE != 1) ? ((q_off + r0) / B) * B : 0;
   const int khi_w = wave_on ? q_off + wlast + 1 : 0;
   const int wglast = (rw0 + RW - 1 < Lq ? rw0 + RW - 1 : Lq - 1);
-  const int klo_g = (MODE == 0) ? ((q_off + rw0) / B) * B : 0;
+  const int klo_g = (MODE != 1) ? ((q_off + rw0) / B) * B : 0;
   const int khi_g = q_off + wglast + 1;
   const int t0 = klo_g / 64, t1 = (khi_g + 63) / 64;
-  const int klo_l = (MODE == 0) ? (pos / B) * B : 0;
+  const int klo_l = (MODE != 1) ? (pos / B) * B : 0;
 
   bf16x8 qf[D / 16];
   load_q<D>(q + (((int64_t)s * Lq + (valid ? r : 0)) * H + h) * D, valid, hh, qf);
@@ -321,7 +326,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_query(
   const int pos_first = q_off + r0;        // smallest query position of the wave
   FlashAcc<D> acc;
   acc.init();
-  TileRegs<D> tr;
+  TileRegs<D, NW> tr;
   tr.setup(Hkv * D, L, tid);
   const int64_t ktile_step = (int64_t)64 * Hkv * D;
   const bf16_t* ktile = kbase + (int64_t)t0 * ktile_step;
@@ -378,6 +383,12 @@ __global__ __launch_bounds__(256, 2) void k_attn_query(
   const float ltot = acc.l + half_swap(acc.l);
   bf16_t* orow = out + (((int64_t)s * Lq + r) * H + h) * D;
   float inv = 1.0f / ltot;
+  if (MODE == 2) {
+    // own-block partial of query-head qh: normalised o (bf16) and log2-sum-exp
+    const int64_t qh = ((int64_t)s * H + h) * Lq + r;
+    orow = const_cast<bf16_t*>(po) + qh * D;
+    if (hh == 0) const_cast<float*>(plse)[qh] = acc.m + __log2f(ltot);
+  }
   if (MODE == 0 && kp > 0) {
     // Merge: out = sum_x 2^(lse_x - M) o_x / sum_x 2^(lse_x - M) over the own
     // partial and the routed partials of this query.
@@ -426,6 +437,85 @@ __global__ __launch_bounds__(256, 2) void k_attn_query(
     }
 }
 
+// Merge of the own-block partial with the routed partials of every
+// query-head: out = sum_x 2^(lse_x - M) o_x / sum_x 2^(lse_x - M).  16 lanes
+// per query-head, D/16 dims per lane.  grid ceil(nqh / 16), 256 threads.
+template <int D>
+__global__ __launch_bounds__(256) void k_merge_partials(
+    const bf16_t* __restrict__ own_o, const float* __restrict__ own_lse,
+    const bf16_t* __restrict__ po, const float* __restrict__ plse, bf16_t* __restrict__ out,
+    int64_t nqh, int64_t Lq, int H, int64_t q_off, int B, int kp) {
+  constexpr int EPL = D / 16;
+  const int64_t qh = (int64_t)blockIdx.x * 16 + threadIdx.x / 16;
+  if (qh >= nqh) return;
+  const int sub = threadIdx.x % 16;
+  const int64_t r = qh % Lq, sh = qh / Lq;
+  const int h = (int)(sh % H);
+  const int64_t s = sh / H;
+  const int64_t own = (q_off + r) / B;
+  const int npast = (int)(kp < own ? kp : own);
+  const float lse0 = own_lse[qh];
+  float M = lse0;
+  for (int t = 0; t < npast; ++t) M = fmaxf(M, plse[qh * kp + t]);
+  float acc[EPL];
+  auto load = [&](const bf16_t* p, float (&x)[EPL]) {
+    if (EPL == 8) {
+      const u32x4 raw = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[2 * i] = __uint_as_float(raw[i] << 16);
+        x[2 * i + 1] = __uint_as_float(raw[i] & 0xffff0000u);
+      }
+    } else {
+      const uint2 raw = *reinterpret_cast<const uint2*>(p);
+      x[0] = __uint_as_float(raw.x << 16);
+      x[1] = __uint_as_float(raw.x & 0xffff0000u);
+      x[2] = __uint_as_float(raw.y << 16);
+      x[3] = __uint_as_float(raw.y & 0xffff0000u);
+    }
+  };
+  float x[EPL];
+  load(own_o + qh * D + sub * EPL, x);
+  const float w0 = __builtin_amdgcn_exp2f(lse0 - M);
+  float wsum = w0;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) acc[i] = w0 * x[i];
+  for (int t = 0; t < npast; ++t) {
+    const float wt = __builtin_amdgcn_exp2f(plse[qh * kp + t] - M);
+    wsum += wt;
+    load(po + (qh * kp + t) * D + sub * EPL, x);
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) acc[i] = fmaf(wt, x[i], acc[i]);
+  }
+  const float inv = 1.0f / wsum;
+  bf16_t* orow = out + ((s * Lq + r) * H + h) * D + sub * EPL;
+  uint32_t wds[EPL / 2];
+#pragma unroll
+  for (int i = 0; i < EPL / 2; ++i)
+    wds[i] = (uint32_t)f32_to_bf16(acc[2 * i] * inv) |
+             ((uint32_t)f32_to_bf16(acc[2 * i + 1] * inv) << 16);
+  if (EPL == 8)
+    *reinterpret_cast<u32x4*>(orow) = u32x4{wds[0], wds[1], wds[EPL / 2 > 2 ? 2 : 0],
+                                            wds[EPL / 2 > 3 ? 3 : 0]};
+  else
+    *reinterpret_cast<uint2*>(orow) = make_uint2(wds[0], wds[1]);
+}
+
+hipError_t launch_merge_partials_bf16(const void* own_o, const float* own_lse, const void* po,
+                                      const float* plse, void* out, const Dims& d,
+                                      hipStream_t st) {
+  const int64_t nqh = (int64_t)d.S * d.H * d.Lq;
+  const unsigned grid = (unsigned)((nqh + 15) / 16);
+#define MOBA_MERGE(DV)                                                                       \
+  hipLaunchKernelGGL(k_merge_partials<DV>, dim3(grid), dim3(256), 0, st,                     \
+                     static_cast<const bf16_t*>(own_o), own_lse,                             \
+                     static_cast<const bf16_t*>(po), plse, static_cast<bf16_t*>(out), nqh,   \
+                     d.Lq, d.H, d.q_off, d.B, d.kp)
+  if (d.D == 128) MOBA_MERGE(128); else MOBA_MERGE(64);
+#undef MOBA_MERGE
+  return hipGetLastError();
+}
+
 static int gcd_int(int a, int b) {
   while (b) { const int t = a % b; a = b; b = t; }
   return a;
@@ -437,13 +527,17 @@ hipError_t launch_attn_routed_bf16(const void* q, const void* k, const void* vt,
                                    const Dims& d, hipStream_t st) {
   const int64_t grid = routed_tile_bound(d);
   const float sl2 = kLog2e / sqrtf((float)d.D);
-#define MOBA_ROUTED(DV)                                                                      \
-  hipLaunchKernelGGL(k_attn_routed<DV>, dim3((unsigned)grid), dim3(256), 0, st,              \
+#define MOBA_ROUTED(DV, NWV)                                                                 \
+  hipLaunchKernelGGL((k_attn_routed<DV, NWV>), dim3((unsigned)grid), dim3(64 * NWV), 0, st,  \
                      static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),           \
                      static_cast<const bf16_t*>(vt), list, bucket_off, tile_off,             \
                      static_cast<bf16_t*>(part_o), part_lse, d.Lq, d.L, d.H, d.Hkv, d.kp,    \
                      d.B, d.nb, d.nrows, sl2, (uint32_t)d.slots)
-  if (d.D == 128) MOBA_ROUTED(128); else MOBA_ROUTED(64);
+  if (d.tile_m == 256) {
+    if (d.D == 128) MOBA_ROUTED(128, 8); else MOBA_ROUTED(64, 8);
+  } else {
+    if (d.D == 128) MOBA_ROUTED(128, 4); else MOBA_ROUTED(64, 4);
+  }
 #undef MOBA_ROUTED
   return hipGetLastError();
 }
@@ -452,20 +546,30 @@ hipError_t launch_attn_query_bf16(const void* q, const void* k, const void* vt,
                                   const void* part_o, const float* part_lse, void* out, int mode,
                                   const Dims& d, hipStream_t st) {
   const int HW = gcd_int(d.G, 4);
-  const int RW = 128 / HW;
+  // eight waves per workgroup when that still gives >= 2048 workgroups
+  const int64_t wgs8 = (d.Lq + 256 / HW - 1) / (256 / HW) * (int64_t)(d.S * d.H / HW);
+  const int NW = wgs8 >= 2048 ? 8 : 4;
+  const int RW = 32 * NW / HW;
   dim3 grid((unsigned)((d.Lq + RW - 1) / RW), d.S * d.H / HW);
   const float sl2 = kLog2e / sqrtf((float)d.D);
-#define MOBA_QUERY(DV, MV)                                                                   \
-  hipLaunchKernelGGL((k_attn_query<DV, MV>), grid, dim3(256), 0, st,                         \
+#define MOBA_QUERY(DV, MV, NWV)                                                              \
+  hipLaunchKernelGGL((k_attn_query<DV, MV, NWV>), grid, dim3(64 * NWV), 0, st,               \
                      static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),           \
                      static_cast<const bf16_t*>(vt), static_cast<const bf16_t*>(part_o),     \
                      part_lse, static_cast<bf16_t*>(out), (int)d.Lq, (int)d.L, (int)d.q_off, \
                      d.H, d.Hkv, d.kp, d.B, HW, sl2)
+#define MOBA_QUERY_NW(DV, MV) \
+  if (NW == 8) MOBA_QUERY(DV, MV, 8); else MOBA_QUERY(DV, MV, 4);
   if (d.D == 128) {
-    if (mode == 0) MOBA_QUERY(128, 0); else MOBA_QUERY(128, 1);
+    if (mode == 0) { MOBA_QUERY_NW(128, 0) }
+    else if (mode == 1) { MOBA_QUERY_NW(128, 1) }
+    else { MOBA_QUERY_NW(128, 2) }
   } else {
-    if (mode == 0) MOBA_QUERY(64, 0); else MOBA_QUERY(64, 1);
+    if (mode == 0) { MOBA_QUERY_NW(64, 0) }
+    else if (mode == 1) { MOBA_QUERY_NW(64, 1) }
+    else { MOBA_QUERY_NW(64, 2) }
   }
+#undef MOBA_QUERY_NW
 #undef MOBA_QUERY
   return hipGetLastError();
 }

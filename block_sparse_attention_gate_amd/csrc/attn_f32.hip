@@ -111,7 +111,7 @@ __global__ __launch_bounds__(F32Tile<D>::NT) void k_attn_routed_f32(
     const uint32_t* __restrict__ list, const uint32_t* __restrict__ bucket_off,
     const uint32_t* __restrict__ tile_off, float* __restrict__ po, float* __restrict__ plse,
     int64_t Lq, int64_t L, int H, int Hkv, int kp, int B, int nb, int nrows, float scale,
-    uint32_t nslots) {
+    uint32_t nslots, int tile_m) {
   using T = F32Tile<D>;
   __shared__ __attribute__((aligned(16))) float ks[32 * D];
   __shared__ __attribute__((aligned(16))) float vs[32 * D];
@@ -124,9 +124,9 @@ __global__ __launch_bounds__(F32Tile<D>::NT) void k_attn_routed_f32(
     if (tile_off[mid] <= tile) lo = mid; else hi = mid;
   }
   const int row = lo;
-  const uint32_t start = (tile - tile_off[row]) * kRoutedTileM;
+  const uint32_t start = (tile - tile_off[row]) * tile_m;
   const uint32_t avail = bucket_off[row + 1] - bucket_off[row] - start;
-  const int cnt = avail < (uint32_t)kRoutedTileM ? (int)avail : kRoutedTileM;
+  const int cnt = avail < (uint32_t)tile_m ? (int)avail : tile_m;
   const int j = row % nb;
   const int sg = row / nb, g = sg % Hkv, s = sg / Hkv;
   const int tid = threadIdx.x;
@@ -255,7 +255,7 @@ hipError_t launch_attn_routed_f32(const void* q, const void* k, const void* v,
                      st, static_cast<const float*>(q), static_cast<const float*>(k),        \
                      static_cast<const float*>(v), list, bucket_off, tile_off,              \
                      static_cast<float*>(part_o), part_lse, d.Lq, d.L, d.H, d.Hkv, d.kp,    \
-                     d.B, d.nb, d.nrows, scale, (uint32_t)d.slots)
+                     d.B, d.nb, d.nrows, scale, (uint32_t)d.slots, d.tile_m)
   if (d.D == 128) MOBA_RF32(128); else MOBA_RF32(64);
 #undef MOBA_RF32
   return hipGetLastError();

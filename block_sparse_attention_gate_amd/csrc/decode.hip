@@ -59,13 +59,16 @@ __global__ __launch_bounds__(64) void k_decode_plan(const int32_t* __restrict__ 
   if (lane == 0) ucount[sg] = base < umax ? base : umax;
 }
 
-// grid (chunks per block, umax, S*Hkv), 256 threads.  GM = max heads per group.
+// 1-D grid over (sequence * KV head) x union slot x chunk with the (sequence,
+// KV head) index fastest: neighbouring workgroups read different KV heads,
+// whose rows interleave in HBM, instead of piling onto one head's rows.
+// 256 threads.  GM = max heads per group.
 template <typename T, int D, int GM>
 __global__ __launch_bounds__(256) void k_decode_attn(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const int32_t* __restrict__ ublk, const uint32_t* __restrict__ umask,
     const int32_t* __restrict__ ucount, float* __restrict__ part, int64_t L, int H, int Hkv,
-    int B, int umax, float scale_log2) {
+    int B, int umax, float scale_log2, int nsg) {
   constexpr int VEC = 16 / sizeof(T);   // elements per 16-byte load
   constexpr int KPT = kDecChunk / 256;  // keys per thread in the score phase
   constexpr int DG = D / 8;             // d-groups of 8 in the P.V phase
@@ -76,8 +79,11 @@ __global__ __launch_bounds__(256) void k_decode_attn(
   __shared__ float stat[GM][2];
   __shared__ float wred[4];
 
-  const int sg = blockIdx.z, u = blockIdx.y, c = blockIdx.x;
-  if (u >= ucount[sg]) return;
+  const int cpb = B / kDecChunk;
+  const int sg = (int)(blockIdx.x % nsg);
+  const int rest = (int)(blockIdx.x / nsg);
+  const int u = rest % umax, c = rest / umax;
+  if (u >= ucount[sg] || c >= cpb) return;
   const int s = sg / Hkv, g = sg % Hkv, G = H / Hkv;
   const int j = ublk[(int64_t)sg * umax + u];
   const uint32_t mask = umask[(int64_t)sg * umax + u];
@@ -95,27 +101,21 @@ __global__ __launch_bounds__(256) void k_decode_attn(
   for (int kk = 0; kk < KPT; ++kk) {
     const int key = tid + 256 * kk;
     const T* krow = kb + (int64_t)key * Hkv * D;
-    float acc[GM];
+    // the whole row is requested before any arithmetic (memory-level parallelism)
+    u32x4 raw[D / VEC];
 #pragma unroll
-    for (int hl = 0; hl < GM; ++hl) acc[hl] = 0.f;
-#pragma unroll 4
-    for (int d0 = 0; d0 < D; d0 += VEC) {
-      const u32x4 raw = *reinterpret_cast<const u32x4*>(krow + d0);
-      const T* e = reinterpret_cast<const T*>(&raw);
-      float x[VEC];
+    for (int i = 0; i < D / VEC; ++i) raw[i] = *reinterpret_cast<const u32x4*>(krow + i * VEC);
+    for (int hl = 0; hl < G; ++hl) {       // heads that kept this block (uniform)
+      if (!((mask >> hl) & 1u)) continue;
+      float acc = 0.f;
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) x[i] = load_as_f32(e + i);
+      for (int ci = 0; ci < D / VEC; ++ci) {
+        const T* e = reinterpret_cast<const T*>(&raw[ci]);
 #pragma unroll
-      for (int hl = 0; hl < GM; ++hl) {
-        if (hl < G && ((mask >> hl) & 1u)) {
-#pragma unroll
-          for (int i = 0; i < VEC; ++i) acc[hl] = fmaf(x[i], qs[hl][d0 + i], acc[hl]);
-        }
+        for (int i = 0; i < VEC; ++i) acc = fmaf(load_as_f32(e + i), qs[hl][ci * VEC + i], acc);
       }
+      ps[hl][key] = acc;
     }
-#pragma unroll
-    for (int hl = 0; hl < GM; ++hl)
-      if (hl < G && ((mask >> hl) & 1u)) ps[hl][key] = acc[hl];
   }
   __syncthreads();
 
@@ -153,31 +153,34 @@ __global__ __launch_bounds__(256) void k_decode_attn(
   for (int hl = 0; hl < GM; ++hl)
 #pragma unroll
     for (int i = 0; i < 8; ++i) o[hl][i] = 0.f;
-  for (int key = kg; key < kDecChunk; key += KG) {
-    const T* vrow = vb + (int64_t)key * Hkv * D;
-    float x[8];
-    if (sizeof(T) == 2) {
-      const u32x4 raw = *reinterpret_cast<const u32x4*>(vrow);
-      const T* e = reinterpret_cast<const T*>(&raw);
+  constexpr int VU = 8;                 // keys whose V rows are in flight together
+  constexpr int LPR = sizeof(T) == 2 ? 1 : 2;   // 16-byte loads per 8 elements
+  for (int key0 = kg; key0 < kDecChunk; key0 += KG * VU) {
+    u32x4 raw[VU][LPR];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] = load_as_f32(e + i);
-    } else {
-      const u32x4 r0 = *reinterpret_cast<const u32x4*>(vrow);
-      const u32x4 r1 = *reinterpret_cast<const u32x4*>(vrow + 4);
-      const T* e0 = reinterpret_cast<const T*>(&r0);
-      const T* e1 = reinterpret_cast<const T*>(&r1);
+    for (int uu = 0; uu < VU; ++uu) {
+      const T* vrow = vb + (int64_t)(key0 + uu * KG) * Hkv * D;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x[i] = load_as_f32(e0 + i);
-        x[4 + i] = load_as_f32(e1 + i);
-      }
+      for (int l2 = 0; l2 < LPR; ++l2)
+        raw[uu][l2] = *reinterpret_cast<const u32x4*>(vrow + l2 * (8 / LPR));
     }
 #pragma unroll
-    for (int hl = 0; hl < GM; ++hl) {
-      if (hl < G && ((mask >> hl) & 1u)) {
-        const float p = ps[hl][key];
+    for (int uu = 0; uu < VU; ++uu) {
+      const int key = key0 + uu * KG;
+      float x[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) o[hl][i] = fmaf(p, x[i], o[hl][i]);
+      for (int l2 = 0; l2 < LPR; ++l2) {
+        const T* e = reinterpret_cast<const T*>(&raw[uu][l2]);
+#pragma unroll
+        for (int i = 0; i < 8 / LPR; ++i) x[l2 * (8 / LPR) + i] = load_as_f32(e + i);
+      }
+#pragma unroll
+      for (int hl = 0; hl < GM; ++hl) {
+        if (hl < G && ((mask >> hl) & 1u)) {
+          const float p = ps[hl][key];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) o[hl][i] = fmaf(p, x[i], o[hl][i]);
+        }
       }
     }
   }
@@ -203,7 +206,10 @@ __global__ __launch_bounds__(256) void k_decode_attn(
   }
 }
 
-// grid S*H, D threads.
+// grid S*H, D threads.  Wave 0 lists this head's partials in a fixed order
+// (union slot, then chunk); then every thread reads the list, so the merge is
+// a few independent load streams instead of a chain of dependent loads.
+constexpr int kMergeMaxItems = 8192;
 template <typename T, int D, int GM>
 __global__ __launch_bounds__(D) void k_decode_merge(const float* __restrict__ part,
                                                     const int32_t* __restrict__ ublk,
@@ -211,36 +217,59 @@ __global__ __launch_bounds__(D) void k_decode_merge(const float* __restrict__ pa
                                                     const int32_t* __restrict__ ucount,
                                                     T* __restrict__ out, int H, int Hkv, int B,
                                                     int umax) {
+  __shared__ int items[kMergeMaxItems];
+  __shared__ float wts[kMergeMaxItems];
+  __shared__ int nitems_s;
+  __shared__ float lsum_s;
   const int sh = blockIdx.x, s = sh / H, h = sh % H, G = H / Hkv, g = h / G, hl = h % G;
   const int sg = s * Hkv + g;
-  const int dd = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int cpb = B / kDecChunk;
   const int n = ucount[sg];
+  if (tid < 64) {
+    int base = 0;
+    const uint64_t lt = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
+    for (int i0 = 0; i0 < n * cpb; i0 += 64) {
+      const int i = i0 + lane;
+      const bool ok = i < n * cpb && ((umask[(int64_t)sg * umax + i / cpb] >> hl) & 1u);
+      const uint64_t bal = __ballot(ok);
+      const int idx = base + __popcll(bal & lt);
+      if (ok && idx < kMergeMaxItems) items[idx] = (int)(((int64_t)sg * umax + i / cpb) * cpb + i % cpb);
+      base += __popcll(bal);
+    }
+    if (lane == 0) nitems_s = base < kMergeMaxItems ? base : kMergeMaxItems;
+  }
+  __syncthreads();
+  const int ni = nitems_s;
   float M = -__builtin_inff();
-  for (int u = 0; u < n; ++u) {
-    if (!((umask[(int64_t)sg * umax + u] >> hl) & 1u)) continue;
-    for (int c = 0; c < cpb; ++c) {
-      const int64_t item = ((int64_t)sg * umax + u) * cpb + c;
-      M = fmaxf(M, part[(item * GM + hl) * (D + 2)]);
-    }
+  for (int t = 0; t < ni; ++t) M = fmaxf(M, part[((int64_t)items[t] * GM + hl) * (D + 2)]);
+  for (int t = tid; t < ni; t += D) {
+    const float* prow = part + ((int64_t)items[t] * GM + hl) * (D + 2);
+    wts[t] = __builtin_amdgcn_exp2f(prow[0] - M);
   }
-  float lsum = 0.f, acc = 0.f;
-  for (int u = 0; u < n; ++u) {
-    if (!((umask[(int64_t)sg * umax + u] >> hl) & 1u)) continue;
-    for (int c = 0; c < cpb; ++c) {
-      const int64_t item = ((int64_t)sg * umax + u) * cpb + c;
-      const float* prow = part + (item * GM + hl) * (D + 2);
-      const float wgt = __builtin_amdgcn_exp2f(prow[0] - M);
-      lsum = fmaf(wgt, prow[1], lsum);
-      acc = fmaf(wgt, prow[2 + dd], acc);
-    }
+  __syncthreads();
+  if (tid == 0) {
+    float l = 0.f;
+    for (int t = 0; t < ni; ++t) l = fmaf(wts[t], part[((int64_t)items[t] * GM + hl) * (D + 2) + 1], l);
+    lsum_s = l;
   }
-  const float r = acc / lsum;
+  float acc = 0.f;
+  int t = 0;
+  for (; t + 4 <= ni; t += 4) {
+    float x[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = part[((int64_t)items[t + e] * GM + hl) * (D + 2) + 2 + tid];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = fmaf(wts[t + e], x[e], acc);
+  }
+  for (; t < ni; ++t) acc = fmaf(wts[t], part[((int64_t)items[t] * GM + hl) * (D + 2) + 2 + tid], acc);
+  __syncthreads();
+  const float r = acc / lsum_s;
   T* orow = out + ((int64_t)s * H + h) * D;
   if (sizeof(T) == 2)
-    reinterpret_cast<bf16_t*>(orow)[dd] = f32_to_bf16(r);
+    reinterpret_cast<bf16_t*>(orow)[tid] = f32_to_bf16(r);
   else
-    reinterpret_cast<float*>(orow)[dd] = r;
+    reinterpret_cast<float*>(orow)[tid] = r;
 }
 
 int decode_umax(const Dims& d) {
@@ -259,7 +288,9 @@ size_t decode_part_floats(const Dims& d) {
 }
 
 bool decode_supported(const Dims& d) {
-  return d.Lq == 1 && d.G <= 8 && d.B % kDecChunk == 0;
+  // the merge lists at most kMergeMaxItems partials per head
+  return d.Lq == 1 && d.G <= 8 && d.B % kDecChunk == 0 &&
+         (int64_t)decode_umax(d) * (d.B / kDecChunk) <= kMergeMaxItems;
 }
 
 hipError_t launch_decode_plan(const int32_t* sel, int32_t* ublk, uint32_t* umask,
@@ -276,13 +307,14 @@ static hipError_t decode_attn_gm(const void* q, const void* k, const void* v,
                                  const int32_t* ucount, float* part, const Dims& d,
                                  hipStream_t st) {
   const int umax = decode_umax(d);
-  dim3 grid(d.B / kDecChunk, umax, d.S * d.Hkv);
+  const int nsg = d.S * d.Hkv;
+  const int64_t nwg = (int64_t)nsg * umax * (d.B / kDecChunk);
   const float sl2 = kLog2e / sqrtf((float)d.D);
 #define MOBA_DEC(GMV)                                                                      \
-  hipLaunchKernelGGL((k_decode_attn<T, D, GMV>), grid, dim3(256), 0, st,                   \
+  hipLaunchKernelGGL((k_decode_attn<T, D, GMV>), dim3((unsigned)nwg), dim3(256), 0, st,    \
                      static_cast<const T*>(q), static_cast<const T*>(k),                   \
                      static_cast<const T*>(v), ublk, umask, ucount, part, d.L, d.H, d.Hkv, \
-                     d.B, umax, sl2)
+                     d.B, umax, sl2, nsg)
   switch (decode_gm(d)) {
     case 1: MOBA_DEC(1); break;
     case 2: MOBA_DEC(2); break;

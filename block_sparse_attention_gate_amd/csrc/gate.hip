@@ -18,36 +18,138 @@ namespace moba {
 // fp32 rounding), so the scores carry fp32 accuracy.  Lane l owns query
 // column l%32 and sees 16 of every 32 blocks; the two lane halves keep their
 // own top list and merge at the end.  grid (ceil(Lq/128), S*H), 256 threads.
+// With `counts` the workgroup (128 rows of one head = one routing chunk) also
+// writes the routing histogram of its kept past blocks: counts[bucket][col]
+// with col = (h - g*G) * nchunk_r + chunk (see route.hip).
 template <int D, int KM>
 __global__ __launch_bounds__(256) void k_gate_topk_bf16(
     const bf16_t* __restrict__ q, const float* __restrict__ kbar, int32_t* __restrict__ sel,
-    int64_t Lq, int64_t q_off, int H, int Hkv, int B, int nb, int topk) {
+    int64_t Lq, int64_t q_off, int H, int Hkv, int B, int nb, int topk,
+    uint32_t* __restrict__ counts, int nchunk_r, int ncols) {
+  extern __shared__ uint32_t ghist[];  // [nb] when counts != nullptr
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int n = lane & 31, hh = lane >> 5;
-  const int sh = blockIdx.y, s = sh / H, h = sh % H, g = h / (H / Hkv);
+  const int sh = blockIdx.y, s = sh / H, h = sh % H, G = H / Hkv, g = h / G;
+  if (counts) {
+    for (int j = threadIdx.x; j < nb; j += 256) ghist[j] = 0u;
+    __syncthreads();
+  }
   const int64_t rbase = (int64_t)blockIdx.x * 128 + w * 32;
-  if (rbase >= Lq) return;
+  const bool wave_on = rbase < Lq;
   const int64_t r = rbase + n;
   const bool valid = r < Lq;
   const int b = valid ? (int)((q_off + r) / B) : 0;
   const int kp = topk - 1;
   const int nkeep = kp < b ? kp : b;
+  TopList<KM> top;
+  top.init();
+  if (wave_on) {
+    bf16x8 qf[D / 16];
+    const bf16_t* qrow = q + (((int64_t)s * Lq + (valid ? r : 0)) * H + h) * D;
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) {
+      qf[t] = ld_bf16x8(qrow + 16 * t + 8 * hh);
+      if (!valid) qf[t] = bf16x8{};
+    }
+    const int64_t rlast = (rbase + 31 < Lq ? rbase + 31 : Lq - 1);
+    const int bmax = (int)((q_off + rlast) / B);
+    const float* kb = kbar + ((int64_t)s * Hkv + g) * nb * D;
+    if (kp > 0) {
+      for (int jt = 0; jt * 32 < bmax; ++jt) {
+        const int jrow = (jt * 32 + n < nb) ? jt * 32 + n : nb - 1;
+        const float* arow = kb + (int64_t)jrow * D + 8 * hh;
+        f32x16 acc = {};
+#pragma unroll
+        for (int t = 0; t < D / 16; ++t) {
+          const float4 x0 = *reinterpret_cast<const float4*>(arow + 16 * t);
+          const float4 x1 = *reinterpret_cast<const float4*>(arow + 16 * t + 4);
+          const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+          bf16x8 a0, a1, a2;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const __bf16 hi = static_cast<__bf16>(xs[e]);
+            const float r1 = xs[e] - static_cast<float>(hi);
+            const __bf16 mid = static_cast<__bf16>(r1);
+            const float r2 = r1 - static_cast<float>(mid);
+            a0[e] = hi;
+            a1[e] = mid;
+            a2[e] = static_cast<__bf16>(r2);
+          }
+          acc = mfma32(a0, qf[t], acc);
+          acc = mfma32(a1, qf[t], acc);
+          acc = mfma32(a2, qf[t], acc);
+        }
+#pragma unroll
+        for (int reg = 0; reg < 16; ++reg) {
+          const int j = jt * 32 + 8 * (reg >> 2) + 4 * hh + (reg & 3);
+          if (j < b) top.insert_ascending(acc[reg], j);
+        }
+      }
+      // Merge the other lane half's list: snapshot it first, since both halves
+      // rewrite their own lists while merging.
+      float os[KM];
+      int oi[KM];
+#pragma unroll
+      for (int t = 0; t < KM; ++t) {
+        os[t] = half_swap(top.s[t]);
+        oi[t] = __shfl_xor(top.i[t], 32);
+      }
+#pragma unroll
+      for (int t = 0; t < KM; ++t) top.insert_any(os[t], oi[t]);
+      top.truncate(kp);
+      top.sort_indices();
+    }
+    if (valid && hh == 0) {
+      int32_t* out = sel + (((int64_t)s * H + h) * Lq + r) * topk;
+#pragma unroll
+      for (int t = 0; t < KM + 1; ++t) {
+        if (t < topk) {
+          const int kept = (t < KM) ? top.i[t < KM ? t : 0] : 0;
+          out[t] = t < nkeep ? kept : (t == nkeep ? b : -1);
+          if (counts && t < nkeep) atomicAdd(&ghist[kept], 1u);
+        }
+      }
+      for (int t = KM + 1; t < topk; ++t) out[t] = -1;
+    }
+  }
+  if (counts) {
+    __syncthreads();
+    const int col = (h - g * G) * nchunk_r + blockIdx.x;
+    for (int j = threadIdx.x; j < nb; j += 256)
+      counts[(((int64_t)s * Hkv + g) * nb + j) * ncols + col] = ghist[j];
+  }
+}
 
+// q_len == 1 (decode), bf16: one workgroup per (sequence, KV head); the G
+// query heads of the group are the MFMA columns (lane l%32 = head), and the
+// four waves take every fourth 32-block tile.  Per-lane lists merge across
+// the lane halves, then across the waves through LDS.  grid S*Hkv, 256 threads.
+template <int D, int KM>
+__global__ __launch_bounds__(256) void k_gate_topk_decode_bf16(
+    const bf16_t* __restrict__ q, const float* __restrict__ kbar, int32_t* __restrict__ sel,
+    int64_t L, int H, int Hkv, int B, int nb, int topk) {
+  __shared__ float ls[4][32][KM];
+  __shared__ int li[4][32][KM];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int n = lane & 31, hh = lane >> 5;
+  const int sg = blockIdx.x, s = sg / Hkv, g = sg % Hkv, G = H / Hkv;
+  const bool valid = n < G;
+  const int h = g * G + (valid ? n : 0);
+  const int b = (int)((L - 1) / B);  // own block of the query at the last position
+  const int kp = topk - 1;
+  const int nkeep = kp < b ? kp : b;
   bf16x8 qf[D / 16];
-  const bf16_t* qrow = q + (((int64_t)s * Lq + (valid ? r : 0)) * H + h) * D;
+  const bf16_t* qrow = q + ((int64_t)s * H + h) * D;
 #pragma unroll
   for (int t = 0; t < D / 16; ++t) {
     qf[t] = ld_bf16x8(qrow + 16 * t + 8 * hh);
     if (!valid) qf[t] = bf16x8{};
   }
-  const int64_t rlast = (rbase + 31 < Lq ? rbase + 31 : Lq - 1);
-  const int bmax = (int)((q_off + rlast) / B);
-
   TopList<KM> top;
   top.init();
   const float* kb = kbar + ((int64_t)s * Hkv + g) * nb * D;
   if (kp > 0) {
-    for (int jt = 0; jt * 32 < bmax; ++jt) {
+    for (int jt = w; jt * 32 < b; jt += 4) {
       const int jrow = (jt * 32 + n < nb) ? jt * 32 + n : nb - 1;
       const float* arow = kb + (int64_t)jrow * D + 8 * hh;
       f32x16 acc = {};
@@ -77,8 +179,6 @@ __global__ __launch_bounds__(256) void k_gate_topk_bf16(
         if (j < b) top.insert_ascending(acc[reg], j);
       }
     }
-    // Merge the other lane half's list: snapshot it first, since both halves
-    // rewrite their own lists while merging.
     float os[KM];
     int oi[KM];
 #pragma unroll
@@ -88,11 +188,24 @@ __global__ __launch_bounds__(256) void k_gate_topk_bf16(
     }
 #pragma unroll
     for (int t = 0; t < KM; ++t) top.insert_any(os[t], oi[t]);
+    if (hh == 0) {
+#pragma unroll
+      for (int t = 0; t < KM; ++t) {
+        ls[w][n][t] = top.s[t];
+        li[w][n][t] = top.i[t];
+      }
+    }
+  }
+  __syncthreads();
+  if (w != 0 || hh != 0 || !valid) return;
+  if (kp > 0) {
+    for (int w2 = 1; w2 < 4; ++w2)
+#pragma unroll
+      for (int t = 0; t < KM; ++t) top.insert_any(ls[w2][n][t], li[w2][n][t]);
     top.truncate(kp);
     top.sort_indices();
   }
-  if (!valid || hh != 0) return;
-  int32_t* out = sel + (((int64_t)s * H + h) * Lq + r) * topk;
+  int32_t* out = sel + ((int64_t)s * H + h) * topk;
 #pragma unroll
   for (int t = 0; t < KM + 1; ++t) {
     if (t < topk) {
@@ -155,15 +268,20 @@ __global__ __launch_bounds__(256) void k_gate_topk_f32(
 
 template <int D>
 static hipError_t gate_dispatch_d(const void* q, const float* kbar, int32_t* sel, const Dims& d,
-                                  hipStream_t st) {
+                                  hipStream_t st, uint32_t* counts) {
   const int kp = d.topk - 1;
 #define MOBA_GATE_CASE(KMV)                                                                  \
   if (kp <= KMV) {                                                                           \
-    if (d.bf16) {                                                                            \
+    if (d.bf16 && d.Lq == 1 && d.G <= 32) {                                                  \
+      hipLaunchKernelGGL((k_gate_topk_decode_bf16<D, KMV>), dim3(d.S * d.Hkv), dim3(256), 0, \
+                         st, static_cast<const bf16_t*>(q), kbar, sel, d.L, d.H, d.Hkv, d.B, \
+                         d.nb, d.topk);                                                      \
+    } else if (d.bf16) {                                                                     \
       dim3 grid((unsigned)((d.Lq + 127) / 128), d.S * d.H);                                  \
-      hipLaunchKernelGGL((k_gate_topk_bf16<D, KMV>), grid, dim3(256), 0, st,                 \
+      hipLaunchKernelGGL((k_gate_topk_bf16<D, KMV>), grid, dim3(256),                        \
+                         counts ? d.nb * sizeof(uint32_t) : 0, st,                           \
                          static_cast<const bf16_t*>(q), kbar, sel, d.Lq, d.q_off, d.H, d.Hkv, \
-                         d.B, d.nb, d.topk);                                                 \
+                         d.B, d.nb, d.topk, counts, d.nchunk_r, d.ncols);                    \
     } else {                                                                                 \
       dim3 grid((unsigned)((d.Lq + 255) / 256), d.S * d.H);                                  \
       hipLaunchKernelGGL((k_gate_topk_f32<D, KMV>), grid, dim3(256), 0, st,                  \
@@ -182,10 +300,15 @@ static hipError_t gate_dispatch_d(const void* q, const float* kbar, int32_t* sel
   return hipErrorInvalidValue;
 }
 
+bool gate_writes_counts(const Dims& d) {
+  return d.bf16 && !(d.Lq == 1 && d.G <= 32) && kRouteChunkRows == 128;
+}
+
 hipError_t launch_gate_topk(const void* q, const float* kbar, int32_t* sel, const Dims& d,
-                            hipStream_t st) {
-  if (d.D == 128) return gate_dispatch_d<128>(q, kbar, sel, d, st);
-  return gate_dispatch_d<64>(q, kbar, sel, d, st);
+                            hipStream_t st, uint32_t* counts) {
+  if (counts && !gate_writes_counts(d)) return hipErrorInvalidValue;
+  if (d.D == 128) return gate_dispatch_d<128>(q, kbar, sel, d, st, counts);
+  return gate_dispatch_d<64>(q, kbar, sel, d, st, counts);
 }
 
 }  // namespace moba

@@ -6,8 +6,7 @@
 
 namespace moba {
 
-constexpr int kRouteChunkRows = 256;   // query rows per routing chunk (one head)
-constexpr int kRoutedTileM = 128;      // routed entries per attention workgroup
+constexpr int kRouteChunkRows = 128;   // query rows per routing chunk (one head)
 constexpr int kMaxBlocks = 8192;       // largest supported number of KV blocks
 constexpr int kMaxTopk = 17;           // largest supported topk (16 routed blocks + own)
 
@@ -31,16 +30,24 @@ struct Dims {
   int ncols = 1;      // G * nchunk_r: columns of the per-bucket count rows
   int nrows = 1;      // S * Hkv * nb buckets
   int64_t slots = 0;  // S * H * Lq * kp routed slots
+  int tile_m = 128;   // routed entries per attention tile (128 or 256)
 };
 
 // Block means; `partial` holds block_mean_partial_floats(d) floats (may be
 // NULL when that is 0).
+// With defer_finalize the split sums stay in `partial` and the following
+// launch_transpose_v (given the same partial / kbar) finishes the means.
 size_t block_mean_partial_floats(const Dims& d);
 hipError_t launch_block_mean(const void* k, float* kbar, float* partial, const Dims& d,
-                             hipStream_t st);
-hipError_t launch_transpose_v(const void* v, void* vt, const Dims& d, hipStream_t st);
+                             hipStream_t st, bool defer_finalize = false);
+hipError_t launch_transpose_v(const void* v, void* vt, const Dims& d, hipStream_t st,
+                              const float* bm_partial = nullptr, float* kbar = nullptr);
+// counts (nullable): when given, the bf16 gate also writes the routing
+// histogram of its 128-row chunk (the route_count step), see route.hip.
 hipError_t launch_gate_topk(const void* q, const float* kbar, int32_t* sel, const Dims& d,
-                            hipStream_t st);
+                            hipStream_t st, uint32_t* counts = nullptr);
+// True when launch_gate_topk can produce the routing counts itself.
+bool gate_writes_counts(const Dims& d);
 hipError_t launch_route_count(const int32_t* sel, uint32_t* counts, const Dims& d,
                               hipStream_t st);
 hipError_t launch_route_scan_rows(uint32_t* counts, uint32_t* bucket_total, const Dims& d,
@@ -60,11 +67,16 @@ hipError_t launch_attn_routed_f32(const void* q, const void* k, const void* v,
                                   const uint32_t* list, const uint32_t* bucket_off,
                                   const uint32_t* tile_off, void* part_o, float* part_lse,
                                   const Dims& d, hipStream_t st);
-// mode 0: own block + merge of the routed partials; mode 1: full causal attention.
+// mode 0: own block + merge of the routed partials; mode 1: full causal attention;
+// mode 2 (bf16 only): own block written as a partial (o to part_o, log2-sum-exp
+// to part_lse, indexed by query-head) for launch_merge_partials_bf16.
 // The bf16 form reads V^T [S, Hkv, D, L]; the fp32 form reads V as given.
 hipError_t launch_attn_query_bf16(const void* q, const void* k, const void* vt,
                                   const void* part_o, const float* part_lse, void* out, int mode,
                                   const Dims& d, hipStream_t st);
+hipError_t launch_merge_partials_bf16(const void* own_o, const float* own_lse, const void* po,
+                                      const float* plse, void* out, const Dims& d,
+                                      hipStream_t st);
 hipError_t launch_attn_query_f32(const void* q, const void* k, const void* v, const void* part_o,
                                  const float* part_lse, void* out, int mode, const Dims& d,
                                  hipStream_t st);

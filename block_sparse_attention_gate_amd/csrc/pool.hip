@@ -94,7 +94,7 @@ size_t block_mean_partial_floats(const Dims& d) {
 }
 
 hipError_t launch_block_mean(const void* k, float* kbar, float* partial, const Dims& d,
-                             hipStream_t st) {
+                             hipStream_t st, bool defer_finalize) {
   const int cols = d.Hkv * d.D;
   const int vec = d.bf16 ? 8 : 4;
   const int tpr = cols / vec;
@@ -108,22 +108,36 @@ hipError_t launch_block_mean(const void* k, float* kbar, float* partial, const D
     hipLaunchKernelGGL(k_block_mean<float>, grid, dim3(256), 0, st,
                        static_cast<const float*>(k), kbar, partial, d.Hkv, d.D, d.L, d.B, d.nb,
                        splits);
-  if (splits > 1)
+  if (splits > 1 && !defer_finalize)
     hipLaunchKernelGGL(k_block_mean_finalize, dim3(d.nb, d.S), dim3(256), 0, st, partial, kbar,
                        d.Hkv, d.D, d.B, d.nb, splits);
   return hipGetLastError();
 }
 
 // V [S, L, Hkv, D] -> V^T [S, Hkv, D, L] (bf16).  grid (L/64, Hkv, S).
+// When bm_partial is given, workgroups (j < nb, g = 0) of sequence s also
+// finish the block mean of block j from the split sums (fixed order).
 template <int D>
 __global__ __launch_bounds__(256) void k_transpose_v(const bf16_t* __restrict__ v,
                                                      bf16_t* __restrict__ vt, int Hkv,
-                                                     int64_t L) {
+                                                     int64_t L, const float* __restrict__ bm_partial,
+                                                     float* __restrict__ kbar, int B, int nb,
+                                                     int splits) {
   constexpr int LD = D + 8;
   __shared__ bf16_t tile[64 * LD];
   const int64_t key0 = (int64_t)blockIdx.x * 64;
   const int g = blockIdx.y, s = blockIdx.z;
   const int tid = threadIdx.x;
+  if (bm_partial && g == 0 && (int)blockIdx.x < nb) {
+    const int j = blockIdx.x, cols = Hkv * D;
+    const float inv = 1.0f / (float)B;
+    for (int c = tid; c < cols; c += 256) {
+      const float* p = bm_partial + ((int64_t)s * nb + j) * splits * cols + c;
+      float sum = 0.f;
+      for (int sp = 0; sp < splits; ++sp) sum += p[(int64_t)sp * cols];
+      kbar[(((int64_t)s * Hkv + c / D) * nb + j) * D + c % D] = sum * inv;
+    }
+  }
   constexpr int CPR = D / 8;  // 16-byte chunks per key row
   for (int c = tid; c < 64 * CPR; c += 256) {
     const int row = c / CPR, cc = c % CPR;
@@ -146,14 +160,18 @@ __global__ __launch_bounds__(256) void k_transpose_v(const bf16_t* __restrict__ 
   }
 }
 
-hipError_t launch_transpose_v(const void* v, void* vt, const Dims& d, hipStream_t st) {
+hipError_t launch_transpose_v(const void* v, void* vt, const Dims& d, hipStream_t st,
+                              const float* bm_partial, float* kbar) {
   dim3 grid((unsigned)(d.L / 64), d.Hkv, d.S);
+  const int splits = bm_partial ? block_mean_splits(d) : 1;
   if (d.D == 128)
     hipLaunchKernelGGL(k_transpose_v<128>, grid, dim3(256), 0, st,
-                       static_cast<const bf16_t*>(v), static_cast<bf16_t*>(vt), d.Hkv, d.L);
+                       static_cast<const bf16_t*>(v), static_cast<bf16_t*>(vt), d.Hkv, d.L,
+                       bm_partial, kbar, d.B, d.nb, splits);
   else
     hipLaunchKernelGGL(k_transpose_v<64>, grid, dim3(256), 0, st,
-                       static_cast<const bf16_t*>(v), static_cast<bf16_t*>(vt), d.Hkv, d.L);
+                       static_cast<const bf16_t*>(v), static_cast<bf16_t*>(vt), d.Hkv, d.L,
+                       bm_partial, kbar, d.B, d.nb, splits);
   return hipGetLastError();
 }
 

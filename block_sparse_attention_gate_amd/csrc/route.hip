@@ -214,7 +214,7 @@ hipError_t launch_route_scan_rows(uint32_t* counts, uint32_t* bucket_total, cons
 hipError_t launch_route_scan_buckets(const uint32_t* bucket_total, uint32_t* bucket_off,
                                      uint32_t* tile_off, const Dims& d, hipStream_t st) {
   hipLaunchKernelGGL(k_route_scan_buckets, dim3(1), dim3(256), 0, st, bucket_total, bucket_off,
-                     tile_off, d.nrows, kRoutedTileM);
+                     tile_off, d.nrows, d.tile_m);
   return hipGetLastError();
 }
 
@@ -229,7 +229,7 @@ hipError_t launch_route_scatter(const int32_t* sel, const uint32_t* counts,
 }
 
 int64_t routed_tile_bound(const Dims& d) {
-  return (d.slots + kRoutedTileM - 1) / kRoutedTileM + d.nrows;
+  return (d.slots + d.tile_m - 1) / d.tile_m + d.nrows;
 }
 
 }  // namespace moba

@@ -34,6 +34,9 @@
  *     pointer after the queued work completes.
  *   - Every call only enqueues work on `stream` (a hipStream_t; NULL is the
  *     default stream) and returns; there is no host synchronisation inside.
+ *     Part of the work may run on an internal stream of the same device that
+ *     is forked from and joined back into `stream` with events, so ordering
+ *     with respect to `stream` is as if all of it ran on `stream`.
  *   - All argument checks run before anything is enqueued: a call that
  *     returns an error has enqueued nothing and written nothing.
  *     MOBA_ERR_INVALID_ARGUMENT: null required pointer, size < 1,
@@ -142,7 +145,10 @@ int32_t moba_abi_version(void);
  * reset.  Names: "block_mean", "transpose_v", "gate_topk", "route_count",
  * "route_scan_rows", "route_scan_buckets", "route_scatter", "attn_routed",
  * "attn_own_merge", "attn_full", "decode_plan", "decode_attn",
- * "decode_merge".  Unknown names give MOBA_ERR_INVALID_ARGUMENT.
+ * "decode_merge", "merge_partials".  Unknown names give
+ * MOBA_ERR_INVALID_ARGUMENT.  (bf16 prefill runs the own-block attention,
+ * "attn_own_merge", on an internal stream of the same device, forked from
+ * and joined back into the caller's stream.)
  */
 moba_status moba_profile_enable(int32_t on);
 moba_status moba_profile_reset(void);
