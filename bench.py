@@ -44,6 +44,35 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+# ------------------------------------------------------------ HBM traffic
+def sources_sha256(paths):
+    import hashlib
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(record_name):
+    """HBM bytes per launch of a kernel from a committed counter record
+    (profiles/<record_name>.json: FETCH_SIZE and WRITE_SIZE in KiB per
+    dispatch from two rocprofv3 --pmc runs, each scaled by the factor the same
+    counter reads for a plain copy of known size).  None when there is no
+    record or the kernel's sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", record_name + ".json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    try:
+        if rec["sources_sha256"] != sources_sha256(rec["sources"]):
+            return None
+        return (rec["fetch_kib_per_dispatch"] * rec["fetch_scale"]
+                + rec["write_kib_per_dispatch"] * rec["write_scale"]) * 1024.0
+    except (KeyError, OSError):
+        return None
+
+
 # ----------------------------------------------------------- work accounting
 def prefill_flops(w):
     """(effective, routed, own, full) FLOPs of a prefill workload.
@@ -155,7 +184,7 @@ def run_prefill(moba, w, steps, warmup, full_steps, full_warmup, with_full=True)
     return res
 
 
-def run_decode(moba, w, steps, warmup):
+def run_decode(moba, w, steps, warmup, with_full=True):
     """Decode against a long cache: one moba_forward_ex call with the block
     means precomputed (untimed, as a decode loop reuses them).  Algorithmic
     bytes = every kept K/V block read once per (sequence, KV head) -- the
@@ -196,20 +225,23 @@ def run_decode(moba, w, steps, warmup):
         t = kern["decode_attn"]["avg_ms"] * 1e-3
         res["roofline"] = {"bound": "hbm", "kernel": "decode_attn", "achieved": kv_bytes / t / 1e9,
                            "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                           "frac": kv_bytes / t / 1e9 / PEAK_HBM_GBS, "traffic": None,
+                           "frac": kv_bytes / t / 1e9 / PEAK_HBM_GBS,
+                           "traffic": measured_traffic(f"decode_attn_{w.name}_bytes"),
                            "avg_launch_ms": kern["decode_attn"]["avg_ms"]}
-    fout = torch.empty_like(q)
-    fws = torch.empty(max(moba.moba_full_workspace_size(q, k, v), 1), dtype=torch.uint8,
-                      device=q.device)
-    ffn = lambda: moba.moba_full_attention_ex(q, k, v, out=fout, workspace=fws)
-    log(f"[bench] {w.name}: timing full-attention decode")
-    fms, _ = time_region(ffn, max(1, steps // 2), max(1, warmup // 2))
-    full_bytes = S * L * Hkv * D * esz * 2 + 2 * q.numel() * esz
-    res["full_ms"] = fms
-    res["full_gbs"] = full_bytes / (fms * 1e-3) / 1e9
-    res["full_frac_of_hbm_peak"] = res["full_gbs"] / PEAK_HBM_GBS
-    res["speedup_vs_full"] = fms / ms
-    del q, k, v, out, ws, fout, fws, kbar
+    if with_full:
+        fout = torch.empty_like(q)
+        fws = torch.empty(max(moba.moba_full_workspace_size(q, k, v), 1), dtype=torch.uint8,
+                          device=q.device)
+        ffn = lambda: moba.moba_full_attention_ex(q, k, v, out=fout, workspace=fws)
+        log(f"[bench] {w.name}: timing full-attention decode")
+        fms, _ = time_region(ffn, max(1, steps // 2), max(1, warmup // 2))
+        full_bytes = S * L * Hkv * D * esz * 2 + 2 * q.numel() * esz
+        res["full_ms"] = fms
+        res["full_gbs"] = full_bytes / (fms * 1e-3) / 1e9
+        res["full_frac_of_hbm_peak"] = res["full_gbs"] / PEAK_HBM_GBS
+        res["speedup_vs_full"] = fms / ms
+        del fout, fws
+    del q, k, v, out, ws, kbar
     torch.cuda.empty_cache()
     return res
 
@@ -222,7 +254,8 @@ def roofline(res):
     achieved = res["routed_flop"] / t / 1e12
     return {"bound": "mfma", "kernel": "attn_routed", "achieved": achieved,
             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-            "traffic": None, "avg_launch_ms": kern["attn_routed"]["avg_ms"]}
+            "traffic": measured_traffic(f"attn_routed_{res['workload']}_bytes"),
+            "avg_launch_ms": kern["attn_routed"]["avg_ms"]}
 
 
 # ------------------------------------------------------------ CPU baseline
@@ -311,10 +344,13 @@ def main():
             log(f"[bench] calibration copy of {args.calib_copy_mib} MiB done")
             del src, dst
         w = moba_inputs.WORKLOADS[args.workload]
-        r = run_prefill(moba, w, args.steps, args.warmup, full_steps=1, full_warmup=0,
-                        with_full=not args.no_full)
-        r["roofline"] = roofline(r)
-        r.pop("_roofline_src")
+        if w.is_decode:
+            r = run_decode(moba, w, args.steps, args.warmup, with_full=not args.no_full)
+        else:
+            r = run_prefill(moba, w, args.steps, args.warmup, full_steps=1, full_warmup=0,
+                            with_full=not args.no_full)
+            r["roofline"] = roofline(r)
+            r.pop("_roofline_src")
         print(json.dumps({"workload": w.name, "steps": args.steps, "warmup": args.warmup,
                           "detail": r}), flush=True)
         return

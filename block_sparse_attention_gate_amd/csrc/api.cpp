@@ -198,10 +198,10 @@ moba_status plan_forward(const moba_args* a, Plan* p) {
   if (slots >= ((int64_t)1 << 32))
     return fail(MOBA_ERR_UNSUPPORTED, "more than 2^32 routed slots");
   d.slots = slots;
-  // Routed tiles of 256 entries (8-wave workgroups) once there are enough of
-  // them to fill the chip several times over; 128 otherwise.  The fp32 path
-  // always uses 128.
-  d.tile_m = (d.bf16 && slots / 256 >= 8192) ? 256 : 128;
+  // Routed tiles of 256 entries (8-wave workgroups, one per CU, twice the
+  // work per K/V tile load) unless there would be too few of them to spread
+  // over the chip; the fp32 path always uses 128.
+  d.tile_m = (d.bf16 && slots / 256 >= 128) ? 256 : 128;
   if ((int64_t)d.S * d.H * d.nchunk_r >= ((int64_t)1 << 31))
     return fail(MOBA_ERR_UNSUPPORTED, "too many routing chunks");
   const int64_t esz = d.bf16 ? 2 : 4;

@@ -295,7 +295,18 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_query(
   using T = Tiles<D, NW>;
   __shared__ __attribute__((aligned(16))) bf16_t lds[2 * T::BUF];
   const int RW = 32 * NW / HW;
-  const int rt = (MODE == 1) ? (int)(gridDim.x - 1 - blockIdx.x) : (int)blockIdx.x;
+  // Longest work first.  Full attention: the last row tiles.  Own block (when
+  // blocks hold whole row tiles): the tiles at the end of every block first.
+  int rt;
+  if (MODE == 1) {
+    rt = (int)(gridDim.x - 1 - blockIdx.x);
+  } else if (q_off % B == 0 && B % RW == 0 && Lq % B == 0) {
+    const int tpb = B / RW, nbq = Lq / B;
+    const int rank = (int)blockIdx.x / nbq, blk = (int)blockIdx.x % nbq;
+    rt = blk * tpb + (tpb - 1 - rank);
+  } else {
+    rt = (int)blockIdx.x;
+  }
   const int hgroups = H / HW;
   const int s = blockIdx.y / hgroups;
   const int h0 = (blockIdx.y % hgroups) * HW;
