@@ -318,4 +318,5 @@ def moba_profile_read(name: str):
 
 KERNEL_NAMES = ("block_mean", "transpose_v", "gate_topk", "route_count", "route_scan_rows",
                 "route_scan_buckets", "route_scatter", "attn_routed", "attn_own_merge",
-                "attn_full", "decode_plan", "decode_attn", "decode_merge", "merge_partials")
+                "attn_full", "decode_plan", "decode_attn", "decode_merge", "merge_partials",
+                "pool_transpose", "block_mean_finalize", "route_scan_small")

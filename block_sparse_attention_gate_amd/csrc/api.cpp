@@ -33,12 +33,13 @@ moba_status fail(moba_status s, const char* fmt, ...) {
 enum KernelId {
   K_BLOCK_MEAN, K_TRANSPOSE_V, K_GATE, K_RCOUNT, K_RSCAN_ROWS, K_RSCAN_BUCKETS, K_RSCATTER,
   K_ATTN_ROUTED, K_ATTN_OWN, K_ATTN_FULL, K_DEC_PLAN, K_DEC_ATTN, K_DEC_MERGE, K_MERGE,
-  K_COUNT
+  K_POOL_TRANSPOSE, K_MEAN_FINALIZE, K_RSCAN_SMALL, K_COUNT
 };
 const char* const kKernelNames[K_COUNT] = {
     "block_mean", "transpose_v", "gate_topk", "route_count", "route_scan_rows",
     "route_scan_buckets", "route_scatter", "attn_routed", "attn_own_merge", "attn_full",
-    "decode_plan", "decode_attn", "decode_merge", "merge_partials"};
+    "decode_plan", "decode_attn", "decode_merge", "merge_partials", "pool_transpose",
+    "block_mean_finalize", "route_scan_small"};
 
 struct ProfRecord {
   int id;
@@ -243,8 +244,8 @@ moba_status plan_forward(const moba_args* a, Plan* p) {
     if (d.bf16 && (int64_t)d.S * d.H * d.Lq <= ((int64_t)1 << 20)) {
       p->split_own = true;
       const size_t nqh = (size_t)d.S * d.H * d.Lq;
-      p->off_own_o = take(nqh * d.D * 2);
-      p->off_own_lse = take(nqh * 4);
+      p->off_own_o = take(2 * nqh * d.D * 2);   // two halves of a split own block
+      p->off_own_lse = take(2 * nqh * 4);
     }
   }
   p->total = off;
@@ -322,6 +323,20 @@ moba_status get_workspace(const moba_args* a, const Plan& p, Workspace* ws) {
   return MOBA_OK;
 }
 
+// Makes `main` wait for the side stream's last event when a call leaves early,
+// so that the stream-ordered free of a library workspace (and the caller's next
+// work) comes after the side stream's kernels.
+struct SideJoin {
+  hipStream_t main = nullptr;
+  hipEvent_t done = nullptr;
+  ~SideJoin() {
+    if (done) {
+      (void)hipStreamWaitEvent(main, done, 0);
+      (void)hipEventDestroy(done);
+    }
+  }
+};
+
 moba_status hip_fail(const Launch& l) {
   return fail(MOBA_ERR_HIP, "launch of %s failed: %s", l.what ? l.what : "?",
               hipGetErrorString(l.err));
@@ -349,49 +364,62 @@ moba_status forward_impl(const moba_args* a) {
 
   Launch l{(hipStream_t)a->stream};
   float* bm_partial = (float*)(w + p.off_bmpart);
-  // the V transpose finishes the block means when both run (one launch less)
-  const bool fold_mean = p.need_kbar && p.need_vt && moba::block_mean_partial_floats(d) > 0;
-  if (p.need_kbar)
-    l.run(K_BLOCK_MEAN, [&] {
-      return moba::launch_block_mean(a->k, kbar, bm_partial, d, l.st, fold_mean);
-    });
-  if (p.need_vt)
-    l.run(K_TRANSPOSE_V, [&] {
-      return moba::launch_transpose_v(a->v, vt, d, l.st, fold_mean ? bm_partial : nullptr,
-                                      fold_mean ? kbar : nullptr);
-    });
-  if (l.err != hipSuccess) return hip_fail(l);
-
-  // Small bf16 problems: the own-block attention (needs only V^T) runs on the
-  // side stream while the gate, routing and routed attention run here.
   void* own_o = (void*)(w + p.off_own_o);
   float* own_lse = (float*)(w + p.off_own_lse);
-  hipStream_t side = nullptr;
-  hipEvent_t join = nullptr;
-  Launch ls{nullptr};
+
+  // Small bf16 problems: one launch pools K and writes V^T; then the own-block
+  // attention (which needs only Q, K and V^T) runs on the side stream while
+  // the gate and the routing run here, and the merge waits for both.
+  SideJoin join;
+  join.main = l.st;
   if (p.split_own) {
+    if (p.need_kbar)
+      l.run(K_POOL_TRANSPOSE, [&] {
+        return moba::launch_pool_transpose(a->k, a->v, kbar, bm_partial, vt, d, l.st);
+      });
+    else
+      l.run(K_TRANSPOSE_V, [&] { return moba::launch_transpose_v(a->v, vt, d, l.st); });
+    if (l.err != hipSuccess) return hip_fail(l);
+    hipStream_t side = nullptr;
     hipEvent_t fork = nullptr;
     hipError_t e = side_stream(&side);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&fork, hipEventDisableTiming);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&join, hipEventDisableTiming);
+    // device-scope release: the events only order work on this device
+    const unsigned evf = hipEventDisableTiming | hipEventReleaseToDevice;
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&fork, evf);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&join.done, evf);
     if (e == hipSuccess) e = hipEventRecord(fork, l.st);
     if (e == hipSuccess) e = hipStreamWaitEvent(side, fork, 0);
     if (fork) (void)hipEventDestroy(fork);
     if (e != hipSuccess) {
-      if (join) (void)hipEventDestroy(join);
+      if (join.done) (void)hipEventDestroy(join.done);
+      join.done = nullptr;
       return fail(MOBA_ERR_HIP, "side stream setup failed: %s", hipGetErrorString(e));
     }
-    ls.st = side;
+    Launch ls{side};
     ls.run(K_ATTN_OWN, [&] {
       return moba::launch_attn_query_bf16(a->q, a->k, vt, own_o, own_lse, nullptr, 2, d, side);
     });
-    const hipError_t ej = hipEventRecord(join, side);
-    if (ls.err != hipSuccess || ej != hipSuccess) {
-      (void)hipEventDestroy(join);
-      if (ls.err != hipSuccess) return hip_fail(ls);
-      return fail(MOBA_ERR_HIP, "side stream join failed: %s", hipGetErrorString(ej));
-    }
+    const hipError_t ed = hipEventRecord(join.done, side);
+    if (ls.err == hipSuccess) ls.err = ed;
+    if (ls.err != hipSuccess) return hip_fail(ls);
+    if (p.need_kbar)
+      l.run(K_MEAN_FINALIZE,
+            [&] { return moba::launch_block_mean_finalize(kbar, bm_partial, d, l.st); });
+  } else {
+    // The V transform finishes the block means when both run (one launch less).
+    const bool fold_mean =
+        p.need_kbar && p.need_vt && moba::block_mean_partial_floats(d) > 0;
+    if (p.need_kbar)
+      l.run(K_BLOCK_MEAN, [&] {
+        return moba::launch_block_mean(a->k, kbar, bm_partial, d, l.st, fold_mean);
+      });
+    if (p.need_vt)
+      l.run(K_TRANSPOSE_V, [&] {
+        return moba::launch_transpose_v(a->v, vt, d, l.st, fold_mean ? bm_partial : nullptr,
+                                        fold_mean ? kbar : nullptr);
+      });
   }
+  if (l.err != hipSuccess) return hip_fail(l);
 
   // the gate writes the routing histogram itself when it can
   const bool gate_counts = p.routed && moba::gate_writes_counts(d);
@@ -417,11 +445,18 @@ moba_status forward_impl(const moba_args* a) {
   if (p.routed) {
     if (!gate_counts)
       l.run(K_RCOUNT, [&] { return moba::launch_route_count(sel, counts, d, l.st); });
-    l.run(K_RSCAN_ROWS, [&] { return moba::launch_route_scan_rows(counts, btotal, d, l.st); });
-    l.run(K_RSCAN_BUCKETS,
-          [&] { return moba::launch_route_scan_buckets(btotal, boff, toff, d, l.st); });
-    l.run(K_RSCATTER,
-          [&] { return moba::launch_route_scatter(sel, counts, boff, list, d, l.st); });
+    const bool small_scan = moba::route_scan_small_fits(d);
+    if (small_scan) {
+      l.run(K_RSCAN_SMALL,
+            [&] { return moba::launch_route_scan_small(counts, boff, toff, d, l.st); });
+    } else {
+      l.run(K_RSCAN_ROWS, [&] { return moba::launch_route_scan_rows(counts, btotal, d, l.st); });
+      l.run(K_RSCAN_BUCKETS,
+            [&] { return moba::launch_route_scan_buckets(btotal, boff, toff, d, l.st); });
+    }
+    l.run(K_RSCATTER, [&] {
+      return moba::launch_route_scatter(sel, counts, boff, list, d, l.st, small_scan);
+    });
     l.run(K_ATTN_ROUTED, [&] {
       return d.bf16 ? moba::launch_attn_routed_bf16(a->q, a->k, vt, list, boff, toff, po, plse,
                                                     d, l.st)
@@ -430,10 +465,13 @@ moba_status forward_impl(const moba_args* a) {
     });
   }
   if (p.split_own) {
-    const hipError_t ew = hipStreamWaitEvent(l.st, join, 0);
-    (void)hipEventDestroy(join);
-    if (ew != hipSuccess)
-      return fail(MOBA_ERR_HIP, "side stream join failed: %s", hipGetErrorString(ew));
+    if (l.err == hipSuccess) {
+      l.err = hipStreamWaitEvent(l.st, join.done, 0);
+      if (l.err == hipSuccess) {
+        (void)hipEventDestroy(join.done);
+        join.done = nullptr;
+      }
+    }
     l.run(K_MERGE, [&] {
       return moba::launch_merge_partials_bf16(own_o, own_lse, po, plse, a->out, d, l.st);
     });

@@ -13,7 +13,10 @@
 //     selected keys.  Mode 1: full causal attention (the topk = all case of
 //     the full/sparse switch, "MoBA" project card, "How It Works").  Mode 2:
 //     the own block only, written as a partial (o, log-sum-exp) for
-//     k_merge_partials, so that it can run concurrently with the routing.
+//     k_merge_partials, so that it can run concurrently with the routing;
+//     workgroups with more than kOwnSplitSteps key tiles split their key
+//     range in two halves, written to two partials (an empty half writes
+//     log-sum-exp = -inf).
 //
 // Wave tile: 32 queries (lane l owns query l%32) x 64 keys per step.
 //   S^T = K Q^T on 32x32x16 MFMA (K rows in the kperm order, see common.h),
@@ -295,17 +298,21 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_query(
   using T = Tiles<D, NW>;
   __shared__ __attribute__((aligned(16))) bf16_t lds[2 * T::BUF];
   const int RW = 32 * NW / HW;
+  // Mode 2: blockIdx.x = 2 * item + part (two halves of the key range).
+  const int item = MODE == 2 ? (int)blockIdx.x >> 1 : (int)blockIdx.x;
+  const int part = MODE == 2 ? (int)blockIdx.x & 1 : 0;
+  const int nitems = MODE == 2 ? (int)gridDim.x >> 1 : (int)gridDim.x;
   // Longest work first.  Full attention: the last row tiles.  Own block (when
   // blocks hold whole row tiles): the tiles at the end of every block first.
   int rt;
   if (MODE == 1) {
-    rt = (int)(gridDim.x - 1 - blockIdx.x);
+    rt = nitems - 1 - item;
   } else if (q_off % B == 0 && B % RW == 0 && Lq % B == 0) {
     const int tpb = B / RW, nbq = Lq / B;
-    const int rank = (int)blockIdx.x / nbq, blk = (int)blockIdx.x % nbq;
+    const int rank = item / nbq, blk = item % nbq;
     rt = blk * tpb + (tpb - 1 - rank);
   } else {
-    rt = (int)blockIdx.x;
+    rt = item;
   }
   const int hgroups = H / HW;
   const int s = blockIdx.y / hgroups;
@@ -327,7 +334,20 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_query(
   const int wglast = (rw0 + RW - 1 < Lq ? rw0 + RW - 1 : Lq - 1);
   const int klo_g = (MODE != 1) ? ((q_off + rw0) / B) * B : 0;
   const int khi_g = q_off + wglast + 1;
-  const int t0 = klo_g / 64, t1 = (khi_g + 63) / 64;
+  int t0 = klo_g / 64, t1 = (khi_g + 63) / 64;
+  if (MODE == 2) {
+    const int nst = t1 - t0;
+    const int ts = nst > kOwnSplitSteps ? t0 + nst / 2 : t1;
+    if (part == 0) t1 = ts; else t0 = ts;
+    if (t0 >= t1) {
+      // empty second half: log-sum-exp -inf, which the merge skips
+      if (valid && hh == 0) {
+        const int64_t nqh = (int64_t)gridDim.y * HW * Lq;
+        const_cast<float*>(plse)[nqh + ((int64_t)s * H + h) * Lq + r] = -__builtin_inff();
+      }
+      return;
+    }
+  }
   const int klo_l = (MODE != 1) ? (pos / B) * B : 0;
 
   bf16x8 qf[D / 16];
@@ -358,6 +378,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_query(
     const int d_ = (pos_first + 1) / 64;
     wd_ = d_ < ws_ ? ws_ : (d_ > we_ ? we_ : d_);
     if (klo_w % 64 != 0) wd_ = ws_;                    // window start not tile-aligned
+    // restrict the phases to this workgroup's tiles [t0, t1)
+    ws_ = ws_ < t0 ? t0 : (ws_ > t1 ? t1 : ws_);
+    we_ = we_ < ws_ ? ws_ : (we_ > t1 ? t1 : we_);
+    wd_ = wd_ < ws_ ? ws_ : (wd_ > we_ ? we_ : wd_);
   }
   int it = t0;
   auto advance = [&](int i) {
@@ -395,10 +419,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_query(
   bf16_t* orow = out + (((int64_t)s * Lq + r) * H + h) * D;
   float inv = 1.0f / ltot;
   if (MODE == 2) {
-    // own-block partial of query-head qh: normalised o (bf16) and log2-sum-exp
-    const int64_t qh = ((int64_t)s * H + h) * Lq + r;
+    // own-block partial (this half) of query-head qh: normalised o (bf16) and
+    // log2-sum-exp; a row with no visible key in this half gets o = 0, -inf
+    const int64_t nqh = (int64_t)gridDim.y * HW * Lq;
+    const int64_t qh = ((int64_t)s * H + h) * Lq + r + part * nqh;
     orow = const_cast<bf16_t*>(po) + qh * D;
-    if (hh == 0) const_cast<float*>(plse)[qh] = acc.m + __log2f(ltot);
+    if (!(ltot > 0.f)) inv = 0.f;
+    if (hh == 0)
+      const_cast<float*>(plse)[qh] = ltot > 0.f ? acc.m + __log2f(ltot) : -__builtin_inff();
   }
   if (MODE == 0 && kp > 0) {
     // Merge: out = sum_x 2^(lse_x - M) o_x / sum_x 2^(lse_x - M) over the own
@@ -448,8 +476,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_query(
     }
 }
 
-// Merge of the own-block partial with the routed partials of every
-// query-head: out = sum_x 2^(lse_x - M) o_x / sum_x 2^(lse_x - M).  16 lanes
+// Merge of the own-block partials (one or two halves) with the routed
+// partials of every query-head: out = sum_x 2^(lse_x - M) o_x / sum_x
+// 2^(lse_x - M).  own_o / own_lse hold the two halves one after the other.  16 lanes
 // per query-head, D/16 dims per lane.  grid ceil(nqh / 16), 256 threads.
 template <int D>
 __global__ __launch_bounds__(256) void k_merge_partials(
@@ -466,7 +495,8 @@ __global__ __launch_bounds__(256) void k_merge_partials(
   const int64_t own = (q_off + r) / B;
   const int npast = (int)(kp < own ? kp : own);
   const float lse0 = own_lse[qh];
-  float M = lse0;
+  const float lse1 = own_lse[nqh + qh];  // second half of a split own block, or -inf
+  float M = fmaxf(lse0, lse1);
   for (int t = 0; t < npast; ++t) M = fmaxf(M, plse[qh * kp + t]);
   float acc[EPL];
   auto load = [&](const bf16_t* p, float (&x)[EPL]) {
@@ -491,6 +521,13 @@ __global__ __launch_bounds__(256) void k_merge_partials(
   float wsum = w0;
 #pragma unroll
   for (int i = 0; i < EPL; ++i) acc[i] = w0 * x[i];
+  if (lse1 > -__builtin_inff()) {
+    const float w1 = __builtin_amdgcn_exp2f(lse1 - M);
+    wsum += w1;
+    load(own_o + (nqh + qh) * D + sub * EPL, x);
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) acc[i] = fmaf(w1, x[i], acc[i]);
+  }
   for (int t = 0; t < npast; ++t) {
     const float wt = __builtin_amdgcn_exp2f(plse[qh * kp + t] - M);
     wsum += wt;
@@ -561,7 +598,7 @@ hipError_t launch_attn_query_bf16(const void* q, const void* k, const void* vt,
   const int64_t wgs8 = (d.Lq + 256 / HW - 1) / (256 / HW) * (int64_t)(d.S * d.H / HW);
   const int NW = wgs8 >= 2048 ? 8 : 4;
   const int RW = 32 * NW / HW;
-  dim3 grid((unsigned)((d.Lq + RW - 1) / RW), d.S * d.H / HW);
+  dim3 grid((unsigned)((d.Lq + RW - 1) / RW * (mode == 2 ? 2 : 1)), d.S * d.H / HW);
   const float sl2 = kLog2e / sqrtf((float)d.D);
 #define MOBA_QUERY(DV, MV, NWV)                                                              \
   hipLaunchKernelGGL((k_attn_query<DV, MV, NWV>), grid, dim3(64 * NWV), 0, st,               \

@@ -8,6 +8,7 @@ namespace moba {
 
 constexpr int kRouteChunkRows = 128;   // query rows per routing chunk (one head)
 constexpr int kMaxBlocks = 8192;       // largest supported number of KV blocks
+constexpr int kOwnSplitSteps = 8;      // own-block tiles longer than this (64-key tiles) split in two
 constexpr int kMaxTopk = 17;           // largest supported topk (16 routed blocks + own)
 
 // Problem dimensions shared by every launch of one call.
@@ -40,6 +41,13 @@ struct Dims {
 size_t block_mean_partial_floats(const Dims& d);
 hipError_t launch_block_mean(const void* k, float* kbar, float* partial, const Dims& d,
                              hipStream_t st, bool defer_finalize = false);
+// bf16: block pooling (sums per split, or means when there is one split) and
+// the V transform in one launch; launch_block_mean_finalize then finishes the
+// means (nothing to do with one split).
+hipError_t launch_pool_transpose(const void* k, const void* v, float* kbar, float* partial,
+                                 void* vt, const Dims& d, hipStream_t st);
+hipError_t launch_block_mean_finalize(float* kbar, const float* partial, const Dims& d,
+                                      hipStream_t st);
 hipError_t launch_transpose_v(const void* v, void* vt, const Dims& d, hipStream_t st,
                               const float* bm_partial = nullptr, float* kbar = nullptr);
 // counts (nullable): when given, the bf16 gate also writes the routing
@@ -54,9 +62,14 @@ hipError_t launch_route_scan_rows(uint32_t* counts, uint32_t* bucket_total, cons
                                   hipStream_t st);
 hipError_t launch_route_scan_buckets(const uint32_t* bucket_total, uint32_t* bucket_off,
                                      uint32_t* tile_off, const Dims& d, hipStream_t st);
+// Small problems (nrows * ncols <= 16K): both scans in one workgroup; counts
+// then hold global list positions (scatter with counts_global).
+bool route_scan_small_fits(const Dims& d);
+hipError_t launch_route_scan_small(uint32_t* counts, uint32_t* bucket_off, uint32_t* tile_off,
+                                   const Dims& d, hipStream_t st);
 hipError_t launch_route_scatter(const int32_t* sel, const uint32_t* counts,
                                 const uint32_t* bucket_off, uint32_t* list, const Dims& d,
-                                hipStream_t st);
+                                hipStream_t st, bool counts_global);
 // Upper bound of the number of routed tiles (grid size of the routed kernel).
 int64_t routed_tile_bound(const Dims& d);
 hipError_t launch_attn_routed_bf16(const void* q, const void* k, const void* vt,

@@ -17,21 +17,20 @@ namespace moba {
 // `partial` [S, nb, splits, Hkv*D] and k_block_mean_finalize adds them in
 // split order (deterministic, no atomics).
 template <typename T>
-__global__ __launch_bounds__(256) void k_block_mean(const T* __restrict__ k,
-                                                    float* __restrict__ kbar,
-                                                    float* __restrict__ partial, int Hkv, int D,
-                                                    int64_t L, int B, int nb, int splits) {
+__device__ __forceinline__ void block_mean_body(const T* __restrict__ k, float* __restrict__ kbar,
+                                                float* __restrict__ partial, int Hkv, int D,
+                                                int64_t L, int B, int nb, int splits, int bx,
+                                                int s, int bz, float* red) {
   constexpr int VEC = 16 / sizeof(T);
-  __shared__ float red[256 * VEC];
   const int cols = Hkv * D;
   const int tpr = cols / VEC;
   const int cw = tpr < 256 ? tpr : 256;  // threads across columns
   const int RS = 256 / cw;               // row slices
   const int tid = threadIdx.x;
   const int ct = tid % cw, rs = tid / cw;
-  const int s = blockIdx.y, j = blockIdx.x / splits, sp = blockIdx.x % splits;
+  const int j = bx / splits, sp = bx % splits;
   const int rows = B / splits;
-  const int col = (blockIdx.z * cw + ct) * VEC;
+  const int col = (bz * cw + ct) * VEC;
   float acc[VEC];
 #pragma unroll
   for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
@@ -52,7 +51,7 @@ __global__ __launch_bounds__(256) void k_block_mean(const T* __restrict__ k,
   __syncthreads();
   const float inv = 1.0f / (float)B;
   for (int e = tid; e < width; e += 256) {
-    const int c = blockIdx.z * width + e;
+    const int c = bz * width + e;
     if (c >= cols) continue;
     float sum = 0.f;
     for (int r = 0; r < RS; ++r) sum += red[r * width + e];
@@ -65,6 +64,33 @@ __global__ __launch_bounds__(256) void k_block_mean(const T* __restrict__ k,
   }
 }
 
+template <typename T>
+__global__ __launch_bounds__(256) void k_block_mean(const T* __restrict__ k,
+                                                    float* __restrict__ kbar,
+                                                    float* __restrict__ partial, int Hkv, int D,
+                                                    int64_t L, int B, int nb, int splits) {
+  __shared__ float red[256 * (16 / sizeof(T))];
+  block_mean_body<T>(k, kbar, partial, Hkv, D, L, B, nb, splits, blockIdx.x, blockIdx.y,
+                     blockIdx.z, red);
+}
+
+// Sum of the split partials of one column in split order (fixed order: the
+// result does not depend on scheduling); loads are issued 8 at a time.
+__device__ __forceinline__ float sum_splits(const float* __restrict__ p, int splits,
+                                            int64_t stride) {
+  float sum = 0.f;
+  int sp = 0;
+  for (; sp + 8 <= splits; sp += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = p[(int64_t)(sp + u) * stride];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) sum += v[u];
+  }
+  for (; sp < splits; ++sp) sum += p[(int64_t)sp * stride];
+  return sum;
+}
+
 // grid (nb, S); 256 threads.
 __global__ __launch_bounds__(256) void k_block_mean_finalize(const float* __restrict__ partial,
                                                              float* __restrict__ kbar, int Hkv,
@@ -72,9 +98,7 @@ __global__ __launch_bounds__(256) void k_block_mean_finalize(const float* __rest
   const int s = blockIdx.y, j = blockIdx.x, cols = Hkv * D;
   const float inv = 1.0f / (float)B;
   for (int c = threadIdx.x; c < cols; c += 256) {
-    const float* p = partial + ((int64_t)s * nb + j) * splits * cols + c;
-    float sum = 0.f;
-    for (int sp = 0; sp < splits; ++sp) sum += p[(int64_t)sp * cols];
+    const float sum = sum_splits(partial + ((int64_t)s * nb + j) * splits * cols + c, splits, cols);
     const int g = c / D, dd = c % D;
     kbar[(((int64_t)s * Hkv + g) * nb + j) * D + dd] = sum * inv;
   }
@@ -114,30 +138,13 @@ hipError_t launch_block_mean(const void* k, float* kbar, float* partial, const D
   return hipGetLastError();
 }
 
-// V [S, L, Hkv, D] -> V^T [S, Hkv, D, L] (bf16).  grid (L/64, Hkv, S).
-// When bm_partial is given, workgroups (j < nb, g = 0) of sequence s also
-// finish the block mean of block j from the split sums (fixed order).
+// V [S, L, Hkv, D] -> V^T [S, Hkv, D, L] (bf16), 64 keys of one KV head.
 template <int D>
-__global__ __launch_bounds__(256) void k_transpose_v(const bf16_t* __restrict__ v,
-                                                     bf16_t* __restrict__ vt, int Hkv,
-                                                     int64_t L, const float* __restrict__ bm_partial,
-                                                     float* __restrict__ kbar, int B, int nb,
-                                                     int splits) {
+__device__ __forceinline__ void transpose_body(const bf16_t* __restrict__ v,
+                                               bf16_t* __restrict__ vt, int Hkv, int64_t L,
+                                               int64_t key0, int g, int s, bf16_t* tile) {
   constexpr int LD = D + 8;
-  __shared__ bf16_t tile[64 * LD];
-  const int64_t key0 = (int64_t)blockIdx.x * 64;
-  const int g = blockIdx.y, s = blockIdx.z;
   const int tid = threadIdx.x;
-  if (bm_partial && g == 0 && (int)blockIdx.x < nb) {
-    const int j = blockIdx.x, cols = Hkv * D;
-    const float inv = 1.0f / (float)B;
-    for (int c = tid; c < cols; c += 256) {
-      const float* p = bm_partial + ((int64_t)s * nb + j) * splits * cols + c;
-      float sum = 0.f;
-      for (int sp = 0; sp < splits; ++sp) sum += p[(int64_t)sp * cols];
-      kbar[(((int64_t)s * Hkv + c / D) * nb + j) * D + c % D] = sum * inv;
-    }
-  }
   constexpr int CPR = D / 8;  // 16-byte chunks per key row
   for (int c = tid; c < 64 * CPR; c += 256) {
     const int row = c / CPR, cc = c % CPR;
@@ -160,6 +167,53 @@ __global__ __launch_bounds__(256) void k_transpose_v(const bf16_t* __restrict__ 
   }
 }
 
+// grid (L/64, Hkv, S).  When bm_partial is given, workgroups (j < nb, g = 0)
+// of sequence s also finish the block mean of block j from the split sums.
+template <int D>
+__global__ __launch_bounds__(256) void k_transpose_v(const bf16_t* __restrict__ v,
+                                                     bf16_t* __restrict__ vt, int Hkv,
+                                                     int64_t L, const float* __restrict__ bm_partial,
+                                                     float* __restrict__ kbar, int B, int nb,
+                                                     int splits) {
+  __shared__ bf16_t tile[64 * (D + 8)];
+  const int g = blockIdx.y, s = blockIdx.z;
+  if (bm_partial && g == 0 && (int)blockIdx.x < nb) {
+    const int j = blockIdx.x, cols = Hkv * D;
+    const float inv = 1.0f / (float)B;
+    for (int c = threadIdx.x; c < cols; c += 256) {
+      const float sum =
+          sum_splits(bm_partial + ((int64_t)s * nb + j) * splits * cols + c, splits, cols);
+      kbar[(((int64_t)s * Hkv + c / D) * nb + j) * D + c % D] = sum * inv;
+    }
+  }
+  transpose_body<D>(v, vt, Hkv, L, (int64_t)blockIdx.x * 64, g, s, tile);
+}
+
+// One launch for the K pooling (block sums or means) and the V transform:
+// flat grid, the first npool workgroups pool (block_mean grid order), the rest
+// transpose (transpose grid order).
+template <int D>
+__global__ __launch_bounds__(256) void k_pool_transpose(const bf16_t* __restrict__ k,
+                                                        const bf16_t* __restrict__ v,
+                                                        float* __restrict__ kbar,
+                                                        float* __restrict__ partial,
+                                                        bf16_t* __restrict__ vt, int Hkv,
+                                                        int64_t L, int B, int nb, int splits,
+                                                        int pool_x, int pool_y, int pool_z) {
+  __shared__ __attribute__((aligned(16))) float lds[64 * (D + 8) / 2 > 256 * 8 ? 64 * (D + 8) / 2 : 256 * 8];
+  const int npool = pool_x * pool_y * pool_z;
+  const int b = blockIdx.x;
+  if (b < npool) {
+    const int bx = b % pool_x, by = (b / pool_x) % pool_y, bz = b / (pool_x * pool_y);
+    block_mean_body<bf16_t>(k, kbar, partial, Hkv, D, L, B, nb, splits, bx, by, bz, lds);
+  } else {
+    const int t = b - npool;
+    const int ntile = (int)(L / 64);
+    const int x = t % ntile, g = (t / ntile) % Hkv, s = t / (ntile * Hkv);
+    transpose_body<D>(v, vt, Hkv, L, (int64_t)x * 64, g, s, reinterpret_cast<bf16_t*>(lds));
+  }
+}
+
 hipError_t launch_transpose_v(const void* v, void* vt, const Dims& d, hipStream_t st,
                               const float* bm_partial, float* kbar) {
   dim3 grid((unsigned)(d.L / 64), d.Hkv, d.S);
@@ -172,6 +226,36 @@ hipError_t launch_transpose_v(const void* v, void* vt, const Dims& d, hipStream_
     hipLaunchKernelGGL(k_transpose_v<64>, grid, dim3(256), 0, st,
                        static_cast<const bf16_t*>(v), static_cast<bf16_t*>(vt), d.Hkv, d.L,
                        bm_partial, kbar, d.B, d.nb, splits);
+  return hipGetLastError();
+}
+
+hipError_t launch_pool_transpose(const void* k, const void* v, float* kbar, float* partial,
+                                 void* vt, const Dims& d, hipStream_t st) {
+  const int cols = d.Hkv * d.D;
+  const int tpr = cols / 8;
+  const int splits = block_mean_splits(d);
+  const int px = d.nb * splits, py = d.S, pz = (tpr + 255) / 256;
+  const int64_t ntr = (d.L / 64) * d.Hkv * d.S;
+  const dim3 grid((unsigned)((int64_t)px * py * pz + ntr));
+  if (d.D == 128)
+    hipLaunchKernelGGL(k_pool_transpose<128>, grid, dim3(256), 0, st,
+                       static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v), kbar,
+                       partial, static_cast<bf16_t*>(vt), d.Hkv, d.L, d.B, d.nb, splits, px, py,
+                       pz);
+  else
+    hipLaunchKernelGGL(k_pool_transpose<64>, grid, dim3(256), 0, st,
+                       static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v), kbar,
+                       partial, static_cast<bf16_t*>(vt), d.Hkv, d.L, d.B, d.nb, splits, px, py,
+                       pz);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_mean_finalize(float* kbar, const float* partial, const Dims& d,
+                                      hipStream_t st) {
+  const int splits = block_mean_splits(d);
+  if (splits > 1)
+    hipLaunchKernelGGL(k_block_mean_finalize, dim3(d.nb, d.S), dim3(256), 0, st, partial, kbar,
+                       d.Hkv, d.D, d.B, d.nb, splits);
   return hipGetLastError();
 }
 

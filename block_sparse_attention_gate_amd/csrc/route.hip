@@ -10,11 +10,14 @@
 // Entry slot id: ((s*H + h)*Lq + r)*kp + t for the t-th past block of query
 // row r of head h (kp = topk - 1).  Buckets are ordered (s, g, j); inside a
 // bucket entries are in ascending slot id (stable counting sort):
-//   1. route_count: per routing chunk (one head, 256 query rows) an LDS
-//      histogram over the blocks, written to counts[bucket][column];
+//   1. route_count: per routing chunk (one head, 128 query rows) an LDS
+//      histogram over the blocks, written to counts[bucket][column] (the
+//      gate kernel writes it itself when it can);
 //   2. route_scan_rows: exclusive scan of each bucket's columns (LDS scan);
 //   3. route_scan_buckets: exclusive scan over buckets -> bucket offsets and
 //      attention-tile offsets;
+//      (small problems: route_scan_small does 2 and 3 in one workgroup with
+//      one flat scan over all counts, which leaves global list positions);
 //   4. route_scatter: each chunk replays its entries in order; a wave ranks
 //      equal buckets among its lanes with ballots and writes the slot ids.
 #include "common.h"
@@ -145,10 +148,12 @@ __global__ __launch_bounds__(256) void k_route_scan_buckets(const uint32_t* __re
   }
 }
 
+// counts_global: counts already hold global list positions (route_scan_small).
 __global__ __launch_bounds__(256) void k_route_scatter(const int32_t* __restrict__ sel,
                                                        const uint32_t* __restrict__ counts,
                                                        const uint32_t* __restrict__ bucket_off,
-                                                       uint32_t* __restrict__ list, RouteArgs a) {
+                                                       uint32_t* __restrict__ list, RouteArgs a,
+                                                       int counts_global) {
   extern __shared__ uint32_t lds_cur[];
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int ci = blockIdx.x * 4 + w;
@@ -160,7 +165,7 @@ __global__ __launch_bounds__(256) void k_route_scatter(const int32_t* __restrict
   const int col = (h - g * a.G) * a.nchunk_r + c;
   for (int j = lane; j < a.nb; j += 64) {
     const int64_t row = ((int64_t)s * a.Hkv + g) * a.nb + j;
-    cur[j] = bucket_off[row] + counts[row * a.ncols + col];
+    cur[j] = (counts_global ? 0u : bucket_off[row]) + counts[row * a.ncols + col];
   }
   const int64_t r0 = (int64_t)c * kRouteChunkRows;
   const int64_t rows = (a.Lq - r0 < kRouteChunkRows) ? a.Lq - r0 : kRouteChunkRows;
@@ -220,11 +225,122 @@ hipError_t launch_route_scan_buckets(const uint32_t* bucket_total, uint32_t* buc
 
 hipError_t launch_route_scatter(const int32_t* sel, const uint32_t* counts,
                                 const uint32_t* bucket_off, uint32_t* list, const Dims& d,
-                                hipStream_t st) {
+                                hipStream_t st, bool counts_global) {
   const RouteArgs a = route_args(d);
   const unsigned grid = (unsigned)((a.nchunks + 3) / 4);
   hipLaunchKernelGGL(k_route_scatter, dim3(grid), dim3(256), 4 * d.nb * sizeof(uint32_t), st,
-                     sel, counts, bucket_off, list, a);
+                     sel, counts, bucket_off, list, a, counts_global ? 1 : 0);
+  return hipGetLastError();
+}
+
+// Small problems: one workgroup turns the whole count matrix [nrows][ncols]
+// into global list positions with one flat exclusive scan (row-major order is
+// bucket order, then column order), and derives the bucket and tile offsets
+// from it.  Thread t scans the contiguous segment [t*seg, (t+1)*seg).
+constexpr int kScanSmallThreads = 1024;
+constexpr int kScanSmallMax = 16 * 1024;   // counts handled by route_scan_small
+
+__global__ __launch_bounds__(kScanSmallThreads) void k_route_scan_small(
+    uint32_t* __restrict__ counts, uint32_t* __restrict__ bucket_off,
+    uint32_t* __restrict__ tile_off, int nrows, int ncols, int tile_m) {
+  __shared__ uint32_t wsum[kScanSmallThreads / 64];
+  __shared__ uint32_t carry_s;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  constexpr int NW = kScanSmallThreads / 64;
+  const int total = nrows * ncols;
+  // segments of a multiple of 4 counts: 16-byte loads and stores (the count
+  // matrix starts 256-byte aligned); the last segment may be ragged
+  const int seg = ((total + kScanSmallThreads - 1) / kScanSmallThreads + 3) & ~3;
+  const int b0 = tid * seg;
+  const int b1 = b0 + seg < total ? b0 + seg : total;
+  uint32_t v[kScanSmallMax / kScanSmallThreads];
+  const int nv = b1 > b0 ? b1 - b0 : 0;
+  uint32_t mine = 0;
+#pragma unroll
+  for (int i = 0; i < kScanSmallMax / kScanSmallThreads; i += 4) {
+    if (i + 4 <= nv) {
+      const u32x4 x = *reinterpret_cast<const u32x4*>(counts + b0 + i);
+      v[i] = x[0]; v[i + 1] = x[1]; v[i + 2] = x[2]; v[i + 3] = x[3];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[i + e] = (i + e < nv) ? counts[b0 + i + e] : 0u;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kScanSmallMax / kScanSmallThreads; ++i) mine += v[i];
+  // workgroup exclusive scan of the segment sums
+  uint32_t incl = mine;
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) wsum[w] = incl;
+  __syncthreads();
+  uint32_t before = 0;
+  for (int i = 0; i < w; ++i) before += wsum[i];
+  uint32_t run = before + incl - mine;
+#pragma unroll
+  for (int i = 0; i < kScanSmallMax / kScanSmallThreads; ++i) {
+    const uint32_t c = v[i];
+    v[i] = run;
+    run += c;
+  }
+#pragma unroll
+  for (int i = 0; i < kScanSmallMax / kScanSmallThreads; i += 4) {
+    if (i + 4 <= nv) {
+      *reinterpret_cast<u32x4*>(counts + b0 + i) = u32x4{v[i], v[i + 1], v[i + 2], v[i + 3]};
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (i + e < nv) counts[b0 + i + e] = v[i + e];
+    }
+  }
+  uint32_t grand = 0;
+  for (int i = 0; i < NW; ++i) grand += wsum[i];
+  __syncthreads();  // every position written before rows read them back
+  // bucket offsets and per-bucket tile counts; scan of the tile counts
+  if (tid == 0) carry_s = 0;
+  __syncthreads();
+  for (int base = 0; base < nrows; base += kScanSmallThreads) {
+    const int row = base + tid;
+    uint32_t t = 0;
+    if (row < nrows) {
+      const uint32_t off = counts[(int64_t)row * ncols];
+      const uint32_t end = row + 1 < nrows ? counts[(int64_t)(row + 1) * ncols] : grand;
+      bucket_off[row] = off;
+      t = (end - off + tile_m - 1) / tile_m;
+    }
+    uint32_t ti = t;
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t y = __shfl_up(ti, o);
+      if (lane >= o) ti += y;
+    }
+    __syncthreads();
+    if (lane == 63) wsum[w] = ti;
+    __syncthreads();
+    uint32_t tb = carry_s;
+    for (int i = 0; i < w; ++i) tb += wsum[i];
+    if (row < nrows) tile_off[row] = tb + ti - t;
+    uint32_t seg_t = 0;
+    for (int i = 0; i < NW; ++i) seg_t += wsum[i];
+    __syncthreads();
+    if (tid == 0) carry_s += seg_t;
+    __syncthreads();
+  }
+  if (tid == 0) {
+    bucket_off[nrows] = grand;
+    tile_off[nrows] = carry_s;
+  }
+}
+
+bool route_scan_small_fits(const Dims& d) {
+  return (int64_t)d.nrows * d.ncols <= kScanSmallMax;
+}
+
+hipError_t launch_route_scan_small(uint32_t* counts, uint32_t* bucket_off, uint32_t* tile_off,
+                                   const Dims& d, hipStream_t st) {
+  hipLaunchKernelGGL(k_route_scan_small, dim3(1), dim3(kScanSmallThreads), 0, st, counts,
+                     bucket_off, tile_off, d.nrows, d.ncols, d.tile_m);
   return hipGetLastError();
 }
 

@@ -145,7 +145,8 @@ int32_t moba_abi_version(void);
  * reset.  Names: "block_mean", "transpose_v", "gate_topk", "route_count",
  * "route_scan_rows", "route_scan_buckets", "route_scatter", "attn_routed",
  * "attn_own_merge", "attn_full", "decode_plan", "decode_attn",
- * "decode_merge", "merge_partials".  Unknown names give
+ * "decode_merge", "merge_partials", "pool_transpose", "block_mean_finalize",
+ * "route_scan_small".  Unknown names give
  * MOBA_ERR_INVALID_ARGUMENT.  (bf16 prefill runs the own-block attention,
  * "attn_own_merge", on an internal stream of the same device, forked from
  * and joined back into the caller's stream.)

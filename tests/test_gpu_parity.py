@@ -169,6 +169,25 @@ def test_run_to_run_bitwise_determinism():
     assert torch.equal(o1.view(torch.int16), o3.view(torch.int16))
 
 
+def test_precomputed_block_means_prefill():
+    """Prefill with block means from moba_block_mean gives the same bits as
+    the call that pools K itself (same sums in the same order), for a batched
+    bf16 case and an fp32 one."""
+    moba = _moba()
+    for w in (moba_inputs.custom("pre_bf16", "bf16", 2, 4096, None, 4, 2, 128, 512, 3, 36),
+              moba_inputs.custom("pre_f32", "f32", 1, 2048, None, 2, 1, 64, 256, 3, 37)):
+        print(f"case {w}", flush=True)
+        q, k, v = moba_inputs.make_inputs(w, device=DEV)
+        kbar = moba.moba_block_mean(k, w.block_size)
+        o1, s1 = moba.moba_forward_ex(q, k, v, w.block_size, w.topk, return_selection=True)
+        o2, s2 = moba.moba_forward_ex(q, k, v, w.block_size, w.topk, k_block_mean=kbar,
+                                      return_selection=True)
+        torch.cuda.synchronize()
+        assert torch.equal(s1, s2)
+        iv = torch.int16 if w.dtype == "bf16" else torch.int32
+        assert torch.equal(o1.view(iv), o2.view(iv))
+
+
 def test_micro_32k_parity():
     """The 32K single-head shape (block 2048, top-k 3): every selection, and
     outputs for block-edge and uniform rows."""
