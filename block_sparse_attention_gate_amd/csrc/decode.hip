@@ -207,8 +207,9 @@ __global__ __launch_bounds__(256) void k_decode_attn(
 }
 
 // grid S*H, D threads.  Wave 0 lists this head's partials in a fixed order
-// (union slot, then chunk); then every thread reads the list, so the merge is
-// a few independent load streams instead of a chain of dependent loads.
+// (union slot, then chunk); the max, the weights and the sum of the partials
+// are then workgroup reductions, and the weighted sum of the partial rows
+// keeps eight loads in flight (fixed order: deterministic).
 constexpr int kMergeMaxItems = 8192;
 template <typename T, int D, int GM>
 __global__ __launch_bounds__(D) void k_decode_merge(const float* __restrict__ part,
@@ -220,7 +221,7 @@ __global__ __launch_bounds__(D) void k_decode_merge(const float* __restrict__ pa
   __shared__ int items[kMergeMaxItems];
   __shared__ float wts[kMergeMaxItems];
   __shared__ int nitems_s;
-  __shared__ float lsum_s;
+  __shared__ float red_s[D / 64];
   const int sh = blockIdx.x, s = sh / H, h = sh % H, G = H / Hkv, g = h / G, hl = h % G;
   const int sg = s * Hkv + g;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -241,30 +242,51 @@ __global__ __launch_bounds__(D) void k_decode_merge(const float* __restrict__ pa
   }
   __syncthreads();
   const int ni = nitems_s;
+  constexpr int NWV = D / 64;  // waves in the workgroup
+  // max of the partial maxima, then the weights and the weighted sum of the
+  // partial sums: one item per thread per pass, reduced across the workgroup
   float M = -__builtin_inff();
-  for (int t = 0; t < ni; ++t) M = fmaxf(M, part[((int64_t)items[t] * GM + hl) * (D + 2)]);
+  for (int t = tid; t < ni; t += D) M = fmaxf(M, part[((int64_t)items[t] * GM + hl) * (D + 2)]);
+  M = wave_max(M);
+  if (lane == 0) red_s[tid >> 6] = M;
+  __syncthreads();
+  M = red_s[0];
+#pragma unroll
+  for (int i = 1; i < NWV; ++i) M = fmaxf(M, red_s[i]);
+  float lp = 0.f;
   for (int t = tid; t < ni; t += D) {
     const float* prow = part + ((int64_t)items[t] * GM + hl) * (D + 2);
-    wts[t] = __builtin_amdgcn_exp2f(prow[0] - M);
+    const float wv = __builtin_amdgcn_exp2f(prow[0] - M);
+    wts[t] = wv;
+    lp = fmaf(wv, prow[1], lp);
   }
+  for (int o = 32; o >= 1; o >>= 1) lp += __shfl_xor(lp, o);
+  __syncthreads();  // M read by every thread before red_s is reused; wts complete
+  if (lane == 0) red_s[tid >> 6] = lp;
   __syncthreads();
-  if (tid == 0) {
-    float l = 0.f;
-    for (int t = 0; t < ni; ++t) l = fmaf(wts[t], part[((int64_t)items[t] * GM + hl) * (D + 2) + 1], l);
-    lsum_s = l;
-  }
-  float acc = 0.f;
+  float lsum = 0.f;
+#pragma unroll
+  for (int i = 0; i < NWV; ++i) lsum += red_s[i];
+  // o: eight partial rows in flight, eight accumulators, fixed order
+  float acc8[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc8[e] = 0.f;
   int t = 0;
-  for (; t + 4 <= ni; t += 4) {
-    float x[4];
+  for (; t + 8 <= ni; t += 8) {
+    float x[8];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) x[e] = part[((int64_t)items[t + e] * GM + hl) * (D + 2) + 2 + tid];
+    for (int e = 0; e < 8; ++e) x[e] = part[((int64_t)items[t + e] * GM + hl) * (D + 2) + 2 + tid];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc = fmaf(wts[t + e], x[e], acc);
+    for (int e = 0; e < 8; ++e) acc8[e] = fmaf(wts[t + e], x[e], acc8[e]);
   }
-  for (; t < ni; ++t) acc = fmaf(wts[t], part[((int64_t)items[t] * GM + hl) * (D + 2) + 2 + tid], acc);
-  __syncthreads();
-  const float r = acc / lsum_s;
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    if (t + e < ni)
+      acc8[e] = fmaf(wts[t + e], part[((int64_t)items[t + e] * GM + hl) * (D + 2) + 2 + tid],
+                     acc8[e]);
+  const float acc = ((acc8[0] + acc8[1]) + (acc8[2] + acc8[3])) +
+                    ((acc8[4] + acc8[5]) + (acc8[6] + acc8[7]));
+  const float r = acc / lsum;
   T* orow = out + ((int64_t)s * H + h) * D;
   if (sizeof(T) == 2)
     reinterpret_cast<bf16_t*>(orow)[tid] = f32_to_bf16(r);

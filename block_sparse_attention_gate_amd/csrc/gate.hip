@@ -120,97 +120,97 @@ __global__ __launch_bounds__(256) void k_gate_topk_bf16(
   }
 }
 
-// q_len == 1 (decode), bf16: one workgroup per (sequence, KV head); the G
-// query heads of the group are the MFMA columns (lane l%32 = head), and the
-// four waves take every fourth 32-block tile.  Per-lane lists merge across
-// the lane halves, then across the waves through LDS.  grid S*Hkv, 256 threads.
+// Decode (one query per head, bf16): one wave per (sequence, head).  Lane l
+// scores the past blocks j = l, l + 64, ... with fp32 dot products (the block
+// mean in fp32, the query widened from bf16) and keeps its own top list; the
+// wave then takes the k-1 best of the 64 lists one at a time: a butterfly
+// arg-max on (score descending, block index ascending), after which the
+// winning lane drops its list head.  grid ceil(S*H/4), 256 threads.
 template <int D, int KM>
 __global__ __launch_bounds__(256) void k_gate_topk_decode_bf16(
     const bf16_t* __restrict__ q, const float* __restrict__ kbar, int32_t* __restrict__ sel,
-    int64_t L, int H, int Hkv, int B, int nb, int topk) {
-  __shared__ float ls[4][32][KM];
-  __shared__ int li[4][32][KM];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int n = lane & 31, hh = lane >> 5;
-  const int sg = blockIdx.x, s = sg / Hkv, g = sg % Hkv, G = H / Hkv;
-  const bool valid = n < G;
-  const int h = g * G + (valid ? n : 0);
+    int64_t L, int H, int Hkv, int B, int nb, int topk, int nsh) {
+  const int lane = threadIdx.x & 63;
+  const int sh = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (sh >= nsh) return;
+  const int s = sh / H, h = sh % H, g = h / (H / Hkv);
   const int b = (int)((L - 1) / B);  // own block of the query at the last position
   const int kp = topk - 1;
   const int nkeep = kp < b ? kp : b;
-  bf16x8 qf[D / 16];
-  const bf16_t* qrow = q + ((int64_t)s * H + h) * D;
+  int kept[KM];
 #pragma unroll
-  for (int t = 0; t < D / 16; ++t) {
-    qf[t] = ld_bf16x8(qrow + 16 * t + 8 * hh);
-    if (!valid) qf[t] = bf16x8{};
-  }
-  TopList<KM> top;
-  top.init();
-  const float* kb = kbar + ((int64_t)s * Hkv + g) * nb * D;
-  if (kp > 0) {
-    for (int jt = w; jt * 32 < b; jt += 4) {
-      const int jrow = (jt * 32 + n < nb) ? jt * 32 + n : nb - 1;
-      const float* arow = kb + (int64_t)jrow * D + 8 * hh;
-      f32x16 acc = {};
+  for (int t = 0; t < KM; ++t) kept[t] = 0x7fffffff;
+  if (nkeep > 0) {
+    float qr[D];
+    const bf16_t* qrow = q + ((int64_t)s * H + h) * D;
 #pragma unroll
-      for (int t = 0; t < D / 16; ++t) {
-        const float4 x0 = *reinterpret_cast<const float4*>(arow + 16 * t);
-        const float4 x1 = *reinterpret_cast<const float4*>(arow + 16 * t + 4);
-        const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-        bf16x8 a0, a1, a2;
+    for (int dd = 0; dd < D; dd += 8) {
+      const u32x4 raw = *reinterpret_cast<const u32x4*>(qrow + dd);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const __bf16 hi = static_cast<__bf16>(xs[e]);
-          const float r1 = xs[e] - static_cast<float>(hi);
-          const __bf16 mid = static_cast<__bf16>(r1);
-          const float r2 = r1 - static_cast<float>(mid);
-          a0[e] = hi;
-          a1[e] = mid;
-          a2[e] = static_cast<__bf16>(r2);
-        }
-        acc = mfma32(a0, qf[t], acc);
-        acc = mfma32(a1, qf[t], acc);
-        acc = mfma32(a2, qf[t], acc);
-      }
-#pragma unroll
-      for (int reg = 0; reg < 16; ++reg) {
-        const int j = jt * 32 + 8 * (reg >> 2) + 4 * hh + (reg & 3);
-        if (j < b) top.insert_ascending(acc[reg], j);
+      for (int e = 0; e < 4; ++e) {
+        qr[dd + 2 * e] = __uint_as_float(raw[e] << 16);
+        qr[dd + 2 * e + 1] = __uint_as_float(raw[e] & 0xffff0000u);
       }
     }
-    float os[KM];
-    int oi[KM];
+    TopList<KM> top;
+    top.init();
+    const float* kb = kbar + ((int64_t)s * Hkv + g) * nb * D;
+    for (int j = lane; j < b; j += 64) {
+      const float* kr = kb + (int64_t)j * D;
+      float acc = 0.f;
+#pragma unroll
+      for (int dd = 0; dd < D; dd += 4) {
+        const float4 x = *reinterpret_cast<const float4*>(kr + dd);
+        acc = fmaf(qr[dd], x.x, acc);
+        acc = fmaf(qr[dd + 1], x.y, acc);
+        acc = fmaf(qr[dd + 2], x.z, acc);
+        acc = fmaf(qr[dd + 3], x.w, acc);
+      }
+      top.insert_ascending(acc, j);
+    }
 #pragma unroll
     for (int t = 0; t < KM; ++t) {
-      os[t] = half_swap(top.s[t]);
-      oi[t] = __shfl_xor(top.i[t], 32);
-    }
+      if (t < nkeep) {
+        float bs = top.s[0];
+        int bi = top.i[0];
 #pragma unroll
-    for (int t = 0; t < KM; ++t) top.insert_any(os[t], oi[t]);
-    if (hh == 0) {
+        for (int o = 32; o >= 1; o >>= 1) {
+          const float os = __shfl_xor(bs, o);
+          const int oi = __shfl_xor(bi, o);
+          if (os > bs || (os == bs && oi < bi)) {
+            bs = os;
+            bi = oi;
+          }
+        }
+        kept[t] = bi;
+        if (top.i[0] == bi) {  // exactly one lane holds block bi
 #pragma unroll
-      for (int t = 0; t < KM; ++t) {
-        ls[w][n][t] = top.s[t];
-        li[w][n][t] = top.i[t];
+          for (int u = 0; u + 1 < KM; ++u) {
+            top.s[u] = top.s[u + 1];
+            top.i[u] = top.i[u + 1];
+          }
+          top.s[KM - 1] = -__builtin_inff();
+          top.i[KM - 1] = 0x7fffffff;
+        }
       }
     }
   }
-  __syncthreads();
-  if (w != 0 || hh != 0 || !valid) return;
-  if (kp > 0) {
-    for (int w2 = 1; w2 < 4; ++w2)
+  if (lane != 0) return;
+  // ascending order (unused slots hold INT_MAX and stay last)
 #pragma unroll
-      for (int t = 0; t < KM; ++t) top.insert_any(ls[w2][n][t], li[w2][n][t]);
-    top.truncate(kp);
-    top.sort_indices();
-  }
+  for (int pass = 0; pass < KM; ++pass)
+#pragma unroll
+    for (int t = (pass & 1); t + 1 < KM; t += 2) {
+      const int x = kept[t], y = kept[t + 1];
+      kept[t] = x < y ? x : y;
+      kept[t + 1] = x < y ? y : x;
+    }
   int32_t* out = sel + ((int64_t)s * H + h) * topk;
 #pragma unroll
   for (int t = 0; t < KM + 1; ++t) {
     if (t < topk) {
-      const int kept = (t < KM) ? top.i[t < KM ? t : 0] : 0;
-      out[t] = t < nkeep ? kept : (t == nkeep ? b : -1);
+      const int kv = (t < KM) ? kept[t < KM ? t : 0] : 0;
+      out[t] = t < nkeep ? kv : (t == nkeep ? b : -1);
     }
   }
   for (int t = KM + 1; t < topk; ++t) out[t] = -1;
@@ -272,10 +272,10 @@ static hipError_t gate_dispatch_d(const void* q, const float* kbar, int32_t* sel
   const int kp = d.topk - 1;
 #define MOBA_GATE_CASE(KMV)                                                                  \
   if (kp <= KMV) {                                                                           \
-    if (d.bf16 && d.Lq == 1 && d.G <= 32) {                                                  \
-      hipLaunchKernelGGL((k_gate_topk_decode_bf16<D, KMV>), dim3(d.S * d.Hkv), dim3(256), 0, \
-                         st, static_cast<const bf16_t*>(q), kbar, sel, d.L, d.H, d.Hkv, d.B, \
-                         d.nb, d.topk);                                                      \
+    if (d.bf16 && d.Lq == 1) {                                                  \
+      hipLaunchKernelGGL((k_gate_topk_decode_bf16<D, KMV>), dim3((d.S * d.H + 3) / 4),      \
+                         dim3(256), 0, st, static_cast<const bf16_t*>(q), kbar, sel, d.L, d.H, \
+                         d.Hkv, d.B, d.nb, d.topk, d.S * d.H);                               \
     } else if (d.bf16) {                                                                     \
       dim3 grid((unsigned)((d.Lq + 127) / 128), d.S * d.H);                                  \
       hipLaunchKernelGGL((k_gate_topk_bf16<D, KMV>), grid, dim3(256),                        \
