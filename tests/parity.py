@@ -8,6 +8,12 @@ within 1e-3 of the oracle's last kept score) and that query's output is
 compared with the oracle evaluated on the GPU's own selection.
 
 Outputs: bf16 max-abs <= 2e-2 and mean-abs <= 2e-3; fp32 max-abs <= 1e-4.
+The absolute bounds are loose once outputs shrink at long context (|o| ~ 1e-2),
+so every compared (head, query) row must also have a relative RMS error
+||o_gpu - o_ref|| / ||o_ref|| below RELRMS (bf16: 2^-6, fp32: 2e-5; the
+measured worst rows sit near 4e-3 = 2^-8, what rounding P and the output to
+bf16 gives, and 2e-6 in fp32): a row attended over a wrong key set misses by
+far more.
 
 Everything works on a sample of query rows given with their positions, so
 the same checks serve the small cases (every row) and the 128K / 1M cases
@@ -24,6 +30,7 @@ from oracle import moba_oracle as O
 
 TIE = 1e-3
 TOL = {"bf16": (2e-2, 2e-3), "f32": (1e-4, 1e-4)}
+RELRMS = {"bf16": 2.0 ** -6, "f32": 2e-5}
 
 
 def to64(t):
@@ -66,6 +73,7 @@ def check_outputs(out_rows, q_rows, positions, sel_gpu, block_size, kv_len, dtyp
     group = H // n_kv_heads
     scale = 1.0 / math.sqrt(D)
     errs = []
+    rel = []
     for h, n in pairs:
         pos = int(positions[n])
         if full:
@@ -74,11 +82,18 @@ def check_outputs(out_rows, q_rows, positions, sel_gpu, block_size, kv_len, dtyp
             keys = O.key_set(sel_gpu[h, n], pos, block_size, kv_len)
         kk, vv = fetch_kv(h // group, keys)
         ref = O.attend(q_rows[n, h], kk, vv, np.arange(keys.size), scale)
-        errs.append(np.abs(out_rows[n, h] - ref))
+        d = out_rows[n, h] - ref
+        errs.append(np.abs(d))
+        rel.append(np.sqrt(np.mean(d * d)) / max(np.sqrt(np.mean(ref * ref)), 1e-30))
     e = np.stack(errs)
+    r = np.array(rel)
     tmax, tmean = TOL[dtype]
     assert e.max() <= tmax, f"max abs error {e.max():.3e} > {tmax}"
     assert e.mean() <= tmean, f"mean abs error {e.mean():.3e} > {tmean}"
+    worst = int(np.argmax(r))
+    assert r.max() <= RELRMS[dtype], (f"relative RMS error {r.max():.3e} > {RELRMS[dtype]:.3e} "
+                                      f"at pair {pairs[worst]}")
+    print(f"  worst relative RMS error {r.max():.2e} (median {np.median(r):.2e})", flush=True)
     return float(e.max()), float(e.mean())
 
 

@@ -103,6 +103,25 @@ def test_small_parity(w):
     _run_case(w)
 
 
+EDGE = [
+    # the largest top-k: 16 routed past blocks per query
+    (moba_inputs.custom("k17_nb40", "bf16", 1, 2560, None, 2, 1, 64, 64, 17, 51), None),
+    # one block: nothing to route, only the own block
+    (moba_inputs.custom("single_block", "bf16", 1, 256, None, 2, 2, 128, 256, 3, 52), None),
+    # two 4096-key blocks (sampled rows: the oracle attends up to 8K keys per row)
+    (moba_inputs.custom("b4096_nb2", "bf16", 1, 8192, None, 1, 1, 128, 4096, 2, 53), 256),
+    # batch of 4 through the small-problem path
+    (moba_inputs.custom("batch4", "bf16", 4, 512, None, 2, 1, 128, 64, 3, 54), None),
+    # fp32 with topk above the block count (full attention)
+    (moba_inputs.custom("f32_k17", "f32", 1, 1024, None, 1, 1, 64, 64, 17, 55), None),
+]
+
+
+@pytest.mark.parametrize("w,n_uniform", EDGE, ids=[w.name for w, _ in EDGE])
+def test_edge_cases(w, n_uniform):
+    _run_case(w, n_uniform=n_uniform)
+
+
 def test_chunked_and_batched_queries():
     """q_len < kv_len (queries at the end of the cache), batch 2, ragged q_len."""
     w = moba_inputs.custom("batch2_q100", "bf16", 2, 100, 1024, 4, 2, 128, 64, 3, 31)
