@@ -119,6 +119,28 @@ def time_region(fn, steps, warmup):
     return e0.elapsed_time(e1) / steps, wall * 1e3
 
 
+def time_cold(fn, steps, flush_mib=512):
+    """Median time of fn with a flush_mib MiB buffer written before every call
+    (evicts the working set from the 256 MB Infinity Cache); each call is
+    bracketed by its own events, the write is outside them."""
+    import torch
+    buf = torch.empty(flush_mib << 20, dtype=torch.uint8, device="cuda:0")
+    st = torch.cuda.current_stream()
+    times = []
+    for _ in range(steps):
+        buf.fill_(1)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        fn()
+        e1.record(st)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    del buf
+    times.sort()
+    return times[len(times) // 2]
+
+
 def kernel_breakdown(moba, fn, steps):
     """Per-kernel average launch time (ms) from the library's HIP events."""
     import torch
@@ -138,7 +160,7 @@ def kernel_breakdown(moba, fn, steps):
     return out
 
 
-def run_prefill(moba, w, steps, warmup, full_steps, full_warmup, with_full=True):
+def run_prefill(moba, w, steps, warmup, full_steps, full_warmup, with_full=True, cold=False):
     import torch
     import moba_inputs
     log(f"[bench] {w.name}: generating inputs")
@@ -151,6 +173,7 @@ def run_prefill(moba, w, steps, warmup, full_steps, full_warmup, with_full=True)
     ms, wall_ms = time_region(fwd, steps, warmup)
     kern = kernel_breakdown(moba, fwd, steps)
     eff, routed, own, full = prefill_flops(w)
+    cold_ms = time_cold(fwd, steps) if cold else None
     res = {
         "workload": w.name, "ms": ms, "wall_ms": wall_ms,
         "effective_tflops": eff / (ms * 1e-3) / 1e12,
@@ -158,6 +181,10 @@ def run_prefill(moba, w, steps, warmup, full_steps, full_warmup, with_full=True)
         "effective_flop": eff, "routed_flop": routed, "own_flop": own,
         "kernels_ms": {k_: round(v_["avg_ms"], 4) for k_, v_ in kern.items()},
     }
+    if cold_ms is not None:
+        # inputs evicted from the Infinity Cache before every call (median)
+        res["cold_ms"] = cold_ms
+        res["cold_effective_tflops"] = eff / (cold_ms * 1e-3) / 1e12
     if "attn_routed" in kern:
         t = kern["attn_routed"]["avg_ms"] * 1e-3
         res["attn_routed_tflops"] = routed / t / 1e12
@@ -313,6 +340,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--skip-1m", action="store_true", help="skip the 1M-token prefill")
+    ap.add_argument("--skip-128k", action="store_true", help="skip the 128K Llama-layer prefill")
     ap.add_argument("--skip-decode", action="store_true", help="skip the 1M-cache decode")
     ap.add_argument("--skip-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
@@ -356,8 +384,15 @@ def main():
         return
     w = moba_inputs.WORKLOADS["micro_32k"]
     main_res = run_prefill(moba, w, args.steps, args.warmup, full_steps=args.steps,
-                           full_warmup=args.warmup)
+                           full_warmup=args.warmup, cold=True)
     also = {}
+    if not args.skip_128k:
+        w3 = moba_inputs.WORKLOADS["llama8b_128k"]
+        r3 = run_prefill(moba, w3, min(args.steps, 10), min(args.warmup, 2), full_steps=3,
+                         full_warmup=1)
+        r3["roofline"] = roofline(r3)
+        r3.pop("_roofline_src")
+        also["llama8b_128k"] = r3
     if not args.skip_1m:
         w1 = moba_inputs.WORKLOADS["prefill_1m"]
         r1 = run_prefill(moba, w1, min(args.steps, 3), min(args.warmup, 1), full_steps=1,
