@@ -132,6 +132,7 @@ struct Plan {
   size_t off_ublk = 0, off_umask = 0, off_ucount = 0, off_part = 0, off_bmpart = 0;
   size_t off_own_o = 0, off_own_lse = 0;
   bool split_own = false;  // own block on the side stream + separate merge
+  int full_parts = 0;      // split full attention: key chunks per row (0: whole rows)
 };
 
 moba_status check_common(const moba_args* a, bool full, Plan* p) {
@@ -287,6 +288,13 @@ moba_status plan_full(const moba_args* a, Plan* p) {
     d.nb = (int)(d.L / 64);
     p->need_vt = d.bf16;
     if (p->need_vt) p->off_vt = take((size_t)d.S * d.Hkv * d.D * d.L * 2);
+    // small problems: key chunks + merge (whole row tiles would leave the chip idle)
+    p->full_parts = moba::full_split_parts(d);
+    if (p->full_parts > 0) {
+      const size_t nqh = (size_t)d.S * d.H * d.Lq;
+      p->off_own_o = take((size_t)p->full_parts * nqh * d.D * 2);
+      p->off_own_lse = take((size_t)p->full_parts * nqh * 4);
+    }
   }
   p->total = off;
   if (a->workspace && a->workspace_bytes < p->total)
@@ -473,7 +481,7 @@ moba_status forward_impl(const moba_args* a) {
       }
     }
     l.run(K_MERGE, [&] {
-      return moba::launch_merge_partials_bf16(own_o, own_lse, po, plse, a->out, d, l.st);
+      return moba::launch_merge_partials_bf16(own_o, own_lse, 2, po, plse, a->out, d, l.st);
     });
     if (l.err != hipSuccess) return hip_fail(l);
     return MOBA_OK;
@@ -517,6 +525,20 @@ moba_status full_impl(const moba_args* a) {
     return MOBA_OK;
   }
   if (p.need_vt) l.run(K_TRANSPOSE_V, [&] { return moba::launch_transpose_v(a->v, vt, d, l.st); });
+  if (p.full_parts > 0) {
+    void* part_o = (void*)(ws.base + p.off_own_o);
+    float* part_lse = (float*)(ws.base + p.off_own_lse);
+    l.run(K_ATTN_FULL, [&] {
+      return moba::launch_attn_query_bf16(a->q, a->k, vt, part_o, part_lse, nullptr, 3, d, l.st,
+                                          p.full_parts);
+    });
+    l.run(K_MERGE, [&] {
+      return moba::launch_merge_partials_bf16(part_o, part_lse, p.full_parts, nullptr, nullptr,
+                                              a->out, d, l.st);
+    });
+    if (l.err != hipSuccess) return hip_fail(l);
+    return MOBA_OK;
+  }
   l.run(K_ATTN_FULL, [&] {
     return d.bf16 ? moba::launch_attn_query_bf16(a->q, a->k, vt, nullptr, nullptr, a->out, 1, d,
                                                  l.st)

@@ -16,7 +16,9 @@
 //     k_merge_partials, so that it can run concurrently with the routing;
 //     workgroups with more than kOwnSplitSteps key tiles split their key
 //     range in two halves, written to two partials (an empty half writes
-//     log-sum-exp = -inf).
+//     log-sum-exp = -inf).  Mode 3: full causal attention split into key
+//     chunks of chunk_tiles 64-key tiles, one partial per chunk, for problems
+//     too small to fill the chip with whole row tiles (the merge follows).
 //
 // Wave tile: 32 queries (lane l owns query l%32) x 64 keys per step.
 //   S^T = K Q^T on 32x32x16 MFMA (K rows in the kperm order, see common.h),
@@ -294,18 +296,20 @@ template <int D, int MODE, int NW>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_query(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ vt,
     const bf16_t* __restrict__ po, const float* __restrict__ plse, bf16_t* __restrict__ out,
-    int Lq, int L, int q_off, int H, int Hkv, int kp, int B, int HW, float sl2) {
+    int Lq, int L, int q_off, int H, int Hkv, int kp, int B, int HW, float sl2, int nparts,
+    int chunk_tiles) {
   using T = Tiles<D, NW>;
   __shared__ __attribute__((aligned(16))) bf16_t lds[2 * T::BUF];
   const int RW = 32 * NW / HW;
-  // Mode 2: blockIdx.x = 2 * item + part (two halves of the key range).
-  const int item = MODE == 2 ? (int)blockIdx.x >> 1 : (int)blockIdx.x;
-  const int part = MODE == 2 ? (int)blockIdx.x & 1 : 0;
-  const int nitems = MODE == 2 ? (int)gridDim.x >> 1 : (int)gridDim.x;
+  // Modes 2 and 3: blockIdx.x = P * item + part (P key-range parts per item).
+  const int P = MODE == 2 ? 2 : (MODE == 3 ? nparts : 1);
+  const int item = (int)blockIdx.x / P;
+  const int part = (int)blockIdx.x % P;
+  const int nitems = (int)gridDim.x / P;
   // Longest work first.  Full attention: the last row tiles.  Own block (when
   // blocks hold whole row tiles): the tiles at the end of every block first.
   int rt;
-  if (MODE == 1) {
+  if (MODE == 1 || MODE == 3) {
     rt = nitems - 1 - item;
   } else if (q_off % B == 0 && B % RW == 0 && Lq % B == 0) {
     const int tpb = B / RW, nbq = Lq / B;
@@ -329,26 +333,32 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_query(
   const int pos = q_off + r;
   // key windows [klo, khi)
   const int wlast = (r0 + 31 < Lq ? r0 + 31 : Lq - 1);
-  const int klo_w = (MODE != 1) ? ((q_off + r0) / B) * B : 0;
+  const int klo_w = (MODE == 0 || MODE == 2) ? ((q_off + r0) / B) * B : 0;
   const int khi_w = wave_on ? q_off + wlast + 1 : 0;
   const int wglast = (rw0 + RW - 1 < Lq ? rw0 + RW - 1 : Lq - 1);
-  const int klo_g = (MODE != 1) ? ((q_off + rw0) / B) * B : 0;
+  const int klo_g = (MODE == 0 || MODE == 2) ? ((q_off + rw0) / B) * B : 0;
   const int khi_g = q_off + wglast + 1;
   int t0 = klo_g / 64, t1 = (khi_g + 63) / 64;
-  if (MODE == 2) {
-    const int nst = t1 - t0;
-    const int ts = nst > kOwnSplitSteps ? t0 + nst / 2 : t1;
-    if (part == 0) t1 = ts; else t0 = ts;
+  if (MODE == 2 || MODE == 3) {
+    if (MODE == 2) {
+      const int nst = t1 - t0;
+      const int ts = nst > kOwnSplitSteps ? t0 + nst / 2 : t1;
+      if (part == 0) t1 = ts; else t0 = ts;
+    } else {
+      const int a0 = t0 + part * chunk_tiles, a1 = a0 + chunk_tiles;
+      t0 = a0;
+      t1 = a1 < t1 ? a1 : t1;
+    }
     if (t0 >= t1) {
-      // empty second half: log-sum-exp -inf, which the merge skips
+      // empty part: log-sum-exp -inf, which the merge skips
       if (valid && hh == 0) {
         const int64_t nqh = (int64_t)gridDim.y * HW * Lq;
-        const_cast<float*>(plse)[nqh + ((int64_t)s * H + h) * Lq + r] = -__builtin_inff();
+        const_cast<float*>(plse)[part * nqh + ((int64_t)s * H + h) * Lq + r] = -__builtin_inff();
       }
       return;
     }
   }
-  const int klo_l = (MODE != 1) ? (pos / B) * B : 0;
+  const int klo_l = (MODE == 0 || MODE == 2) ? (pos / B) * B : 0;
 
   bf16x8 qf[D / 16];
   load_q<D>(q + (((int64_t)s * Lq + (valid ? r : 0)) * H + h) * D, valid, hh, qf);
@@ -418,9 +428,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_query(
   const float ltot = acc.l + half_swap(acc.l);
   bf16_t* orow = out + (((int64_t)s * Lq + r) * H + h) * D;
   float inv = 1.0f / ltot;
-  if (MODE == 2) {
-    // own-block partial (this half) of query-head qh: normalised o (bf16) and
-    // log2-sum-exp; a row with no visible key in this half gets o = 0, -inf
+  if (MODE == 2 || MODE == 3) {
+    // partial (this part of the key range) of query-head qh: normalised o
+    // (bf16) and log2-sum-exp; a row with no visible key here gets o = 0, -inf
     const int64_t nqh = (int64_t)gridDim.y * HW * Lq;
     const int64_t qh = ((int64_t)s * H + h) * Lq + r + part * nqh;
     orow = const_cast<bf16_t*>(po) + qh * D;
@@ -436,7 +446,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_query(
     const float lse_own = acc.m + __log2f(ltot);
     float M = lse_own;
     const int64_t sbase = (((int64_t)s * H + h) * Lq + r) * kp;
-    for (int t = 0; t < npast; ++t) M = fmaxf(M, plse[sbase + t]);
+    // all routed log-sum-exps first (independent loads), then the partial
+    // rows four at a time (four loads in flight per lane instead of one)
+    float lsv[kMaxTopk - 1];
+#pragma unroll
+    for (int t = 0; t < kMaxTopk - 1; ++t)
+      lsv[t] = t < npast ? plse[sbase + t] : -__builtin_inff();
+#pragma unroll
+    for (int t = 0; t < kMaxTopk - 1; ++t) M = fmaxf(M, lsv[t]);
     const float w_own = __builtin_amdgcn_exp2f(lse_own - M);
     float wsum = w_own;
     const float sc = w_own / ltot;
@@ -444,22 +461,36 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_query(
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
       for (int reg = 0; reg < 16; ++reg) acc.o[dt][reg] *= sc;
-    for (int t = 0; t < npast; ++t) {
-      const float wt = __builtin_amdgcn_exp2f(plse[sbase + t] - M);
-      wsum += wt;
-      const bf16_t* prow = po + (sbase + t) * D;
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
+    for (int t0 = 0; t0 < kMaxTopk - 1; t0 += 4) {
+      if (t0 < npast) {
+        uint2 raw[4][D / 32][4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint2 raw = *reinterpret_cast<const uint2*>(prow + 32 * dt + 8 * i + 4 * hh);
-          acc.o[dt][4 * i] = fmaf(wt, __uint_as_float(raw.x << 16), acc.o[dt][4 * i]);
-          acc.o[dt][4 * i + 1] =
-              fmaf(wt, __uint_as_float(raw.x & 0xffff0000u), acc.o[dt][4 * i + 1]);
-          acc.o[dt][4 * i + 2] = fmaf(wt, __uint_as_float(raw.y << 16), acc.o[dt][4 * i + 2]);
-          acc.o[dt][4 * i + 3] =
-              fmaf(wt, __uint_as_float(raw.y & 0xffff0000u), acc.o[dt][4 * i + 3]);
+        for (int u = 0; u < 4; ++u) {
+          const bf16_t* prow = po + (sbase + (t0 + u < npast ? t0 + u : t0)) * D;
+#pragma unroll
+          for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              raw[u][dt][i] = *reinterpret_cast<const uint2*>(prow + 32 * dt + 8 * i + 4 * hh);
         }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          // a slot past npast re-reads slot t0 with weight 0
+          const float wt = t0 + u < npast ? __builtin_amdgcn_exp2f(lsv[t0 + u] - M) : 0.f;
+          wsum += wt;
+#pragma unroll
+          for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const uint2 x = raw[u][dt][i];
+              acc.o[dt][4 * i] = fmaf(wt, __uint_as_float(x.x << 16), acc.o[dt][4 * i]);
+              acc.o[dt][4 * i + 1] = fmaf(wt, __uint_as_float(x.x & 0xffff0000u), acc.o[dt][4 * i + 1]);
+              acc.o[dt][4 * i + 2] = fmaf(wt, __uint_as_float(x.y << 16), acc.o[dt][4 * i + 2]);
+              acc.o[dt][4 * i + 3] = fmaf(wt, __uint_as_float(x.y & 0xffff0000u), acc.o[dt][4 * i + 3]);
+            }
+        }
+      }
     }
     inv = 1.0f / wsum;
   }
@@ -476,13 +507,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_query(
     }
 }
 
-// Merge of the own-block partials (one or two halves) with the routed
-// partials of every query-head: out = sum_x 2^(lse_x - M) o_x / sum_x
-// 2^(lse_x - M).  own_o / own_lse hold the two halves one after the other.  16 lanes
+// Merge of the key-range partials (two halves of the own block, or the key
+// chunks of split full attention; nown of them, one after the other in
+// own_o / own_lse) with the routed partials of every query-head:
+// out = sum_x 2^(lse_x - M) o_x / sum_x 2^(lse_x - M).  16 lanes
 // per query-head, D/16 dims per lane.  grid ceil(nqh / 16), 256 threads.
 template <int D>
 __global__ __launch_bounds__(256) void k_merge_partials(
-    const bf16_t* __restrict__ own_o, const float* __restrict__ own_lse,
+    const bf16_t* __restrict__ own_o, const float* __restrict__ own_lse, int nown,
     const bf16_t* __restrict__ po, const float* __restrict__ plse, bf16_t* __restrict__ out,
     int64_t nqh, int64_t Lq, int H, int64_t q_off, int B, int kp) {
   constexpr int EPL = D / 16;
@@ -494,9 +526,10 @@ __global__ __launch_bounds__(256) void k_merge_partials(
   const int64_t s = sh / H;
   const int64_t own = (q_off + r) / B;
   const int npast = (int)(kp < own ? kp : own);
+  // part 0 always holds keys (the first key of the range is visible)
   const float lse0 = own_lse[qh];
-  const float lse1 = own_lse[nqh + qh];  // second half of a split own block, or -inf
-  float M = fmaxf(lse0, lse1);
+  float M = lse0;
+  for (int p = 1; p < nown; ++p) M = fmaxf(M, own_lse[p * nqh + qh]);
   for (int t = 0; t < npast; ++t) M = fmaxf(M, plse[qh * kp + t]);
   float acc[EPL];
   auto load = [&](const bf16_t* p, float (&x)[EPL]) {
@@ -521,10 +554,12 @@ __global__ __launch_bounds__(256) void k_merge_partials(
   float wsum = w0;
 #pragma unroll
   for (int i = 0; i < EPL; ++i) acc[i] = w0 * x[i];
-  if (lse1 > -__builtin_inff()) {
-    const float w1 = __builtin_amdgcn_exp2f(lse1 - M);
+  for (int p = 1; p < nown; ++p) {
+    const float lp = own_lse[p * nqh + qh];
+    if (!(lp > -__builtin_inff())) continue;  // empty part
+    const float w1 = __builtin_amdgcn_exp2f(lp - M);
     wsum += w1;
-    load(own_o + (nqh + qh) * D + sub * EPL, x);
+    load(own_o + (p * nqh + qh) * D + sub * EPL, x);
 #pragma unroll
     for (int i = 0; i < EPL; ++i) acc[i] = fmaf(w1, x[i], acc[i]);
   }
@@ -549,14 +584,14 @@ __global__ __launch_bounds__(256) void k_merge_partials(
     *reinterpret_cast<uint2*>(orow) = make_uint2(wds[0], wds[1]);
 }
 
-hipError_t launch_merge_partials_bf16(const void* own_o, const float* own_lse, const void* po,
-                                      const float* plse, void* out, const Dims& d,
-                                      hipStream_t st) {
+hipError_t launch_merge_partials_bf16(const void* own_o, const float* own_lse, int nown,
+                                      const void* po, const float* plse, void* out,
+                                      const Dims& d, hipStream_t st) {
   const int64_t nqh = (int64_t)d.S * d.H * d.Lq;
   const unsigned grid = (unsigned)((nqh + 15) / 16);
 #define MOBA_MERGE(DV)                                                                       \
   hipLaunchKernelGGL(k_merge_partials<DV>, dim3(grid), dim3(256), 0, st,                     \
-                     static_cast<const bf16_t*>(own_o), own_lse,                             \
+                     static_cast<const bf16_t*>(own_o), own_lse, nown,                       \
                      static_cast<const bf16_t*>(po), plse, static_cast<bf16_t*>(out), nqh,   \
                      d.Lq, d.H, d.q_off, d.B, d.kp)
   if (d.D == 128) MOBA_MERGE(128); else MOBA_MERGE(64);
@@ -590,32 +625,53 @@ hipError_t launch_attn_routed_bf16(const void* q, const void* k, const void* vt,
   return hipGetLastError();
 }
 
+// Workgroup shape of the query kernels: HW heads of one KV group per
+// workgroup, NW waves; eight waves when that still gives >= 2048 workgroups.
+static void query_shape(const Dims& d, int* HW, int* NW) {
+  *HW = gcd_int(d.G, 4);
+  const int64_t wgs8 = (d.Lq + 256 / *HW - 1) / (256 / *HW) * (int64_t)(d.S * d.H / *HW);
+  *NW = wgs8 >= 2048 ? 8 : 4;
+}
+
+int full_split_parts(const Dims& d) {
+  if (!d.bf16) return 0;
+  const int HW = gcd_int(d.G, 4);
+  const int RW = 256 / HW;  // eight-wave workgroups
+  const int64_t wgs = (d.Lq + RW - 1) / RW * (int64_t)(d.S * d.H / HW);
+  if (wgs >= 1024) return 0;  // whole row tiles already fill the chip
+  const int64_t tiles = (d.q_off + d.Lq + 63) / 64;  // key tiles of the longest row
+  const int64_t p = (tiles + kFullChunkTiles - 1) / kFullChunkTiles;
+  return p > 1 && p <= kFullMaxParts ? (int)p : 0;
+}
+
 hipError_t launch_attn_query_bf16(const void* q, const void* k, const void* vt,
                                   const void* part_o, const float* part_lse, void* out, int mode,
-                                  const Dims& d, hipStream_t st) {
-  const int HW = gcd_int(d.G, 4);
-  // eight waves per workgroup when that still gives >= 2048 workgroups
-  const int64_t wgs8 = (d.Lq + 256 / HW - 1) / (256 / HW) * (int64_t)(d.S * d.H / HW);
-  const int NW = wgs8 >= 2048 ? 8 : 4;
+                                  const Dims& d, hipStream_t st, int nparts) {
+  int HW, NW;
+  query_shape(d, &HW, &NW);
+  if (mode == 3) NW = 8;
   const int RW = 32 * NW / HW;
-  dim3 grid((unsigned)((d.Lq + RW - 1) / RW * (mode == 2 ? 2 : 1)), d.S * d.H / HW);
+  const int per = mode == 2 ? 2 : (mode == 3 ? nparts : 1);
+  dim3 grid((unsigned)((d.Lq + RW - 1) / RW * per), d.S * d.H / HW);
   const float sl2 = kLog2e / sqrtf((float)d.D);
 #define MOBA_QUERY(DV, MV, NWV)                                                              \
   hipLaunchKernelGGL((k_attn_query<DV, MV, NWV>), grid, dim3(64 * NWV), 0, st,               \
                      static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),           \
                      static_cast<const bf16_t*>(vt), static_cast<const bf16_t*>(part_o),     \
                      part_lse, static_cast<bf16_t*>(out), (int)d.Lq, (int)d.L, (int)d.q_off, \
-                     d.H, d.Hkv, d.kp, d.B, HW, sl2)
+                     d.H, d.Hkv, d.kp, d.B, HW, sl2, nparts, kFullChunkTiles)
 #define MOBA_QUERY_NW(DV, MV) \
   if (NW == 8) MOBA_QUERY(DV, MV, 8); else MOBA_QUERY(DV, MV, 4);
   if (d.D == 128) {
     if (mode == 0) { MOBA_QUERY_NW(128, 0) }
     else if (mode == 1) { MOBA_QUERY_NW(128, 1) }
-    else { MOBA_QUERY_NW(128, 2) }
+    else if (mode == 2) { MOBA_QUERY_NW(128, 2) }
+    else { MOBA_QUERY(128, 3, 8); }
   } else {
     if (mode == 0) { MOBA_QUERY_NW(64, 0) }
     else if (mode == 1) { MOBA_QUERY_NW(64, 1) }
-    else { MOBA_QUERY_NW(64, 2) }
+    else if (mode == 2) { MOBA_QUERY_NW(64, 2) }
+    else { MOBA_QUERY(64, 3, 8); }
   }
 #undef MOBA_QUERY_NW
 #undef MOBA_QUERY

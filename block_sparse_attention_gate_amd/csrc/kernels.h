@@ -8,7 +8,9 @@ namespace moba {
 
 constexpr int kRouteChunkRows = 128;   // query rows per routing chunk (one head)
 constexpr int kMaxBlocks = 8192;       // largest supported number of KV blocks
-constexpr int kOwnSplitSteps = 8;      // own-block tiles longer than this (64-key tiles) split in two
+constexpr int kOwnSplitSteps = 8;
+constexpr int kFullChunkTiles = 64;    // key chunk (64-key tiles) of split full attention
+constexpr int kFullMaxParts = 64;      // at most this many chunks per row      // own-block tiles longer than this (64-key tiles) split in two
 constexpr int kMaxTopk = 17;           // largest supported topk (16 routed blocks + own)
 
 // Problem dimensions shared by every launch of one call.
@@ -84,12 +86,18 @@ hipError_t launch_attn_routed_f32(const void* q, const void* k, const void* v,
 // mode 2 (bf16 only): own block written as a partial (o to part_o, log2-sum-exp
 // to part_lse, indexed by query-head) for launch_merge_partials_bf16.
 // The bf16 form reads V^T [S, Hkv, D, L]; the fp32 form reads V as given.
+// mode 3: full causal attention in key chunks of kFullChunkTiles tiles, one
+// partial per chunk ([nparts, S*H*Lq, D] and log2-sum-exp [nparts, S*H*Lq]).
 hipError_t launch_attn_query_bf16(const void* q, const void* k, const void* vt,
                                   const void* part_o, const float* part_lse, void* out, int mode,
-                                  const Dims& d, hipStream_t st);
-hipError_t launch_merge_partials_bf16(const void* own_o, const float* own_lse, const void* po,
-                                      const float* plse, void* out, const Dims& d,
-                                      hipStream_t st);
+                                  const Dims& d, hipStream_t st, int nparts = 0);
+// Chunks of split full attention for a bf16 problem too small to fill the
+// chip with whole row tiles, else 0.
+int full_split_parts(const Dims& d);
+// Merge of nown key-range partials per query-head with its kp routed ones.
+hipError_t launch_merge_partials_bf16(const void* own_o, const float* own_lse, int nown,
+                                      const void* po, const float* plse, void* out,
+                                      const Dims& d, hipStream_t st);
 hipError_t launch_attn_query_f32(const void* q, const void* k, const void* v, const void* part_o,
                                  const float* part_lse, void* out, int mode, const Dims& d,
                                  hipStream_t st);

@@ -157,6 +157,31 @@ def test_full_attention_parity(dtype):
     assert err.max() <= tmax and err.mean() <= tmean
 
 
+@pytest.mark.parametrize("w", [
+    moba_inputs.custom("full_split2", "bf16", 1, 8192, None, 2, 1, 128, 64, 1, 38),
+    moba_inputs.custom("full_split3_chunk", "bf16", 2, 1500, 12288, 2, 1, 64, 64, 1, 39),
+], ids=["full_split2", "full_split3_chunk"])
+def test_full_attention_split_parity(w):
+    """Full attention small enough to run in key chunks + merge (two and
+    three chunks per row, ragged queries at a cache offset that is not a
+    multiple of 64): every row against the oracle."""
+    moba = _moba()
+    print(f"case {w}", flush=True)
+    q, k, v = moba_inputs.make_inputs(w, device=DEV)
+    out = moba.moba_full_attention_ex(q, k, v)
+    torch.cuda.synchronize()
+    batched = q.dim() == 4
+    for s in range(q.shape[0] if batched else 1):
+        qs, ks, vs, os_ = (q[s], k[s], v[s], out[s]) if batched else (q, k, v, out)
+        qh, kh, vh = to64(qs), to64(ks), to64(vs)
+        Lq, L = qh.shape[0], kh.shape[0]
+        positions = (L - Lq) + np.arange(Lq)
+        pairs = [(h, n) for h in range(qh.shape[1]) for n in range(Lq)]
+        emax, emean = check_outputs(to64(os_), qh, positions, None, 64, L, "bf16", pairs,
+                                    host_fetch(kh, vh), kh.shape[1], full=True)
+        print(f"  seq {s}: max {emax:.2e} mean {emean:.2e}")
+
+
 def test_duplicate_block_tie_goes_to_lower_index():
     """An exact copy of block 2 in block 5 ties exactly in the gate; the GPU
     computes identical scores for both and must keep block 2."""
