@@ -49,8 +49,10 @@
  *     MOBA_ERR_HIP: a HIP launch or runtime call failed.  Faults inside the
  *       kernels surface at the caller's next synchronisation.
  *   - moba_last_error() returns a thread-local text for the last failure.
- *   - Concurrent calls on different streams are safe; the profiling switch
- *     below is process-wide and not meant for concurrent use.
+ *   - Concurrent calls on different streams are safe (the internal stream
+ *     is one per device, so the parts of concurrent calls that run on it
+ *     queue behind each other); the profiling switch below is process-wide
+ *     and not meant for concurrent use.
  */
 #ifndef MOBA_H_
 #define MOBA_H_
@@ -86,8 +88,11 @@ moba_status moba_forward(const void* q, const void* k, const void* v, int64_t se
 
 /*
  * Full causal attention (every key t <= position), the topk = all comparator
- * of the sparse/full switch.  No workspace for bf16 beyond a transposed copy
- * of V, allocated stream-ordered.
+ * of the sparse/full switch.  kv_len must be a multiple of 64.  Workspace
+ * (allocated stream-ordered): a transposed copy of V for bf16; for bf16
+ * problems too small to fill the GPU with whole query rows, also one partial
+ * output per 4096-key chunk of every row (merged at the end); with q_len 1,
+ * split-K partials over 512-key chunks.
  */
 moba_status moba_full_attention(const void* q, const void* k, const void* v, int64_t seq_len,
                                 int32_t n_heads, int32_t n_kv_heads, int32_t head_dim,

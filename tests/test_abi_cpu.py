@@ -90,6 +90,35 @@ def test_workspace_size_of_the_1m_prefill():
     assert "head_dim" in moba.moba_last_error()
 
 
+def test_workspace_size_of_the_32k_prefill():
+    """Small problem (32K tokens, one head, block 2048, top-k 3): V^T, routed
+    partials for 2 past blocks per query and the two own-block halves."""
+    import block_sparse_attention_gate_amd as moba
+    L = 1 << 15
+    a = _args(n_heads=1, n_kv_heads=1, block_size=2048, topk=3, q_len=L, kv_len=L)
+    n = moba._lib.moba_workspace_size(ctypes.byref(a))
+    vt = L * 128 * 2
+    routed = L * 2 * (128 * 2 + 4 + 4)     # partial o, lse, list entry per slot
+    own = 2 * L * (128 * 2 + 4)            # two own-block halves
+    expect_min = vt + routed + own
+    assert expect_min <= n <= expect_min * 1.1, (n, expect_min)
+
+
+def test_full_workspace_sizes():
+    """Full attention: at 32K one head the rows run in 4096-key chunks (8
+    partials per query); at 1M x 32 heads whole rows fill the chip (V^T only)."""
+    import block_sparse_attention_gate_amd as moba
+    L = 1 << 15
+    a = _args(n_heads=1, n_kv_heads=1, q_len=L, kv_len=L)
+    n = moba._lib.moba_full_workspace_size(ctypes.byref(a))
+    expect_min = L * 128 * 2 + 8 * L * (128 * 2 + 4)
+    assert expect_min <= n <= expect_min * 1.01, (n, expect_min)
+    big = _args()
+    n = moba._lib.moba_full_workspace_size(ctypes.byref(big))
+    vt = (1 << 20) * 8 * 128 * 2
+    assert vt <= n <= vt * 1.01, n
+
+
 def test_too_small_workspace_is_rejected():
     import block_sparse_attention_gate_amd as moba
     a = _args()
