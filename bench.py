@@ -353,7 +353,8 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              f"(this build runs on a single MI355X)", file=sys.stderr)
+              f"(the library runs on one MI355X; multi-GPU execution is not implemented)",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch

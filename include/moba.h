@@ -44,7 +44,9 @@
  *       too small.
  *     MOBA_ERR_UNSUPPORTED: head_dim not 64 or 128, block_size not a multiple
  *       of 64, kv_len not a multiple of block_size, topk > 17, more than 8192
- *       blocks, or more than 2^32 routed slots.
+ *       blocks, more than 2^32 routed slots, batch * n_heads > 65535,
+ *       kv_len >= 2^31, or 2^31 or more routing chunks (128 query rows of
+ *       one head each).
  *     MOBA_ERR_OUT_OF_MEMORY: the internal workspace could not be allocated.
  *     MOBA_ERR_HIP: a HIP launch or runtime call failed.  Faults inside the
  *       kernels surface at the caller's next synchronisation.
