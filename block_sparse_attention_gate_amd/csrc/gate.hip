@@ -120,12 +120,58 @@ __global__ __launch_bounds__(256) void k_gate_topk_bf16(
   }
 }
 
+// Wave-wide best (score, index) pair: larger score first, lower index on
+// ties.  Butterfly over DPP lane moves (quad permutes, half-row and row
+// mirrors) and the gfx950 16- and 32-lane swaps; every level combines each
+// lane with a partner from the other half of its current group, so after six
+// levels every lane holds the wave's best pair.
+__device__ __forceinline__ void best_pair_step(float& s, int& i, float os, int oi) {
+  if (os > s || (os == s && oi < i)) {
+    s = os;
+    i = oi;
+  }
+}
+template <int CTRL>
+__device__ __forceinline__ void best_pair_dpp(float& s, int& i) {
+  const float os = __int_as_float(
+      __builtin_amdgcn_update_dpp(0, __float_as_int(s), CTRL, 0xf, 0xf, false));
+  const int oi = __builtin_amdgcn_update_dpp(0, i, CTRL, 0xf, 0xf, false);
+  best_pair_step(s, i, os, oi);
+}
+__device__ __forceinline__ void wave_best_pair(float& s, int& i) {
+  best_pair_dpp<0xB1>(s, i);   // quad_perm [1,0,3,2]
+  best_pair_dpp<0x4E>(s, i);   // quad_perm [2,3,0,1]
+  best_pair_dpp<0x141>(s, i);  // row_half_mirror: lane l <-> 7 - l in each 8
+  best_pair_dpp<0x140>(s, i);  // row_mirror: lane l <-> 15 - l in each 16
+  {
+    const auto rs = __builtin_amdgcn_permlane16_swap(__float_as_uint(s), __float_as_uint(s),
+                                                     false, false);
+    const auto ri = __builtin_amdgcn_permlane16_swap((uint32_t)i, (uint32_t)i, false, false);
+    // each lane now sees its own pair and the one 16 lanes away, in some order
+    float s0 = __uint_as_float(rs[0]);
+    int i0 = (int)ri[0];
+    best_pair_step(s0, i0, __uint_as_float(rs[1]), (int)ri[1]);
+    s = s0;
+    i = i0;
+  }
+  {
+    const auto rs = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s),
+                                                     false, false);
+    const auto ri = __builtin_amdgcn_permlane32_swap((uint32_t)i, (uint32_t)i, false, false);
+    float s0 = __uint_as_float(rs[0]);
+    int i0 = (int)ri[0];
+    best_pair_step(s0, i0, __uint_as_float(rs[1]), (int)ri[1]);
+    s = s0;
+    i = i0;
+  }
+}
+
 // Decode (one query per head, bf16): one wave per (sequence, head).  Lane l
 // scores the past blocks j = l, l + 64, ... with fp32 dot products (the block
-// mean in fp32, the query widened from bf16) and keeps its own top list; the
-// wave then takes the k-1 best of the 64 lists one at a time: a butterfly
-// arg-max on (score descending, block index ascending), after which the
-// winning lane drops its list head.  grid ceil(S*H/4), 256 threads.
+// mean in fp32, the query widened from bf16), two blocks at a time, and keeps
+// its own top list; the wave then takes the k-1 best of the 64 lists one at a
+// time (wave_best_pair on the list heads, after which the winning lane drops
+// its head).  grid ceil(S*H/4), 256 threads.
 template <int D, int KM>
 __global__ __launch_bounds__(256) void k_gate_topk_decode_bf16(
     const bf16_t* __restrict__ q, const float* __restrict__ kbar, int32_t* __restrict__ sel,
@@ -155,33 +201,34 @@ __global__ __launch_bounds__(256) void k_gate_topk_decode_bf16(
     TopList<KM> top;
     top.init();
     const float* kb = kbar + ((int64_t)s * Hkv + g) * nb * D;
-    for (int j = lane; j < b; j += 64) {
-      const float* kr = kb + (int64_t)j * D;
-      float acc = 0.f;
+    for (int j0 = lane; j0 < b; j0 += 128) {
+      // blocks j0 and j0 + 64 (the second may be past b: it reads block j0
+      // again and is not inserted)
+      const float* kr0 = kb + (int64_t)j0 * D;
+      const float* kr1 = kb + (int64_t)(j0 + 64 < b ? j0 + 64 : j0) * D;
+      float a0 = 0.f, a1 = 0.f;
 #pragma unroll
       for (int dd = 0; dd < D; dd += 4) {
-        const float4 x = *reinterpret_cast<const float4*>(kr + dd);
-        acc = fmaf(qr[dd], x.x, acc);
-        acc = fmaf(qr[dd + 1], x.y, acc);
-        acc = fmaf(qr[dd + 2], x.z, acc);
-        acc = fmaf(qr[dd + 3], x.w, acc);
+        const float4 x = *reinterpret_cast<const float4*>(kr0 + dd);
+        const float4 y = *reinterpret_cast<const float4*>(kr1 + dd);
+        a0 = fmaf(qr[dd], x.x, a0);
+        a0 = fmaf(qr[dd + 1], x.y, a0);
+        a0 = fmaf(qr[dd + 2], x.z, a0);
+        a0 = fmaf(qr[dd + 3], x.w, a0);
+        a1 = fmaf(qr[dd], y.x, a1);
+        a1 = fmaf(qr[dd + 1], y.y, a1);
+        a1 = fmaf(qr[dd + 2], y.z, a1);
+        a1 = fmaf(qr[dd + 3], y.w, a1);
       }
-      top.insert_ascending(acc, j);
+      top.insert_ascending(a0, j0);
+      if (j0 + 64 < b) top.insert_ascending(a1, j0 + 64);
     }
 #pragma unroll
     for (int t = 0; t < KM; ++t) {
       if (t < nkeep) {
         float bs = top.s[0];
         int bi = top.i[0];
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) {
-          const float os = __shfl_xor(bs, o);
-          const int oi = __shfl_xor(bi, o);
-          if (os > bs || (os == bs && oi < bi)) {
-            bs = os;
-            bi = oi;
-          }
-        }
+        wave_best_pair(bs, bi);
         kept[t] = bi;
         if (top.i[0] == bi) {  // exactly one lane holds block bi
 #pragma unroll

@@ -164,7 +164,7 @@ def test_full_attention_parity(dtype):
 def test_full_attention_split_parity(w):
     """Full attention small enough to run in key chunks + merge (two and
     three chunks per row, ragged queries at a cache offset that is not a
-    multiple of 64): every row against the oracle."""
+    multiple of 64): a third of the rows of every head against the oracle."""
     moba = _moba()
     print(f"case {w}", flush=True)
     q, k, v = moba_inputs.make_inputs(w, device=DEV)
@@ -176,7 +176,10 @@ def test_full_attention_split_parity(w):
         qh, kh, vh = to64(qs), to64(ks), to64(vs)
         Lq, L = qh.shape[0], kh.shape[0]
         positions = (L - Lq) + np.arange(Lq)
-        pairs = [(h, n) for h in range(qh.shape[1]) for n in range(Lq)]
+        # every 3rd row of every head plus each head's last row (all chunk
+        # counts occur; the oracle loops per row)
+        rows = sorted(set(range(0, Lq, 3)) | {Lq - 1})
+        pairs = [(h, n) for h in range(qh.shape[1]) for n in rows]
         emax, emean = check_outputs(to64(os_), qh, positions, None, 64, L, "bf16", pairs,
                                     host_fetch(kh, vh), kh.shape[1], full=True)
         print(f"  seq {s}: max {emax:.2e} mean {emean:.2e}")
