@@ -1,9 +1,9 @@
 // Flash-style attention on MFMA (bf16 inputs, fp32 accumulation).
 //
 // Two kernels share one inner step:
-//   k_attn_routed: one tile = up to 128 routed entries of one (sequence, KV
-//     head, block) bucket; the block is a selected PAST block, so all of its
-//     keys are visible (no mask).  Writes, per entry, the normalised partial
+//   k_attn_routed: one tile = up to 32 * NW routed entries (128 or 256) of
+//     one (sequence, KV head, block) bucket; the block is a selected PAST
+//     block, so all of its keys are visible (no mask).  Writes, per entry, the normalised partial
 //     output (bf16) and its log2-sum-exp (fp32) to the entry's slot.
 //   k_attn_query: query-centric causal attention.  Mode 0 (own block): keys
 //     from the start of the query's block up to and including the query
@@ -24,8 +24,10 @@
 //   S^T = K Q^T on 32x32x16 MFMA (K rows in the kperm order, see common.h),
 //   online softmax in fp32 (base-2, scale folded into one FMA),
 //   O^T += V^T P^T on 32x32x16 MFMA; V^T rows come from the transposed V.
-// Workgroup: 4 waves sharing double-buffered LDS tiles of K [64][D] and
-// V^T [D][64] (rows padded by 16 bytes against bank conflicts).
+// Workgroup: NW = 4 or 8 waves sharing double-buffered LDS tiles of K [64][D]
+// and V^T [D][64] (rows padded by 16 bytes against bank conflicts); all
+// threads stage the next tile from HBM through registers while the current
+// one is used.
 #include "common.h"
 #include "kernels.h"
 
@@ -287,10 +289,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_routed(
 }
 
 // ---------------------------------------------------------------------------
-// Query-centric causal attention (own block + merge, or full).
-// A workgroup covers HW heads of one KV group x RW query rows (HW*RW = 128);
+// Query-centric causal attention (own block + merge, own-block partials,
+// full, full in key chunks).
+// A workgroup covers HW heads of one KV group x RW query rows (HW*RW = 32*NW);
 // wave w takes head h0 + w % HW and rows [r0 + 32*(w / HW), +32).
-// grid (ceil(Lq / RW), S * H / HW).
+// grid (ceil(Lq / RW) * P, S * H / HW), P = 2 in mode 2, nparts in mode 3,
+// else 1.
 // ---------------------------------------------------------------------------
 template <int D, int MODE, int NW>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_query(

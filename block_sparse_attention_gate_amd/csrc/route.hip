@@ -5,7 +5,7 @@
 // "MoBAの主な機能": FlashAttention combined with MoE optimisation).  Here
 // every (query, selected PAST block) pair is a routed entry and is regrouped
 // into the bucket of (sequence, KV head, block), so that one attention tile
-// reads one block's K/V for up to 128 routed queries.
+// reads one block's K/V for up to 128 or 256 routed queries.
 //
 // Entry slot id: ((s*H + h)*Lq + r)*kp + t for the t-th past block of query
 // row r of head h (kp = topk - 1).  Buckets are ordered (s, g, j); inside a
