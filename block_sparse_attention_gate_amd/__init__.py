@@ -165,6 +165,9 @@ def _args(q, k, v, out, block_size=64, topk=1, k_block_mean=None, sel_out=None) 
     a.q, a.k, a.v, a.out = q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr()
     if k_block_mean is not None:
         _dev_tensor(k_block_mean, "k_block_mean", torch.float32)
+        nb = -(-L // int(block_size)) if block_size > 0 else 0
+        if tuple(k_block_mean.shape) != (S, Hkv, nb, D):
+            raise ValueError(f"k_block_mean must be float32 [{S}, {Hkv}, {nb}, {D}]")
         a.k_block_mean = k_block_mean.data_ptr()
     if sel_out is not None:
         _dev_tensor(sel_out, "sel_out", torch.int32)
@@ -274,13 +277,18 @@ def moba_full_attention_ex(q, k, v, *, out=None, workspace=None):
 
 
 def moba_block_mean(k, block_size, out=None):
-    """Block-mean keys: k [S, L, Hkv, D] (or [L, Hkv, D]) -> fp32 [S, Hkv, nb, D]."""
+    """Block-mean keys: k [S, L, Hkv, D] (or [L, Hkv, D]) -> fp32 [S, Hkv, nb, D],
+    nb = ceil(L / block_size); a partial last block is the mean of the keys it holds."""
     _dev_tensor(k, "k")
     k4 = k if k.dim() == 4 else k.unsqueeze(0)
     S, L, Hkv, D = k4.shape
-    nb = L // int(block_size) if block_size > 0 else 0
-    out = torch.empty((S, Hkv, max(nb, 1), D), dtype=torch.float32, device=k.device) \
-        if out is None else _dev_tensor(out, "out", torch.float32)
+    nb = -(-L // int(block_size)) if block_size > 0 else 0
+    if out is None:
+        out = torch.empty((S, Hkv, max(nb, 1), D), dtype=torch.float32, device=k.device)
+    else:
+        _dev_tensor(out, "out", torch.float32)
+        if out.numel() < S * Hkv * nb * D:
+            raise ValueError(f"out holds {out.numel()} floats, needs {S * Hkv * nb * D}")
     st = _lib.moba_block_mean(k4.data_ptr(), S, L, Hkv, D, int(block_size), out.data_ptr(),
                               _dtype_code(k4), _stream_ptr(k.device))
     _check(st, "moba_block_mean")

@@ -131,6 +131,8 @@ struct Plan {
          off_toff = 0, off_list = 0, off_po = 0, off_plse = 0, total = 0;
   size_t off_ublk = 0, off_umask = 0, off_ucount = 0, off_part = 0, off_bmpart = 0;
   size_t off_own_o = 0, off_own_lse = 0;
+  size_t off_ktail = 0;    // bf16 with L % 64 != 0: last K tile, zero padded
+  bool need_ktail = false;
   bool split_own = false;  // own block on the side stream + separate merge
   int full_parts = 0;      // split full attention: key chunks per row (0: whole rows)
 };
@@ -172,6 +174,10 @@ moba_status check_common(const moba_args* a, bool full, Plan* p) {
   if ((int64_t)d.S * d.H > 65535)
     return fail(MOBA_ERR_UNSUPPORTED, "batch * n_heads > 65535");
   if (d.L >= ((int64_t)1 << 31)) return fail(MOBA_ERR_UNSUPPORTED, "kv_len >= 2^31");
+  d.Lv = (d.L + 63) / 64 * 64;
+  // bf16 prefill kernels address the transposed V [.., D, Lv] with 32-bit offsets
+  if (d.bf16 && d.Lq > 1 && d.Lv * d.D >= ((int64_t)1 << 31))
+    return fail(MOBA_ERR_UNSUPPORTED, "kv_len * head_dim >= 2^31 with bf16 and q_len > 1");
   return MOBA_OK;
 }
 
@@ -181,11 +187,9 @@ moba_status plan_forward(const moba_args* a, Plan* p) {
   Dims& d = p->d;
   if (a->block_size % 64 != 0)
     return fail(MOBA_ERR_UNSUPPORTED, "block_size %d is not a multiple of 64", a->block_size);
-  if (d.L % a->block_size != 0)
-    return fail(MOBA_ERR_UNSUPPORTED, "kv_len is not a multiple of block_size");
   if (a->topk > moba::kMaxTopk)
     return fail(MOBA_ERR_UNSUPPORTED, "topk %d > %d", a->topk, moba::kMaxTopk);
-  const int64_t nb = d.L / a->block_size;
+  const int64_t nb = (d.L + a->block_size - 1) / a->block_size;  // last block may be partial
   if (nb > moba::kMaxBlocks) return fail(MOBA_ERR_UNSUPPORTED, "more than %d blocks", moba::kMaxBlocks);
   d.B = a->block_size;
   d.topk = a->topk;
@@ -229,7 +233,9 @@ moba_status plan_forward(const moba_args* a, Plan* p) {
     p->off_ucount = take((size_t)d.S * d.Hkv * 4);
     p->off_part = take(moba::decode_part_floats(d) * 4);
   }
-  if (p->need_vt) p->off_vt = take((size_t)d.S * d.Hkv * d.D * d.L * 2);
+  if (p->need_vt) p->off_vt = take((size_t)d.S * d.Hkv * d.D * d.Lv * 2);
+  p->need_ktail = p->need_vt && d.L % 64 != 0;
+  if (p->need_ktail) p->off_ktail = take((size_t)d.S * 64 * d.Hkv * d.D * 2);
   if (p->need_sel) p->off_sel = take((size_t)d.S * d.H * d.Lq * d.topk * 4);
   if (p->routed) {
     p->off_counts = take((size_t)d.nrows * d.ncols * 4);
@@ -260,7 +266,6 @@ moba_status plan_full(const moba_args* a, Plan* p) {
   moba_status st = check_common(a, true, p);
   if (st != MOBA_OK) return st;
   Dims& d = p->d;
-  if (d.L % 64 != 0) return fail(MOBA_ERR_UNSUPPORTED, "kv_len is not a multiple of 64");
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -270,9 +275,9 @@ moba_status plan_full(const moba_args* a, Plan* p) {
   // q_len 1: split-K over 512-key chunks with every chunk kept by every head
   Dims dd = d;
   dd.B = moba::decode_chunk();
-  dd.nb = (int)(d.L / dd.B);
+  dd.nb = (int)((d.L + dd.B - 1) / dd.B);
   dd.topk = dd.nb;
-  if (d.L % dd.B == 0 && dd.nb <= moba::kMaxBlocks && moba::decode_supported(dd)) {
+  if (dd.nb <= moba::kMaxBlocks && moba::decode_supported(dd)) {
     d = dd;
     d.kp = 0;
     p->decode = true;
@@ -285,9 +290,11 @@ moba_status plan_full(const moba_args* a, Plan* p) {
     d.B = 64;
     d.topk = 1;
     d.kp = 0;
-    d.nb = (int)(d.L / 64);
+    d.nb = (int)((d.L + 63) / 64);
     p->need_vt = d.bf16;
-    if (p->need_vt) p->off_vt = take((size_t)d.S * d.Hkv * d.D * d.L * 2);
+    if (p->need_vt) p->off_vt = take((size_t)d.S * d.Hkv * d.D * d.Lv * 2);
+    p->need_ktail = p->need_vt && d.L % 64 != 0;
+    if (p->need_ktail) p->off_ktail = take((size_t)d.S * 64 * d.Hkv * d.D * 2);
     // small problems: key chunks + merge (whole row tiles would leave the chip idle)
     p->full_parts = moba::full_split_parts(d);
     if (p->full_parts > 0) {
@@ -361,6 +368,7 @@ moba_status forward_impl(const moba_args* a) {
   char* w = ws.base;
   float* kbar = p.need_kbar ? (float*)(w + p.off_kbar) : const_cast<float*>(a->k_block_mean);
   void* vt = p.need_vt ? (void*)(w + p.off_vt) : nullptr;
+  void* ktail = p.need_ktail ? (void*)(w + p.off_ktail) : nullptr;
   int32_t* sel = p.need_sel ? (int32_t*)(w + p.off_sel) : a->sel_out;
   uint32_t* counts = (uint32_t*)(w + p.off_counts);
   uint32_t* btotal = (uint32_t*)(w + p.off_btotal);
@@ -383,10 +391,11 @@ moba_status forward_impl(const moba_args* a) {
   if (p.split_own) {
     if (p.need_kbar)
       l.run(K_POOL_TRANSPOSE, [&] {
-        return moba::launch_pool_transpose(a->k, a->v, kbar, bm_partial, vt, d, l.st);
+        return moba::launch_pool_transpose(a->k, a->v, kbar, bm_partial, vt, ktail, d, l.st);
       });
     else
-      l.run(K_TRANSPOSE_V, [&] { return moba::launch_transpose_v(a->v, vt, d, l.st); });
+      l.run(K_TRANSPOSE_V,
+            [&] { return moba::launch_transpose_v(a->k, a->v, vt, ktail, d, l.st); });
     if (l.err != hipSuccess) return hip_fail(l);
     hipStream_t side = nullptr;
     hipEvent_t fork = nullptr;
@@ -405,7 +414,8 @@ moba_status forward_impl(const moba_args* a) {
     }
     Launch ls{side};
     ls.run(K_ATTN_OWN, [&] {
-      return moba::launch_attn_query_bf16(a->q, a->k, vt, own_o, own_lse, nullptr, 2, d, side);
+      return moba::launch_attn_query_bf16(a->q, a->k, vt, ktail, own_o, own_lse, nullptr, 2, d,
+                                          side);
     });
     const hipError_t ed = hipEventRecord(join.done, side);
     if (ls.err == hipSuccess) ls.err = ed;
@@ -423,7 +433,8 @@ moba_status forward_impl(const moba_args* a) {
       });
     if (p.need_vt)
       l.run(K_TRANSPOSE_V, [&] {
-        return moba::launch_transpose_v(a->v, vt, d, l.st, fold_mean ? bm_partial : nullptr,
+        return moba::launch_transpose_v(a->k, a->v, vt, ktail, d, l.st,
+                                        fold_mean ? bm_partial : nullptr,
                                         fold_mean ? kbar : nullptr);
       });
   }
@@ -489,7 +500,8 @@ moba_status forward_impl(const moba_args* a) {
   Dims dq = d;
   if (!p.routed) dq.kp = 0;  // nothing to merge
   l.run(K_ATTN_OWN, [&] {
-    return d.bf16 ? moba::launch_attn_query_bf16(a->q, a->k, vt, po, plse, a->out, 0, dq, l.st)
+    return d.bf16 ? moba::launch_attn_query_bf16(a->q, a->k, vt, ktail, po, plse, a->out, 0, dq,
+                                                 l.st)
                   : moba::launch_attn_query_f32(a->q, a->k, a->v, po, plse, a->out, 0, dq,
                                                 l.st);
   });
@@ -506,6 +518,7 @@ moba_status full_impl(const moba_args* a) {
   if (st != MOBA_OK) return st;
   const Dims& d = p.d;
   void* vt = p.need_vt ? (void*)(ws.base + p.off_vt) : nullptr;
+  void* ktail = p.need_ktail ? (void*)(ws.base + p.off_ktail) : nullptr;
   Launch l{(hipStream_t)a->stream};
   if (p.decode) {
     char* w = ws.base;
@@ -524,13 +537,15 @@ moba_status full_impl(const moba_args* a) {
     if (l.err != hipSuccess) return hip_fail(l);
     return MOBA_OK;
   }
-  if (p.need_vt) l.run(K_TRANSPOSE_V, [&] { return moba::launch_transpose_v(a->v, vt, d, l.st); });
+  if (p.need_vt)
+    l.run(K_TRANSPOSE_V,
+          [&] { return moba::launch_transpose_v(a->k, a->v, vt, ktail, d, l.st); });
   if (p.full_parts > 0) {
     void* part_o = (void*)(ws.base + p.off_own_o);
     float* part_lse = (float*)(ws.base + p.off_own_lse);
     l.run(K_ATTN_FULL, [&] {
-      return moba::launch_attn_query_bf16(a->q, a->k, vt, part_o, part_lse, nullptr, 3, d, l.st,
-                                          p.full_parts);
+      return moba::launch_attn_query_bf16(a->q, a->k, vt, ktail, part_o, part_lse, nullptr, 3,
+                                          d, l.st, p.full_parts);
     });
     l.run(K_MERGE, [&] {
       return moba::launch_merge_partials_bf16(part_o, part_lse, p.full_parts, nullptr, nullptr,
@@ -540,8 +555,8 @@ moba_status full_impl(const moba_args* a) {
     return MOBA_OK;
   }
   l.run(K_ATTN_FULL, [&] {
-    return d.bf16 ? moba::launch_attn_query_bf16(a->q, a->k, vt, nullptr, nullptr, a->out, 1, d,
-                                                 l.st)
+    return d.bf16 ? moba::launch_attn_query_bf16(a->q, a->k, vt, ktail, nullptr, nullptr, a->out,
+                                                 1, d, l.st)
                   : moba::launch_attn_query_f32(a->q, a->k, a->v, nullptr, nullptr, a->out, 1,
                                                 d, l.st);
   });
@@ -659,13 +674,12 @@ moba_status moba_block_mean(const void* k, int32_t batch, int64_t kv_len, int32_
       return fail(MOBA_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", head_dim);
     if (block_size % 64 != 0)
       return fail(MOBA_ERR_UNSUPPORTED, "block_size is not a multiple of 64");
-    if (kv_len % block_size != 0)
-      return fail(MOBA_ERR_UNSUPPORTED, "kv_len is not a multiple of block_size");
-    if (kv_len / block_size > moba::kMaxBlocks || batch > 65535)
+    const int64_t nb = (kv_len + block_size - 1) / block_size;  // last block may be partial
+    if (nb > moba::kMaxBlocks || batch > 65535)
       return fail(MOBA_ERR_UNSUPPORTED, "too many blocks or sequences");
     Dims d;
     d.S = batch; d.L = kv_len; d.Hkv = n_kv_heads; d.D = head_dim; d.B = block_size;
-    d.nb = (int)(kv_len / block_size); d.bf16 = dtype == MOBA_DTYPE_BF16;
+    d.nb = (int)nb; d.bf16 = dtype == MOBA_DTYPE_BF16;
     Launch l{(hipStream_t)stream};
     const size_t pbytes = moba::block_mean_partial_floats(d) * 4;
     void* partial = nullptr;

@@ -58,7 +58,7 @@ struct TileRegs {
   int kls[T::KCH];    // LDS element offsets
   int vls[T::VCH];
 
-  __device__ __forceinline__ void setup(int krow_stride, int L, int tid) {
+  __device__ __forceinline__ void setup(int krow_stride, int Lv, int tid) {
 #pragma unroll
     for (int i = 0; i < T::KCH; ++i) {
       const int c = tid + T::NT * i;
@@ -70,7 +70,7 @@ struct TileRegs {
     for (int i = 0; i < T::VCH; ++i) {
       const int c = tid + T::NT * i;
       const int dd = c / 8, kc = c % 8;
-      voff[i] = dd * L + kc * 8;
+      voff[i] = dd * Lv + kc * 8;
       vls[i] = T::KE + dd * T::VS + kc * 8;
     }
   }
@@ -198,8 +198,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_routed(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ vt,
     const uint32_t* __restrict__ list, const uint32_t* __restrict__ bucket_off,
     const uint32_t* __restrict__ tile_off, bf16_t* __restrict__ po, float* __restrict__ plse,
-    int64_t Lq, int64_t L, int H, int Hkv, int kp, int B, int nb, int nrows, float sl2,
-    uint32_t nslots) {
+    int64_t Lq, int64_t L, int64_t Lv, int H, int Hkv, int kp, int B, int nb, int nrows,
+    float sl2, uint32_t nslots) {
   using T = Tiles<D, NW>;
   constexpr int TM = 32 * NW;  // routed entries per tile
   __shared__ __attribute__((aligned(16))) bf16_t lds[2 * T::BUF];
@@ -235,13 +235,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_routed(
   load_q<D>(q + (((int64_t)s * Lq + r) * H + h) * D, valid, hh, qf);
 
   const bf16_t* kbase = k + ((int64_t)s * L * Hkv + g) * D;
-  const bf16_t* vtbase = vt + ((int64_t)s * Hkv + g) * D * L;
+  const bf16_t* vtbase = vt + ((int64_t)s * Hkv + g) * D * Lv;
   const int64_t kstart = (int64_t)j * B;
-  const int nsteps = B / 64;
+  const int nsteps = B / 64;  // a selected past block is always whole
   FlashAcc<D> acc;
   acc.init();
   TileRegs<D, NW> tr;
-  tr.setup(Hkv * D, (int)L, tid);
+  tr.setup(Hkv * D, (int)Lv, tid);
   const int64_t ktile_step = (int64_t)64 * Hkv * D;
   const bf16_t* ktile = kbase + kstart * Hkv * D;
   const bf16_t* vttile = vtbase + kstart;
@@ -300,8 +300,8 @@ template <int D, int MODE, int NW>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_query(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ vt,
     const bf16_t* __restrict__ po, const float* __restrict__ plse, bf16_t* __restrict__ out,
-    int Lq, int L, int q_off, int H, int Hkv, int kp, int B, int HW, float sl2, int nparts,
-    int chunk_tiles) {
+    const bf16_t* __restrict__ ktail, int Lq, int L, int Lv, int q_off, int H, int Hkv, int kp,
+    int B, int HW, float sl2, int nparts, int chunk_tiles) {
   using T = Tiles<D, NW>;
   __shared__ __attribute__((aligned(16))) bf16_t lds[2 * T::BUF];
   const int RW = 32 * NW / HW;
@@ -367,16 +367,24 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_query(
   bf16x8 qf[D / 16];
   load_q<D>(q + (((int64_t)s * Lq + (valid ? r : 0)) * H + h) * D, valid, hh, qf);
   const bf16_t* kbase = k + ((int64_t)s * L * Hkv + g) * D;
-  const bf16_t* vtbase = vt + ((int64_t)s * Hkv + g) * D * L;
+  const bf16_t* vtbase = vt + ((int64_t)s * Hkv + g) * D * Lv;
   const int pos_first = q_off + r0;        // smallest query position of the wave
   FlashAcc<D> acc;
   acc.init();
   TileRegs<D, NW> tr;
-  tr.setup(Hkv * D, L, tid);
+  tr.setup(Hkv * D, Lv, tid);
   const int64_t ktile_step = (int64_t)64 * Hkv * D;
   const bf16_t* ktile = kbase + (int64_t)t0 * ktile_step;
   const bf16_t* vttile = vtbase + (int64_t)t0 * 64;
-  tr.load(ktile, vttile);
+  // The tile holding the end of a sequence whose length is not a multiple of
+  // 64 reads its K rows from `ktail` ([S, 64, Hkv, D], the same row stride as
+  // K, rows past L zero) so that no load passes the end of K; its keys past L
+  // are never visible (every tile from the one holding the wave's first
+  // query on runs under the causal mask).  A uniform pointer choice.
+  const int ttail = (L % 64) ? L / 64 : -1;
+  const bf16_t* ktail_sg = ttail >= 0 ? ktail + ((int64_t)s * 64 * Hkv + g) * D : kbase;
+  auto load_tile = [&](int ti) { tr.load(ti == ttail ? ktail_sg : ktile, vttile); };
+  load_tile(t0);
   tr.store(lds);
   __syncthreads();
   // Per wave the workgroup's tiles [t0, t1) split into: idle before the
@@ -402,7 +410,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_query(
     const bool more = i + 1 < t1;
     ktile += ktile_step;
     vttile += 64;
-    if (more) tr.load(ktile, vttile);
+    if (more) load_tile(i + 1);
     return more;
   };
   for (; it < ws_; ++it) {
@@ -618,8 +626,8 @@ hipError_t launch_attn_routed_bf16(const void* q, const void* k, const void* vt,
   hipLaunchKernelGGL((k_attn_routed<DV, NWV>), dim3((unsigned)grid), dim3(64 * NWV), 0, st,  \
                      static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),           \
                      static_cast<const bf16_t*>(vt), list, bucket_off, tile_off,             \
-                     static_cast<bf16_t*>(part_o), part_lse, d.Lq, d.L, d.H, d.Hkv, d.kp,    \
-                     d.B, d.nb, d.nrows, sl2, (uint32_t)d.slots)
+                     static_cast<bf16_t*>(part_o), part_lse, d.Lq, d.L, d.Lv, d.H, d.Hkv,    \
+                     d.kp, d.B, d.nb, d.nrows, sl2, (uint32_t)d.slots)
   if (d.tile_m == 256) {
     if (d.D == 128) MOBA_ROUTED(128, 8); else MOBA_ROUTED(64, 8);
   } else {
@@ -649,8 +657,10 @@ int full_split_parts(const Dims& d) {
 }
 
 hipError_t launch_attn_query_bf16(const void* q, const void* k, const void* vt,
-                                  const void* part_o, const float* part_lse, void* out, int mode,
-                                  const Dims& d, hipStream_t st, int nparts) {
+                                  const void* ktail, const void* part_o, const float* part_lse,
+                                  void* out, int mode, const Dims& d, hipStream_t st,
+                                  int nparts) {
+  if (d.L % 64 != 0 && ktail == nullptr) return hipErrorInvalidValue;
   int HW, NW;
   query_shape(d, &HW, &NW);
   if (mode == 3) NW = 8;
@@ -662,8 +672,9 @@ hipError_t launch_attn_query_bf16(const void* q, const void* k, const void* vt,
   hipLaunchKernelGGL((k_attn_query<DV, MV, NWV>), grid, dim3(64 * NWV), 0, st,               \
                      static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),           \
                      static_cast<const bf16_t*>(vt), static_cast<const bf16_t*>(part_o),     \
-                     part_lse, static_cast<bf16_t*>(out), (int)d.Lq, (int)d.L, (int)d.q_off, \
-                     d.H, d.Hkv, d.kp, d.B, HW, sl2, nparts, kFullChunkTiles)
+                     part_lse, static_cast<bf16_t*>(out), static_cast<const bf16_t*>(ktail), \
+                     (int)d.Lq, (int)d.L, (int)d.Lv, (int)d.q_off, d.H, d.Hkv, d.kp, d.B, HW,  \
+                     sl2, nparts, kFullChunkTiles)
 #define MOBA_QUERY_NW(DV, MV) \
   if (NW == 8) MOBA_QUERY(DV, MV, 8); else MOBA_QUERY(DV, MV, 4);
   if (d.D == 128) {

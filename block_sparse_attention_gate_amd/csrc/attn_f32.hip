@@ -19,16 +19,20 @@ struct F32Tile {
   static constexpr int CH = KEYS * D / 4 / NT;  // float4 chunks per thread per tensor
 };
 
+// Stages keys [key0, key0 + 32); rows at or past L (the end of a sequence
+// whose length is not a multiple of 32) repeat row L - 1.  Those keys lie
+// past every query position, so the causal mask drops them.
 template <int D>
 __device__ __forceinline__ void f32_load_tile(float* ks, float* vs, const float* kbase,
                                               const float* vbase, int64_t stride, int64_t key0,
-                                              int tid) {
+                                              int64_t L, int tid) {
   using T = F32Tile<D>;
 #pragma unroll
   for (int i = 0; i < T::CH; ++i) {
     const int c = tid + T::NT * i;
     const int row = c / (D / 4), cc = c % (D / 4);
-    const int64_t off = (key0 + row) * stride + cc * 4;
+    const int64_t key = key0 + row < L ? key0 + row : L - 1;
+    const int64_t off = key * stride + cc * 4;
     reinterpret_cast<float4*>(ks)[c] = *reinterpret_cast<const float4*>(kbase + off);
     reinterpret_cast<float4*>(vs)[c] = *reinterpret_cast<const float4*>(vbase + off);
   }
@@ -149,7 +153,7 @@ __global__ __launch_bounds__(F32Tile<D>::NT) void k_attn_routed_f32(
   const float* vbase = v + ((int64_t)s * L * Hkv + g) * D;
   for (int64_t key0 = (int64_t)j * B; key0 < (int64_t)(j + 1) * B; key0 += 32) {
     __syncthreads();
-    f32_load_tile<D>(ks, vs, kbase, vbase, stride, key0, tid);
+    f32_load_tile<D>(ks, vs, kbase, vbase, stride, key0, L, tid);
     __syncthreads();
     f32_step<D, false>(ks, vs, qr, a, dbase, scale, key0, 0, 0);
   }
@@ -197,7 +201,7 @@ __global__ __launch_bounds__(F32Tile<D>::NT) void k_attn_query_f32(
   const float* vbase = v + ((int64_t)s * L * Hkv + g) * D;
   for (int64_t key0 = (klo_g / 32) * 32; key0 < khi_g; key0 += 32) {
     __syncthreads();
-    f32_load_tile<D>(ks, vs, kbase, vbase, stride, key0, tid);
+    f32_load_tile<D>(ks, vs, kbase, vbase, stride, key0, L, tid);
     __syncthreads();
     if (key0 + 31 <= pos && key0 >= klo_l)
       f32_step<D, false>(ks, vs, qr, a, dbase, scale, key0, 0, 0);

@@ -13,7 +13,9 @@
 //   k_decode_merge: per (sequence, head): log-sum-exp merge of the partials
 //                   of the head's kept blocks -> out.
 // With q_len = 1 the query sits at the last cache position, so every kept
-// block, its own block included, is fully visible (no mask).
+// block is visible up to the end of the cache: past blocks whole, the own
+// block up to the query (a chunk past the end holds no key and writes an
+// empty partial).
 #include "common.h"
 #include "kernels.h"
 
@@ -89,6 +91,18 @@ __global__ __launch_bounds__(256) void k_decode_attn(
   const uint32_t mask = umask[(int64_t)sg * umax + u];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int64_t key0 = (int64_t)j * B + (int64_t)c * kDecChunk;
+  const int64_t item = ((int64_t)sg * umax + u) * (B / kDecChunk) + c;
+  // keys of this chunk that exist: a chunk of a partial last block may hold
+  // fewer than kDecChunk, or none (then its partial is empty: max -inf)
+  const int nkey = L - key0 >= kDecChunk ? kDecChunk : (L > key0 ? (int)(L - key0) : 0);
+  if (nkey == 0) {
+    for (int hl = 0; hl < G && hl < GM; ++hl) {
+      if (!((mask >> hl) & 1u)) continue;
+      float* prow = part + (item * GM + hl) * (D + 2);
+      for (int dd = tid; dd < D + 2; dd += 256) prow[dd] = dd == 0 ? -__builtin_inff() : 0.f;
+    }
+    return;
+  }
 
   for (int e = tid; e < G * D; e += 256) {
     const int hl = e / D, dd = e % D;
@@ -100,7 +114,8 @@ __global__ __launch_bounds__(256) void k_decode_attn(
   const T* kb = k + (((int64_t)s * L + key0) * Hkv + g) * D;
   for (int kk = 0; kk < KPT; ++kk) {
     const int key = tid + 256 * kk;
-    const T* krow = kb + (int64_t)key * Hkv * D;
+    // a key past the end re-reads the last row and is masked below
+    const T* krow = kb + (int64_t)(key < nkey ? key : nkey - 1) * Hkv * D;
     // the whole row is requested before any arithmetic (memory-level parallelism)
     u32x4 raw[D / VEC];
 #pragma unroll
@@ -114,7 +129,7 @@ __global__ __launch_bounds__(256) void k_decode_attn(
 #pragma unroll
         for (int i = 0; i < VEC; ++i) acc = fmaf(load_as_f32(e + i), qs[hl][ci * VEC + i], acc);
       }
-      ps[hl][key] = acc;
+      ps[hl][key] = key < nkey ? acc : -__builtin_inff();
     }
   }
   __syncthreads();
@@ -159,7 +174,8 @@ __global__ __launch_bounds__(256) void k_decode_attn(
     u32x4 raw[VU][LPR];
 #pragma unroll
     for (int uu = 0; uu < VU; ++uu) {
-      const T* vrow = vb + (int64_t)(key0 + uu * KG) * Hkv * D;
+      const int kv = key0 + uu * KG;  // past the end: the last row, with p = 0
+      const T* vrow = vb + (int64_t)(kv < nkey ? kv : nkey - 1) * Hkv * D;
 #pragma unroll
       for (int l2 = 0; l2 < LPR; ++l2)
         raw[uu][l2] = *reinterpret_cast<const u32x4*>(vrow + l2 * (8 / LPR));
@@ -185,7 +201,6 @@ __global__ __launch_bounds__(256) void k_decode_attn(
     }
   }
   // reduce over key groups, one head at a time; write (max, sum, o)
-  const int64_t item = ((int64_t)sg * umax + u) * (B / kDecChunk) + c;
 #pragma unroll
   for (int hl = 0; hl < GM; ++hl) {
     if (!(hl < G && ((mask >> hl) & 1u))) continue;

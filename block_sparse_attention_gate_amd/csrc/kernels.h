@@ -8,9 +8,9 @@ namespace moba {
 
 constexpr int kRouteChunkRows = 128;   // query rows per routing chunk (one head)
 constexpr int kMaxBlocks = 8192;       // largest supported number of KV blocks
-constexpr int kOwnSplitSteps = 8;
+constexpr int kOwnSplitSteps = 8;      // own-block tiles longer than this (64-key tiles) split in two
 constexpr int kFullChunkTiles = 64;    // key chunk (64-key tiles) of split full attention
-constexpr int kFullMaxParts = 64;      // at most this many chunks per row      // own-block tiles longer than this (64-key tiles) split in two
+constexpr int kFullMaxParts = 64;      // at most this many chunks per row
 constexpr int kMaxTopk = 17;           // largest supported topk (16 routed blocks + own)
 
 // Problem dimensions shared by every launch of one call.
@@ -23,9 +23,10 @@ struct Dims {
   int B = 64;         // block size
   int topk = 1;       // blocks per query, own block included
   int kp = 0;         // topk - 1: routed (past) blocks per query at most
-  int nb = 1;         // number of KV blocks
+  int nb = 1;         // number of KV blocks, ceil(L / B); the last one may be partial
   int64_t Lq = 1;     // queries per sequence
   int64_t L = 1;      // keys per sequence
+  int64_t Lv = 64;    // row stride of the transposed V: L rounded up to a multiple of 64
   int64_t q_off = 0;  // position of query row 0 (L - Lq)
   bool bf16 = true;   // element type of q, k, v, out
   // routing
@@ -46,12 +47,15 @@ hipError_t launch_block_mean(const void* k, float* kbar, float* partial, const D
 // bf16: block pooling (sums per split, or means when there is one split) and
 // the V transform in one launch; launch_block_mean_finalize then finishes the
 // means (nothing to do with one split).
+// ktail [S, 64, Hkv, D] (needed when L % 64 != 0, else may be NULL): the
+// last, partial 64-key tile of K, zero padded, read by the query kernels.
 hipError_t launch_pool_transpose(const void* k, const void* v, float* kbar, float* partial,
-                                 void* vt, const Dims& d, hipStream_t st);
+                                 void* vt, void* ktail, const Dims& d, hipStream_t st);
 hipError_t launch_block_mean_finalize(float* kbar, const float* partial, const Dims& d,
                                       hipStream_t st);
-hipError_t launch_transpose_v(const void* v, void* vt, const Dims& d, hipStream_t st,
-                              const float* bm_partial = nullptr, float* kbar = nullptr);
+hipError_t launch_transpose_v(const void* k, const void* v, void* vt, void* ktail,
+                              const Dims& d, hipStream_t st, const float* bm_partial = nullptr,
+                              float* kbar = nullptr);
 // counts (nullable): when given, the bf16 gate also writes the routing
 // histogram of its 128-row chunk (the route_count step), see route.hip.
 hipError_t launch_gate_topk(const void* q, const float* kbar, int32_t* sel, const Dims& d,
@@ -88,9 +92,12 @@ hipError_t launch_attn_routed_f32(const void* q, const void* k, const void* v,
 // The bf16 form reads V^T [S, Hkv, D, L]; the fp32 form reads V as given.
 // mode 3: full causal attention in key chunks of kFullChunkTiles tiles, one
 // partial per chunk ([nparts, S*H*Lq, D] and log2-sum-exp [nparts, S*H*Lq]).
+// ktail: as written by launch_pool_transpose / launch_transpose_v (needed
+// when L % 64 != 0).
 hipError_t launch_attn_query_bf16(const void* q, const void* k, const void* vt,
-                                  const void* part_o, const float* part_lse, void* out, int mode,
-                                  const Dims& d, hipStream_t st, int nparts = 0);
+                                  const void* ktail, const void* part_o, const float* part_lse,
+                                  void* out, int mode, const Dims& d, hipStream_t st,
+                                  int nparts = 0);
 // Chunks of split full attention for a bf16 problem too small to fill the
 // chip with whole row tiles, else 0.
 int full_split_parts(const Dims& d);

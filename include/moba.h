@@ -20,6 +20,9 @@
  *     head gates on its own;
  *   - query row r of a sequence sits at position kv_len - q_len + r.
  *   - topk >= number of blocks is full causal attention.
+ *   - kv_len need not be a multiple of block_size: there are
+ *     nb = ceil(kv_len / block_size) blocks and the last one, when partial,
+ *     holds (and is averaged over) the keys that exist.
  *
  * Conventions for every entry point:
  *   - Tensor pointers are DEVICE pointers, contiguous, 16-byte aligned.
@@ -43,10 +46,10 @@
  *       n_heads % n_kv_heads != 0, q_len > kv_len, size overflow, workspace
  *       too small.
  *     MOBA_ERR_UNSUPPORTED: head_dim not 64 or 128, block_size not a multiple
- *       of 64, kv_len not a multiple of block_size, topk > 17, more than 8192
- *       blocks, more than 2^32 routed slots, batch * n_heads > 65535,
- *       kv_len >= 2^31, or 2^31 or more routing chunks (128 query rows of
- *       one head each).
+ *       of 64, topk > 17, more than 8192 blocks, more than 2^32 routed slots,
+ *       batch * n_heads > 65535, kv_len >= 2^31, kv_len * head_dim >= 2^31
+ *       for bf16 with q_len > 1 (kv_len rounded up to 64), or 2^31 or more
+ *       routing chunks (128 query rows of one head each).
  *     MOBA_ERR_OUT_OF_MEMORY: the internal workspace could not be allocated.
  *     MOBA_ERR_HIP: a HIP launch or runtime call failed.  Faults inside the
  *       kernels surface at the caller's next synchronisation.
@@ -90,11 +93,11 @@ moba_status moba_forward(const void* q, const void* k, const void* v, int64_t se
 
 /*
  * Full causal attention (every key t <= position), the topk = all comparator
- * of the sparse/full switch.  kv_len must be a multiple of 64.  Workspace
- * (allocated stream-ordered): a transposed copy of V for bf16; for bf16
- * problems too small to fill the GPU with whole query rows, also one partial
- * output per 4096-key chunk of every row (merged at the end); with q_len 1,
- * split-K partials over 512-key chunks.
+ * of the sparse/full switch.  Workspace (allocated stream-ordered): a
+ * transposed copy of V for bf16 (plus the last K tile when kv_len is not a
+ * multiple of 64); for bf16 problems too small to fill the GPU with whole
+ * query rows, also one partial output per 4096-key chunk of every row
+ * (merged at the end); with q_len 1, split-K partials over 512-key chunks.
  */
 moba_status moba_full_attention(const void* q, const void* k, const void* v, int64_t seq_len,
                                 int32_t n_heads, int32_t n_kv_heads, int32_t head_dim,
@@ -134,8 +137,9 @@ size_t moba_workspace_size(const moba_args* a);
 size_t moba_full_workspace_size(const moba_args* a);
 
 /* Block-mean keys: k_block_mean[s, g, j, :] = mean of k[s, t, g, :] over the
- * block_size keys of block j (fp32 accumulation).  The decode path reuses it
- * across calls on the same cache. */
+ * keys of block j, j < ceil(kv_len / block_size) (a partial last block: over
+ * the keys it holds; fp32 accumulation).  The decode path reuses it across
+ * calls on the same cache. */
 moba_status moba_block_mean(const void* k, int32_t batch, int64_t kv_len, int32_t n_kv_heads,
                             int32_t head_dim, int32_t block_size, float* k_block_mean,
                             moba_dtype dtype, void* stream);

@@ -68,7 +68,7 @@ def _args(**kw):
 def test_validation_rejects_before_any_launch(field, value, status):
     import block_sparse_attention_gate_amd as moba
     a = _args(**{field: value})
-    if field == "kv_len":      # q_len > kv_len is invalid; also not a block multiple
+    if field == "kv_len":      # q_len > kv_len is invalid
         a.q_len = value + 64
     st = moba._lib.moba_forward_ex(ctypes.byref(a))
     assert st == status, (field, value, st, moba.moba_last_error())
@@ -117,6 +117,26 @@ def test_full_workspace_sizes():
     n = moba._lib.moba_full_workspace_size(ctypes.byref(big))
     vt = (1 << 20) * 8 * 128 * 2
     assert vt <= n <= vt * 1.01, n
+
+
+def test_ragged_lengths_are_accepted():
+    """kv_len need not be a multiple of the block size or of 64: the bf16
+    workspace then holds V^T padded to a multiple of 64 keys and the last,
+    partial K tile of every sequence and KV head."""
+    import block_sparse_attention_gate_amd as moba
+    for L in (1000, 37, 4097):
+        a = _args(n_heads=4, n_kv_heads=2, block_size=128, topk=3, q_len=L, kv_len=L)
+        n = moba._lib.moba_workspace_size(ctypes.byref(a))
+        lv = -(-L // 64) * 64
+        assert n >= 2 * lv * 128 * 2 + 64 * 2 * 128 * 2, (L, n, moba.moba_last_error())
+        assert moba._lib.moba_full_workspace_size(ctypes.byref(a)) >= 2 * lv * 128 * 2
+    dec = _args(batch=2, q_len=1, kv_len=(1 << 20) + 5)
+    assert moba._lib.moba_workspace_size(ctypes.byref(dec)) > 0, moba.moba_last_error()
+    # the transposed V is addressed with 32-bit offsets in the bf16 prefill
+    big = _args(n_heads=1, n_kv_heads=1, block_size=4096, topk=2, q_len=1 << 24,
+                kv_len=1 << 24)
+    assert moba._lib.moba_workspace_size(ctypes.byref(big)) == 0
+    assert "2^31" in moba.moba_last_error()
 
 
 def test_too_small_workspace_is_rejected():

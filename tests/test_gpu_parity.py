@@ -122,6 +122,38 @@ def test_edge_cases(w, n_uniform):
     _run_case(w, n_uniform=n_uniform)
 
 
+# Lengths that are not a multiple of the block size (the last block is
+# partial: its mean is over the keys it holds) nor of the 64-key tile.
+RAGGED = [
+    # small-problem path (own block on the side stream): last block 104 keys
+    moba_inputs.custom("ragged_1000", "bf16", 1, 1000, None, 4, 2, 128, 128, 3, 61),
+    # shorter than one tile and one block
+    moba_inputs.custom("ragged_37", "bf16", 1, 37, None, 2, 1, 128, 64, 2, 62),
+    # head_dim 64, block 256, one key past a tile
+    moba_inputs.custom("ragged_d64", "bf16", 1, 1601, None, 2, 2, 64, 256, 4, 63),
+    # chunked prefill into a ragged cache, batch 2
+    moba_inputs.custom("ragged_chunk", "bf16", 2, 77, 1234, 4, 2, 128, 128, 3, 64),
+    # fp32 (32-key staging: a tail of 28 keys), and chunked fp32
+    moba_inputs.custom("ragged_f32", "f32", 1, 700, None, 2, 1, 64, 64, 3, 65),
+    moba_inputs.custom("ragged_f32_chunk", "f32", 2, 300, 1003, 2, 1, 128, 128, 2, 66),
+]
+
+
+@pytest.mark.parametrize("w", RAGGED, ids=[w.name for w in RAGGED])
+def test_ragged_length_parity(w):
+    _run_case(w)
+
+
+def test_ragged_length_fused_path_sampled():
+    """A problem large enough for the fused own-block + merge kernel and
+    256-entry routed tiles (128 heads x 8255 rows), length 8255: last block
+    63 keys, last tile 63 keys; selection on a row sample of every head,
+    outputs on block-edge and uniform rows of three heads."""
+    _run_large(moba_inputs.custom("ragged_fused", "bf16", 1, 8255, None, 128, 16, 64, 256, 4,
+                                  67),
+               n_sel_rows=1024, n_out_rows=48, heads_out=(0, 77, 127), n_edge_rows=32)
+
+
 def test_chunked_and_batched_queries():
     """q_len < kv_len (queries at the end of the cache), batch 2, ragged q_len."""
     w = moba_inputs.custom("batch2_q100", "bf16", 2, 100, 1024, 4, 2, 128, 64, 3, 31)
@@ -141,11 +173,11 @@ def test_topk_all_equals_full_attention():
     assert d.max().item() <= 2e-2 and d.mean().item() <= 2e-3
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_full_attention_parity(dtype):
+@pytest.mark.parametrize("dtype,L", [("bf16", 1024), ("f32", 512), ("bf16", 1000),
+                                     ("f32", 700)])
+def test_full_attention_parity(dtype, L):
     moba = _moba()
-    w = moba_inputs.custom("full_" + dtype, dtype, 1, 1024 if dtype == "bf16" else 512, None,
-                           4, 2, 128, 64, 1, 34)
+    w = moba_inputs.custom(f"full_{dtype}_{L}", dtype, 1, L, None, 4, 2, 128, 64, 1, 34)
     q, k, v = moba_inputs.make_inputs(w, device=DEV)
     out = moba.moba_full_attention(q, k, v)
     torch.cuda.synchronize()
@@ -160,7 +192,8 @@ def test_full_attention_parity(dtype):
 @pytest.mark.parametrize("w", [
     moba_inputs.custom("full_split2", "bf16", 1, 8192, None, 2, 1, 128, 64, 1, 38),
     moba_inputs.custom("full_split3_chunk", "bf16", 2, 1500, 12288, 2, 1, 64, 64, 1, 39),
-], ids=["full_split2", "full_split3_chunk"])
+    moba_inputs.custom("full_split_ragged", "bf16", 1, 5000, None, 2, 1, 128, 64, 1, 40),
+], ids=["full_split2", "full_split3_chunk", "full_split_ragged"])
 def test_full_attention_split_parity(w):
     """Full attention small enough to run in key chunks + merge (two and
     three chunks per row, ragged queries at a cache offset that is not a
@@ -222,7 +255,8 @@ def test_precomputed_block_means_prefill():
     bf16 case and an fp32 one."""
     moba = _moba()
     for w in (moba_inputs.custom("pre_bf16", "bf16", 2, 4096, None, 4, 2, 128, 512, 3, 36),
-              moba_inputs.custom("pre_f32", "f32", 1, 2048, None, 2, 1, 64, 256, 3, 37)):
+              moba_inputs.custom("pre_f32", "f32", 1, 2048, None, 2, 1, 64, 256, 3, 37),
+              moba_inputs.custom("pre_ragged", "bf16", 2, 3000, None, 4, 2, 128, 512, 3, 68)):
         print(f"case {w}", flush=True)
         q, k, v = moba_inputs.make_inputs(w, device=DEV)
         kbar = moba.moba_block_mean(k, w.block_size)
@@ -291,6 +325,11 @@ DECODE = [
     moba_inputs.custom("dec_b1024_g1", "bf16", 2, 1, 16384, 2, 2, 64, 1024, 4, 42),
     moba_inputs.custom("dec_g8_k1", "bf16", 2, 1, 4096, 8, 1, 128, 512, 1, 43),
     moba_inputs.custom("dec_f32", "f32", 2, 1, 4096, 4, 1, 128, 512, 3, 44),
+    # caches whose length is not a block multiple: the own block is partial
+    # (block 1024: its first 512-key chunk partial, the second one empty)
+    moba_inputs.custom("dec_ragged_b512", "bf16", 3, 1, 8192 + 300, 8, 2, 128, 512, 5, 46),
+    moba_inputs.custom("dec_ragged_b1024", "bf16", 2, 1, 16384 + 300, 2, 2, 64, 1024, 4, 47),
+    moba_inputs.custom("dec_ragged_f32", "f32", 2, 1, 4096 + 1, 4, 1, 128, 512, 3, 48),
 ]
 
 
@@ -322,11 +361,12 @@ def test_decode_kernels_parity(w):
         print(f"  seq {s}: tie {ntie} max|err| {emax:.2e} mean|err| {emean:.2e}")
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_full_attention_decode_parity(dtype):
-    """Full causal attention with q_len = 1 (split-K over the whole cache)."""
+@pytest.mark.parametrize("dtype,L", [("bf16", 8192), ("f32", 8192), ("bf16", 8192 + 77)])
+def test_full_attention_decode_parity(dtype, L):
+    """Full causal attention with q_len = 1 (split-K over the whole cache,
+    the last 512-key chunk partial when L is not a multiple of 512)."""
     moba = _moba()
-    w = moba_inputs.custom("full_dec_" + dtype, dtype, 2, 1, 8192, 8, 2, 128, 512, 1, 45)
+    w = moba_inputs.custom(f"full_dec_{dtype}_{L}", dtype, 2, 1, L, 8, 2, 128, 512, 1, 45)
     q, k, v = moba_inputs.make_inputs(w, device=DEV)
     out = moba.moba_full_attention_ex(q, k, v)
     torch.cuda.synchronize()
