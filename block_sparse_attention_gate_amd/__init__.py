@@ -73,6 +73,8 @@ _SIGNATURES = {
     "moba_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(MobaArgs)]),
     "moba_full_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(MobaArgs)]),
     "moba_block_mean": (_ST, [_P, _I32, _I64, _I32, _I32, _I32, _P, ctypes.c_int, _P]),
+    "moba_block_mean_update": (_ST, [_P, _I32, _I64, _I32, _I32, _I32, _I32, _P, ctypes.c_int,
+                                     _P]),
     "moba_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "moba_last_error": (ctypes.c_char_p, []),
     "moba_abi_version": (_I32, []),
@@ -276,23 +278,40 @@ def moba_full_attention_ex(q, k, v, *, out=None, workspace=None):
     return out
 
 
-def moba_block_mean(k, block_size, out=None):
+def moba_block_mean(k, block_size, out=None, first_block=0):
     """Block-mean keys: k [S, L, Hkv, D] (or [L, Hkv, D]) -> fp32 [S, Hkv, nb, D],
-    nb = ceil(L / block_size); a partial last block is the mean of the keys it holds."""
+    nb = ceil(L / block_size); a partial last block is the mean of the keys it holds.
+
+    first_block > 0 recomputes only blocks first_block..nb-1 of ``out`` (which
+    must then be given) and leaves the others as they are: the incremental
+    update of a growing cache (moba_block_mean_update)."""
     _dev_tensor(k, "k")
     k4 = k if k.dim() == 4 else k.unsqueeze(0)
     S, L, Hkv, D = k4.shape
     nb = -(-L // int(block_size)) if block_size > 0 else 0
     if out is None:
+        if first_block:
+            raise ValueError("first_block > 0 updates an existing out tensor")
         out = torch.empty((S, Hkv, max(nb, 1), D), dtype=torch.float32, device=k.device)
     else:
         _dev_tensor(out, "out", torch.float32)
-        if out.numel() < S * Hkv * nb * D:
-            raise ValueError(f"out holds {out.numel()} floats, needs {S * Hkv * nb * D}")
-    st = _lib.moba_block_mean(k4.data_ptr(), S, L, Hkv, D, int(block_size), out.data_ptr(),
-                              _dtype_code(k4), _stream_ptr(k.device))
-    _check(st, "moba_block_mean")
+        if tuple(out.shape) not in ((S, Hkv, nb, D), (Hkv, nb, D) if S == 1 else ()):
+            raise ValueError(f"out must be float32 [{S}, {Hkv}, {nb}, {D}]")
+    if first_block:
+        st = _lib.moba_block_mean_update(k4.data_ptr(), S, L, Hkv, D, int(block_size),
+                                         int(first_block), out.data_ptr(), _dtype_code(k4),
+                                         _stream_ptr(k.device))
+    else:
+        st = _lib.moba_block_mean(k4.data_ptr(), S, L, Hkv, D, int(block_size), out.data_ptr(),
+                                  _dtype_code(k4), _stream_ptr(k.device))
+    _check(st, "moba_block_mean_update" if first_block else "moba_block_mean")
     return out
+
+
+def moba_block_mean_update(k, block_size, first_block, out):
+    """Recompute blocks first_block..nb-1 of the block means ``out`` in place
+    (a cache that grew); blocks before first_block are left as they are."""
+    return moba_block_mean(k, block_size, out=out, first_block=int(first_block))
 
 
 def moba_status_string(status: int) -> str:

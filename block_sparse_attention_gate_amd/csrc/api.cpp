@@ -658,9 +658,10 @@ size_t moba_full_workspace_size(const moba_args* a) {
   }
 }
 
-moba_status moba_block_mean(const void* k, int32_t batch, int64_t kv_len, int32_t n_kv_heads,
-                            int32_t head_dim, int32_t block_size, float* k_block_mean,
-                            moba_dtype dtype, void* stream) {
+static moba_status block_mean_impl(const void* k, int32_t batch, int64_t kv_len,
+                                   int32_t n_kv_heads, int32_t head_dim, int32_t block_size,
+                                   int32_t first_block, float* k_block_mean, moba_dtype dtype,
+                                   void* stream) {
   return guarded([&]() -> moba_status {
     if (!k || !k_block_mean)
       return fail(MOBA_ERR_INVALID_ARGUMENT, "k and k_block_mean must be non-NULL");
@@ -677,11 +678,15 @@ moba_status moba_block_mean(const void* k, int32_t batch, int64_t kv_len, int32_
     const int64_t nb = (kv_len + block_size - 1) / block_size;  // last block may be partial
     if (nb > moba::kMaxBlocks || batch > 65535)
       return fail(MOBA_ERR_UNSUPPORTED, "too many blocks or sequences");
+    if (kv_len >= ((int64_t)1 << 31)) return fail(MOBA_ERR_UNSUPPORTED, "kv_len >= 2^31");
+    if (first_block < 0 || first_block >= nb)
+      return fail(MOBA_ERR_INVALID_ARGUMENT, "first_block %d outside [0, %lld)", first_block,
+                  (long long)nb);
     Dims d;
     d.S = batch; d.L = kv_len; d.Hkv = n_kv_heads; d.D = head_dim; d.B = block_size;
     d.nb = (int)nb; d.bf16 = dtype == MOBA_DTYPE_BF16;
     Launch l{(hipStream_t)stream};
-    const size_t pbytes = moba::block_mean_partial_floats(d) * 4;
+    const size_t pbytes = moba::block_mean_update_partial_floats(d, first_block) * 4;
     void* partial = nullptr;
     if (pbytes) {
       const hipError_t e = hipMallocAsync(&partial, pbytes, l.st);
@@ -691,12 +696,28 @@ moba_status moba_block_mean(const void* k, int32_t batch, int64_t kv_len, int32_
       }
     }
     l.run(K_BLOCK_MEAN, [&] {
-      return moba::launch_block_mean(k, k_block_mean, (float*)partial, d, l.st);
+      return moba::launch_block_mean(k, k_block_mean, (float*)partial, d, l.st, false,
+                                     first_block);
     });
     if (partial) (void)hipFreeAsync(partial, l.st);
     if (l.err != hipSuccess) return hip_fail(l);
     return MOBA_OK;
   });
+}
+
+moba_status moba_block_mean(const void* k, int32_t batch, int64_t kv_len, int32_t n_kv_heads,
+                            int32_t head_dim, int32_t block_size, float* k_block_mean,
+                            moba_dtype dtype, void* stream) {
+  return block_mean_impl(k, batch, kv_len, n_kv_heads, head_dim, block_size, 0, k_block_mean,
+                         dtype, stream);
+}
+
+moba_status moba_block_mean_update(const void* k, int32_t batch, int64_t kv_len,
+                                   int32_t n_kv_heads, int32_t head_dim, int32_t block_size,
+                                   int32_t first_block, float* k_block_mean, moba_dtype dtype,
+                                   void* stream) {
+  return block_mean_impl(k, batch, kv_len, n_kv_heads, head_dim, block_size, first_block,
+                         k_block_mean, dtype, stream);
 }
 
 const char* moba_status_string(moba_status s) {

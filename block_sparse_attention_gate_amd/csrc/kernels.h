@@ -41,9 +41,12 @@ struct Dims {
 // NULL when that is 0).
 // With defer_finalize the split sums stay in `partial` and the following
 // launch_transpose_v (given the same partial / kbar) finishes the means.
+// j0 > 0 computes only blocks j0 .. nb-1 (partial then holds
+// block_mean_update_partial_floats(d, j0) floats; no defer_finalize).
 size_t block_mean_partial_floats(const Dims& d);
+size_t block_mean_update_partial_floats(const Dims& d, int j0);
 hipError_t launch_block_mean(const void* k, float* kbar, float* partial, const Dims& d,
-                             hipStream_t st, bool defer_finalize = false);
+                             hipStream_t st, bool defer_finalize = false, int j0 = 0);
 // bf16: block pooling (sums per split, or means when there is one split) and
 // the V transform in one launch; launch_block_mean_finalize then finishes the
 // means (nothing to do with one split).

@@ -19,17 +19,18 @@ __device__ __forceinline__ int block_keys(int64_t L, int B, int j) {
   return left < B ? (int)left : B;
 }
 
-// grid (nb * splits, S, column groups); 256 threads.  Workgroup (j, split)
-// accumulates VEC columns over rows [split*rows, (split+1)*rows) of block j in
-// fp32; the row slices inside the workgroup are summed in a fixed order.
-// splits == 1 writes the mean directly; otherwise the per-split sums go to
-// `partial` [S, nb, splits, Hkv*D] and k_block_mean_finalize adds them in
-// split order (deterministic, no atomics).
+// grid ((nb - j0) * splits, S, column groups); 256 threads: blocks j0 .. nb-1.
+// Workgroup (j, split) accumulates VEC columns over rows
+// [split*rows, (split+1)*rows) of block j in fp32; the row slices inside the
+// workgroup are summed in a fixed order.  splits == 1 writes the mean
+// directly; otherwise the per-split sums go to `partial`
+// [S, nb - j0, splits, Hkv*D] and k_block_mean_finalize adds them in split
+// order (deterministic, no atomics).
 template <typename T>
 __device__ __forceinline__ void block_mean_body(const T* __restrict__ k, float* __restrict__ kbar,
                                                 float* __restrict__ partial, int Hkv, int D,
-                                                int64_t L, int B, int nb, int splits, int bx,
-                                                int s, int bz, float* red) {
+                                                int64_t L, int B, int nb, int j0, int splits,
+                                                int bx, int s, int bz, float* red) {
   constexpr int VEC = 16 / sizeof(T);
   const int cols = Hkv * D;
   const int tpr = cols / VEC;
@@ -37,7 +38,8 @@ __device__ __forceinline__ void block_mean_body(const T* __restrict__ k, float* 
   const int RS = 256 / cw;               // row slices
   const int tid = threadIdx.x;
   const int ct = tid % cw, rs = tid / cw;
-  const int j = bx / splits, sp = bx % splits;
+  const int jl = bx / splits, sp = bx % splits;
+  const int j = j0 + jl, nbl = nb - j0;
   const int rows = B / splits;
   // rows of this split that exist (a partial last block has fewer)
   const int64_t first = (int64_t)j * B + (int64_t)sp * rows;
@@ -71,7 +73,7 @@ __device__ __forceinline__ void block_mean_body(const T* __restrict__ k, float* 
       const int g = c / D, dd = c % D;
       kbar[(((int64_t)s * Hkv + g) * nb + j) * D + dd] = sum * inv;
     } else {
-      partial[(((int64_t)s * nb + j) * splits + sp) * cols + c] = sum;
+      partial[(((int64_t)s * nbl + jl) * splits + sp) * cols + c] = sum;
     }
   }
 }
@@ -80,9 +82,10 @@ template <typename T>
 __global__ __launch_bounds__(256) void k_block_mean(const T* __restrict__ k,
                                                     float* __restrict__ kbar,
                                                     float* __restrict__ partial, int Hkv, int D,
-                                                    int64_t L, int B, int nb, int splits) {
+                                                    int64_t L, int B, int nb, int j0,
+                                                    int splits) {
   __shared__ float red[256 * (16 / sizeof(T))];
-  block_mean_body<T>(k, kbar, partial, Hkv, D, L, B, nb, splits, blockIdx.x, blockIdx.y,
+  block_mean_body<T>(k, kbar, partial, Hkv, D, L, B, nb, j0, splits, blockIdx.x, blockIdx.y,
                      blockIdx.z, red);
 }
 
@@ -103,15 +106,16 @@ __device__ __forceinline__ float sum_splits(const float* __restrict__ p, int spl
   return sum;
 }
 
-// grid (nb, S); 256 threads.
+// grid (nb - j0, S); 256 threads.
 __global__ __launch_bounds__(256) void k_block_mean_finalize(const float* __restrict__ partial,
                                                              float* __restrict__ kbar, int Hkv,
                                                              int D, int64_t L, int B, int nb,
-                                                             int splits) {
-  const int s = blockIdx.y, j = blockIdx.x, cols = Hkv * D;
+                                                             int j0, int splits) {
+  const int s = blockIdx.y, jl = blockIdx.x, j = j0 + jl, nbl = nb - j0, cols = Hkv * D;
   const float inv = 1.0f / (float)block_keys(L, B, j);
   for (int c = threadIdx.x; c < cols; c += 256) {
-    const float sum = sum_splits(partial + ((int64_t)s * nb + j) * splits * cols + c, splits, cols);
+    const float sum =
+        sum_splits(partial + ((int64_t)s * nbl + jl) * splits * cols + c, splits, cols);
     const int g = c / D, dd = c % D;
     kbar[(((int64_t)s * Hkv + g) * nb + j) * D + dd] = sum * inv;
   }
@@ -130,24 +134,34 @@ size_t block_mean_partial_floats(const Dims& d) {
   return sp > 1 ? (size_t)d.S * d.nb * sp * d.Hkv * d.D : 0;
 }
 
+// The split count is that of the whole problem also when only blocks j0..
+// are computed, so that every block's sum is formed in the same order (the
+// same bits) as by the full computation.
+size_t block_mean_update_partial_floats(const Dims& d, int j0) {
+  const int sp = block_mean_splits(d);
+  return sp > 1 ? (size_t)d.S * (d.nb - j0) * sp * d.Hkv * d.D : 0;
+}
+
 hipError_t launch_block_mean(const void* k, float* kbar, float* partial, const Dims& d,
-                             hipStream_t st, bool defer_finalize) {
+                             hipStream_t st, bool defer_finalize, int j0) {
+  if (j0 < 0 || j0 >= d.nb || (defer_finalize && j0 != 0)) return hipErrorInvalidValue;
+  const int nbl = d.nb - j0;
   const int cols = d.Hkv * d.D;
   const int vec = d.bf16 ? 8 : 4;
   const int tpr = cols / vec;
   const int splits = block_mean_splits(d);
-  dim3 grid(d.nb * splits, d.S, (tpr + 255) / 256);
+  dim3 grid(nbl * splits, d.S, (tpr + 255) / 256);
   if (d.bf16)
     hipLaunchKernelGGL(k_block_mean<bf16_t>, grid, dim3(256), 0, st,
                        static_cast<const bf16_t*>(k), kbar, partial, d.Hkv, d.D, d.L, d.B, d.nb,
-                       splits);
+                       j0, splits);
   else
     hipLaunchKernelGGL(k_block_mean<float>, grid, dim3(256), 0, st,
                        static_cast<const float*>(k), kbar, partial, d.Hkv, d.D, d.L, d.B, d.nb,
-                       splits);
+                       j0, splits);
   if (splits > 1 && !defer_finalize)
-    hipLaunchKernelGGL(k_block_mean_finalize, dim3(d.nb, d.S), dim3(256), 0, st, partial, kbar,
-                       d.Hkv, d.D, d.L, d.B, d.nb, splits);
+    hipLaunchKernelGGL(k_block_mean_finalize, dim3(nbl, d.S), dim3(256), 0, st, partial, kbar,
+                       d.Hkv, d.D, d.L, d.B, d.nb, j0, splits);
   return hipGetLastError();
 }
 
@@ -243,7 +257,7 @@ __global__ __launch_bounds__(256) void k_pool_transpose(const bf16_t* __restrict
   const int b = blockIdx.x;
   if (b < npool) {
     const int bx = b % pool_x, by = (b / pool_x) % pool_y, bz = b / (pool_x * pool_y);
-    block_mean_body<bf16_t>(k, kbar, partial, Hkv, D, L, B, nb, splits, bx, by, bz, lds);
+    block_mean_body<bf16_t>(k, kbar, partial, Hkv, D, L, B, nb, 0, splits, bx, by, bz, lds);
   } else {
     const int t = b - npool;
     const int ntile = (int)(Lv / 64);
@@ -299,7 +313,7 @@ hipError_t launch_block_mean_finalize(float* kbar, const float* partial, const D
   const int splits = block_mean_splits(d);
   if (splits > 1)
     hipLaunchKernelGGL(k_block_mean_finalize, dim3(d.nb, d.S), dim3(256), 0, st, partial, kbar,
-                       d.Hkv, d.D, d.L, d.B, d.nb, splits);
+                       d.Hkv, d.D, d.L, d.B, d.nb, 0, splits);
   return hipGetLastError();
 }
 

@@ -144,6 +144,17 @@ moba_status moba_block_mean(const void* k, int32_t batch, int64_t kv_len, int32_
                             int32_t head_dim, int32_t block_size, float* k_block_mean,
                             moba_dtype dtype, void* stream);
 
+/* Incremental form for a cache that grows (decode): recomputes the means of
+ * blocks first_block .. ceil(kv_len / block_size) - 1 only, with the same
+ * arithmetic (the same bits) as moba_block_mean, and leaves blocks before
+ * first_block untouched.  The gate only scores complete past blocks, so after
+ * appending tokens it suffices to pass the first block that was incomplete
+ * before the append.  first_block outside [0, nb) is INVALID_ARGUMENT. */
+moba_status moba_block_mean_update(const void* k, int32_t batch, int64_t kv_len,
+                                   int32_t n_kv_heads, int32_t head_dim, int32_t block_size,
+                                   int32_t first_block, float* k_block_mean, moba_dtype dtype,
+                                   void* stream);
+
 const char* moba_status_string(moba_status s);
 const char* moba_last_error(void);
 int32_t moba_abi_version(void);

@@ -403,3 +403,56 @@ def test_decode_1m_parity():
         emax, emean = check_outputs(to64(out[s]), qh, positions, sel_np, w.block_size, L,
                                     w.dtype, pairs, device_fetch(k[s], v[s]), k.shape[2])
         print(f"  seq {s}: tie {ntie} max|err| {emax:.2e} mean|err| {emean:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_block_mean_update_matches_full(dtype):
+    """moba_block_mean_update recomputes blocks first_block.. with the bits of
+    the full computation and leaves the blocks before it untouched (ragged
+    cache: last block 392 of 512 keys)."""
+    moba = _moba()
+    w = moba_inputs.custom("bm_update_" + dtype, dtype, 3, 1, 5000, 4, 2, 128, 512, 3, 81)
+    _, k, _ = moba_inputs.make_inputs(w, device=DEV)
+    full = moba.moba_block_mean(k, w.block_size)
+    nb = full.shape[2]
+    for j0 in (1, 7, nb - 1):
+        out = torch.full_like(full, 7.0)
+        moba.moba_block_mean_update(k, w.block_size, j0, out)
+        torch.cuda.synchronize()
+        assert torch.equal(out[:, :, j0:].view(torch.int32), full[:, :, j0:].view(torch.int32))
+        assert bool((out[:, :, :j0] == 7.0).all())
+    kb = O.block_mean(to64(k[1]), w.block_size)
+    np.testing.assert_allclose(full[1].double().cpu().numpy(), kb, rtol=0, atol=1e-5)
+
+
+def test_decode_loop_with_incremental_block_means():
+    """A decode loop over a growing cache (one token appended per step,
+    crossing the end of a block): block means kept with moba_block_mean_update
+    (one call when a block completes) give the same selection and the same
+    output bits as calls that pool K themselves."""
+    moba = _moba()
+    B, L0, L1 = 512, 2045, 2052
+    w = moba_inputs.custom("dec_loop", "bf16", 1, 1, L1, 8, 2, 128, B, 3, 82)
+    q_all, k_all, v_all = moba_inputs.make_inputs(w, device=DEV)   # q [1, 1, 8, 128]
+    kbar = moba.moba_block_mean(k_all[:, :L0], B)
+    for L in range(L0 + 1, L1 + 1):
+        k, v = k_all[:, :L], v_all[:, :L]
+        nb = -(-L // B)
+        if kbar.shape[2] < nb:       # a new (partial) own block: not scored yet
+            kbar = torch.cat([kbar, torch.zeros_like(kbar[:, :, :1])], dim=2).contiguous()
+        if L % B == 0:               # block nb-1 just completed
+            moba.moba_block_mean_update(k, B, nb - 1, kbar)
+        q = q_all * (1.0 + 0.01 * L)
+        o1, s1 = moba.moba_forward_ex(q, k, v, B, w.topk, k_block_mean=kbar,
+                                      return_selection=True)
+        o2, s2 = moba.moba_forward_ex(q, k, v, B, w.topk, return_selection=True)
+        torch.cuda.synchronize()
+        assert torch.equal(s1, s2), L
+        assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)), L
+        qh, kh, vh = to64(q[0]), to64(k[0]), to64(v[0])
+        positions = np.array([L - 1])
+        kb = O.block_mean(kh, B)
+        sel_np = s1[0].cpu().numpy()
+        check_selection(qh, positions, kb, sel_np, B, w.topk)
+        check_outputs(to64(o1[0]), qh, positions, sel_np, B, L, "bf16",
+                      [(h, 0) for h in range(qh.shape[1])], host_fetch(kh, vh), kh.shape[1])
