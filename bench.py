@@ -12,9 +12,12 @@ region.  Prints one JSON line.
                up to i).
   speedup      time of the library's own full causal attention at the same
                shape / time of the MoBA forward.
-  also         the same figures at the 1M-token prefill (32/8 heads, block
-               4096, top-k 12), and the batch-8 decode against a 1M-token
-               cache in GB/s of algorithmic bytes against the HBM peak.
+  also         the same figures at the 128K Llama-layer prefill and the
+               1M-token prefill (32/8 heads, block 4096, top-k 12), at 10M
+               tokens with one head (block 4096, top-k 12; the full attention
+               it is compared with runs once, about half a minute), and the
+               batch-8 decode against a 1M-token cache in GB/s of algorithmic
+               bytes against the HBM peak.
   roofline     the dominant kernel (routed attention): its algorithmic FLOPs
                per launch / its average launch time from HIP events recorded
                on the launch stream, against the 2.5 PFLOP/s bf16 dense MFMA
@@ -342,6 +345,8 @@ def main():
     ap.add_argument("--skip-1m", action="store_true", help="skip the 1M-token prefill")
     ap.add_argument("--skip-128k", action="store_true", help="skip the 128K Llama-layer prefill")
     ap.add_argument("--skip-decode", action="store_true", help="skip the 1M-cache decode")
+    ap.add_argument("--skip-10m", action="store_true",
+                    help="skip the 10M-token single-head prefill")
     ap.add_argument("--skip-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--workload", default=None,
@@ -401,6 +406,13 @@ def main():
         r1["roofline"] = roofline(r1)
         r1.pop("_roofline_src")
         also["prefill_1m"] = r1
+    if not args.skip_10m:
+        w10 = moba_inputs.WORKLOADS["prefill_10m"]
+        r10 = run_prefill(moba, w10, min(args.steps, 3), min(args.warmup, 1), full_steps=1,
+                          full_warmup=0)
+        r10["roofline"] = roofline(r10)
+        r10.pop("_roofline_src")
+        also["prefill_10m"] = r10
     if not args.skip_decode:
         also["decode_1m"] = run_decode(moba, moba_inputs.WORKLOADS["decode_1m"], args.steps,
                                        args.warmup)

@@ -60,6 +60,9 @@ WORKLOADS = {
     "llama8b_128k": Workload("llama8b_128k", "bf16", 1, 131072, 131072, 32, 8, 128, 4096, 12, 1003),
     "prefill_1m": Workload("prefill_1m", "bf16", 1, 1048576, 1048576, 32, 8, 128, 4096, 12, 1004),
     "decode_1m": Workload("decode_1m", "bf16", 8, 1, 1048576, 32, 8, 128, 4096, 12, 1005),
+    # the 10M-token regime, one head (full attention at 32 heads would take minutes)
+    "prefill_10m": Workload("prefill_10m", "bf16", 1, 10485760, 10485760, 1, 1, 128, 4096, 12,
+                            1006),
 }
 
 

@@ -302,6 +302,13 @@ def test_prefill_1m_parity_sampled():
                heads_out=(0, 17), n_edge_rows=24)
 
 
+def test_prefill_10m_parity_sampled():
+    """10M tokens, one head (block 4096 -> 2560 blocks, top-k 12; 115M routed
+    entries), sampled like the 1M case."""
+    _run_large(moba_inputs.WORKLOADS["prefill_10m"], n_sel_rows=4096, n_out_rows=24,
+               heads_out=(0,), n_edge_rows=24)
+
+
 def test_full_attention_32k_sampled():
     """Full causal attention at the 32K single-head shape, sampled rows."""
     moba = _moba()
