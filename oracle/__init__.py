@@ -1,4 +1,4 @@
-"""CPU oracle for the MoBA causal block-sparse attention forward.
+"""CPU oracle for the MoBA causal block-sparse attention forward and its gradients.
 
 TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import or call anything in this
@@ -21,4 +21,7 @@ from .moba_oracle import (  # noqa: F401
     brute_force_select,
     routing_table,
     moba_decode_reference,
+    attend_lse,
+    moba_lse_reference,
+    moba_backward_reference,
 )

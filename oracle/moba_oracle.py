@@ -38,6 +38,11 @@ Readings where the pages are silent (each is listed in the design notes):
 * R10 queries are bottom-right aligned: query row r sits at position
   ``kv_len - q_len + r``.
 * R11 a partial last block is averaged over the keys it holds.
+* R15 training (the [MoBA card] "Highlighted Details" and the [Dev Tutorial]
+  step 1 note: MoBA needs continued training; the pages give no backward
+  pass): the top-k selection is piecewise constant and passes no gradient, so
+  the gate and the block means receive none; the gradients are those of the
+  softmax attention of every query over its fixed key set.
 
 Layouts (one sequence): q ``[Lq, H, D]``, k and v ``[L, Hkv, D]``, all float64.
 """
@@ -239,6 +244,77 @@ def moba_reference(q, k, v, block_size, topk, q_offset=None, scale=None,
         keys = key_set(sel[h, r], q_offset + r, block_size, L)
         out[r, h] = attend(q[r, h], k[:, g, :], v[:, g, :], keys, scale)
     return out, sel, gap
+
+
+def attend_lse(q_vec, k_g, keys, scale):
+    """Natural log of the softmax normaliser ``log sum_t exp(scale * k_t . q)``
+    over ``keys`` (the max is taken out first)."""
+    z = (k_g[keys] @ q_vec) * scale
+    m = z.max()
+    return m + np.log(np.exp(z - m).sum())
+
+
+def moba_lse_reference(q, k, block_size, sel, q_offset=None, scale=None):
+    """Log-sum-exp ``[H, Lq]`` of every query's logits over its key set (the
+    statistic a forward keeps for the backward)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    lq, h_n, d = q.shape
+    L, hkv, _ = k.shape
+    group = h_n // hkv
+    if q_offset is None:
+        q_offset = L - lq
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    lse = np.empty((h_n, lq))
+    for h in range(h_n):
+        for r in range(lq):
+            keys = key_set(sel[h, r], q_offset + r, block_size, L)
+            lse[h, r] = attend_lse(q[r, h], k[:, h // group, :], keys, scale)
+    return lse
+
+
+# --------------------------------------------------------------------------
+# Step 5 (training, reading R15): gradients of the attention over the fixed
+# key sets.  Loss = sum(out * dout); for one query with key set T,
+#   z_t = c k_t.q, p = softmax(z), o = sum_t p_t v_t,
+#   dv_t += p_t dO,  dp_t = dO . v_t,  ds_t = p_t (dp_t - dO . o),
+#   dq = c sum_t ds_t k_t,  dk_t += c ds_t q.
+# --------------------------------------------------------------------------
+def moba_backward_reference(q, k, v, dout, block_size, sel, q_offset=None, scale=None):
+    """Returns ``(dq [Lq, H, D], dk [L, Hkv, D], dv [L, Hkv, D])`` for the
+    selection ``sel [H, Lq, topk]`` (held fixed).  GQA: a KV head's gradients
+    sum over the query heads of its group (R8)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    lq, h_n, d = q.shape
+    L, hkv, _ = k.shape
+    group = h_n // hkv
+    if q_offset is None:
+        q_offset = L - lq
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for h in range(h_n):
+        g = h // group
+        for r in range(lq):
+            keys = key_set(sel[h, r], q_offset + r, block_size, L)
+            kk, vv = k[keys, g, :], v[keys, g, :]
+            z = (kk @ q[r, h]) * scale
+            p = np.exp(z - z.max())
+            p /= p.sum()
+            o = p @ vv
+            do = dout[r, h]
+            dp = vv @ do
+            ds = p * (dp - do @ o)
+            dq[r, h] = scale * (ds @ kk)
+            dk[keys, g, :] += scale * np.outer(ds, q[r, h])
+            dv[keys, g, :] += np.outer(p, do)
+    return dq, dk, dv
 
 
 def full_reference(q, k, v, q_offset=None, scale=None, pairs=None):

@@ -328,3 +328,119 @@ def test_select_all_explicit_positions_match_offsets():
     sel2, gap2 = O.select_all(q[rows], kb, B, topk, positions=rows)
     np.testing.assert_array_equal(sel2, sel[:, rows])
     np.testing.assert_array_equal(gap2, gap[:, rows])
+
+
+# ------------------------------------------------- backward (R15) pins -----
+def _selection_mask(sel, L, Lq, B, q_off):
+    """Boolean [H, Lq, L] mask of the keys each query attends (selected
+    blocks, causal inside)."""
+    H = sel.shape[0]
+    t = np.arange(L)
+    mask = np.zeros((H, Lq, L), dtype=bool)
+    for h in range(H):
+        for r in range(Lq):
+            chosen = [j for j in sel[h, r] if j >= 0]
+            mask[h, r] = np.isin(t // B, chosen) & (t <= q_off + r)
+    return mask
+
+
+def _autograd(q, k, v, dout, mask=None, causal=False):
+    """torch float64 autograd of SDPA; KV heads repeated (their gradients
+    summed back by autograd)."""
+    H, Hkv = q.shape[1], k.shape[1]
+    qt, kt, vt = (torch.from_numpy(x.copy()).requires_grad_() for x in (q, k, v))
+    rep = lambda t: t.permute(1, 0, 2).repeat_interleave(H // Hkv, 0)[None]
+    m = None if mask is None else torch.from_numpy(mask)[None]
+    o = torch.nn.functional.scaled_dot_product_attention(
+        qt.permute(1, 0, 2)[None], rep(kt), rep(vt), attn_mask=m, is_causal=causal)
+    (o[0].permute(1, 0, 2) * torch.from_numpy(dout)).sum().backward()
+    return qt.grad.numpy(), kt.grad.numpy(), vt.grad.numpy()
+
+
+@pytest.mark.parametrize("seed,L,Lq,B,topk,H,Hkv", [(61, 72, 72, 8, 4, 4, 2),
+                                                    (62, 50, 50, 16, 2, 2, 2),
+                                                    (63, 90, 37, 8, 3, 2, 1)])
+def test_backward_equals_autograd_of_the_mask_form(seed, L, Lq, B, topk, H, Hkv):
+    """R15: with the selection fixed, the oracle's hand-written gradients equal
+    torch autograd through SDPA with the selection's boolean mask (ragged last
+    block, GQA 2:1, and queries at the end of a longer cache)."""
+    q, k, v = _case(seed, L, H, Hkv, 16, B)
+    q = q[L - Lq:]
+    dout = np.random.default_rng(seed + 100).standard_normal(q.shape)
+    kbar = O.block_mean(k, B)
+    sel, _ = O.select_all(q, kbar, B, topk, q_offset=L - Lq)
+    dq, dk, dv = O.moba_backward_reference(q, k, v, dout, B, sel)
+    aq, ak, av = _autograd(q, k, v, dout, mask=_selection_mask(sel, L, Lq, B, L - Lq))
+    np.testing.assert_allclose(dq, aq, atol=1e-11, rtol=0)
+    np.testing.assert_allclose(dk, ak, atol=1e-11, rtol=0)
+    np.testing.assert_allclose(dv, av, atol=1e-11, rtol=0)
+
+
+def test_backward_topk_all_equals_causal_sdpa_gradients():
+    """topk >= nb: the gradients of full causal attention (SDPA is_causal)."""
+    L, B, D = 40, 8, 16
+    q, k, v = _case(64, L, 4, 1, D, B)
+    dout = np.random.default_rng(7).standard_normal(q.shape)
+    sel, _ = O.select_all(q, O.block_mean(k, B), B, 6)
+    got = O.moba_backward_reference(q, k, v, dout, B, sel)
+    want = _autograd(q, k, v, dout, causal=True)
+    for g_, w_ in zip(got, want):
+        np.testing.assert_allclose(g_, w_, atol=1e-11, rtol=0)
+
+
+def test_backward_central_differences():
+    """The definition of the derivative: central differences of
+    sum(out * dout) (selection held fixed) on sampled coordinates of q, k, v."""
+    L, B, topk, D = 24, 4, 3, 6
+    q, k, v = _case(65, L, 2, 1, D, B)
+    dout = np.random.default_rng(8).standard_normal(q.shape)
+    sel, _ = O.select_all(q, O.block_mean(k, B), B, topk)
+    grads = O.moba_backward_reference(q, k, v, dout, B, sel)
+
+    def loss(q_, k_, v_):
+        out, _, _ = O.moba_reference(q_, k_, v_, B, topk, sel=sel)
+        return float((out * dout).sum())
+
+    rng = np.random.default_rng(9)
+    eps = 1e-6
+    for which, g_ in enumerate(grads):
+        base = (q, k, v)[which]
+        for _ in range(8):
+            idx = tuple(int(rng.integers(0, n)) for n in base.shape)
+            args_p = [x.copy() for x in (q, k, v)]
+            args_m = [x.copy() for x in (q, k, v)]
+            args_p[which][idx] += eps
+            args_m[which][idx] -= eps
+            fd = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+            assert abs(fd - g_[idx]) <= 1e-7 + 1e-6 * abs(fd), (which, idx, fd, g_[idx])
+
+
+def test_backward_closed_form_sums():
+    """Softmax gradients sum to zero over each query's keys, so the dK of a
+    KV head sums to zero over all keys; the probabilities sum to one, so its
+    dV sums to the group's dO summed over queries (chunked queries, GQA)."""
+    L, Lq, B, topk, H, Hkv, D = 80, 30, 8, 3, 4, 2, 8
+    q, k, v = _case(66, L, H, Hkv, D, B)
+    q = q[L - Lq:]
+    dout = np.random.default_rng(10).standard_normal(q.shape)
+    sel, _ = O.select_all(q, O.block_mean(k, B), B, topk, q_offset=L - Lq)
+    dq, dk, dv = O.moba_backward_reference(q, k, v, dout, B, sel)
+    G = H // Hkv
+    for g in range(Hkv):
+        np.testing.assert_allclose(dk[:, g].sum(axis=0), 0.0, atol=1e-12)
+        want = dout[:, g * G:(g + 1) * G].sum(axis=(0, 1))
+        np.testing.assert_allclose(dv[:, g].sum(axis=0), want, atol=1e-12)
+
+
+def test_lse_equals_logsumexp_of_the_masked_logits():
+    """The kept log-sum-exp is torch.logsumexp of the scaled logits over each
+    query's key set (masked logits at -inf)."""
+    L, B, topk, H, Hkv, D = 60, 8, 3, 2, 1, 16
+    q, k, v = _case(67, L, H, Hkv, D, B)
+    sel, _ = O.select_all(q, O.block_mean(k, B), B, topk)
+    lse = O.moba_lse_reference(q, k, B, sel)
+    mask = _selection_mask(sel, L, L, B, 0)
+    for h in range(H):
+        z = torch.from_numpy(q[:, h] @ k[:, h // (H // Hkv)].T / math.sqrt(D))
+        z = z.masked_fill(~torch.from_numpy(mask[h]), -math.inf)
+        np.testing.assert_allclose(lse[h], torch.logsumexp(z, dim=1).numpy(), atol=1e-12)
