@@ -58,6 +58,7 @@ class MobaArgs(ctypes.Structure):
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
         ("stream", ctypes.c_void_p),
+        ("lse_out", ctypes.c_void_p),
     ]
 
 
@@ -242,15 +243,26 @@ def _workspace_tensor(nbytes: int, device, workspace):
 
 
 def moba_forward_ex(q, k, v, block_size, topk, *, out=None, k_block_mean=None, sel_out=None,
-                    return_selection=False, workspace=None):
+                    return_selection=False, workspace=None, lse_out=None, return_lse=False):
     """General MoBA forward (C ``moba_forward_ex``): batches, q_len <= kv_len,
-    optional precomputed block means, optional selection output.  The
-    workspace is a torch allocation (or the given uint8 tensor)."""
+    optional precomputed block means, optional selection and log-sum-exp
+    outputs (what moba_backward_ex needs).  The workspace is a torch
+    allocation (or the given uint8 tensor).  Returns ``out``, then the
+    selection ``[S, H, Lq, topk]`` if asked, then the log-sum-exp
+    ``[S, H, Lq]`` if asked (``[H, ...]`` without the batch axis for 3-D q)."""
     out = torch.empty_like(q) if out is None else out
+    S, Lq, H, D, L, Hkv = _shape4(q, k, v)
     if return_selection and sel_out is None:
-        S, Lq, H, D, L, Hkv = _shape4(q, k, v)
         sel_out = torch.empty((S, H, Lq, int(topk)), dtype=torch.int32, device=q.device)
+    if return_lse and lse_out is None:
+        lse_out = torch.empty((S, H, Lq), dtype=torch.float32, device=q.device)
+    if lse_out is not None:
+        _dev_tensor(lse_out, "lse_out", torch.float32)
+        if lse_out.numel() != S * H * Lq:
+            raise ValueError(f"lse_out must be float32 [{S}, {H}, {Lq}]")
     a = _args(q, k, v, out, block_size, topk, k_block_mean, sel_out)
+    if lse_out is not None:
+        a.lse_out = lse_out.data_ptr()
     need = int(_lib.moba_workspace_size(ctypes.byref(a)))
     if need == 0 and _lib.moba_last_error():
         _check(_lib.moba_forward_ex(ctypes.byref(a)), "moba_forward_ex")  # raises the error
@@ -259,9 +271,12 @@ def moba_forward_ex(q, k, v, block_size, topk, *, out=None, k_block_mean=None, s
         a.workspace = ws.data_ptr()
         a.workspace_bytes = ws.numel() * ws.element_size()
     _check(_lib.moba_forward_ex(ctypes.byref(a)), "moba_forward_ex")
+    res = [out]
     if return_selection:
-        return out, (sel_out[0] if q.dim() == 3 else sel_out)
-    return out
+        res.append(sel_out[0] if q.dim() == 3 else sel_out)
+    if return_lse:
+        res.append(lse_out.view(S, H, Lq)[0] if q.dim() == 3 else lse_out.view(S, H, Lq))
+    return res[0] if len(res) == 1 else tuple(res)
 
 
 def moba_full_attention_ex(q, k, v, *, out=None, workspace=None):

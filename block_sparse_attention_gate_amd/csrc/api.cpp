@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
+#include <cstddef>
 #include <cstdio>
 #include <cstring>
 #include <mutex>
@@ -18,6 +19,21 @@ using moba::Dims;
 namespace {
 
 thread_local std::string g_last_error;
+
+// Size of the version-1 moba_args (without lse_out), still accepted.
+constexpr size_t kArgsV1Size = offsetof(moba_args, lse_out);
+
+// Copies the caller's struct (either version) into a full one, so that no
+// field past the caller's struct_size is read; lse_out defaults to NULL.
+moba_args load_args(const moba_args* a) {
+  moba_args b;
+  std::memset(&b, 0, sizeof(b));
+  size_t n = 0;
+  std::memcpy(&n, a, sizeof(size_t));   // struct_size comes first in every version
+  if (n == sizeof(moba_args) || n == kArgsV1Size) std::memcpy(&b, a, n);
+  else b.struct_size = n;               // rejected by check_common
+  return b;
+}
 
 moba_status fail(moba_status s, const char* fmt, ...) {
   char buf[512];
@@ -139,7 +155,7 @@ struct Plan {
 
 moba_status check_common(const moba_args* a, bool full, Plan* p) {
   if (!a) return fail(MOBA_ERR_INVALID_ARGUMENT, "args is NULL");
-  if (a->struct_size != sizeof(moba_args))
+  if (a->struct_size != sizeof(moba_args) && a->struct_size != kArgsV1Size)
     return fail(MOBA_ERR_INVALID_ARGUMENT, "struct_size %zu != sizeof(moba_args) %zu",
                 a->struct_size, sizeof(moba_args));
   if (!a->q || !a->k || !a->v || !a->out)
@@ -162,6 +178,8 @@ moba_status check_common(const moba_args* a, bool full, Plan* p) {
   if (align & 15) return fail(MOBA_ERR_INVALID_ARGUMENT, "pointers must be 16-byte aligned");
   if (a->sel_out && ((uintptr_t)a->sel_out & 3))
     return fail(MOBA_ERR_INVALID_ARGUMENT, "sel_out must be 4-byte aligned");
+  if (a->lse_out && ((uintptr_t)a->lse_out & 3))
+    return fail(MOBA_ERR_INVALID_ARGUMENT, "lse_out must be 4-byte aligned");
 
   Dims& d = p->d;
   d.S = a->batch; d.H = a->n_heads; d.Hkv = a->n_kv_heads; d.G = d.H / d.Hkv; d.D = a->head_dim;
@@ -456,7 +474,7 @@ moba_status forward_impl(const moba_args* a) {
       return moba::launch_decode_attn(a->q, a->k, a->v, ublk, umask, ucount, part, d, l.st);
     });
     l.run(K_DEC_MERGE, [&] {
-      return moba::launch_decode_merge(part, ublk, umask, ucount, a->out, d, l.st);
+      return moba::launch_decode_merge(part, ublk, umask, ucount, a->out, d, l.st, a->lse_out);
     });
     if (l.err != hipSuccess) return hip_fail(l);
     return MOBA_OK;
@@ -492,7 +510,8 @@ moba_status forward_impl(const moba_args* a) {
       }
     }
     l.run(K_MERGE, [&] {
-      return moba::launch_merge_partials_bf16(own_o, own_lse, 2, po, plse, a->out, d, l.st);
+      return moba::launch_merge_partials_bf16(own_o, own_lse, 2, po, plse, a->out, d, l.st,
+                                              a->lse_out);
     });
     if (l.err != hipSuccess) return hip_fail(l);
     return MOBA_OK;
@@ -501,9 +520,9 @@ moba_status forward_impl(const moba_args* a) {
   if (!p.routed) dq.kp = 0;  // nothing to merge
   l.run(K_ATTN_OWN, [&] {
     return d.bf16 ? moba::launch_attn_query_bf16(a->q, a->k, vt, ktail, po, plse, a->out, 0, dq,
-                                                 l.st)
+                                                 l.st, 0, a->lse_out)
                   : moba::launch_attn_query_f32(a->q, a->k, a->v, po, plse, a->out, 0, dq,
-                                                l.st);
+                                                l.st, a->lse_out);
   });
   if (l.err != hipSuccess) return hip_fail(l);
   return MOBA_OK;
@@ -615,11 +634,19 @@ moba_status moba_full_attention(const void* q, const void* k, const void* v, int
 }
 
 moba_status moba_forward_ex(const moba_args* a) {
-  return guarded([&] { return forward_impl(a); });
+  return guarded([&]() -> moba_status {
+    if (!a) return fail(MOBA_ERR_INVALID_ARGUMENT, "args is NULL");
+    const moba_args b = load_args(a);
+    return forward_impl(&b);
+  });
 }
 
 moba_status moba_full_attention_ex(const moba_args* a) {
-  return guarded([&] { return full_impl(a); });
+  return guarded([&]() -> moba_status {
+    if (!a) return fail(MOBA_ERR_INVALID_ARGUMENT, "args is NULL");
+    const moba_args b = load_args(a);
+    return full_impl(&b);
+  });
 }
 
 size_t moba_workspace_size(const moba_args* a) {
@@ -629,7 +656,7 @@ size_t moba_workspace_size(const moba_args* a) {
       fail(MOBA_ERR_INVALID_ARGUMENT, "args is NULL");
       return 0;
     }
-    moba_args b = *a;
+    moba_args b = load_args(a);
     b.workspace = nullptr;
     b.workspace_bytes = 0;
     Plan p;
@@ -647,7 +674,7 @@ size_t moba_full_workspace_size(const moba_args* a) {
       fail(MOBA_ERR_INVALID_ARGUMENT, "args is NULL");
       return 0;
     }
-    moba_args b = *a;
+    moba_args b = load_args(a);
     b.workspace = nullptr;
     b.workspace_bytes = 0;
     Plan p;

@@ -300,8 +300,8 @@ template <int D, int MODE, int NW>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_query(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ vt,
     const bf16_t* __restrict__ po, const float* __restrict__ plse, bf16_t* __restrict__ out,
-    const bf16_t* __restrict__ ktail, int Lq, int L, int Lv, int q_off, int H, int Hkv, int kp,
-    int B, int HW, float sl2, int nparts, int chunk_tiles) {
+    const bf16_t* __restrict__ ktail, float* __restrict__ lse_out, int Lq, int L, int Lv,
+    int q_off, int H, int Hkv, int kp, int B, int HW, float sl2, int nparts, int chunk_tiles) {
   using T = Tiles<D, NW>;
   __shared__ __attribute__((aligned(16))) bf16_t lds[2 * T::BUF];
   const int RW = 32 * NW / HW;
@@ -450,6 +450,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_query(
     if (hh == 0)
       const_cast<float*>(plse)[qh] = ltot > 0.f ? acc.m + __log2f(ltot) : -__builtin_inff();
   }
+  // log2 of the softmax normaliser over all of the query's keys (scaled
+  // logits), kept for the backward as a natural log (mode 0)
+  float lse_all = acc.m + __log2f(ltot);
   if (MODE == 0 && kp > 0) {
     // Merge: out = sum_x 2^(lse_x - M) o_x / sum_x 2^(lse_x - M) over the own
     // partial and the routed partials of this query.
@@ -505,7 +508,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_query(
       }
     }
     inv = 1.0f / wsum;
+    lse_all = M + __log2f(wsum);
   }
+  if (MODE == 0 && lse_out != nullptr && hh == 0)
+    lse_out[((int64_t)s * H + h) * Lq + r] = lse_all * kLn2;
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -528,7 +534,7 @@ template <int D>
 __global__ __launch_bounds__(256) void k_merge_partials(
     const bf16_t* __restrict__ own_o, const float* __restrict__ own_lse, int nown,
     const bf16_t* __restrict__ po, const float* __restrict__ plse, bf16_t* __restrict__ out,
-    int64_t nqh, int64_t Lq, int H, int64_t q_off, int B, int kp) {
+    float* __restrict__ lse_out, int64_t nqh, int64_t Lq, int H, int64_t q_off, int B, int kp) {
   constexpr int EPL = D / 16;
   const int64_t qh = (int64_t)blockIdx.x * 16 + threadIdx.x / 16;
   if (qh >= nqh) return;
@@ -583,6 +589,7 @@ __global__ __launch_bounds__(256) void k_merge_partials(
     for (int i = 0; i < EPL; ++i) acc[i] = fmaf(wt, x[i], acc[i]);
   }
   const float inv = 1.0f / wsum;
+  if (lse_out != nullptr && sub == 0) lse_out[qh] = (M + __log2f(wsum)) * kLn2;
   bf16_t* orow = out + ((s * Lq + r) * H + h) * D + sub * EPL;
   uint32_t wds[EPL / 2];
 #pragma unroll
@@ -598,14 +605,14 @@ __global__ __launch_bounds__(256) void k_merge_partials(
 
 hipError_t launch_merge_partials_bf16(const void* own_o, const float* own_lse, int nown,
                                       const void* po, const float* plse, void* out,
-                                      const Dims& d, hipStream_t st) {
+                                      const Dims& d, hipStream_t st, float* lse_out) {
   const int64_t nqh = (int64_t)d.S * d.H * d.Lq;
   const unsigned grid = (unsigned)((nqh + 15) / 16);
 #define MOBA_MERGE(DV)                                                                       \
   hipLaunchKernelGGL(k_merge_partials<DV>, dim3(grid), dim3(256), 0, st,                     \
                      static_cast<const bf16_t*>(own_o), own_lse, nown,                       \
-                     static_cast<const bf16_t*>(po), plse, static_cast<bf16_t*>(out), nqh,   \
-                     d.Lq, d.H, d.q_off, d.B, d.kp)
+                     static_cast<const bf16_t*>(po), plse, static_cast<bf16_t*>(out),        \
+                     lse_out, nqh, d.Lq, d.H, d.q_off, d.B, d.kp)
   if (d.D == 128) MOBA_MERGE(128); else MOBA_MERGE(64);
 #undef MOBA_MERGE
   return hipGetLastError();
@@ -659,7 +666,7 @@ int full_split_parts(const Dims& d) {
 hipError_t launch_attn_query_bf16(const void* q, const void* k, const void* vt,
                                   const void* ktail, const void* part_o, const float* part_lse,
                                   void* out, int mode, const Dims& d, hipStream_t st,
-                                  int nparts) {
+                                  int nparts, float* lse_out) {
   if (d.L % 64 != 0 && ktail == nullptr) return hipErrorInvalidValue;
   int HW, NW;
   query_shape(d, &HW, &NW);
@@ -673,8 +680,8 @@ hipError_t launch_attn_query_bf16(const void* q, const void* k, const void* vt,
                      static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),           \
                      static_cast<const bf16_t*>(vt), static_cast<const bf16_t*>(part_o),     \
                      part_lse, static_cast<bf16_t*>(out), static_cast<const bf16_t*>(ktail), \
-                     (int)d.Lq, (int)d.L, (int)d.Lv, (int)d.q_off, d.H, d.Hkv, d.kp, d.B, HW,  \
-                     sl2, nparts, kFullChunkTiles)
+                     mode == 0 ? lse_out : nullptr, (int)d.Lq, (int)d.L, (int)d.Lv,            \
+                     (int)d.q_off, d.H, d.Hkv, d.kp, d.B, HW, sl2, nparts, kFullChunkTiles)
 #define MOBA_QUERY_NW(DV, MV) \
   if (NW == 8) MOBA_QUERY(DV, MV, 8); else MOBA_QUERY(DV, MV, 4);
   if (d.D == 128) {

@@ -173,7 +173,8 @@ template <int D, int MODE>
 __global__ __launch_bounds__(F32Tile<D>::NT) void k_attn_query_f32(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const float* __restrict__ po, const float* __restrict__ plse, float* __restrict__ out,
-    int64_t Lq, int64_t L, int64_t q_off, int H, int Hkv, int kp, int B, float scale) {
+    float* __restrict__ lse_out, int64_t Lq, int64_t L, int64_t q_off, int H, int Hkv, int kp,
+    int B, float scale) {
   using T = F32Tile<D>;
   __shared__ __attribute__((aligned(16))) float ks[32 * D];
   __shared__ __attribute__((aligned(16))) float vs[32 * D];
@@ -235,12 +236,15 @@ __global__ __launch_bounds__(F32Tile<D>::NT) void k_attn_query_f32(
       }
     }
     const float inv = 1.0f / wsum;
+    if (lse_out != nullptr && dbase == 0) lse_out[((int64_t)s * H + h) * Lq + r] = M + logf(wsum);
 #pragma unroll
     for (int dd = 0; dd < 64; dd += 4)
       *reinterpret_cast<float4*>(orow + dd) =
           make_float4(a.o[dd] * inv, a.o[dd + 1] * inv, a.o[dd + 2] * inv, a.o[dd + 3] * inv);
     return;
   }
+  if (MODE == 0 && lse_out != nullptr && dbase == 0)
+    lse_out[((int64_t)s * H + h) * Lq + r] = a.m + logf(a.l);
   const float inv = 1.0f / a.l;
 #pragma unroll
   for (int dd = 0; dd < 64; dd += 4)
@@ -267,15 +271,15 @@ hipError_t launch_attn_routed_f32(const void* q, const void* k, const void* v,
 
 hipError_t launch_attn_query_f32(const void* q, const void* k, const void* v, const void* part_o,
                                  const float* part_lse, void* out, int mode, const Dims& d,
-                                 hipStream_t st) {
+                                 hipStream_t st, float* lse_out) {
   dim3 grid((unsigned)((d.Lq + 127) / 128), d.S * d.H);
   const float scale = 1.0f / sqrtf((float)d.D);
 #define MOBA_QF32(DV, MV)                                                                    \
   hipLaunchKernelGGL((k_attn_query_f32<DV, MV>), grid, dim3(F32Tile<DV>::NT), 0, st,         \
                      static_cast<const float*>(q), static_cast<const float*>(k),             \
                      static_cast<const float*>(v), static_cast<const float*>(part_o),        \
-                     part_lse, static_cast<float*>(out), d.Lq, d.L, d.q_off, d.H, d.Hkv,     \
-                     d.kp, d.B, scale)
+                     part_lse, static_cast<float*>(out), mode == 0 ? lse_out : nullptr,      \
+                     d.Lq, d.L, d.q_off, d.H, d.Hkv, d.kp, d.B, scale)
   if (d.D == 128) {
     if (mode == 0) MOBA_QF32(128, 0); else MOBA_QF32(128, 1);
   } else {

@@ -231,8 +231,9 @@ __global__ __launch_bounds__(D) void k_decode_merge(const float* __restrict__ pa
                                                     const int32_t* __restrict__ ublk,
                                                     const uint32_t* __restrict__ umask,
                                                     const int32_t* __restrict__ ucount,
-                                                    T* __restrict__ out, int H, int Hkv, int B,
-                                                    int umax) {
+                                                    T* __restrict__ out,
+                                                    float* __restrict__ lse_out, int H, int Hkv,
+                                                    int B, int umax) {
   __shared__ int items[kMergeMaxItems];
   __shared__ float wts[kMergeMaxItems];
   __shared__ int nitems_s;
@@ -302,6 +303,7 @@ __global__ __launch_bounds__(D) void k_decode_merge(const float* __restrict__ pa
   const float acc = ((acc8[0] + acc8[1]) + (acc8[2] + acc8[3])) +
                     ((acc8[4] + acc8[5]) + (acc8[6] + acc8[7]));
   const float r = acc / lsum;
+  if (lse_out != nullptr && tid == 0) lse_out[sh] = (M + __log2f(lsum)) * kLn2;
   T* orow = out + ((int64_t)s * H + h) * D;
   if (sizeof(T) == 2)
     reinterpret_cast<bf16_t*>(orow)[tid] = f32_to_bf16(r);
@@ -376,11 +378,11 @@ hipError_t launch_decode_attn(const void* q, const void* k, const void* v, const
 template <typename T, int D>
 static hipError_t decode_merge_gm(const float* part, const int32_t* ublk, const uint32_t* umask,
                                   const int32_t* ucount, void* out, const Dims& d,
-                                  hipStream_t st) {
+                                  hipStream_t st, float* lse_out) {
   const int umax = decode_umax(d);
 #define MOBA_DM(GMV)                                                                         \
   hipLaunchKernelGGL((k_decode_merge<T, D, GMV>), dim3(d.S * d.H), dim3(D), 0, st, part, ublk, \
-                     umask, ucount, static_cast<T*>(out), d.H, d.Hkv, d.B, umax)
+                     umask, ucount, static_cast<T*>(out), lse_out, d.H, d.Hkv, d.B, umax)
   switch (decode_gm(d)) {
     case 1: MOBA_DM(1); break;
     case 2: MOBA_DM(2); break;
@@ -393,13 +395,15 @@ static hipError_t decode_merge_gm(const float* part, const int32_t* ublk, const 
 
 hipError_t launch_decode_merge(const float* part, const int32_t* ublk, const uint32_t* umask,
                                const int32_t* ucount, void* out, const Dims& d,
-                               hipStream_t st) {
+                               hipStream_t st, float* lse_out) {
   if (d.bf16) {
-    if (d.D == 128) return decode_merge_gm<bf16_t, 128>(part, ublk, umask, ucount, out, d, st);
-    return decode_merge_gm<bf16_t, 64>(part, ublk, umask, ucount, out, d, st);
+    if (d.D == 128)
+      return decode_merge_gm<bf16_t, 128>(part, ublk, umask, ucount, out, d, st, lse_out);
+    return decode_merge_gm<bf16_t, 64>(part, ublk, umask, ucount, out, d, st, lse_out);
   }
-  if (d.D == 128) return decode_merge_gm<float, 128>(part, ublk, umask, ucount, out, d, st);
-  return decode_merge_gm<float, 64>(part, ublk, umask, ucount, out, d, st);
+  if (d.D == 128)
+    return decode_merge_gm<float, 128>(part, ublk, umask, ucount, out, d, st, lse_out);
+  return decode_merge_gm<float, 64>(part, ublk, umask, ucount, out, d, st, lse_out);
 }
 
 }  // namespace moba

@@ -97,20 +97,22 @@ hipError_t launch_attn_routed_f32(const void* q, const void* k, const void* v,
 // partial per chunk ([nparts, S*H*Lq, D] and log2-sum-exp [nparts, S*H*Lq]).
 // ktail: as written by launch_pool_transpose / launch_transpose_v (needed
 // when L % 64 != 0).
+// lse_out (nullable, mode 0): natural log-sum-exp [S, H, Lq] of each query's
+// scaled logits over all its keys.
 hipError_t launch_attn_query_bf16(const void* q, const void* k, const void* vt,
                                   const void* ktail, const void* part_o, const float* part_lse,
                                   void* out, int mode, const Dims& d, hipStream_t st,
-                                  int nparts = 0);
+                                  int nparts = 0, float* lse_out = nullptr);
 // Chunks of split full attention for a bf16 problem too small to fill the
 // chip with whole row tiles, else 0.
 int full_split_parts(const Dims& d);
 // Merge of nown key-range partials per query-head with its kp routed ones.
 hipError_t launch_merge_partials_bf16(const void* own_o, const float* own_lse, int nown,
                                       const void* po, const float* plse, void* out,
-                                      const Dims& d, hipStream_t st);
+                                      const Dims& d, hipStream_t st, float* lse_out = nullptr);
 hipError_t launch_attn_query_f32(const void* q, const void* k, const void* v, const void* part_o,
                                  const float* part_lse, void* out, int mode, const Dims& d,
-                                 hipStream_t st);
+                                 hipStream_t st, float* lse_out = nullptr);
 
 // Decode (q_len == 1): union of kept blocks per (sequence, KV head), split-K
 // attention over 512-key chunks, log-sum-exp merge.
@@ -124,6 +126,7 @@ hipError_t launch_decode_attn(const void* q, const void* k, const void* v, const
                               const uint32_t* umask, const int32_t* ucount, float* part,
                               const Dims& d, hipStream_t st);
 hipError_t launch_decode_merge(const float* part, const int32_t* ublk, const uint32_t* umask,
-                               const int32_t* ucount, void* out, const Dims& d, hipStream_t st);
+                               const int32_t* ucount, void* out, const Dims& d, hipStream_t st,
+                               float* lse_out = nullptr);
 
 }  // namespace moba

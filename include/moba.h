@@ -69,7 +69,9 @@
 extern "C" {
 #endif
 
-#define MOBA_ABI_VERSION 1
+/* 2: moba_args gained lse_out (a version-1 struct, without it, is still
+ * accepted); moba_backward_ex and moba_block_mean_update were added. */
+#define MOBA_ABI_VERSION 2
 
 typedef enum { MOBA_DTYPE_F32 = 0, MOBA_DTYPE_BF16 = 1 } moba_dtype;
 
@@ -124,7 +126,14 @@ typedef struct moba_args {
                                   library allocates it stream-ordered */
   size_t workspace_bytes;
   void* stream;                /* hipStream_t, NULL = default stream */
+  float* lse_out;              /* nullable: fp32 [batch, n_heads, q_len], the
+                                  natural log of each query's softmax
+                                  normaliser over its selected keys (scaled
+                                  logits), kept for moba_backward_ex; ignored
+                                  by the full-attention calls */
 } moba_args;
+/* struct_size may also be that of the version-1 struct (up to and including
+ * `stream`); lse_out is then taken as NULL. */
 
 moba_status moba_forward_ex(const moba_args* a);
 /* Full attention in the general form; block_size, topk, k_block_mean and

@@ -39,7 +39,7 @@ def test_binding_covers_the_header():
 
 def test_version_and_status_strings():
     import block_sparse_attention_gate_amd as moba
-    assert moba.moba_abi_version() == 1
+    assert moba.moba_abi_version() == 2
     assert moba.moba_status_string(0) == "MOBA_OK"
     assert moba.moba_status_string(2) == "MOBA_ERR_UNSUPPORTED"
     assert moba.moba_status_string(99) == "MOBA_STATUS_UNKNOWN"
@@ -162,3 +162,17 @@ def test_profile_names():
         assert moba.moba_profile_read(n) == (0.0, 0)
     with pytest.raises(ValueError):
         moba.moba_profile_read("nope")
+
+
+def test_version_one_struct_is_accepted():
+    """A caller built against the version-1 header (moba_args without
+    lse_out) passes the smaller struct_size; it is accepted and lse_out is
+    taken as NULL."""
+    import block_sparse_attention_gate_amd as moba
+    a = _args()
+    v1 = moba.MobaArgs.lse_out.offset
+    a.struct_size = v1
+    assert moba._lib.moba_workspace_size(ctypes.byref(a)) > 0, moba.moba_last_error()
+    a.struct_size = v1 + 4
+    assert moba._lib.moba_workspace_size(ctypes.byref(a)) == 0
+    assert "struct_size" in moba.moba_last_error()

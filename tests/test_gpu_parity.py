@@ -463,3 +463,50 @@ def test_decode_loop_with_incremental_block_means():
         check_selection(qh, positions, kb, sel_np, B, w.topk)
         check_outputs(to64(o1[0]), qh, positions, sel_np, B, L, "bf16",
                       [(h, 0) for h in range(qh.shape[1])], host_fetch(kh, vh), kh.shape[1])
+
+
+LSE_CASES = [
+    moba_inputs.custom("lse_small", "bf16", 1, 1000, None, 4, 2, 128, 128, 3, 91),
+    moba_inputs.custom("lse_fused", "bf16", 1, 8200, None, 128, 16, 64, 256, 4, 92),
+    moba_inputs.custom("lse_f32", "f32", 1, 700, None, 2, 1, 64, 64, 3, 93),
+    moba_inputs.custom("lse_decode", "bf16", 2, 1, 8192 + 300, 8, 2, 128, 512, 5, 94),
+    moba_inputs.custom("lse_k1", "bf16", 1, 640, None, 2, 1, 128, 64, 1, 95),
+]
+
+
+@pytest.mark.parametrize("w", LSE_CASES, ids=[w.name for w in LSE_CASES])
+def test_lse_out_parity(w):
+    """The kept log-sum-exp (natural log, scaled logits over each query's
+    selected keys) against the oracle on the GPU's selection, for the
+    small-problem merge, the fused own-block kernel, fp32, decode and top-k 1;
+    the output is unchanged by asking for it."""
+    moba = _moba()
+    print(f"case {w}", flush=True)
+    q, k, v = moba_inputs.make_inputs(w, device=DEV)
+    out, sel, lse = moba.moba_forward_ex(q, k, v, w.block_size, w.topk, return_selection=True,
+                                         return_lse=True)
+    out2 = moba.moba_forward_ex(q, k, v, w.block_size, w.topk)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16 if w.dtype == "bf16" else torch.int32),
+                       out2.view(torch.int16 if w.dtype == "bf16" else torch.int32))
+    batched = q.dim() == 4
+    rng = np.random.default_rng(3)
+    worst = 0.0
+    for s in range(q.shape[0] if batched else 1):
+        qs, ks, ss, ls = (q[s], k[s], sel[s], lse[s]) if batched else (q, k, sel, lse)
+        qh, kh = to64(qs), to64(ks)
+        Lq, H, L = qh.shape[0], qh.shape[1], kh.shape[0]
+        rows = np.unique(np.concatenate([rng.integers(0, Lq, size=min(Lq, 200)), [Lq - 1]]))
+        heads = rng.choice(H, size=min(H, 4), replace=False)
+        sel_np = ss.cpu().numpy()
+        lse_np = ls.double().cpu().numpy()
+        G = H // kh.shape[1]
+        for h in heads:
+            for r in rows:
+                keys = O.key_set(sel_np[h, r], L - Lq + r, w.block_size, L)
+                ref = O.attend_lse(qh[r, h], kh[:, h // G, :], keys, 1.0 / np.sqrt(qh.shape[2]))
+                worst = max(worst, abs(lse_np[h, r] - ref))
+    # fp32 sums of bf16-exact logits: measured ~1e-6; a wrong base (log2 vs
+    # log) or a dropped partial would be off by O(0.1)
+    print(f"  worst |lse error| {worst:.2e}")
+    assert worst <= 1e-4
