@@ -281,10 +281,15 @@ def moba_lse_reference(q, k, block_size, sel, q_offset=None, scale=None):
 #   dv_t += p_t dO,  dp_t = dO . v_t,  ds_t = p_t (dp_t - dO . o),
 #   dq = c sum_t ds_t k_t,  dk_t += c ds_t q.
 # --------------------------------------------------------------------------
-def moba_backward_reference(q, k, v, dout, block_size, sel, q_offset=None, scale=None):
+def moba_backward_reference(q, k, v, dout, block_size, sel, q_offset=None, scale=None,
+                            out=None):
     """Returns ``(dq [Lq, H, D], dk [L, Hkv, D], dv [L, Hkv, D])`` for the
     selection ``sel [H, Lq, topk]`` (held fixed).  GQA: a KV head's gradients
-    sum over the query heads of its group (R8)."""
+    sum over the query heads of its group (R8).
+
+    ``out`` (optional, ``[Lq, H, D]``): a stored forward output that the term
+    ``dO . o`` is to read instead of the exact output, as an algorithm that is
+    handed the forward's (rounded) output computes it; None: exact."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -307,7 +312,7 @@ def moba_backward_reference(q, k, v, dout, block_size, sel, q_offset=None, scale
             z = (kk @ q[r, h]) * scale
             p = np.exp(z - z.max())
             p /= p.sum()
-            o = p @ vv
+            o = p @ vv if out is None else np.asarray(out[r, h], dtype=np.float64)
             do = dout[r, h]
             dp = vv @ do
             ds = p * (dp - do @ o)

@@ -444,3 +444,37 @@ def test_lse_equals_logsumexp_of_the_masked_logits():
         z = torch.from_numpy(q[:, h] @ k[:, h // (H // Hkv)].T / math.sqrt(D))
         z = z.masked_fill(~torch.from_numpy(mask[h]), -math.inf)
         np.testing.assert_allclose(lse[h], torch.logsumexp(z, dim=1).numpy(), atol=1e-12)
+
+
+def test_backward_with_a_given_output_differs_by_the_closed_form():
+    """Reading dO.o from a given output o' = o + delta changes only the
+    softmax term: ds_t changes by -p_t (dO.delta), so dq changes by
+    -c (dO.delta) sum_t p_t k_t, dk_t by -c (dO.delta) p_t q, and dv not at
+    all (closed form of the change, per query)."""
+    L, B, topk, H, Hkv, D = 48, 8, 3, 2, 1, 8
+    q, k, v = _case(68, L, H, Hkv, D, B)
+    rng = np.random.default_rng(11)
+    dout = rng.standard_normal(q.shape)
+    sel, _ = O.select_all(q, O.block_mean(k, B), B, topk)
+    out, _, _ = O.moba_reference(q, k, v, B, topk, sel=sel)
+    delta = rng.standard_normal(out.shape) * 1e-2
+    base = O.moba_backward_reference(q, k, v, dout, B, sel)
+    same = O.moba_backward_reference(q, k, v, dout, B, sel, out=out)
+    for a_, b_ in zip(base, same):
+        np.testing.assert_allclose(a_, b_, atol=1e-12, rtol=0)
+    dq2, dk2, dv2 = O.moba_backward_reference(q, k, v, dout, B, sel, out=out + delta)
+    c = 1.0 / math.sqrt(D)
+    want_dq = base[0].copy()
+    want_dk = base[1].copy()
+    for h in range(H):
+        for i in range(L):
+            keys = O.key_set(sel[h, i], i, B, L)
+            z = k[keys, 0] @ q[i, h] * c
+            p = np.exp(z - z.max())
+            p /= p.sum()
+            e = dout[i, h] @ delta[i, h]
+            want_dq[i, h] -= c * e * (p @ k[keys, 0])
+            want_dk[keys, 0] -= c * e * np.outer(p, q[i, h])
+    np.testing.assert_allclose(dq2, want_dq, atol=1e-12, rtol=0)
+    np.testing.assert_allclose(dk2, want_dk, atol=1e-12, rtol=0)
+    np.testing.assert_allclose(dv2, base[2], atol=0, rtol=0)
