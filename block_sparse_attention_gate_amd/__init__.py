@@ -62,6 +62,36 @@ class MobaArgs(ctypes.Structure):
     ]
 
 
+class MobaBwdArgs(ctypes.Structure):
+    """Mirror of ``moba_bwd_args`` in include/moba.h."""
+
+    _fields_ = [
+        ("struct_size", ctypes.c_size_t),
+        ("q", ctypes.c_void_p),
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("out", ctypes.c_void_p),
+        ("dout", ctypes.c_void_p),
+        ("lse", ctypes.c_void_p),
+        ("sel", ctypes.c_void_p),
+        ("dq", ctypes.c_void_p),
+        ("dk", ctypes.c_void_p),
+        ("dv", ctypes.c_void_p),
+        ("batch", ctypes.c_int32),
+        ("n_heads", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("topk", ctypes.c_int32),
+        ("q_len", ctypes.c_int64),
+        ("kv_len", ctypes.c_int64),
+        ("dtype", ctypes.c_int),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+        ("stream", ctypes.c_void_p),
+    ]
+
+
 _P = ctypes.c_void_p
 _I32, _I64 = ctypes.c_int32, ctypes.c_int64
 _ST = ctypes.c_int
@@ -73,6 +103,8 @@ _SIGNATURES = {
     "moba_full_attention_ex": (_ST, [ctypes.POINTER(MobaArgs)]),
     "moba_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(MobaArgs)]),
     "moba_full_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(MobaArgs)]),
+    "moba_backward_ex": (_ST, [ctypes.POINTER(MobaBwdArgs)]),
+    "moba_backward_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(MobaBwdArgs)]),
     "moba_block_mean": (_ST, [_P, _I32, _I64, _I32, _I32, _I32, _P, ctypes.c_int, _P]),
     "moba_block_mean_update": (_ST, [_P, _I32, _I64, _I32, _I32, _I32, _I32, _P, ctypes.c_int,
                                      _P]),
@@ -279,6 +311,70 @@ def moba_forward_ex(q, k, v, block_size, topk, *, out=None, k_block_mean=None, s
     return res[0] if len(res) == 1 else tuple(res)
 
 
+def _bwd_args(q, k, v, out, dout, lse, sel, dq, dk, dv, block_size, topk) -> MobaBwdArgs:
+    for name, t in (("q", q), ("out", out), ("dout", dout), ("dq", dq)):
+        _dev_tensor(t, name, q.dtype)
+        if tuple(t.shape) != tuple(q.shape):
+            raise ValueError(f"{name} must have the shape of q")
+    for name, t in (("k", k), ("v", v), ("dk", dk), ("dv", dv)):
+        _dev_tensor(t, name, q.dtype)
+        if tuple(t.shape) != tuple(k.shape):
+            raise ValueError(f"{name} must have the shape of k")
+    S, Lq, H, D, L, Hkv = _shape4(q, k, v)
+    _dev_tensor(lse, "lse", torch.float32)
+    if lse.numel() != S * H * Lq:
+        raise ValueError(f"lse must be float32 [{S}, {H}, {Lq}]")
+    _dev_tensor(sel, "sel", torch.int32)
+    if sel.numel() != S * H * Lq * int(topk):
+        raise ValueError(f"sel must be int32 [{S}, {H}, {Lq}, {topk}]")
+    a = MobaBwdArgs()
+    a.struct_size = ctypes.sizeof(MobaBwdArgs)
+    a.q, a.k, a.v, a.out, a.dout = (t.data_ptr() for t in (q, k, v, out, dout))
+    a.lse, a.sel = lse.data_ptr(), sel.data_ptr()
+    a.dq, a.dk, a.dv = dq.data_ptr(), dk.data_ptr(), dv.data_ptr()
+    a.batch, a.n_heads, a.n_kv_heads, a.head_dim = S, H, Hkv, D
+    a.block_size, a.topk = int(block_size), int(topk)
+    a.q_len, a.kv_len = Lq, L
+    a.dtype = _dtype_code(q)
+    a.stream = _stream_ptr(q.device)
+    return a
+
+
+def moba_backward_ex(q, k, v, out, dout, lse, sel, block_size, topk, *, dq=None, dk=None,
+                     dv=None, workspace=None):
+    """Gradients ``(dq, dk, dv)`` of ``sum(out * dout)`` for a bf16 MoBA forward
+    (C ``moba_backward_ex``); ``lse`` and ``sel`` are the forward's
+    ``return_lse`` / ``return_selection`` outputs for the same q, k, v."""
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    a = _bwd_args(q, k, v, out, dout, lse, sel, dq, dk, dv, block_size, topk)
+    need = int(_lib.moba_backward_workspace_size(ctypes.byref(a)))
+    if need == 0 and _lib.moba_last_error():
+        _check(_lib.moba_backward_ex(ctypes.byref(a)), "moba_backward_ex")  # raises the error
+    ws = _workspace_tensor(need, q.device, workspace)
+    if ws is not None:
+        a.workspace = ws.data_ptr()
+        a.workspace_bytes = ws.numel() * ws.element_size()
+    _check(_lib.moba_backward_ex(ctypes.byref(a)), "moba_backward_ex")
+    return dq, dk, dv
+
+
+def moba_backward_workspace_size(q, k, v, block_size, topk) -> int:
+    """Workspace bytes moba_backward_ex needs for these shapes (0 and
+    moba_last_error() for an invalid set)."""
+    S, Lq, H, D, L, Hkv = _shape4(q, k, v)
+    a = MobaBwdArgs()
+    a.struct_size = ctypes.sizeof(MobaBwdArgs)
+    fake = 1 << 40   # only checked for NULL and alignment, never dereferenced
+    a.q = a.k = a.v = a.out = a.dout = a.lse = a.sel = a.dq = a.dk = a.dv = fake
+    a.batch, a.n_heads, a.n_kv_heads, a.head_dim = S, H, Hkv, D
+    a.block_size, a.topk = int(block_size), int(topk)
+    a.q_len, a.kv_len = Lq, L
+    a.dtype = _dtype_code(q)
+    return int(_lib.moba_backward_workspace_size(ctypes.byref(a)))
+
+
 def moba_full_attention_ex(q, k, v, *, out=None, workspace=None):
     out = torch.empty_like(q) if out is None else out
     a = _args(q, k, v, out)
@@ -361,4 +457,5 @@ def moba_profile_read(name: str):
 KERNEL_NAMES = ("block_mean", "transpose_v", "gate_topk", "route_count", "route_scan_rows",
                 "route_scan_buckets", "route_scatter", "attn_routed", "attn_own_merge",
                 "attn_full", "decode_plan", "decode_attn", "decode_merge", "merge_partials",
-                "pool_transpose", "block_mean_finalize", "route_scan_small")
+                "pool_transpose", "block_mean_finalize", "route_scan_small", "bwd_dot",
+                "bwd_transform", "bwd_dq_routed", "bwd_dq_own", "bwd_dkdv")

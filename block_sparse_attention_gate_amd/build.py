@@ -14,7 +14,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build", "moba")
 LIB_PATH = os.path.join(PKG, "libmoba.so")
 
-SOURCES = ["api.cpp", "pool.hip", "gate.hip", "route.hip", "attn_bf16.hip", "attn_f32.hip",
+SOURCES = ["api.cpp", "pool.hip", "gate.hip", "route.hip", "attn_bf16.hip", "attn_bwd.hip",
+           "attn_f32.hip",
            "decode.hip"]
 
 HIPCC_FLAGS = [

@@ -49,13 +49,15 @@ moba_status fail(moba_status s, const char* fmt, ...) {
 enum KernelId {
   K_BLOCK_MEAN, K_TRANSPOSE_V, K_GATE, K_RCOUNT, K_RSCAN_ROWS, K_RSCAN_BUCKETS, K_RSCATTER,
   K_ATTN_ROUTED, K_ATTN_OWN, K_ATTN_FULL, K_DEC_PLAN, K_DEC_ATTN, K_DEC_MERGE, K_MERGE,
-  K_POOL_TRANSPOSE, K_MEAN_FINALIZE, K_RSCAN_SMALL, K_COUNT
+  K_POOL_TRANSPOSE, K_MEAN_FINALIZE, K_RSCAN_SMALL, K_BWD_DOT, K_BWD_TRANSFORM,
+  K_BWD_DQ_ROUTED, K_BWD_DQ_OWN, K_BWD_DKDV, K_COUNT
 };
 const char* const kKernelNames[K_COUNT] = {
     "block_mean", "transpose_v", "gate_topk", "route_count", "route_scan_rows",
     "route_scan_buckets", "route_scatter", "attn_routed", "attn_own_merge", "attn_full",
     "decode_plan", "decode_attn", "decode_merge", "merge_partials", "pool_transpose",
-    "block_mean_finalize", "route_scan_small"};
+    "block_mean_finalize", "route_scan_small", "bwd_dot", "bwd_transform", "bwd_dq_routed",
+    "bwd_dq_own", "bwd_dkdv"};
 
 struct ProfRecord {
   int id;
@@ -199,7 +201,8 @@ moba_status check_common(const moba_args* a, bool full, Plan* p) {
   return MOBA_OK;
 }
 
-moba_status plan_forward(const moba_args* a, Plan* p) {
+// Argument checks and the dimensions shared by the forward and the backward.
+moba_status forward_dims(const moba_args* a, Plan* p) {
   moba_status st = check_common(a, false, p);
   if (st != MOBA_OK) return st;
   Dims& d = p->d;
@@ -228,6 +231,13 @@ moba_status plan_forward(const moba_args* a, Plan* p) {
   d.tile_m = (d.bf16 && slots / 256 >= 128) ? 256 : 128;
   if ((int64_t)d.S * d.H * d.nchunk_r >= ((int64_t)1 << 31))
     return fail(MOBA_ERR_UNSUPPORTED, "too many routing chunks");
+  return MOBA_OK;
+}
+
+moba_status plan_forward(const moba_args* a, Plan* p) {
+  moba_status st = forward_dims(a, p);
+  if (st != MOBA_OK) return st;
+  Dims& d = p->d;
   const int64_t esz = d.bf16 ? 2 : 4;
   p->need_kbar = a->k_block_mean == nullptr;
   p->need_sel = a->sel_out == nullptr;
@@ -583,6 +593,138 @@ moba_status full_impl(const moba_args* a) {
   return MOBA_OK;
 }
 
+// ------------------------------------------------------------------ backward
+struct BwdPlan {
+  Plan f;                  // dims (forward_dims) and the routing-table offsets
+  bool routed = false, need_tail = false;
+  size_t off_dvec = 0, off_kt = 0, off_ktail = 0, off_vtail = 0, off_dqp = 0, total = 0;
+};
+
+moba_status plan_backward(const moba_bwd_args* b, BwdPlan* bp) {
+  if (!b) return fail(MOBA_ERR_INVALID_ARGUMENT, "args is NULL");
+  if (b->struct_size != sizeof(moba_bwd_args))
+    return fail(MOBA_ERR_INVALID_ARGUMENT, "struct_size %zu != sizeof(moba_bwd_args) %zu",
+                b->struct_size, sizeof(moba_bwd_args));
+  if (!b->dout || !b->lse || !b->sel || !b->dq || !b->dk || !b->dv)
+    return fail(MOBA_ERR_INVALID_ARGUMENT, "dout, lse, sel, dq, dk and dv must be non-NULL");
+  if (((uintptr_t)b->dout | (uintptr_t)b->dq | (uintptr_t)b->dk | (uintptr_t)b->dv) & 15)
+    return fail(MOBA_ERR_INVALID_ARGUMENT, "pointers must be 16-byte aligned");
+  if (((uintptr_t)b->lse | (uintptr_t)b->sel) & 3)
+    return fail(MOBA_ERR_INVALID_ARGUMENT, "lse and sel must be 4-byte aligned");
+  moba_args a;
+  std::memset(&a, 0, sizeof(a));
+  a.struct_size = sizeof(moba_args);
+  a.q = b->q; a.k = b->k; a.v = b->v; a.out = const_cast<void*>(b->out);
+  a.batch = b->batch; a.n_heads = b->n_heads; a.n_kv_heads = b->n_kv_heads;
+  a.head_dim = b->head_dim; a.block_size = b->block_size; a.topk = b->topk;
+  a.q_len = b->q_len; a.kv_len = b->kv_len; a.dtype = b->dtype; a.stream = b->stream;
+  moba_status st = forward_dims(&a, &bp->f);
+  if (st != MOBA_OK) return st;
+  Dims& d = bp->f.d;
+  if (!d.bf16) return fail(MOBA_ERR_UNSUPPORTED, "the backward supports bf16 only");
+  d.tile_m = 128;  // four-wave routed dq tiles (eight waves would spill)
+  if (d.Lv * d.D >= ((int64_t)1 << 31))
+    return fail(MOBA_ERR_UNSUPPORTED, "kv_len * head_dim >= 2^31");
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  Plan& p = bp->f;
+  bp->off_dvec = take((size_t)d.S * d.H * d.Lq * 4);
+  bp->off_kt = take((size_t)d.S * d.Hkv * d.D * d.Lv * 2);
+  bp->need_tail = d.L % 64 != 0;
+  if (bp->need_tail) {
+    bp->off_ktail = take((size_t)d.S * 64 * d.Hkv * d.D * 2);
+    bp->off_vtail = take((size_t)d.S * 64 * d.Hkv * d.D * 2);
+  }
+  bp->routed = d.kp > 0 && d.nb > 1;
+  if (bp->routed) {
+    p.off_counts = take((size_t)d.nrows * d.ncols * 4);
+    p.off_btotal = take((size_t)d.nrows * 4);
+    p.off_boff = take((size_t)(d.nrows + 1) * 4);
+    p.off_toff = take((size_t)(d.nrows + 1) * 4);
+    p.off_list = take((size_t)d.slots * 4);
+    bp->off_dqp = take((size_t)d.slots * d.D * 2);
+  }
+  bp->total = off;
+  if (b->workspace && b->workspace_bytes < bp->total)
+    return fail(MOBA_ERR_INVALID_ARGUMENT, "workspace too small: %zu < %zu bytes",
+                b->workspace_bytes, bp->total);
+  if (b->workspace && ((uintptr_t)b->workspace & 15))
+    return fail(MOBA_ERR_INVALID_ARGUMENT, "pointers must be 16-byte aligned");
+  return MOBA_OK;
+}
+
+moba_status backward_impl(const moba_bwd_args* b) {
+  BwdPlan bp;
+  moba_status st = plan_backward(b, &bp);
+  if (st != MOBA_OK) return st;
+  const Dims& d = bp.f.d;
+  Workspace ws;
+  ws.st = (hipStream_t)b->stream;
+  if (b->workspace) {
+    ws.base = (char*)b->workspace;
+  } else if (bp.total) {
+    void* ptr = nullptr;
+    const hipError_t e = hipMallocAsync(&ptr, bp.total, ws.st);
+    if (e != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      return fail(MOBA_ERR_OUT_OF_MEMORY, "hipMallocAsync(%zu bytes) failed: %s", bp.total,
+                  hipGetErrorString(e));
+    }
+    ws.base = (char*)ptr;
+    ws.owned = true;
+  }
+  char* w = ws.base;
+  float* dvec = (float*)(w + bp.off_dvec);
+  void* kt = (void*)(w + bp.off_kt);
+  void* ktail = bp.need_tail ? (void*)(w + bp.off_ktail) : nullptr;
+  void* vtail = bp.need_tail ? (void*)(w + bp.off_vtail) : nullptr;
+  const Plan& p = bp.f;
+  uint32_t* counts = bp.routed ? (uint32_t*)(w + p.off_counts) : nullptr;
+  uint32_t* btotal = bp.routed ? (uint32_t*)(w + p.off_btotal) : nullptr;
+  uint32_t* boff = bp.routed ? (uint32_t*)(w + p.off_boff) : nullptr;
+  uint32_t* toff = bp.routed ? (uint32_t*)(w + p.off_toff) : nullptr;
+  uint32_t* list = bp.routed ? (uint32_t*)(w + p.off_list) : nullptr;
+  void* dqp = bp.routed ? (void*)(w + bp.off_dqp) : nullptr;
+
+  Launch l{ws.st};
+  l.run(K_BWD_DOT, [&] { return moba::launch_bwd_dot(b->out, b->dout, dvec, d, l.st); });
+  l.run(K_BWD_TRANSFORM,
+        [&] { return moba::launch_bwd_transform(b->k, b->v, kt, ktail, vtail, d, l.st); });
+  if (bp.routed) {
+    l.run(K_RCOUNT, [&] { return moba::launch_route_count(b->sel, counts, d, l.st); });
+    const bool small_scan = moba::route_scan_small_fits(d);
+    if (small_scan) {
+      l.run(K_RSCAN_SMALL,
+            [&] { return moba::launch_route_scan_small(counts, boff, toff, d, l.st); });
+    } else {
+      l.run(K_RSCAN_ROWS, [&] { return moba::launch_route_scan_rows(counts, btotal, d, l.st); });
+      l.run(K_RSCAN_BUCKETS,
+            [&] { return moba::launch_route_scan_buckets(btotal, boff, toff, d, l.st); });
+    }
+    l.run(K_RSCATTER, [&] {
+      return moba::launch_route_scatter(b->sel, counts, boff, list, d, l.st, small_scan);
+    });
+    l.run(K_BWD_DQ_ROUTED, [&] {
+      return moba::launch_bwd_dq_routed(b->q, b->dout, b->k, b->v, kt, b->lse, dvec, list, boff,
+                                        toff, dqp, d, l.st);
+    });
+  }
+  l.run(K_BWD_DQ_OWN, [&] {
+    return moba::launch_bwd_dq_own(b->q, b->dout, b->k, b->v, kt, ktail, vtail, b->lse, dvec,
+                                   dqp, b->dq, d, l.st);
+  });
+  l.run(K_BWD_DKDV, [&] {
+    return moba::launch_bwd_dkdv(b->q, b->dout, b->k, b->v, b->lse, dvec, list, boff, b->dk,
+                                 b->dv, d, l.st);
+  });
+  if (l.err != hipSuccess) return hip_fail(l);
+  return MOBA_OK;
+}
+
 moba_args simple_args(const void* q, const void* k, const void* v, int64_t seq_len,
                       int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, int32_t block_size,
                       int32_t topk, void* out, moba_dtype dtype, void* stream) {
@@ -662,6 +804,33 @@ size_t moba_workspace_size(const moba_args* a) {
     Plan p;
     if (plan_forward(&b, &p) != MOBA_OK) return 0;
     return p.total;
+  } catch (...) {
+    return 0;
+  }
+}
+
+moba_status moba_backward_ex(const moba_bwd_args* a) {
+  return guarded([&] { return backward_impl(a); });
+}
+
+size_t moba_backward_workspace_size(const moba_bwd_args* a) {
+  g_last_error.clear();
+  try {
+    if (!a) {
+      fail(MOBA_ERR_INVALID_ARGUMENT, "args is NULL");
+      return 0;
+    }
+    if (a->struct_size != sizeof(moba_bwd_args)) {
+      fail(MOBA_ERR_INVALID_ARGUMENT, "struct_size %zu != sizeof(moba_bwd_args) %zu",
+           a->struct_size, sizeof(moba_bwd_args));
+      return 0;
+    }
+    moba_bwd_args b = *a;
+    b.workspace = nullptr;
+    b.workspace_bytes = 0;
+    BwdPlan bp;
+    if (plan_backward(&b, &bp) != MOBA_OK) return 0;
+    return bp.total;
   } catch (...) {
     return 0;
   }

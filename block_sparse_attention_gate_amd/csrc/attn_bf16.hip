@@ -400,6 +400,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_query(
     const int d_ = (pos_first + 1) / 64;
     wd_ = d_ < ws_ ? ws_ : (d_ > we_ ? we_ : d_);
     if (klo_w % 64 != 0) wd_ = ws_;                    // window start not tile-aligned
+    // rows of the wave in two blocks (queries at an offset that is not a
+    // multiple of 32): the lanes' windows start at different keys, so every
+    // tile takes the per-lane mask
+    if ((MODE == 0 || MODE == 2) && ((q_off + wlast) / B) * B != klo_w) wd_ = ws_;
     // restrict the phases to this workgroup's tiles [t0, t1)
     ws_ = ws_ < t0 ? t0 : (ws_ > t1 ? t1 : ws_);
     we_ = we_ < ws_ ? ws_ : (we_ > t1 ? t1 : we_);

@@ -140,6 +140,47 @@ moba_status moba_forward_ex(const moba_args* a);
  * sel_out are ignored. */
 moba_status moba_full_attention_ex(const moba_args* a);
 
+/*
+ * Backward of moba_forward_ex for continued training (the pages require it:
+ * "MoBA" project card, "Highlighted Details"; they give no backward pass).
+ * Gradients of sum(out * dout) with respect to q, k and v with the forward's
+ * selection held fixed: top-k is piecewise constant and passes no gradient,
+ * so the gate and the block means get none.  For a query with key set T,
+ * p = softmax(c K_T q), c = 1/sqrt(head_dim):
+ *   dv_t += p_t dO,  ds_t = p_t (dO.v_t - dO.o),  dq = c sum_t ds_t k_t,
+ *   dk_t += c ds_t q   (GQA: a KV head sums over its group's query heads).
+ * bf16 only (fp32 is UNSUPPORTED); the other limits are the forward's, and
+ * kv_len * head_dim (kv_len rounded up to 64) must stay below 2^31.
+ * sel and lse are what moba_forward_ex wrote to sel_out and lse_out for the
+ * same q, k, v.  dq, dk, dv are fully overwritten (keys no query attends get
+ * zero gradients).  Workspace (stream-ordered when NULL): dO.o per
+ * query-head, K^T, the routing tables rebuilt from sel and one bf16 dq
+ * partial per routed slot.
+ */
+typedef struct moba_bwd_args {
+  size_t struct_size;          /* = sizeof(moba_bwd_args) */
+  const void* q;               /* [batch, q_len, n_heads, head_dim] */
+  const void* k;               /* [batch, kv_len, n_kv_heads, head_dim] */
+  const void* v;               /* [batch, kv_len, n_kv_heads, head_dim] */
+  const void* out;             /* forward output, layout of q */
+  const void* dout;            /* upstream gradient, layout of q */
+  const float* lse;            /* [batch, n_heads, q_len] (lse_out of the forward) */
+  const int32_t* sel;          /* [batch, n_heads, q_len, topk] (sel_out of the forward) */
+  void* dq;                    /* layout of q */
+  void* dk;                    /* layout of k */
+  void* dv;                    /* layout of v */
+  int32_t batch;
+  int32_t n_heads, n_kv_heads, head_dim, block_size, topk;
+  int64_t q_len, kv_len;
+  moba_dtype dtype;
+  void* workspace;             /* nullable, >= moba_backward_workspace_size bytes */
+  size_t workspace_bytes;
+  void* stream;                /* hipStream_t, NULL = default stream */
+} moba_bwd_args;
+
+moba_status moba_backward_ex(const moba_bwd_args* a);
+size_t moba_backward_workspace_size(const moba_bwd_args* a);
+
 /* Workspace bytes moba_forward_ex / moba_full_attention_ex need for `a`
  * (0 for an invalid argument set; read moba_last_error()). */
 size_t moba_workspace_size(const moba_args* a);
@@ -177,7 +218,8 @@ int32_t moba_abi_version(void);
  * "route_scan_rows", "route_scan_buckets", "route_scatter", "attn_routed",
  * "attn_own_merge", "attn_full", "decode_plan", "decode_attn",
  * "decode_merge", "merge_partials", "pool_transpose", "block_mean_finalize",
- * "route_scan_small".  Unknown names give
+ * "route_scan_small", and for the backward "bwd_dot", "bwd_transform",
+ * "bwd_dq_routed", "bwd_dq_own", "bwd_dkdv".  Unknown names give
  * MOBA_ERR_INVALID_ARGUMENT.  (bf16 prefill runs the own-block attention,
  * "attn_own_merge", on an internal stream of the same device, forked from
  * and joined back into the caller's stream.)
