@@ -12,7 +12,10 @@ region.  Prints one JSON line.
                up to i).
   speedup      time of the library's own full causal attention at the same
                shape / time of the MoBA forward.
-  also         the same figures at the 128K Llama-layer prefill and the
+  also         the backward (moba_backward_ex) at 32K and 128K in effective
+               TFLOP/s (five products per selected pair, 2.5 x the forward's
+               FLOPs) with the dk/dv kernel's roofline; the same figures as
+               above at the 128K Llama-layer prefill and the
                1M-token prefill (32/8 heads, block 4096, top-k 12), at 10M
                tokens with one head (block 4096, top-k 12; the full attention
                it is compared with runs once, about half a minute), and the
@@ -214,6 +217,46 @@ def run_prefill(moba, w, steps, warmup, full_steps, full_warmup, with_full=True,
     return res
 
 
+def run_backward(moba, w, steps, warmup):
+    """One step = one moba_backward_ex call (the forward's selection and
+    log-sum-exp precomputed, workspace preallocated).  Algorithmic work: five
+    products per (query, selected key) pair (S, dP, dV, dK, dQ) = 2.5 x the
+    forward's selected-block FLOPs; the dk/dv kernel does four of them."""
+    import torch
+    import moba_inputs  # noqa: F401
+    log(f"[bench] {w.name}: backward inputs")
+    q, k, v = moba_inputs.make_inputs(w, device="cuda:0")
+    out, sel, lse = moba.moba_forward_ex(q, k, v, w.block_size, w.topk, return_selection=True,
+                                         return_lse=True)
+    g = torch.Generator(device="cuda:0").manual_seed(w.seed + 7)
+    dout = torch.randn(q.shape, generator=g, device="cuda:0",
+                       dtype=torch.float32).to(q.dtype)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(max(moba.moba_backward_workspace_size(q, k, v, w.block_size, w.topk), 1),
+                     dtype=torch.uint8, device=q.device)
+    bwd = lambda: moba.moba_backward_ex(q, k, v, out, dout, lse, sel, w.block_size, w.topk,
+                                        dq=dq, dk=dk, dv=dv, workspace=ws)
+    log(f"[bench] {w.name}: workspace {ws.numel() / 2**30:.2f} GiB; timing MoBA backward")
+    ms, wall_ms = time_region(bwd, steps, warmup)
+    kern = kernel_breakdown(moba, bwd, steps)
+    eff, _, _, _ = prefill_flops(w)
+    res = {"workload": w.name + "_backward", "ms": ms, "wall_ms": wall_ms,
+           "effective_tflops": 2.5 * eff / (ms * 1e-3) / 1e12,
+           "frac_of_bf16_peak": 2.5 * eff / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+           "effective_flop": 2.5 * eff,
+           "kernels_ms": {k_: round(v_["avg_ms"], 4) for k_, v_ in kern.items()}}
+    if "bwd_dkdv" in kern:
+        t = kern["bwd_dkdv"]["avg_ms"] * 1e-3
+        a = 2.0 * eff / t / 1e12
+        res["roofline"] = {"bound": "mfma", "kernel": "bwd_dkdv", "achieved": a,
+                           "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                           "frac": a / PEAK_BF16_TFLOPS, "traffic": None,
+                           "avg_launch_ms": kern["bwd_dkdv"]["avg_ms"]}
+    del q, k, v, out, sel, lse, dout, dq, dk, dv, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def run_decode(moba, w, steps, warmup, with_full=True):
     """Decode against a long cache: one moba_forward_ex call with the block
     means precomputed (untimed, as a decode loop reuses them).  Algorithmic
@@ -347,11 +390,15 @@ def main():
     ap.add_argument("--skip-decode", action="store_true", help="skip the 1M-cache decode")
     ap.add_argument("--skip-10m", action="store_true",
                     help="skip the 10M-token single-head prefill")
+    ap.add_argument("--skip-backward", action="store_true",
+                    help="skip the backward (32K and 128K)")
     ap.add_argument("--skip-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--workload", default=None,
                     help="time only this prefill workload's MoBA forward (profiling runs)")
     ap.add_argument("--no-full", action="store_true", help="with --workload: skip full attention")
+    ap.add_argument("--backward", action="store_true",
+                    help="with --workload: time the backward of that prefill workload")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="with --workload: also run a plain device copy of this many MiB "
                          "(reference for the HBM byte counters)")
@@ -378,7 +425,9 @@ def main():
             log(f"[bench] calibration copy of {args.calib_copy_mib} MiB done")
             del src, dst
         w = moba_inputs.WORKLOADS[args.workload]
-        if w.is_decode:
+        if args.backward:
+            r = run_backward(moba, w, args.steps, args.warmup)
+        elif w.is_decode:
             r = run_decode(moba, w, args.steps, args.warmup, with_full=not args.no_full)
         else:
             r = run_prefill(moba, w, args.steps, args.warmup, full_steps=1, full_warmup=0,
@@ -413,6 +462,12 @@ def main():
         r10["roofline"] = roofline(r10)
         r10.pop("_roofline_src")
         also["prefill_10m"] = r10
+    if not args.skip_backward:
+        also["micro_32k_backward"] = run_backward(moba, w, args.steps, args.warmup)
+        if not args.skip_128k:
+            also["llama8b_128k_backward"] = run_backward(
+                moba, moba_inputs.WORKLOADS["llama8b_128k"], min(args.steps, 3),
+                min(args.warmup, 1))
     if not args.skip_decode:
         also["decode_1m"] = run_decode(moba, moba_inputs.WORKLOADS["decode_1m"], args.steps,
                                        args.warmup)

@@ -470,23 +470,25 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_bwd_dq_own(
 }
 
 // ============================================================ dk, dv kernel
-template <int D, int NW>
+// QN = 32 NQ queries per step.
+template <int D, int NW, int NQ>
 struct KvTiles {
   static constexpr int NT = 64 * NW;
-  static constexpr int QS = D + 8;              // Q / dO tile row stride (32 rows)
-  static constexpr int TS = 32 + 8;             // Q^T / dO^T tile row stride (D rows)
-  static constexpr int QE = 32 * QS;
+  static constexpr int QN = 32 * NQ;
+  static constexpr int QS = D + 8;              // Q / dO tile row stride (QN rows)
+  static constexpr int TS = QN + 8;             // Q^T / dO^T tile row stride (D rows)
+  static constexpr int QE = QN * QS;
   static constexpr int TE = D * TS;
   static constexpr int BUF = 2 * QE + 2 * TE;   // Q, dO, Q^T, dO^T (bf16 elements)
-  static constexpr int CH = 32 * (D / 8) / NT;  // 16-byte chunks per thread per tensor
+  static constexpr int CH = QN * (D / 8) / NT;  // 16-byte chunks per thread per tensor
 };
 
 // Key-stationary: workgroup (s, g, block j, chunk c) owns keys
 // [jB + c*32*NW, +32*NW) of the block (wave w the 32 from +32w) and loops over
-// the block's routed entries, then its own queries (one head at a time, 32
-// positions per step, causal mask), 32 queries per step.  grid
+// the block's routed entries, then its own queries (one head at a time, QN
+// positions per step, causal mask), QN = 32 NQ queries per step.  grid
 // (S * Hkv * nb * ceil(B / (32 NW))), 64*NW threads.
-template <int D, int NW>
+template <int D, int NW, int NQ>
 __global__ __launch_bounds__(64 * NW, 1) void k_bwd_dkdv(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ dout,
     const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, const float* __restrict__ lse,
@@ -494,9 +496,10 @@ __global__ __launch_bounds__(64 * NW, 1) void k_bwd_dkdv(
     const uint32_t* __restrict__ bucket_off, bf16_t* __restrict__ dk, bf16_t* __restrict__ dv,
     int Lq, int L, int q_off, int H, int Hkv, int kp, int B, int nb, int nchunk, FastDiv fd_kp,
     FastDiv fd_lq, float sl2, float scale) {
-  using T = KvTiles<D, NW>;
+  using T = KvTiles<D, NW, NQ>;
+  constexpr int QN = T::QN;
   __shared__ __attribute__((aligned(16))) bf16_t lds[2 * T::BUF];
-  __shared__ __attribute__((aligned(16))) float stat[2][2][32];  // [buffer][lse2, Dv][query]
+  __shared__ __attribute__((aligned(16))) float stat[2][2][QN];  // [buffer][lse2, Dv][query]
   const int KC = 32 * NW;
   const int item = blockIdx.x;
   const int c = item % nchunk;
@@ -535,36 +538,34 @@ __global__ __launch_bounds__(64 * NW, 1) void k_bwd_dkdv(
     dva[dt] = f32x16{};
   }
 
-  // steps: routed entries (32 per step), then own queries (head by head, 32
+  // steps: routed entries (QN per step), then own queries (head by head, QN
   // positions per step starting at the first position that sees a key here)
   const bool routed = bucket_off != nullptr;   // no routing tables: no past blocks
   const uint32_t rbase = routed ? bucket_off[row] : 0u;
   const int nrt = routed ? (int)(bucket_off[row + 1] - rbase) : 0;
-  const int rsteps = (nrt + 31) / 32;
+  const int rsteps = (nrt + QN - 1) / QN;
   int p0 = kc0 > q_off ? kc0 : q_off;                      // first own query position
   const int pend = bend;                                   // one past the last
   const int npos = pend > p0 ? pend - p0 : 0;
-  const int psteps_h = (npos + 31) / 32;
+  const int psteps_h = (npos + QN - 1) / QN;
   const int nsteps = rsteps + G * psteps_h;
 
-  // Staging, four steps in flight: the entry ids of step it+3 (routed steps
-  // read them from the list), the Q / dO rows and the two statistics of steps
-  // it+2 and it+1 (gathered rows: two steps of latency cover an HBM access),
-  // and the LDS tiles of step it.  Thread chunk i covers query
-  // qi = (tid + NT i) % 32, dims cc*8.. with cc = (tid + NT i) / 32: the 32
-  // lanes of a transposed store then write 32 different queries of one row.
-  struct RowSet {
-    u32x4 q[T::CH], d[T::CH];
-    float l, dv;                     // threads < 32: lse2, Dv of query tid
-  };
-  RowSet ra, rb;                     // rows of steps it+1 (ra) and it+2 (rb)
-  uint32_t ida[T::CH];               // entry ids of the next step to fetch rows for
-  uint32_t sida = 0u;                // threads < 32: the id of query tid
+  // Staging, three steps in flight: the entry ids of step it+2 (routed steps
+  // read them from the list), the Q / dO rows and the two statistics of step
+  // it+1 (requested once step it's first products are issued), and the LDS
+  // tiles of step it.
+  // Thread chunk i covers query qi = (tid + NT i) % QN, dims cc*8.. with
+  // cc = (tid + NT i) / QN: the lanes of a transposed store then write
+  // different queries of one row.
+  u32x4 qr[T::CH], dr[T::CH];
+  float st_l = 0.f, st_d = 0.f;      // threads < QN: lse2, Dv of query tid (step it+1)
+  uint32_t ida[T::CH];               // entry ids of step it+1, then it+2
+  uint32_t sida = 0u;                // threads < QN: the id of query tid
   // query (row offset, query-head index) of query qi of a step, or false
   auto query_at = [&](int step, int qi, uint32_t id, int64_t& qrow, int64_t& qhi) -> bool {
     int r, h;
     if (step < rsteps) {
-      if (step * 32 + qi >= nrt) return false;
+      if (step * QN + qi >= nrt) return false;
       const uint32_t qhh = fdiv(id, fd_kp);             // (s*H + h)*Lq + r
       const uint32_t sh = fdiv(qhh, fd_lq);             // s*H + h
       r = (int)(qhh - sh * fd_lq.d);
@@ -573,7 +574,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_bwd_dkdv(
     } else {
       const int st = step - rsteps;
       const int hl = st / psteps_h, pc = st - hl * psteps_h;
-      const int p = p0 + pc * 32 + qi;
+      const int p = p0 + pc * QN + qi;
       if (p >= pend) return false;
       r = p - q_off;
       h = g * G + hl;
@@ -582,85 +583,83 @@ __global__ __launch_bounds__(64 * NW, 1) void k_bwd_dkdv(
     qhi = ((int64_t)s * H + h) * Lq + r;
     return true;
   };
-  auto fetch_ids = [&](int step, uint32_t (&ids)[T::CH], uint32_t& sid) {
+  auto fetch_ids = [&](int step) {
     if (step >= rsteps) return;  // own steps need no ids
 #pragma unroll
     for (int i = 0; i < T::CH; ++i) {
-      const int e = step * 32 + (tid + T::NT * i) % 32;
-      ids[i] = e < nrt ? list[rbase + e] : 0u;
+      const int e = step * QN + (tid + T::NT * i) % QN;
+      ida[i] = e < nrt ? list[rbase + e] : 0u;
     }
-    if (tid < 32) {
-      const int e = step * 32 + tid;
-      sid = e < nrt ? list[rbase + e] : 0u;
+    if (tid < QN) {
+      const int e = step * QN + tid;
+      sida = e < nrt ? list[rbase + e] : 0u;
     }
   };
-  auto fetch_rows = [&](int step, const uint32_t (&ids)[T::CH], uint32_t sid, RowSet& rs) {
+  auto fetch_rows = [&](int step) {
 #pragma unroll
     for (int i = 0; i < T::CH; ++i) {
       const int cidx = tid + T::NT * i;
-      const int qi = cidx % 32, cc = cidx / 32;
+      const int qi = cidx % QN, cc = cidx / QN;
       int64_t qrow = 0, qhi = 0;
-      const bool ok = query_at(step, qi, ids[i], qrow, qhi);
-      rs.q[i] = ok ? *reinterpret_cast<const u32x4*>(q + qrow + cc * 8) : u32x4{0u, 0u, 0u, 0u};
-      rs.d[i] = ok ? *reinterpret_cast<const u32x4*>(dout + qrow + cc * 8) : u32x4{0u, 0u, 0u, 0u};
+      const bool ok = query_at(step, qi, ida[i], qrow, qhi);
+      qr[i] = ok ? *reinterpret_cast<const u32x4*>(q + qrow + cc * 8) : u32x4{0u, 0u, 0u, 0u};
+      dr[i] = ok ? *reinterpret_cast<const u32x4*>(dout + qrow + cc * 8) : u32x4{0u, 0u, 0u, 0u};
     }
-    if (tid < 32) {
+    if (tid < QN) {
       int64_t qrow = 0, qhi = 0;
-      const bool ok = query_at(step, tid, sid, qrow, qhi);
+      const bool ok = query_at(step, tid, sida, qrow, qhi);
       // an invalid query gets lse2 = +inf, hence p = 0 (its rows are zero)
-      rs.l = ok ? lse[qhi] * kLog2e : __builtin_inff();
-      rs.dv = ok ? dvec[qhi] : 0.f;
+      st_l = ok ? lse[qhi] * kLog2e : __builtin_inff();
+      st_d = ok ? dvec[qhi] : 0.f;
     }
   };
-  auto stage_store = [&](int buf, const RowSet& rs) {
+  auto stage_store = [&](int buf) {
     bf16_t* b = lds + buf * T::BUF;
 #pragma unroll
     for (int i = 0; i < T::CH; ++i) {
       const int cidx = tid + T::NT * i;
-      const int qi = cidx % 32, cc = cidx / 32;
-      *reinterpret_cast<u32x4*>(b + qi * T::QS + cc * 8) = rs.q[i];
-      *reinterpret_cast<u32x4*>(b + T::QE + qi * T::QS + cc * 8) = rs.d[i];
-      const bf16_t* qe = reinterpret_cast<const bf16_t*>(&rs.q[i]);
-      const bf16_t* de = reinterpret_cast<const bf16_t*>(&rs.d[i]);
+      const int qi = cidx % QN, cc = cidx / QN;
+      *reinterpret_cast<u32x4*>(b + qi * T::QS + cc * 8) = qr[i];
+      *reinterpret_cast<u32x4*>(b + T::QE + qi * T::QS + cc * 8) = dr[i];
+      const bf16_t* qe = reinterpret_cast<const bf16_t*>(&qr[i]);
+      const bf16_t* de = reinterpret_cast<const bf16_t*>(&dr[i]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         b[2 * T::QE + (cc * 8 + e) * T::TS + qi] = qe[e];
         b[2 * T::QE + T::TE + (cc * 8 + e) * T::TS + qi] = de[e];
       }
     }
-    if (tid < 32) {
-      stat[buf][0][tid] = rs.l;
-      stat[buf][1][tid] = rs.dv;
+    if (tid < QN) {
+      stat[buf][0][tid] = st_l;
+      stat[buf][1][tid] = st_d;
     }
   };
 
-  // prologue: rows of steps 0 and 1 in flight, ids of step 2; tiles of step 0
+  // prologue: tiles of step 0, ids of step 1
   if (nsteps > 0) {
-    fetch_ids(0, ida, sida);
-    fetch_rows(0, ida, sida, rb);
-    if (nsteps > 1) {
-      fetch_ids(1, ida, sida);
-      fetch_rows(1, ida, sida, ra);
-    }
-    if (nsteps > 2) fetch_ids(2, ida, sida);
-    stage_store(0, rb);
+    fetch_ids(0);
+    fetch_rows(0);
+    stage_store(0);
+    if (nsteps > 1) fetch_ids(1);
   }
   __syncthreads();
   for (int it = 0; it < nsteps; ++it) {
     const int cb = it & 1;
     const bool more = it + 1 < nsteps;
-    if (it + 2 < nsteps) {
-      fetch_rows(it + 2, ida, sida, rb);
-      if (it + 3 < nsteps) fetch_ids(it + 3, ida, sida);
-    }
     const bf16_t* b = lds + cb * T::BUF;
     const bool own_step = it >= rsteps;
-    // S = Q K^T and dP = dO V^T (32 queries x the wave's 32 keys); A rows in
-    // the kperm order
-    f32x16 sacc = f32x16{}, dpacc = f32x16{};
-    {
-      const bf16_t* qa = b + kperm(n) * T::QS + 8 * hh;
-      const bf16_t* da = b + T::QE + kperm(n) * T::QS + 8 * hh;
+    // S = Q K^T and dP = dO V^T (32 queries per block x the wave's 32 keys);
+    // A rows in the kperm order
+    f32x16 sacc[NQ], dpacc[NQ];
+#pragma unroll
+    for (int qb = 0; qb < NQ; ++qb) {
+      sacc[qb] = f32x16{};
+      dpacc[qb] = f32x16{};
+    }
+#pragma unroll
+    for (int qb = 0; qb < NQ; ++qb) {
+      const bf16_t* qa = b + (32 * qb + kperm(n)) * T::QS + 8 * hh;
+      const bf16_t* da = b + T::QE + (32 * qb + kperm(n)) * T::QS + 8 * hh;
       bf16x8 fa[D / 16], fd[D / 16];
 #pragma unroll
       for (int t = 0; t < D / 16; ++t) fa[t] = ld_bf16x8(qa + 16 * t);
@@ -668,34 +667,41 @@ __global__ __launch_bounds__(64 * NW, 1) void k_bwd_dkdv(
       for (int t = 0; t < D / 16; ++t) fd[t] = ld_bf16x8(da + 16 * t);
 #pragma unroll
       for (int t = 0; t < D / 16; ++t) {
-        sacc = mfma32(fa[t], kb[t], sacc);
-        dpacc = mfma32(fd[t], vb[t], dpacc);
+        sacc[qb] = mfma32(fa[t], kb[t], sacc[qb]);
+        dpacc[qb] = mfma32(fd[t], vb[t], dpacc[qb]);
       }
     }
-    // register 4i + jj of half hh holds query acc_key(4i + jj, hh): four
-    // consecutive queries per i
+    // the next step's rows are requested while this step's math runs
+    if (more) {
+      fetch_rows(it + 1);
+      if (it + 2 < nsteps) fetch_ids(it + 2);
+    }
+    // register 4i + jj of half hh of query block qb holds query
+    // 32 qb + acc_key(4i + jj, hh): four consecutive queries per i
     int ppos0 = 0;
     if (own_step) {
       const int st = it - rsteps;
       const int hl = st / psteps_h;
-      ppos0 = p0 + (st - hl * psteps_h) * 32;
+      ppos0 = p0 + (st - hl * psteps_h) * QN;
     }
-    bf16x8 pb[2], dsb[2];
+    bf16x8 pb[2 * NQ], dsb[2 * NQ];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int qi0 = acc_key(4 * i, hh);
-      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&stat[cb][0][qi0]);
-      const f32x4 d4 = *reinterpret_cast<const f32x4*>(&stat[cb][1][qi0]);
+    for (int qb = 0; qb < NQ; ++qb)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int reg = 4 * i + jj;
-        float p = __builtin_amdgcn_exp2f(fmaf(sacc[reg], sl2, -l4[jj]));
-        if (own_step && ppos0 + qi0 + jj < key) p = 0.f;   // causal: query before the key
-        const float ds = p * (dpacc[reg] - d4[jj]);
-        pb[reg >> 3][reg & 7] = static_cast<__bf16>(p);
-        dsb[reg >> 3][reg & 7] = static_cast<__bf16>(ds);
+      for (int i = 0; i < 4; ++i) {
+        const int qi0 = 32 * qb + acc_key(4 * i, hh);
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&stat[cb][0][qi0]);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&stat[cb][1][qi0]);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int reg = 4 * i + jj;
+          float p = __builtin_amdgcn_exp2f(fmaf(sacc[qb][reg], sl2, -l4[jj]));
+          if (own_step && ppos0 + qi0 + jj < key) p = 0.f;   // causal: query before the key
+          const float ds = p * (dpacc[qb][reg] - d4[jj]);
+          pb[2 * qb + (reg >> 3)][reg & 7] = static_cast<__bf16>(p);
+          dsb[2 * qb + (reg >> 3)][reg & 7] = static_cast<__bf16>(ds);
+        }
       }
-    }
     // dV^T += dO^T P, dK^T += Q^T dS: A = the transposed tiles (rows d,
     // k-slots queries 16 c2 + 8 hh + [0, 8)), B = P / dS
     {
@@ -704,15 +710,14 @@ __global__ __launch_bounds__(64 * NW, 1) void k_bwd_dkdv(
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2) {
+        for (int c2 = 0; c2 < 2 * NQ; ++c2) {
           const bf16x8 ad = ld_bf16x8(dtp + 32 * dt * T::TS + 16 * c2);
           const bf16x8 aq = ld_bf16x8(qt + 32 * dt * T::TS + 16 * c2);
           dva[dt] = mfma32(ad, pb[c2], dva[dt]);
           dka[dt] = mfma32(aq, dsb[c2], dka[dt]);
         }
     }
-    if (more) stage_store(cb ^ 1, ra);
-    ra = rb;
+    if (more) stage_store(cb ^ 1);
     __syncthreads();
   }
   if (!key_ok) return;
@@ -821,6 +826,7 @@ hipError_t launch_bwd_dq_own(const void* q, const void* dout, const void* k, con
 }
 
 int bwd_dkdv_waves(const Dims& d) { return d.B % 128 == 0 ? 4 : 2; }
+constexpr int kDkdvNQ = 2;   // 64 queries per step
 
 hipError_t launch_bwd_dkdv(const void* q, const void* dout, const void* k, const void* v,
                            const float* lse, const float* dvec, const uint32_t* list,
@@ -835,7 +841,7 @@ hipError_t launch_bwd_dkdv(const void* q, const void* dout, const void* k, const
   const FastDiv fkp = make_fastdiv((uint32_t)(d.kp > 0 ? d.kp : 1));
   const FastDiv flq = make_fastdiv((uint32_t)d.Lq);
 #define MOBA_BKV(DV, NWV)                                                                       \
-  hipLaunchKernelGGL((k_bwd_dkdv<DV, NWV>), dim3((unsigned)grid), dim3(64 * NWV), 0, st,        \
+  hipLaunchKernelGGL((k_bwd_dkdv<DV, NWV, kDkdvNQ>), dim3((unsigned)grid), dim3(64 * NWV), 0, st, \
                      static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(dout),           \
                      static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v), lse, dvec,   \
                      list, bucket_off, static_cast<bf16_t*>(dk), static_cast<bf16_t*>(dv),      \
