@@ -597,7 +597,9 @@ moba_status full_impl(const moba_args* a) {
 struct BwdPlan {
   Plan f;                  // dims (forward_dims) and the routing-table offsets
   bool routed = false, need_tail = false;
-  size_t off_dvec = 0, off_kt = 0, off_ktail = 0, off_vtail = 0, off_dqp = 0, total = 0;
+  size_t off_dvec = 0, off_kt = 0, off_ktail = 0, off_vtail = 0, off_dqp = 0, off_kvpart = 0,
+         total = 0;
+  bool need_kvpart = false;
 };
 
 moba_status plan_backward(const moba_bwd_args* b, BwdPlan* bp) {
@@ -648,6 +650,9 @@ moba_status plan_backward(const moba_bwd_args* b, BwdPlan* bp) {
     p.off_list = take((size_t)d.slots * 4);
     bp->off_dqp = take((size_t)d.slots * d.D * 2);
   }
+  const size_t kvp = moba::bwd_dkdv_partial_floats(d);
+  bp->need_kvpart = kvp > 0;
+  if (bp->need_kvpart) bp->off_kvpart = take(kvp * 4);
   bp->total = off;
   if (b->workspace && b->workspace_bytes < bp->total)
     return fail(MOBA_ERR_INVALID_ARGUMENT, "workspace too small: %zu < %zu bytes",
@@ -718,8 +723,9 @@ moba_status backward_impl(const moba_bwd_args* b) {
                                    dqp, b->dq, d, l.st);
   });
   l.run(K_BWD_DKDV, [&] {
+    float* kvpart = bp.need_kvpart ? (float*)(w + bp.off_kvpart) : nullptr;
     return moba::launch_bwd_dkdv(b->q, b->dout, b->k, b->v, b->lse, dvec, list, boff, b->dk,
-                                 b->dv, d, l.st);
+                                 b->dv, kvpart, d, l.st);
   });
   if (l.err != hipSuccess) return hip_fail(l);
   return MOBA_OK;

@@ -483,25 +483,29 @@ struct KvTiles {
   static constexpr int CH = QN * (D / 8) / NT;  // 16-byte chunks per thread per tensor
 };
 
-// Key-stationary: workgroup (s, g, block j, chunk c) owns keys
+// Key-stationary: workgroup (s, g, block j, chunk c, segment) owns keys
 // [jB + c*32*NW, +32*NW) of the block (wave w the 32 from +32w) and loops over
-// the block's routed entries, then its own queries (one head at a time, QN
-// positions per step, causal mask), QN = 32 NQ queries per step.  grid
-// (S * Hkv * nb * ceil(B / (32 NW))), 64*NW threads.
+// its segment of the block's routed entries, then of its own queries (one
+// head at a time, QN positions per step, causal mask), QN = 32 NQ queries per
+// step.  With nseg = 1 it writes dk, dv; with more segments (small problems,
+// whose few long buckets would leave the chip idle) each segment writes fp32
+// partials [nseg][2][S, L, Hkv, D] that k_bwd_reduce_kv adds in segment order.
+// grid (S * Hkv * nb * ceil(B / (32 NW)) * nseg), 64*NW threads.
 template <int D, int NW, int NQ>
 __global__ __launch_bounds__(64 * NW, 1) void k_bwd_dkdv(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ dout,
     const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, const float* __restrict__ lse,
     const float* __restrict__ dvec, const uint32_t* __restrict__ list,
     const uint32_t* __restrict__ bucket_off, bf16_t* __restrict__ dk, bf16_t* __restrict__ dv,
-    int Lq, int L, int q_off, int H, int Hkv, int kp, int B, int nb, int nchunk, FastDiv fd_kp,
-    FastDiv fd_lq, float sl2, float scale) {
+    float* __restrict__ kvpart, int Lq, int L, int q_off, int H, int Hkv, int kp, int B, int nb,
+    int nchunk, int nseg, FastDiv fd_kp, FastDiv fd_lq, float sl2, float scale) {
   using T = KvTiles<D, NW, NQ>;
   constexpr int QN = T::QN;
   __shared__ __attribute__((aligned(16))) bf16_t lds[2 * T::BUF];
   __shared__ __attribute__((aligned(16))) float stat[2][2][QN];  // [buffer][lse2, Dv][query]
   const int KC = 32 * NW;
-  const int item = blockIdx.x;
+  const int seg = (int)(blockIdx.x % nseg);
+  const int item = (int)(blockIdx.x / nseg);
   const int c = item % nchunk;
   const int row = item / nchunk;          // bucket (s, g, j)
   const int j = row % nb;
@@ -541,14 +545,18 @@ __global__ __launch_bounds__(64 * NW, 1) void k_bwd_dkdv(
   // steps: routed entries (QN per step), then own queries (head by head, QN
   // positions per step starting at the first position that sees a key here)
   const bool routed = bucket_off != nullptr;   // no routing tables: no past blocks
-  const uint32_t rbase = routed ? bucket_off[row] : 0u;
-  const int nrt = routed ? (int)(bucket_off[row + 1] - rbase) : 0;
+  const int nrt_all = routed ? (int)(bucket_off[row + 1] - bucket_off[row]) : 0;
+  const int rlo = (int)((int64_t)nrt_all * seg / nseg);   // this segment's entries
+  const int nrt = (int)((int64_t)nrt_all * (seg + 1) / nseg) - rlo;
+  const uint32_t rbase = routed ? bucket_off[row] + (uint32_t)rlo : 0u;
   const int rsteps = (nrt + QN - 1) / QN;
   int p0 = kc0 > q_off ? kc0 : q_off;                      // first own query position
   const int pend = bend;                                   // one past the last
   const int npos = pend > p0 ? pend - p0 : 0;
   const int psteps_h = (npos + QN - 1) / QN;
-  const int nsteps = rsteps + G * psteps_h;
+  const int nown_all = G * psteps_h;                       // own steps of all segments
+  const int olo = (int)((int64_t)nown_all * seg / nseg);   // this segment's own steps
+  const int nsteps = rsteps + (int)((int64_t)nown_all * (seg + 1) / nseg) - olo;
 
   // Staging, three steps in flight: the entry ids of step it+2 (routed steps
   // read them from the list), the Q / dO rows and the two statistics of step
@@ -572,7 +580,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_bwd_dkdv(
       h = (int)(sh - (uint32_t)s * H);
       if (r < 0 || r >= Lq || h < 0 || h >= H) return false;  // never for a routed slot
     } else {
-      const int st = step - rsteps;
+      const int st = step - rsteps + olo;
       const int hl = st / psteps_h, pc = st - hl * psteps_h;
       const int p = p0 + pc * QN + qi;
       if (p >= pend) return false;
@@ -680,7 +688,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_bwd_dkdv(
     // 32 qb + acc_key(4i + jj, hh): four consecutive queries per i
     int ppos0 = 0;
     if (own_step) {
-      const int st = it - rsteps;
+      const int st = it - rsteps + olo;
       const int hl = st / psteps_h;
       ppos0 = p0 + (st - hl * psteps_h) * QN;
     }
@@ -724,6 +732,25 @@ __global__ __launch_bounds__(64 * NW, 1) void k_bwd_dkdv(
   // dK^T / dV^T accumulators: lane = key, register 4i + jj = dim
   // 32 dt + 8 i + 4 hh + jj
   const int64_t orow = ((int64_t)s * L + key) * krs + (int64_t)g * D;
+  if (nseg > 1) {
+    // one plane holds S*L*Hkv*D floats; gridDim.x = S*Hkv*nb*nchunk*nseg
+    const int64_t nseq = (int64_t)gridDim.x / ((int64_t)nseg * nchunk * nb * Hkv);
+    const int64_t plane = nseq * L * krs;
+    float* pk = kvpart + (int64_t)(2 * seg) * plane + orow;
+    float* pv = pk + plane;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d0 = 32 * dt + 8 * i + 4 * hh;
+        *reinterpret_cast<f32x4*>(pk + d0) =
+            f32x4{dka[dt][4 * i] * scale, dka[dt][4 * i + 1] * scale,
+                  dka[dt][4 * i + 2] * scale, dka[dt][4 * i + 3] * scale};
+        *reinterpret_cast<f32x4*>(pv + d0) =
+            f32x4{dva[dt][4 * i], dva[dt][4 * i + 1], dva[dt][4 * i + 2], dva[dt][4 * i + 3]};
+      }
+    return;
+  }
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -740,6 +767,27 @@ __global__ __launch_bounds__(64 * NW, 1) void k_bwd_dkdv(
       *reinterpret_cast<uint2*>(dk + orow + d0) = make_uint2(k0, k1);
       *reinterpret_cast<uint2*>(dv + orow + d0) = make_uint2(v0, v1);
     }
+}
+
+// Sum of the dk / dv segment partials in segment order (deterministic) ->
+// bf16.  n = S*L*Hkv*D elements per plane, 4 per thread.
+__global__ __launch_bounds__(256) void k_bwd_reduce_kv(const float* __restrict__ part,
+                                                       bf16_t* __restrict__ dk,
+                                                       bf16_t* __restrict__ dv, int64_t n,
+                                                       int nseg) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= n) return;
+  f32x4 ak = f32x4{0.f, 0.f, 0.f, 0.f}, av = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int sgi = 0; sgi < nseg; ++sgi) {
+    ak += *reinterpret_cast<const f32x4*>(part + (int64_t)(2 * sgi) * n + i);
+    av += *reinterpret_cast<const f32x4*>(part + (int64_t)(2 * sgi + 1) * n + i);
+  }
+  const uint32_t k0 = (uint32_t)f32_to_bf16(ak[0]) | ((uint32_t)f32_to_bf16(ak[1]) << 16);
+  const uint32_t k1 = (uint32_t)f32_to_bf16(ak[2]) | ((uint32_t)f32_to_bf16(ak[3]) << 16);
+  const uint32_t v0 = (uint32_t)f32_to_bf16(av[0]) | ((uint32_t)f32_to_bf16(av[1]) << 16);
+  const uint32_t v1 = (uint32_t)f32_to_bf16(av[2]) | ((uint32_t)f32_to_bf16(av[3]) << 16);
+  *reinterpret_cast<uint2*>(dk + i) = make_uint2(k0, k1);
+  *reinterpret_cast<uint2*>(dv + i) = make_uint2(v0, v1);
 }
 
 // ================================================================ launchers
@@ -828,14 +876,29 @@ hipError_t launch_bwd_dq_own(const void* q, const void* dout, const void* k, con
 int bwd_dkdv_waves(const Dims& d) { return d.B % 128 == 0 ? 4 : 2; }
 constexpr int kDkdvNQ = 2;   // 64 queries per step
 
+int bwd_dkdv_segments(const Dims& d) {
+  const int KC = 32 * bwd_dkdv_waves(d);
+  const int64_t wgs = (int64_t)d.S * d.Hkv * d.nb * ((d.B + KC - 1) / KC);
+  if (wgs >= 1024) return 1;
+  const int64_t sgs = (1024 + wgs - 1) / wgs;
+  return sgs > 8 ? 8 : (int)sgs;
+}
+
+size_t bwd_dkdv_partial_floats(const Dims& d) {
+  const int nseg = bwd_dkdv_segments(d);
+  return nseg > 1 ? (size_t)nseg * 2 * d.S * d.L * d.Hkv * d.D : 0;
+}
+
 hipError_t launch_bwd_dkdv(const void* q, const void* dout, const void* k, const void* v,
                            const float* lse, const float* dvec, const uint32_t* list,
-                           const uint32_t* bucket_off, void* dk, void* dv, const Dims& d,
-                           hipStream_t st) {
+                           const uint32_t* bucket_off, void* dk, void* dv, float* kvpart,
+                           const Dims& d, hipStream_t st) {
   const int NWv = bwd_dkdv_waves(d);
   const int KC = 32 * NWv;
   const int nchunk = (d.B + KC - 1) / KC;
-  const int64_t grid = (int64_t)d.S * d.Hkv * d.nb * nchunk;
+  const int nseg = bwd_dkdv_segments(d);
+  if (nseg > 1 && kvpart == nullptr) return hipErrorInvalidValue;
+  const int64_t grid = (int64_t)d.S * d.Hkv * d.nb * nchunk * nseg;
   const float sl2 = kLog2e / sqrtf((float)d.D);
   const float scale = 1.0f / sqrtf((float)d.D);
   const FastDiv fkp = make_fastdiv((uint32_t)(d.kp > 0 ? d.kp : 1));
@@ -845,14 +908,19 @@ hipError_t launch_bwd_dkdv(const void* q, const void* dout, const void* k, const
                      static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(dout),           \
                      static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v), lse, dvec,   \
                      list, bucket_off, static_cast<bf16_t*>(dk), static_cast<bf16_t*>(dv),      \
-                     (int)d.Lq, (int)d.L, (int)d.q_off, d.H, d.Hkv, d.kp, d.B, d.nb, nchunk,    \
-                     fkp, flq, sl2, scale)
+                     kvpart, (int)d.Lq, (int)d.L, (int)d.q_off, d.H, d.Hkv, d.kp, d.B, d.nb,    \
+                     nchunk, nseg, fkp, flq, sl2, scale)
   if (NWv == 4) {
     if (d.D == 128) MOBA_BKV(128, 4); else MOBA_BKV(64, 4);
   } else {
     if (d.D == 128) MOBA_BKV(128, 2); else MOBA_BKV(64, 2);
   }
 #undef MOBA_BKV
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || nseg == 1) return e;
+  const int64_t n = (int64_t)d.S * d.L * d.Hkv * d.D;   // a multiple of 4 (D is)
+  hipLaunchKernelGGL(k_bwd_reduce_kv, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, st,
+                     kvpart, static_cast<bf16_t*>(dk), static_cast<bf16_t*>(dv), n, nseg);
   return hipGetLastError();
 }
 

@@ -146,9 +146,12 @@ hipError_t launch_bwd_dq_own(const void* q, const void* dout, const void* k, con
                              const float* lse, const float* dvec, const void* dqp, void* dq,
                              const Dims& d, hipStream_t st);
 // list / bucket_off NULL: no routed entries (top-k 1 or a single block).
+// kvpart: bwd_dkdv_partial_floats(d) floats (small problems split every
+// bucket into segments whose fp32 partials are added afterwards; else NULL).
+size_t bwd_dkdv_partial_floats(const Dims& d);
 hipError_t launch_bwd_dkdv(const void* q, const void* dout, const void* k, const void* v,
                            const float* lse, const float* dvec, const uint32_t* list,
-                           const uint32_t* bucket_off, void* dk, void* dv, const Dims& d,
-                           hipStream_t st);
+                           const uint32_t* bucket_off, void* dk, void* dv, float* kvpart,
+                           const Dims& d, hipStream_t st);
 
 }  // namespace moba

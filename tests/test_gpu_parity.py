@@ -530,6 +530,9 @@ BWD = [
     moba_inputs.custom("bwd_straddle", "bf16", 1, 200, 300, 2, 1, 128, 128, 2, 106),
     moba_inputs.custom("bwd_k1", "bf16", 1, 384, None, 2, 1, 128, 64, 1, 107),
     moba_inputs.custom("bwd_single_block", "bf16", 1, 200, None, 2, 1, 64, 256, 3, 108),
+    # 8 KV heads x 64 blocks x 2 key chunks = 1024 dk/dv workgroups: one
+    # segment per bucket (the shapes above split theirs into fp32 partials)
+    moba_inputs.custom("bwd_unsplit", "bf16", 1, 16384, None, 8, 8, 64, 256, 3, 110),
 ]
 
 # Rows against the oracle that reads dO.o from the same (bf16) forward output
