@@ -12,7 +12,7 @@ region.  Prints one JSON line.
                up to i).
   speedup      time of the library's own full causal attention at the same
                shape / time of the MoBA forward.
-  also         the backward (moba_backward_ex) at 32K and 128K in effective
+  also         the backward (moba_backward_ex) at 32K, 128K and 1M in effective
                TFLOP/s (five products per selected pair, 2.5 x the forward's
                FLOPs) with the dk/dv kernel's roofline; the same figures as
                above at the 128K Llama-layer prefill and the
@@ -391,7 +391,7 @@ def main():
     ap.add_argument("--skip-10m", action="store_true",
                     help="skip the 10M-token single-head prefill")
     ap.add_argument("--skip-backward", action="store_true",
-                    help="skip the backward (32K and 128K)")
+                    help="skip the backward (32K, 128K and 1M)")
     ap.add_argument("--skip-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--workload", default=None,
@@ -468,6 +468,9 @@ def main():
             also["llama8b_128k_backward"] = run_backward(
                 moba, moba_inputs.WORKLOADS["llama8b_128k"], min(args.steps, 3),
                 min(args.warmup, 1))
+        if not args.skip_1m:
+            also["prefill_1m_backward"] = run_backward(
+                moba, moba_inputs.WORKLOADS["prefill_1m"], 1, 1)
     if not args.skip_decode:
         also["decode_1m"] = run_decode(moba, moba_inputs.WORKLOADS["decode_1m"], args.steps,
                                        args.warmup)

@@ -282,14 +282,16 @@ def moba_lse_reference(q, k, block_size, sel, q_offset=None, scale=None):
 #   dq = c sum_t ds_t k_t,  dk_t += c ds_t q.
 # --------------------------------------------------------------------------
 def moba_backward_reference(q, k, v, dout, block_size, sel, q_offset=None, scale=None,
-                            out=None):
+                            out=None, pairs=None):
     """Returns ``(dq [Lq, H, D], dk [L, Hkv, D], dv [L, Hkv, D])`` for the
     selection ``sel [H, Lq, topk]`` (held fixed).  GQA: a KV head's gradients
     sum over the query heads of its group (R8).
 
     ``out`` (optional, ``[Lq, H, D]``): a stored forward output that the term
     ``dO . o`` is to read instead of the exact output, as an algorithm that is
-    handed the forward's (rounded) output computes it; None: exact."""
+    handed the forward's (rounded) output computes it; None: exact.
+    ``pairs`` (optional iterable of ``(h, r)``): only these query rows are
+    processed (their dq rows; dk and dv then hold only their contributions)."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -304,21 +306,22 @@ def moba_backward_reference(q, k, v, dout, block_size, sel, q_offset=None, scale
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
-    for h in range(h_n):
+    if pairs is None:
+        pairs = [(h, r) for h in range(h_n) for r in range(lq)]
+    for h, r in pairs:
         g = h // group
-        for r in range(lq):
-            keys = key_set(sel[h, r], q_offset + r, block_size, L)
-            kk, vv = k[keys, g, :], v[keys, g, :]
-            z = (kk @ q[r, h]) * scale
-            p = np.exp(z - z.max())
-            p /= p.sum()
-            o = p @ vv if out is None else np.asarray(out[r, h], dtype=np.float64)
-            do = dout[r, h]
-            dp = vv @ do
-            ds = p * (dp - do @ o)
-            dq[r, h] = scale * (ds @ kk)
-            dk[keys, g, :] += scale * np.outer(ds, q[r, h])
-            dv[keys, g, :] += np.outer(p, do)
+        keys = key_set(sel[h, r], q_offset + r, block_size, L)
+        kk, vv = k[keys, g, :], v[keys, g, :]
+        z = (kk @ q[r, h]) * scale
+        p = np.exp(z - z.max())
+        p /= p.sum()
+        o = p @ vv if out is None else np.asarray(out[r, h], dtype=np.float64)
+        do = dout[r, h]
+        dp = vv @ do
+        ds = p * (dp - do @ o)
+        dq[r, h] = scale * (ds @ kk)
+        dk[keys, g, :] += scale * np.outer(ds, q[r, h])
+        dv[keys, g, :] += np.outer(p, do)
     return dq, dk, dv
 
 

@@ -478,3 +478,21 @@ def test_backward_with_a_given_output_differs_by_the_closed_form():
     np.testing.assert_allclose(dq2, want_dq, atol=1e-12, rtol=0)
     np.testing.assert_allclose(dk2, want_dk, atol=1e-12, rtol=0)
     np.testing.assert_allclose(dv2, base[2], atol=0, rtol=0)
+
+
+def test_backward_restricted_to_rows_adds_up():
+    """``pairs`` restricts the backward to some query rows: those rows' dq
+    equal the full computation's, and dk, dv of two disjoint row sets add up
+    to the full ones (each query contributes independently)."""
+    L, B, topk, H, Hkv, D = 40, 8, 3, 2, 1, 8
+    q, k, v = _case(69, L, H, Hkv, D, B)
+    dout = np.random.default_rng(12).standard_normal(q.shape)
+    sel, _ = O.select_all(q, O.block_mean(k, B), B, topk)
+    full = O.moba_backward_reference(q, k, v, dout, B, sel)
+    every = [(h, r) for h in range(H) for r in range(L)]
+    a = O.moba_backward_reference(q, k, v, dout, B, sel, pairs=every[::2])
+    b = O.moba_backward_reference(q, k, v, dout, B, sel, pairs=every[1::2])
+    for h, r in every[::2]:
+        np.testing.assert_array_equal(a[0][r, h], full[0][r, h])
+    np.testing.assert_allclose(a[1] + b[1], full[1], atol=1e-12, rtol=0)
+    np.testing.assert_allclose(a[2] + b[2], full[2], atol=1e-12, rtol=0)
