@@ -43,6 +43,25 @@ def _compile(src: str) -> str:
     return obj
 
 
+CONSUMER_PATH = os.path.join(PKG, "c_abi_consumer")
+
+
+def build_consumer() -> str:
+    """Compile the plain-C consumer of the ABI (csrc/c_abi_consumer.c) with gcc
+    against libmoba.so and the HIP C runtime API."""
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    cmd = [shutil.which("gcc") or "gcc", "-O2", "-std=c11", "-Wall", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(rocm, "include"), "-I", INCLUDE,
+           os.path.join(CSRC, "c_abi_consumer.c"), "-L", PKG, "-lmoba",
+           "-L", os.path.join(rocm, "lib"), "-lamdhip64", "-lm",
+           "-Wl,-rpath,$ORIGIN", "-Wl,-rpath," + os.path.join(rocm, "lib"),
+           "-o", CONSUMER_PATH]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"gcc failed for c_abi_consumer.c:\n{res.stdout}\n{res.stderr}")
+    return CONSUMER_PATH
+
+
 def build_library(jobs: int | None = None) -> str:
     """Compile every source and link libmoba.so next to this file."""
     os.makedirs(BUILD_DIR, exist_ok=True)

@@ -176,3 +176,19 @@ def test_version_one_struct_is_accepted():
     a.struct_size = v1 + 4
     assert moba._lib.moba_workspace_size(ctypes.byref(a)) == 0
     assert "struct_size" in moba.moba_last_error()
+
+
+def test_plain_c_consumer_host_checks():
+    """A C program built with gcc against include/moba.h and libmoba.so (no
+    Python, no C++) checks the version, status strings and argument
+    validation without a GPU."""
+    import subprocess
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "moba_build", os.path.join(ROOT, "block_sparse_attention_gate_amd", "build.py"))
+    b = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(b)
+    exe = b.CONSUMER_PATH if os.path.exists(b.CONSUMER_PATH) else b.build_consumer()
+    res = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    print(res.stdout)
+    assert res.returncode == 0 and res.stdout.strip().endswith("passed"), res.stdout + res.stderr

@@ -663,3 +663,17 @@ def test_backward_128k_sampled():
         exe.append(np.linalg.norm(got - exact) / np.linalg.norm(exact))
     print(f"  dq worst row rel RMS {max(errs):.2e}; vs exact over the sample {max(exe):.2e}")
     assert max(errs) <= BWD_RELRMS and max(exe) <= BWD_EXACT_REL
+
+
+def test_plain_c_consumer_on_the_gpu():
+    """The C consumer (built by build() next to the library) runs moba_forward
+    and moba_full_attention on buffers it allocates with the HIP C API; with
+    one common V row every output row must equal it."""
+    import os
+    import subprocess
+    exe = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                       "block_sparse_attention_gate_amd", "c_abi_consumer")
+    assert os.path.exists(exe), "build the library first (it builds the consumer too)"
+    res = subprocess.run([exe, "--gpu"], capture_output=True, text=True, timeout=120)
+    print(res.stdout)
+    assert res.returncode == 0 and res.stdout.strip().endswith("passed"), res.stdout + res.stderr
