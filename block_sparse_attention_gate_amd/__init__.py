@@ -15,6 +15,7 @@ from __future__ import annotations
 import ctypes
 import os
 
+import numpy as np
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -92,6 +93,36 @@ class MobaBwdArgs(ctypes.Structure):
     ]
 
 
+class MobaVarlenArgs(ctypes.Structure):
+    """Mirror of ``moba_varlen_args`` in include/moba.h."""
+
+    _fields_ = [
+        ("struct_size", ctypes.c_size_t),
+        ("q", ctypes.c_void_p),
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("out", ctypes.c_void_p),
+        ("dout", ctypes.c_void_p),
+        ("dq", ctypes.c_void_p),
+        ("dk", ctypes.c_void_p),
+        ("dv", ctypes.c_void_p),
+        ("cu_seqlens_q", ctypes.c_void_p),
+        ("cu_seqlens_k", ctypes.c_void_p),
+        ("sel", ctypes.c_void_p),
+        ("lse", ctypes.c_void_p),
+        ("batch", ctypes.c_int32),
+        ("n_heads", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("topk", ctypes.c_int32),
+        ("dtype", ctypes.c_int),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+        ("stream", ctypes.c_void_p),
+    ]
+
+
 _P = ctypes.c_void_p
 _I32, _I64 = ctypes.c_int32, ctypes.c_int64
 _ST = ctypes.c_int
@@ -104,6 +135,9 @@ _SIGNATURES = {
     "moba_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(MobaArgs)]),
     "moba_full_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(MobaArgs)]),
     "moba_backward_ex": (_ST, [ctypes.POINTER(MobaBwdArgs)]),
+    "moba_forward_varlen": (_ST, [ctypes.POINTER(MobaVarlenArgs)]),
+    "moba_backward_varlen": (_ST, [ctypes.POINTER(MobaVarlenArgs)]),
+    "moba_varlen_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(MobaVarlenArgs), _I32]),
     "moba_backward_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(MobaBwdArgs)]),
     "moba_block_mean": (_ST, [_P, _I32, _I64, _I32, _I32, _I32, _P, ctypes.c_int, _P]),
     "moba_block_mean_update": (_ST, [_P, _I32, _I64, _I32, _I32, _I32, _I32, _P, ctypes.c_int,
@@ -373,6 +407,109 @@ def moba_backward_workspace_size(q, k, v, block_size, topk) -> int:
     a.q_len, a.kv_len = Lq, L
     a.dtype = _dtype_code(q)
     return int(_lib.moba_backward_workspace_size(ctypes.byref(a)))
+
+
+def _cu_array(cu, batch=None):
+    a = np.ascontiguousarray(np.asarray(cu.cpu() if hasattr(cu, "cpu") else cu, dtype=np.int64))
+    if a.ndim != 1 or a.size < 2 or (batch is not None and a.size != batch + 1):
+        raise ValueError("cu_seqlens must be a 1-D sequence of batch + 1 offsets")
+    return a
+
+
+def _varlen_args(q, k, v, out, cu_q, cu_k, block_size, topk, sel=None, lse=None):
+    for name, t, ref in (("q", q, q), ("out", out, q)):
+        _dev_tensor(t, name, q.dtype)
+        if t.dim() != 3 or tuple(t.shape) != tuple(ref.shape):
+            raise ValueError(f"{name} must be [total_q, n_heads, head_dim]")
+    for name, t in (("k", k), ("v", v)):
+        _dev_tensor(t, name, q.dtype)
+        if t.dim() != 3 or tuple(t.shape) != tuple(k.shape):
+            raise ValueError(f"{name} must be [total_k, n_kv_heads, head_dim]")
+    Tq, H, D = q.shape
+    Tk, Hkv, _ = k.shape
+    if cu_q[-1] != Tq or cu_k[-1] != Tk or cu_q.size != cu_k.size:
+        raise ValueError("cu_seqlens must end at the packed lengths and have equal sizes")
+    a = MobaVarlenArgs()
+    a.struct_size = ctypes.sizeof(MobaVarlenArgs)
+    a.q, a.k, a.v, a.out = q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr()
+    a.cu_seqlens_q = cu_q.ctypes.data
+    a.cu_seqlens_k = cu_k.ctypes.data
+    if sel is not None:
+        _dev_tensor(sel, "sel", torch.int32)
+        if sel.numel() != H * Tq * int(topk):
+            raise ValueError(f"sel must hold n_heads * total_q * topk = {H * Tq * int(topk)} int32")
+        a.sel = sel.data_ptr()
+    if lse is not None:
+        _dev_tensor(lse, "lse", torch.float32)
+        if lse.numel() != H * Tq:
+            raise ValueError(f"lse must hold n_heads * total_q = {H * Tq} float32")
+        a.lse = lse.data_ptr()
+    a.batch = cu_q.size - 1
+    a.n_heads, a.n_kv_heads, a.head_dim = H, Hkv, D
+    a.block_size, a.topk = int(block_size), int(topk)
+    a.dtype = _dtype_code(q)
+    a.stream = _stream_ptr(q.device)
+    return a
+
+
+def _varlen_run(fn, a, backward, device, workspace, what):
+    need = int(_lib.moba_varlen_workspace_size(ctypes.byref(a), int(backward)))
+    if need == 0 and _lib.moba_last_error():
+        _check(fn(ctypes.byref(a)), what)  # raises the error
+    ws = _workspace_tensor(need, device, workspace)
+    if ws is not None:
+        a.workspace = ws.data_ptr()
+        a.workspace_bytes = ws.numel() * ws.element_size()
+    _check(fn(ctypes.byref(a)), what)
+
+
+def moba_forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, block_size, topk, *, out=None,
+                        return_selection=False, return_lse=False, workspace=None):
+    """Packed variable-length MoBA forward (C ``moba_forward_varlen``): q
+    [total_q, H, D], k and v [total_k, Hkv, D], sequence s at rows
+    cu_seqlens_q[s]:cu_seqlens_q[s+1] of q and cu_seqlens_k[s]:... of k (host
+    offsets).  The selection (flat, per sequence an [H, q_len_s, topk] block)
+    and log-sum-exp (per sequence [H, q_len_s]) come back flat when asked."""
+    cu_q = _cu_array(cu_seqlens_q)
+    cu_k = _cu_array(cu_seqlens_k, cu_q.size - 1)
+    out = torch.empty_like(q) if out is None else out
+    H = q.shape[1]
+    sel = (torch.empty(H * q.shape[0] * int(topk), dtype=torch.int32, device=q.device)
+           if return_selection else None)
+    lse = (torch.empty(H * q.shape[0], dtype=torch.float32, device=q.device)
+           if return_lse else None)
+    a = _varlen_args(q, k, v, out, cu_q, cu_k, block_size, topk, sel, lse)
+    _varlen_run(_lib.moba_forward_varlen, a, False, q.device, workspace, "moba_forward_varlen")
+    res = [out] + ([sel] if return_selection else []) + ([lse] if return_lse else [])
+    return res[0] if len(res) == 1 else tuple(res)
+
+
+def moba_backward_varlen(q, k, v, out, dout, lse, sel, cu_seqlens_q, cu_seqlens_k, block_size,
+                         topk, *, workspace=None):
+    """Packed variable-length backward (C ``moba_backward_varlen``): the
+    forward's flat selection and log-sum-exp in, (dq, dk, dv) out."""
+    cu_q = _cu_array(cu_seqlens_q)
+    cu_k = _cu_array(cu_seqlens_k, cu_q.size - 1)
+    _dev_tensor(dout, "dout", q.dtype)
+    if tuple(dout.shape) != tuple(q.shape):
+        raise ValueError("dout must have the shape of q")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    a = _varlen_args(q, k, v, out, cu_q, cu_k, block_size, topk, sel, lse)
+    a.dout, a.dq, a.dk, a.dv = dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr()
+    _varlen_run(_lib.moba_backward_varlen, a, True, q.device, workspace, "moba_backward_varlen")
+    return dq, dk, dv
+
+
+def moba_varlen_workspace_size(q, k, v, cu_seqlens_q, cu_seqlens_k, block_size, topk,
+                               backward=False) -> int:
+    """Workspace bytes of moba_forward_varlen (or moba_backward_varlen)."""
+    cu_q = _cu_array(cu_seqlens_q)
+    cu_k = _cu_array(cu_seqlens_k, cu_q.size - 1)
+    a = _varlen_args(q, k, v, q, cu_q, cu_k, block_size, topk)
+    if backward:
+        fake = 1 << 40   # only checked for NULL, never dereferenced by a size query
+        a.dout = a.dq = a.dk = a.dv = a.sel = a.lse = fake
+    return int(_lib.moba_varlen_workspace_size(ctypes.byref(a), int(bool(backward))))
 
 
 def moba_full_attention_ex(q, k, v, *, out=None, workspace=None):

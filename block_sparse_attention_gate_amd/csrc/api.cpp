@@ -731,6 +731,140 @@ moba_status backward_impl(const moba_bwd_args* b) {
   return MOBA_OK;
 }
 
+// ------------------------------------------------------------------ varlen
+// One batch-1 call per sequence on slices of the packed tensors, sharing one
+// workspace sized for the largest sequence (calls are ordered on the stream).
+struct VarlenPlan {
+  std::vector<moba_args> fwd;        // per sequence with queries (forward)
+  std::vector<moba_bwd_args> bwd;    // per sequence with queries (backward)
+  std::vector<std::pair<int64_t, int64_t>> zero_kv;  // backward: (first key, keys) to zero
+  size_t ws = 0;
+};
+
+moba_status plan_varlen(const moba_varlen_args* a, bool backward, VarlenPlan* vp) {
+  if (!a) return fail(MOBA_ERR_INVALID_ARGUMENT, "args is NULL");
+  if (a->struct_size != sizeof(moba_varlen_args))
+    return fail(MOBA_ERR_INVALID_ARGUMENT, "struct_size %zu != sizeof(moba_varlen_args) %zu",
+                a->struct_size, sizeof(moba_varlen_args));
+  if (!a->q || !a->k || !a->v || !a->out)
+    return fail(MOBA_ERR_INVALID_ARGUMENT, "q, k, v and out must be non-NULL");
+  if (backward && (!a->dout || !a->dq || !a->dk || !a->dv || !a->sel || !a->lse))
+    return fail(MOBA_ERR_INVALID_ARGUMENT, "dout, dq, dk, dv, sel and lse must be non-NULL");
+  if (!a->cu_seqlens_q || !a->cu_seqlens_k)
+    return fail(MOBA_ERR_INVALID_ARGUMENT, "cu_seqlens_q and cu_seqlens_k must be non-NULL");
+  if (a->batch < 1) return fail(MOBA_ERR_INVALID_ARGUMENT, "batch must be >= 1");
+  if (a->n_heads < 1 || a->n_kv_heads < 1 || a->head_dim < 1 || a->topk < 1)
+    return fail(MOBA_ERR_INVALID_ARGUMENT, "sizes must be >= 1");
+  if (a->dtype != MOBA_DTYPE_F32 && a->dtype != MOBA_DTYPE_BF16)
+    return fail(MOBA_ERR_UNSUPPORTED, "unknown dtype %d", (int)a->dtype);
+  const int64_t esz = a->dtype == MOBA_DTYPE_BF16 ? 2 : 4;
+  const int64_t qrow = (int64_t)a->n_heads * a->head_dim * esz;     // bytes per query row
+  const int64_t krow = (int64_t)a->n_kv_heads * a->head_dim * esz;  // bytes per key row
+  const int64_t* cq = a->cu_seqlens_q;
+  const int64_t* ck = a->cu_seqlens_k;
+  if (cq[0] != 0 || ck[0] != 0)
+    return fail(MOBA_ERR_INVALID_ARGUMENT, "cu_seqlens must start at 0");
+  for (int32_t s = 0; s < a->batch; ++s) {
+    const int64_t qn = cq[s + 1] - cq[s], kn = ck[s + 1] - ck[s];
+    if (qn < 0 || kn < 0)
+      return fail(MOBA_ERR_INVALID_ARGUMENT, "cu_seqlens decrease at sequence %d", s);
+    if (qn > kn)
+      return fail(MOBA_ERR_INVALID_ARGUMENT, "sequence %d: q_len %lld > kv_len %lld", s,
+                  (long long)qn, (long long)kn);
+    if (qn == 0) {
+      if (backward && kn > 0) vp->zero_kv.push_back({ck[s], kn});
+      continue;
+    }
+    const char* q = (const char*)a->q + cq[s] * qrow;
+    const char* k = (const char*)a->k + ck[s] * krow;
+    const char* v = (const char*)a->v + ck[s] * krow;
+    char* out = (char*)a->out + cq[s] * qrow;
+    int32_t* sel = a->sel ? a->sel + (int64_t)a->n_heads * cq[s] * a->topk : nullptr;
+    float* lse = a->lse ? a->lse + (int64_t)a->n_heads * cq[s] : nullptr;
+    moba_status st;
+    size_t need = 0;
+    if (!backward) {
+      moba_args f;
+      std::memset(&f, 0, sizeof(f));
+      f.struct_size = sizeof(f);
+      f.q = q; f.k = k; f.v = v; f.out = out; f.sel_out = sel; f.lse_out = lse;
+      f.batch = 1; f.n_heads = a->n_heads; f.n_kv_heads = a->n_kv_heads;
+      f.head_dim = a->head_dim; f.block_size = a->block_size; f.topk = a->topk;
+      f.q_len = qn; f.kv_len = kn; f.dtype = a->dtype; f.stream = a->stream;
+      Plan p;
+      st = plan_forward(&f, &p);
+      need = p.total;
+      vp->fwd.push_back(f);
+    } else {
+      moba_bwd_args b;
+      std::memset(&b, 0, sizeof(b));
+      b.struct_size = sizeof(b);
+      b.q = q; b.k = k; b.v = v; b.out = out;
+      b.dout = (const char*)a->dout + cq[s] * qrow;
+      b.lse = lse; b.sel = sel;
+      b.dq = (char*)a->dq + cq[s] * qrow;
+      b.dk = (char*)a->dk + ck[s] * krow;
+      b.dv = (char*)a->dv + ck[s] * krow;
+      b.batch = 1; b.n_heads = a->n_heads; b.n_kv_heads = a->n_kv_heads;
+      b.head_dim = a->head_dim; b.block_size = a->block_size; b.topk = a->topk;
+      b.q_len = qn; b.kv_len = kn; b.dtype = a->dtype; b.stream = a->stream;
+      BwdPlan bp;
+      st = plan_backward(&b, &bp);
+      need = bp.total;
+      vp->bwd.push_back(b);
+    }
+    if (st != MOBA_OK) {
+      const std::string why = g_last_error;
+      return fail(st, "sequence %d: %s", s, why.c_str());
+    }
+    if (need > vp->ws) vp->ws = need;
+  }
+  if (a->workspace && a->workspace_bytes < vp->ws)
+    return fail(MOBA_ERR_INVALID_ARGUMENT, "workspace too small: %zu < %zu bytes",
+                a->workspace_bytes, vp->ws);
+  return MOBA_OK;
+}
+
+moba_status varlen_impl(const moba_varlen_args* a, bool backward) {
+  VarlenPlan vp;
+  moba_status st = plan_varlen(a, backward, &vp);
+  if (st != MOBA_OK) return st;
+  Workspace ws;
+  ws.st = (hipStream_t)a->stream;
+  if (a->workspace) {
+    ws.base = (char*)a->workspace;
+  } else if (vp.ws) {
+    void* ptr = nullptr;
+    const hipError_t e = hipMallocAsync(&ptr, vp.ws, ws.st);
+    if (e != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      return fail(MOBA_ERR_OUT_OF_MEMORY, "hipMallocAsync(%zu bytes) failed: %s", vp.ws,
+                  hipGetErrorString(e));
+    }
+    ws.base = (char*)ptr;
+    ws.owned = true;
+  }
+  for (auto& f : vp.fwd) {
+    f.workspace = ws.base;
+    f.workspace_bytes = vp.ws;
+    st = forward_impl(&f);
+    if (st != MOBA_OK) return st;
+  }
+  for (auto& b : vp.bwd) {
+    b.workspace = ws.base;
+    b.workspace_bytes = vp.ws;
+    st = backward_impl(&b);
+    if (st != MOBA_OK) return st;
+  }
+  const int64_t krow = (int64_t)a->n_kv_heads * a->head_dim * (a->dtype == MOBA_DTYPE_BF16 ? 2 : 4);
+  for (const auto& z : vp.zero_kv) {
+    hipError_t e = hipMemsetAsync((char*)a->dk + z.first * krow, 0, z.second * krow, ws.st);
+    if (e == hipSuccess) e = hipMemsetAsync((char*)a->dv + z.first * krow, 0, z.second * krow, ws.st);
+    if (e != hipSuccess) return fail(MOBA_ERR_HIP, "hipMemsetAsync failed: %s", hipGetErrorString(e));
+  }
+  return MOBA_OK;
+}
+
 moba_args simple_args(const void* q, const void* k, const void* v, int64_t seq_len,
                       int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, int32_t block_size,
                       int32_t topk, void* out, moba_dtype dtype, void* stream) {
@@ -837,6 +971,37 @@ size_t moba_backward_workspace_size(const moba_bwd_args* a) {
     BwdPlan bp;
     if (plan_backward(&b, &bp) != MOBA_OK) return 0;
     return bp.total;
+  } catch (...) {
+    return 0;
+  }
+}
+
+moba_status moba_forward_varlen(const moba_varlen_args* a) {
+  return guarded([&] { return varlen_impl(a, false); });
+}
+
+moba_status moba_backward_varlen(const moba_varlen_args* a) {
+  return guarded([&] { return varlen_impl(a, true); });
+}
+
+size_t moba_varlen_workspace_size(const moba_varlen_args* a, int32_t backward) {
+  g_last_error.clear();
+  try {
+    if (!a) {
+      fail(MOBA_ERR_INVALID_ARGUMENT, "args is NULL");
+      return 0;
+    }
+    if (a->struct_size != sizeof(moba_varlen_args)) {
+      fail(MOBA_ERR_INVALID_ARGUMENT, "struct_size %zu != sizeof(moba_varlen_args) %zu",
+           a->struct_size, sizeof(moba_varlen_args));
+      return 0;
+    }
+    moba_varlen_args b = *a;
+    b.workspace = nullptr;
+    b.workspace_bytes = 0;
+    VarlenPlan vp;
+    if (plan_varlen(&b, backward != 0, &vp) != MOBA_OK) return 0;
+    return vp.ws;
   } catch (...) {
     return 0;
   }

@@ -70,7 +70,8 @@ extern "C" {
 #endif
 
 /* 2: moba_args gained lse_out (a version-1 struct, without it, is still
- * accepted); moba_backward_ex and moba_block_mean_update were added. */
+ * accepted); moba_backward_ex, moba_block_mean_update and the packed
+ * variable-length calls were added. */
 #define MOBA_ABI_VERSION 2
 
 typedef enum { MOBA_DTYPE_F32 = 0, MOBA_DTYPE_BF16 = 1 } moba_dtype;
@@ -180,6 +181,53 @@ typedef struct moba_bwd_args {
 
 moba_status moba_backward_ex(const moba_bwd_args* a);
 size_t moba_backward_workspace_size(const moba_bwd_args* a);
+
+/*
+ * Packed variable-length batches: `batch` sequences laid one after the other
+ * along the token axis, q and out [total_q, n_heads, head_dim], k and v
+ * [total_k, n_kv_heads, head_dim]; sequence s owns query rows
+ * cu_seqlens_q[s] .. cu_seqlens_q[s+1]-1 and keys cu_seqlens_k[s] ..
+ * cu_seqlens_k[s+1]-1 (HOST arrays of batch + 1 int64 entries starting at 0,
+ * non-decreasing; a sequence's query count may not exceed its key count, and
+ * its queries sit at the end of its keys, as in moba_forward_ex).  Lengths
+ * may be anything, including zero (the sequence is skipped).  Each sequence
+ * is computed as its own moba_forward_ex / moba_backward_ex call on the
+ * caller's stream (no interaction between sequences); one workspace sized for
+ * the largest sequence serves all of them.  sel_out / lse_out (and sel / lse
+ * of the backward) hold per sequence a [n_heads, q_len_s, topk] /
+ * [n_heads, q_len_s] block, the blocks one after the other in sequence order
+ * (sequence s's block starts at element n_heads * cu_seqlens_q[s] * topk of
+ * sel and n_heads * cu_seqlens_q[s] of lse).  Every sequence is checked
+ * before anything is enqueued; a HIP failure part-way returns MOBA_ERR_HIP
+ * with the earlier sequences' work already enqueued.  The backward writes
+ * zero dk, dv for the keys of a sequence that has no queries.
+ */
+typedef struct moba_varlen_args {
+  size_t struct_size;          /* = sizeof(moba_varlen_args) */
+  const void* q;               /* [total_q, n_heads, head_dim] */
+  const void* k;               /* [total_k, n_kv_heads, head_dim] */
+  const void* v;
+  void* out;                   /* forward: written; backward: the forward output (read) */
+  const void* dout;            /* backward only: upstream gradient, layout of q */
+  void* dq;                    /* backward only: layout of q */
+  void* dk;                    /* backward only: layout of k */
+  void* dv;                    /* backward only: layout of v */
+  const int64_t* cu_seqlens_q; /* host, batch + 1 */
+  const int64_t* cu_seqlens_k; /* host, batch + 1 */
+  int32_t* sel;                /* forward: nullable output; backward: input (required) */
+  float* lse;                  /* forward: nullable output; backward: input (required) */
+  int32_t batch;
+  int32_t n_heads, n_kv_heads, head_dim, block_size, topk;
+  moba_dtype dtype;
+  void* workspace;             /* nullable, >= moba_varlen_workspace_size bytes */
+  size_t workspace_bytes;
+  void* stream;                /* hipStream_t, NULL = default stream */
+} moba_varlen_args;
+
+moba_status moba_forward_varlen(const moba_varlen_args* a);
+moba_status moba_backward_varlen(const moba_varlen_args* a);
+/* backward = 0: workspace of moba_forward_varlen; 1: of moba_backward_varlen. */
+size_t moba_varlen_workspace_size(const moba_varlen_args* a, int32_t backward);
 
 /* Workspace bytes moba_forward_ex / moba_full_attention_ex need for `a`
  * (0 for an invalid argument set; read moba_last_error()). */

@@ -192,3 +192,43 @@ def test_plain_c_consumer_host_checks():
     res = subprocess.run([exe], capture_output=True, text=True, timeout=60)
     print(res.stdout)
     assert res.returncode == 0 and res.stdout.strip().endswith("passed"), res.stdout + res.stderr
+
+
+def _varlen(cu_q, cu_k, **kw):
+    import block_sparse_attention_gate_amd as moba
+    import numpy as np
+    a = moba.MobaVarlenArgs()
+    a.struct_size = ctypes.sizeof(moba.MobaVarlenArgs)
+    fake = 1 << 40   # never dereferenced: sizes only
+    a.q = a.k = a.v = a.out = fake
+    cq = np.asarray(cu_q, dtype=np.int64)
+    ck = np.asarray(cu_k, dtype=np.int64)
+    a.cu_seqlens_q, a.cu_seqlens_k = cq.ctypes.data, ck.ctypes.data
+    a.batch = len(cu_q) - 1
+    a.n_heads, a.n_kv_heads, a.head_dim, a.block_size, a.topk = 4, 2, 128, 128, 3
+    a.dtype = moba.MOBA_DTYPE_BF16
+    for k_, v_ in kw.items():
+        setattr(a, k_, v_)
+    return a, (cq, ck)
+
+
+def test_varlen_validation_before_any_launch():
+    """Packed batches: every sequence is planned up front; lengths may be zero;
+    decreasing offsets, a sequence with more queries than keys, or a bad
+    sequence (head_dim) are refused with the sequence named."""
+    import block_sparse_attention_gate_amd as moba
+    a, keep = _varlen([0, 300, 300, 377, 1377], [0, 300, 300, 1534, 2534])
+    assert moba._lib.moba_varlen_workspace_size(ctypes.byref(a), 0) > 0, moba.moba_last_error()
+    a.dout = a.dq = a.dk = a.dv = a.sel = a.lse = 1 << 40
+    assert moba._lib.moba_varlen_workspace_size(ctypes.byref(a), 1) > 0, moba.moba_last_error()
+    a, keep = _varlen([0, 300, 200], [0, 300, 400])
+    assert moba._lib.moba_varlen_workspace_size(ctypes.byref(a), 0) == 0
+    assert "decrease" in moba.moba_last_error()
+    a, keep = _varlen([0, 300, 700], [0, 300, 500])
+    assert moba._lib.moba_varlen_workspace_size(ctypes.byref(a), 0) == 0
+    assert "sequence 1" in moba.moba_last_error()
+    a, keep = _varlen([0, 64], [0, 64], head_dim=96)
+    assert moba._lib.moba_varlen_workspace_size(ctypes.byref(a), 0) == 0
+    assert "sequence 0" in moba.moba_last_error() and "head_dim" in moba.moba_last_error()
+    a, keep = _varlen([0, 64], [0, 64])   # backward without its inputs
+    assert moba._lib.moba_backward_varlen(ctypes.byref(a)) == moba.MOBA_ERR_INVALID_ARGUMENT

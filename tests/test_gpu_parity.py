@@ -677,3 +677,92 @@ def test_plain_c_consumer_on_the_gpu():
     res = subprocess.run([exe, "--gpu"], capture_output=True, text=True, timeout=120)
     print(res.stdout)
     assert res.returncode == 0 and res.stdout.strip().endswith("passed"), res.stdout + res.stderr
+
+
+VARLEN_LENS = [(300, 300), (0, 0), (77, 1234), (1000, 1000), (0, 50), (1, 700), (129, 129)]
+
+
+def _packed(dtype, seed, H=4, Hkv=2, D=128, B=128):
+    """Packed q/k/v of the VARLEN_LENS sequences, each drawn like a workload of
+    its own shape (offset per block of its keys)."""
+    qs, ks, vs = [], [], []
+    for i, (qn, kn) in enumerate(VARLEN_LENS):
+        if kn == 0:
+            continue
+        w = moba_inputs.custom("varlen", dtype, 1, max(qn, 1), kn, H, Hkv, D, B, 3, seed + i)
+        q, k, v = moba_inputs.make_inputs(w, device=DEV)
+        q4 = q.view(1, -1, H, D) if q.dim() == 3 else q
+        k4 = k.view(1, -1, Hkv, D) if k.dim() == 3 else k
+        v4 = v.view(1, -1, Hkv, D) if v.dim() == 3 else v
+        qs.append(q4[0, :qn])
+        ks.append(k4[0])
+        vs.append(v4[0])
+    cu_q = np.concatenate([[0], np.cumsum([qn for qn, _ in VARLEN_LENS])])
+    cu_k = np.concatenate([[0], np.cumsum([kn for _, kn in VARLEN_LENS])])
+    return (torch.cat(qs).contiguous(), torch.cat(ks).contiguous(), torch.cat(vs).contiguous(),
+            cu_q, cu_k)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_varlen_forward_equals_per_sequence_calls(dtype):
+    """Packed variable lengths (zero-length, keys-only, chunked, one query,
+    ragged): every sequence's output, selection and log-sum-exp are the bits
+    of its own moba_forward_ex call, and its outputs match the oracle."""
+    moba = _moba()
+    B, topk = 128, 3
+    q, k, v, cu_q, cu_k = _packed(dtype, 120)
+    out, sel, lse = moba.moba_forward_varlen(q, k, v, cu_q, cu_k, B, topk, return_selection=True,
+                                             return_lse=True)
+    torch.cuda.synchronize()
+    H = q.shape[1]
+    iv = torch.int16 if dtype == "bf16" else torch.int32
+    for s, (qn, kn) in enumerate(VARLEN_LENS):
+        if qn == 0:
+            continue
+        qs = q[cu_q[s]:cu_q[s + 1]].unsqueeze(0)
+        ks = k[cu_k[s]:cu_k[s + 1]].unsqueeze(0)
+        vs = v[cu_k[s]:cu_k[s + 1]].unsqueeze(0)
+        o1, s1, l1 = moba.moba_forward_ex(qs, ks, vs, B, topk, return_selection=True,
+                                          return_lse=True)
+        torch.cuda.synchronize()
+        o_v = out[cu_q[s]:cu_q[s + 1]]
+        s_v = sel[H * cu_q[s] * topk:H * cu_q[s + 1] * topk].view(H, qn, topk)
+        l_v = lse[H * cu_q[s]:H * cu_q[s + 1]].view(H, qn)
+        assert torch.equal(o_v.view(iv), o1[0].view(iv)), s
+        assert torch.equal(s_v, s1[0]) and torch.equal(l_v, l1[0]), s
+        qh, kh, vh = to64(qs[0]), to64(ks[0]), to64(vs[0])
+        positions = (kn - qn) + np.arange(qn)
+        sel_np = s_v.cpu().numpy()
+        check_selection(qh, positions, O.block_mean(kh, B), sel_np, B, topk)
+        check_outputs(to64(o_v), qh, positions, sel_np, B, kn, dtype,
+                      [(h, r) for h in range(H) for r in range(qn)], host_fetch(kh, vh),
+                      kh.shape[1])
+
+
+def test_varlen_backward_equals_per_sequence_calls():
+    """Packed backward: every sequence's dq, dk, dv are the bits of its own
+    moba_backward_ex call; the keys of a sequence without queries get zeros."""
+    moba = _moba()
+    B, topk = 128, 3
+    q, k, v, cu_q, cu_k = _packed("bf16", 140)
+    out, sel, lse = moba.moba_forward_varlen(q, k, v, cu_q, cu_k, B, topk, return_selection=True,
+                                             return_lse=True)
+    g = torch.Generator(device=DEV).manual_seed(141)
+    dout = torch.randn(q.shape, generator=g, device=DEV, dtype=torch.float32).to(torch.bfloat16)
+    dq, dk, dv = moba.moba_backward_varlen(q, k, v, out, dout, lse, sel, cu_q, cu_k, B, topk)
+    torch.cuda.synchronize()
+    H = q.shape[1]
+    for s, (qn, kn) in enumerate(VARLEN_LENS):
+        ksl = slice(cu_k[s], cu_k[s + 1])
+        if qn == 0:
+            assert not dk[ksl].any() and not dv[ksl].any(), s
+            continue
+        qsl = slice(cu_q[s], cu_q[s + 1])
+        r = moba.moba_backward_ex(
+            q[qsl].unsqueeze(0), k[ksl].unsqueeze(0), v[ksl].unsqueeze(0),
+            out[qsl].unsqueeze(0), dout[qsl].unsqueeze(0),
+            lse[H * cu_q[s]:H * cu_q[s + 1]].view(1, H, qn),
+            sel[H * cu_q[s] * topk:H * cu_q[s + 1] * topk].view(1, H, qn, topk), B, topk)
+        torch.cuda.synchronize()
+        for got, want in zip((dq[qsl], dk[ksl], dv[ksl]), r):
+            assert torch.equal(got.view(torch.int16), want[0].view(torch.int16)), s
