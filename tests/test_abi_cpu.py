@@ -232,3 +232,15 @@ def test_varlen_validation_before_any_launch():
     assert "sequence 0" in moba.moba_last_error() and "head_dim" in moba.moba_last_error()
     a, keep = _varlen([0, 64], [0, 64])   # backward without its inputs
     assert moba._lib.moba_backward_varlen(ctypes.byref(a)) == moba.MOBA_ERR_INVALID_ARGUMENT
+
+
+def test_block_count_limit():
+    """8192 blocks is the largest supported count (LDS histograms of the
+    routing kernels); one more is refused before any launch."""
+    import block_sparse_attention_gate_amd as moba
+    a = _args(n_heads=1, n_kv_heads=1, head_dim=64, block_size=64, topk=3,
+              q_len=8192 * 64, kv_len=8192 * 64)
+    assert moba._lib.moba_workspace_size(ctypes.byref(a)) > 0, moba.moba_last_error()
+    a.q_len = a.kv_len = 8192 * 64 + 1
+    assert moba._lib.moba_workspace_size(ctypes.byref(a)) == 0
+    assert "8192" in moba.moba_last_error()

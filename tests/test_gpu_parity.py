@@ -317,6 +317,15 @@ def test_prefill_10m_parity_sampled():
                heads_out=(0,), n_edge_rows=24)
 
 
+def test_largest_block_count_sampled():
+    """8192 blocks of 64 keys (524,288 tokens, one head, D 64, top-k 3): the
+    largest block count the library takes (routing histograms of 8192
+    buckets in LDS), sampled like the other large cases."""
+    _run_large(moba_inputs.custom("max_blocks", "bf16", 1, 8192 * 64, None, 1, 1, 64, 64, 3,
+                                  150),
+               n_sel_rows=2048, n_out_rows=32, heads_out=(0,), n_edge_rows=32)
+
+
 def test_full_attention_32k_sampled():
     """Full causal attention at the 32K single-head shape, sampled rows."""
     moba = _moba()
