@@ -95,6 +95,9 @@ SMALL = [
     moba_inputs.custom("f32_d128", "f32", 1, 512, None, 2, 1, 128, 64, 3, 27),
     moba_inputs.custom("f32_gqa", "f32", 1, 768, None, 4, 2, 64, 64, 4, 28),
     moba_inputs.WORKLOADS["tiny_f32_1k"],
+    # group sizes 3 (one head per query-kernel tile) and 16
+    moba_inputs.custom("g3", "bf16", 1, 640, None, 6, 2, 128, 64, 3, 29),
+    moba_inputs.custom("g16", "bf16", 1, 512, None, 16, 1, 64, 128, 4, 30),
 ]
 
 
@@ -354,6 +357,10 @@ DECODE = [
     moba_inputs.custom("dec_ragged_b512", "bf16", 3, 1, 8192 + 300, 8, 2, 128, 512, 5, 46),
     moba_inputs.custom("dec_ragged_b1024", "bf16", 2, 1, 16384 + 300, 2, 2, 64, 1024, 4, 47),
     moba_inputs.custom("dec_ragged_f32", "f32", 2, 1, 4096 + 1, 4, 1, 128, 512, 3, 48),
+    # group of 3 (decode kernels), group of 16 (more than the decode kernels
+    # take: the general path)
+    moba_inputs.custom("dec_g3", "bf16", 2, 1, 4096, 6, 2, 128, 512, 3, 49),
+    moba_inputs.custom("dec_g16", "bf16", 1, 1, 4096, 16, 1, 128, 512, 3, 50),
 ]
 
 
@@ -539,6 +546,7 @@ BWD = [
     moba_inputs.custom("bwd_straddle", "bf16", 1, 200, 300, 2, 1, 128, 128, 2, 106),
     moba_inputs.custom("bwd_k1", "bf16", 1, 384, None, 2, 1, 128, 64, 1, 107),
     moba_inputs.custom("bwd_single_block", "bf16", 1, 200, None, 2, 1, 64, 256, 3, 108),
+    moba_inputs.custom("bwd_g3", "bf16", 1, 600, None, 6, 2, 64, 64, 3, 111),
     # 8 KV heads x 64 blocks x 2 key chunks = 1024 dk/dv workgroups: one
     # segment per bucket (the shapes above split theirs into fp32 partials)
     moba_inputs.custom("bwd_unsplit", "bf16", 1, 16384, None, 8, 8, 64, 256, 3, 110),
