@@ -71,10 +71,8 @@ __global__ __launch_bounds__(256) void k_decode_attn(
     const int32_t* __restrict__ ublk, const uint32_t* __restrict__ umask,
     const int32_t* __restrict__ ucount, float* __restrict__ part, int64_t L, int H, int Hkv,
     int B, int umax, float scale_log2, int nsg) {
-  constexpr int VEC = 16 / sizeof(T);   // elements per 16-byte load
-  constexpr int KPT = kDecChunk / 256;  // keys per thread in the score phase
-  constexpr int DG = D / 8;             // d-groups of 8 in the P.V phase
-  constexpr int KG = 256 / DG;          // key groups in the P.V phase
+  constexpr int DG = D / 8;             // d-groups of 8 (score and P.V phases)
+  constexpr int KG = 256 / DG;          // key groups
   __shared__ float qs[GM][D];
   __shared__ float ps[GM][kDecChunk];
   __shared__ float red[KG][D];
@@ -110,26 +108,52 @@ __global__ __launch_bounds__(256) void k_decode_attn(
   }
   __syncthreads();
 
-  // scores (base 2, scale folded into q)
-  const T* kb = k + (((int64_t)s * L + key0) * Hkv + g) * D;
-  for (int kk = 0; kk < KPT; ++kk) {
-    const int key = tid + 256 * kk;
-    // a key past the end re-reads the last row and is masked below
-    const T* krow = kb + (int64_t)(key < nkey ? key : nkey - 1) * Hkv * D;
-    // the whole row is requested before any arithmetic (memory-level parallelism)
-    u32x4 raw[D / VEC];
+  // scores (base 2, scale folded into q).  Thread (key group kg, dim group
+  // dg): the DG lanes of a key group read one key row's D elements
+  // contiguously (16 bytes each; a wave load covers whole rows), multiply
+  // their 8 dims with the query slices, and add the partial dots across the
+  // group with butterfly shuffles.
+  constexpr int SU = 4;                   // keys in flight per thread
+  constexpr int LPRS = sizeof(T) == 2 ? 1 : 2;   // 16-byte loads per 8 elements
+  {
+    const int dgs = tid % DG, kgs = tid / DG;
+    const T* kb = k + (((int64_t)s * L + key0) * Hkv + g) * D + dgs * 8;
+    float qv[GM][8];
 #pragma unroll
-    for (int i = 0; i < D / VEC; ++i) raw[i] = *reinterpret_cast<const u32x4*>(krow + i * VEC);
-    for (int hl = 0; hl < G; ++hl) {       // heads that kept this block (uniform)
-      if (!((mask >> hl) & 1u)) continue;
-      float acc = 0.f;
+    for (int hl = 0; hl < GM; ++hl)
 #pragma unroll
-      for (int ci = 0; ci < D / VEC; ++ci) {
-        const T* e = reinterpret_cast<const T*>(&raw[ci]);
+      for (int i = 0; i < 8; ++i) qv[hl][i] = hl < G ? qs[hl][dgs * 8 + i] : 0.f;
+    for (int kb0 = kgs; kb0 < kDecChunk; kb0 += KG * SU) {
+      u32x4 raw[SU][LPRS];
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) acc = fmaf(load_as_f32(e + i), qs[hl][ci * VEC + i], acc);
+      for (int uu = 0; uu < SU; ++uu) {
+        const int kk = kb0 + uu * KG;     // a key past the end re-reads the last row (masked)
+        const T* krow = kb + (int64_t)(kk < nkey ? kk : nkey - 1) * Hkv * D;
+#pragma unroll
+        for (int l2 = 0; l2 < LPRS; ++l2)
+          raw[uu][l2] = *reinterpret_cast<const u32x4*>(krow + l2 * (8 / LPRS));
       }
-      ps[hl][key] = key < nkey ? acc : -__builtin_inff();
+#pragma unroll
+      for (int uu = 0; uu < SU; ++uu) {
+        const int kk = kb0 + uu * KG;
+        float x[8];
+#pragma unroll
+        for (int l2 = 0; l2 < LPRS; ++l2) {
+          const T* e = reinterpret_cast<const T*>(&raw[uu][l2]);
+#pragma unroll
+          for (int i = 0; i < 8 / LPRS; ++i) x[l2 * (8 / LPRS) + i] = load_as_f32(e + i);
+        }
+#pragma unroll
+        for (int hl = 0; hl < GM; ++hl) {
+          if (!(hl < G && ((mask >> hl) & 1u))) continue;   // uniform
+          float part = 0.f;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) part = fmaf(x[i], qv[hl][i], part);
+#pragma unroll
+          for (int o = DG / 2; o >= 1; o >>= 1) part += __shfl_xor(part, o);
+          if (dgs == 0) ps[hl][kk] = kk < nkey ? part : -__builtin_inff();
+        }
+      }
     }
   }
   __syncthreads();
