@@ -89,10 +89,15 @@ struct TileRegs {
   }
 };
 
+// Largest base-2 gap between a row's logits and its running reference max
+// before the accumulators are rescaled (probabilities stay <= 2^8, far from
+// fp32 or bf16 overflow).
+constexpr float kRescaleSlack = 8.0f;
+
 template <int D>
 struct FlashAcc {
   f32x16 o[D / 32];
-  float m;  // running max of the scaled logits (base 2)
+  float m;  // reference max of the scaled logits (base 2), within kRescaleSlack of the max
   float l;  // running sum of this lane half's probabilities
   __device__ __forceinline__ void init() {
 #pragma unroll
@@ -138,8 +143,24 @@ __device__ __forceinline__ void flash_step(const bf16_t* buf, const bf16x8 (&qf)
 #pragma unroll
     for (int reg = 0; reg < 16; ++reg) mx = fmaxf(mx, s[kt][reg]);
   mx = fmaxf(mx, half_swap(mx));
-  const float mnew = fmaxf(acc.m, mx * sl2);
-  const float mref = (mnew == -__builtin_inff()) ? 0.f : mnew;
+  // Lazy rescale: the reference max acc.m moves only when some row's tile
+  // max passes it by more than kRescaleSlack (base-2 units); otherwise the
+  // tile's probabilities are taken against the old reference and stay below
+  // 2^kRescaleSlack.  Exact up to rounding: the normaliser acc.l uses the
+  // same reference, and the output is divided by it at the end.
+  const float mt = mx * sl2;
+  if (__any(mt > acc.m + kRescaleSlack)) {
+    const float mnew = fmaxf(acc.m, mt);
+    const float alpha =
+        __builtin_amdgcn_exp2f(acc.m - ((mnew == -__builtin_inff()) ? 0.f : mnew));
+    acc.l *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int reg = 0; reg < 16; ++reg) acc.o[dt][reg] *= alpha;
+    acc.m = mnew;
+  }
+  const float mref = (acc.m == -__builtin_inff()) ? 0.f : acc.m;
   float psum = 0.f;
   bf16x8 pb[2][2];
 #pragma unroll
@@ -152,17 +173,7 @@ __device__ __forceinline__ void flash_step(const bf16_t* buf, const bf16x8 (&qf)
         psum += p;
         pb[kt][c][r] = static_cast<__bf16>(p);
       }
-  // Rescale only when some row's max moved (exact: otherwise alpha == 1).
-  if (__any(mnew > acc.m)) {
-    const float alpha = __builtin_amdgcn_exp2f(acc.m - mref);
-    acc.l *= alpha;
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-      for (int reg = 0; reg < 16; ++reg) acc.o[dt][reg] *= alpha;
-  }
   acc.l += psum;
-  acc.m = mnew;
   // O^T += V^T P^T: the D/32 accumulators are independent; interleave them.
   const bf16_t* vbase = buf + T::KE + 8 * hh + n * T::VS;
   bf16x8 va[D / 32][4];
