@@ -166,6 +166,10 @@ def kernel_breakdown(moba, fn, steps):
     return out
 
 
+# largest workspace of the timed mask-based form (its dense matrices)
+NAIVE_MAX_BYTES = 16 << 30
+
+
 def run_prefill(moba, w, steps, warmup, full_steps, full_warmup, with_full=True, cold=False):
     import torch
     import moba_inputs
@@ -211,6 +215,20 @@ def run_prefill(moba, w, steps, warmup, full_steps, full_warmup, with_full=True,
         res["speedup_vs_full"] = fms / ms
         res["full_kernels_ms"] = {k_: round(v_["avg_ms"], 4) for k_, v_ in fk.items()}
         del fout, fws
+    nbytes = moba.moba_naive_workspace_size(q, k, v, w.block_size, w.topk) if with_full else 0
+    if 0 < nbytes <= NAIVE_MAX_BYTES:
+        # the mask-based form (dense scores, block mask, softmax, P V): the
+        # baseline of the pages' efficient-vs-naive ratio at this shape
+        nout = torch.empty_like(q)
+        nws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+        nfn = lambda: moba.moba_naive_ex(q, k, v, w.block_size, w.topk, out=nout, workspace=nws)
+        log(f"[bench] {w.name}: timing the mask-based (naive) form")
+        nms, _ = time_region(nfn, min(steps, 5), min(warmup, 2))
+        nk = kernel_breakdown(moba, nfn, 1)
+        res["naive_ms"] = nms
+        res["speedup_vs_naive"] = nms / ms
+        res["naive_kernels_ms"] = {k_: round(v_["avg_ms"], 4) for k_, v_ in nk.items()}
+        del nout, nws
     res["_roofline_src"] = kern
     del q, k, v, out, ws
     torch.cuda.empty_cache()
@@ -494,6 +512,7 @@ def main():
                    "n_heads": w.n_heads, "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
                    "block_size": w.block_size, "topk": w.topk, "parallelism": "single GPU"},
         "speedup_vs_full": main_res.get("speedup_vs_full"),
+        "speedup_vs_naive": main_res.get("speedup_vs_naive"),
         "detail": main_res,
         "roofline": rl,
         "cpu_baseline": cpu,

@@ -134,6 +134,8 @@ _SIGNATURES = {
     "moba_full_attention_ex": (_ST, [ctypes.POINTER(MobaArgs)]),
     "moba_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(MobaArgs)]),
     "moba_full_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(MobaArgs)]),
+    "moba_naive_ex": (_ST, [ctypes.POINTER(MobaArgs)]),
+    "moba_naive_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(MobaArgs)]),
     "moba_backward_ex": (_ST, [ctypes.POINTER(MobaBwdArgs)]),
     "moba_forward_varlen": (_ST, [ctypes.POINTER(MobaVarlenArgs)]),
     "moba_backward_varlen": (_ST, [ctypes.POINTER(MobaVarlenArgs)]),
@@ -526,6 +528,39 @@ def moba_full_attention_ex(q, k, v, *, out=None, workspace=None):
     return out
 
 
+def moba_naive_workspace_size(q, k, v, block_size, topk, k_block_mean=None, sel_out=None) -> int:
+    """Workspace bytes moba_naive_ex needs (C ``moba_naive_workspace_size``)."""
+    a = _args(q, k, v, q, block_size, topk, k_block_mean, sel_out)
+    n = int(_lib.moba_naive_workspace_size(ctypes.byref(a)))
+    if n == 0 and _lib.moba_last_error():
+        raise ValueError(f"moba_naive_workspace_size: {_lib.moba_last_error().decode()}")
+    return n
+
+
+def moba_naive_ex(q, k, v, block_size, topk, *, out=None, k_block_mean=None, sel_out=None,
+                  return_selection=False, workspace=None):
+    """Mask-based MoBA (C ``moba_naive_ex``): the same gate and selection as
+    moba_forward_ex, then dense scores for every (query, key) pair, the block
+    mask, row softmax and P V.  A comparison baseline; bf16 only.  Returns
+    ``out`` (and the selection ``[S, H, Lq, topk]`` if asked)."""
+    out = torch.empty_like(q) if out is None else out
+    S, Lq, H, D, L, Hkv = _shape4(q, k, v)
+    if return_selection and sel_out is None:
+        sel_out = torch.empty((S, H, Lq, int(topk)), dtype=torch.int32, device=q.device)
+    a = _args(q, k, v, out, block_size, topk, k_block_mean, sel_out)
+    need = int(_lib.moba_naive_workspace_size(ctypes.byref(a)))
+    if need == 0 and _lib.moba_last_error():
+        _check(_lib.moba_naive_ex(ctypes.byref(a)), "moba_naive_ex")  # raises the error
+    ws = _workspace_tensor(need, q.device, workspace)
+    if ws is not None:
+        a.workspace = ws.data_ptr()
+        a.workspace_bytes = ws.numel() * ws.element_size()
+    _check(_lib.moba_naive_ex(ctypes.byref(a)), "moba_naive_ex")
+    if return_selection:
+        return out, (sel_out[0] if q.dim() == 3 else sel_out)
+    return out
+
+
 def moba_block_mean(k, block_size, out=None, first_block=0):
     """Block-mean keys: k [S, L, Hkv, D] (or [L, Hkv, D]) -> fp32 [S, Hkv, nb, D],
     nb = ceil(L / block_size); a partial last block is the mean of the keys it holds.
@@ -595,4 +630,5 @@ KERNEL_NAMES = ("block_mean", "transpose_v", "gate_topk", "route_count", "route_
                 "route_scan_buckets", "route_scatter", "attn_routed", "attn_own_merge",
                 "attn_full", "decode_plan", "decode_attn", "decode_merge", "merge_partials",
                 "pool_transpose", "block_mean_finalize", "route_scan_small", "bwd_dot",
-                "bwd_transform", "bwd_dq_routed", "bwd_dq_own", "bwd_dkdv")
+                "bwd_transform", "bwd_dq_routed", "bwd_dq_own", "bwd_dkdv", "naive_scores",
+                "naive_softmax", "naive_pv")

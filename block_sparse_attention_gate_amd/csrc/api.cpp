@@ -50,14 +50,15 @@ enum KernelId {
   K_BLOCK_MEAN, K_TRANSPOSE_V, K_GATE, K_RCOUNT, K_RSCAN_ROWS, K_RSCAN_BUCKETS, K_RSCATTER,
   K_ATTN_ROUTED, K_ATTN_OWN, K_ATTN_FULL, K_DEC_PLAN, K_DEC_ATTN, K_DEC_MERGE, K_MERGE,
   K_POOL_TRANSPOSE, K_MEAN_FINALIZE, K_RSCAN_SMALL, K_BWD_DOT, K_BWD_TRANSFORM,
-  K_BWD_DQ_ROUTED, K_BWD_DQ_OWN, K_BWD_DKDV, K_COUNT
+  K_BWD_DQ_ROUTED, K_BWD_DQ_OWN, K_BWD_DKDV, K_NAIVE_SCORES, K_NAIVE_SOFTMAX, K_NAIVE_PV,
+  K_COUNT
 };
 const char* const kKernelNames[K_COUNT] = {
     "block_mean", "transpose_v", "gate_topk", "route_count", "route_scan_rows",
     "route_scan_buckets", "route_scatter", "attn_routed", "attn_own_merge", "attn_full",
     "decode_plan", "decode_attn", "decode_merge", "merge_partials", "pool_transpose",
     "block_mean_finalize", "route_scan_small", "bwd_dot", "bwd_transform", "bwd_dq_routed",
-    "bwd_dq_own", "bwd_dkdv"};
+    "bwd_dq_own", "bwd_dkdv", "naive_scores", "naive_softmax", "naive_pv"};
 
 struct ProfRecord {
   int id;
@@ -150,6 +151,7 @@ struct Plan {
   size_t off_ublk = 0, off_umask = 0, off_ucount = 0, off_part = 0, off_bmpart = 0;
   size_t off_own_o = 0, off_own_lse = 0;
   size_t off_ktail = 0;    // bf16 with L % 64 != 0: last K tile, zero padded
+  size_t off_sc = 0, off_p = 0;  // mask-based form: dense scores and probabilities
   bool need_ktail = false;
   bool split_own = false;  // own block on the side stream + separate merge
   int full_parts = 0;      // split full attention: key chunks per row (0: whole rows)
@@ -283,6 +285,46 @@ moba_status plan_forward(const moba_args* a, Plan* p) {
       p->off_own_lse = take(2 * nqh * 4);
     }
   }
+  p->total = off;
+  if (a->workspace && a->workspace_bytes < p->total)
+    return fail(MOBA_ERR_INVALID_ARGUMENT, "workspace too small: %zu < %zu bytes",
+                a->workspace_bytes, p->total);
+  return MOBA_OK;
+}
+
+// Mask-based form: the forward's gate, then dense scores, masked softmax and
+// P.V.  Workspace: block means (when not given), the selection (when not
+// requested), V^T (+ the K tail tile), fp32 scores and bf16 probabilities of
+// every (query, key) pair.
+moba_status plan_naive(const moba_args* a, Plan* p) {
+  moba_status st = forward_dims(a, p);
+  if (st != MOBA_OK) return st;
+  Dims& d = p->d;
+  if (!d.bf16) return fail(MOBA_ERR_UNSUPPORTED, "moba_naive_ex: bf16 only");
+  int64_t pairs = 0;
+  if (!mul_ok((int64_t)d.S * d.H, d.Lq, &pairs) || pairs >= ((int64_t)1 << 31) ||
+      !mul_ok(pairs, d.Lv, &pairs) || !mul_ok(pairs, 6, &pairs))
+    return fail(MOBA_ERR_UNSUPPORTED, "moba_naive_ex: score matrix too large");
+  p->need_kbar = a->k_block_mean == nullptr;
+  p->need_sel = a->sel_out == nullptr;
+  p->need_vt = true;
+  p->need_ktail = d.L % 64 != 0;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  if (p->need_kbar) {
+    p->off_kbar = take((size_t)d.S * d.Hkv * d.nb * d.D * 4);
+    p->off_bmpart = take(moba::block_mean_partial_floats(d) * 4);
+  }
+  if (p->need_sel) p->off_sel = take((size_t)d.S * d.H * d.Lq * d.topk * 4);
+  p->off_vt = take((size_t)d.S * d.Hkv * d.D * d.Lv * 2);
+  if (p->need_ktail) p->off_ktail = take((size_t)d.S * 64 * d.Hkv * d.D * 2);
+  const size_t n = (size_t)d.S * d.H * d.Lq * d.Lv;
+  p->off_sc = take(n * 4);
+  p->off_p = take(n * 2);
   p->total = off;
   if (a->workspace && a->workspace_bytes < p->total)
     return fail(MOBA_ERR_INVALID_ARGUMENT, "workspace too small: %zu < %zu bytes",
@@ -534,6 +576,34 @@ moba_status forward_impl(const moba_args* a) {
                   : moba::launch_attn_query_f32(a->q, a->k, a->v, po, plse, a->out, 0, dq,
                                                 l.st, a->lse_out);
   });
+  if (l.err != hipSuccess) return hip_fail(l);
+  return MOBA_OK;
+}
+
+moba_status naive_impl(const moba_args* a) {
+  Plan p;
+  moba_status st = plan_naive(a, &p);
+  if (st != MOBA_OK) return st;
+  Workspace ws;
+  st = get_workspace(a, p, &ws);
+  if (st != MOBA_OK) return st;
+  const Dims& d = p.d;
+  char* w = ws.base;
+  float* kbar = p.need_kbar ? (float*)(w + p.off_kbar) : const_cast<float*>(a->k_block_mean);
+  float* bm_partial = (float*)(w + p.off_bmpart);
+  int32_t* sel = p.need_sel ? (int32_t*)(w + p.off_sel) : a->sel_out;
+  void* vt = (void*)(w + p.off_vt);
+  void* ktail = p.need_ktail ? (void*)(w + p.off_ktail) : nullptr;
+  float* sc = (float*)(w + p.off_sc);
+  void* prob = (void*)(w + p.off_p);
+  Launch l{(hipStream_t)a->stream};
+  if (p.need_kbar)
+    l.run(K_BLOCK_MEAN, [&] { return moba::launch_block_mean(a->k, kbar, bm_partial, d, l.st); });
+  l.run(K_TRANSPOSE_V, [&] { return moba::launch_transpose_v(a->k, a->v, vt, ktail, d, l.st); });
+  l.run(K_GATE, [&] { return moba::launch_gate_topk(a->q, kbar, sel, d, l.st); });
+  l.run(K_NAIVE_SCORES, [&] { return moba::launch_naive_scores(a->q, a->k, sc, d, l.st); });
+  l.run(K_NAIVE_SOFTMAX, [&] { return moba::launch_naive_softmax(sc, sel, prob, d, l.st); });
+  l.run(K_NAIVE_PV, [&] { return moba::launch_naive_pv(prob, vt, a->out, d, l.st); });
   if (l.err != hipSuccess) return hip_fail(l);
   return MOBA_OK;
 }
@@ -929,6 +999,32 @@ moba_status moba_full_attention_ex(const moba_args* a) {
     const moba_args b = load_args(a);
     return full_impl(&b);
   });
+}
+
+moba_status moba_naive_ex(const moba_args* a) {
+  return guarded([&]() -> moba_status {
+    if (!a) return fail(MOBA_ERR_INVALID_ARGUMENT, "args is NULL");
+    const moba_args b = load_args(a);
+    return naive_impl(&b);
+  });
+}
+
+size_t moba_naive_workspace_size(const moba_args* a) {
+  g_last_error.clear();
+  try {
+    if (!a) {
+      fail(MOBA_ERR_INVALID_ARGUMENT, "args is NULL");
+      return 0;
+    }
+    moba_args b = load_args(a);
+    b.workspace = nullptr;
+    b.workspace_bytes = 0;
+    Plan p;
+    if (plan_naive(&b, &p) != MOBA_OK) return 0;
+    return p.total;
+  } catch (...) {
+    return 0;
+  }
 }
 
 size_t moba_workspace_size(const moba_args* a) {

@@ -154,4 +154,13 @@ hipError_t launch_bwd_dkdv(const void* q, const void* dout, const void* k, const
                            const uint32_t* bucket_off, void* dk, void* dv, float* kvpart,
                            const Dims& d, hipStream_t st);
 
+// Mask-based form (see naive.hip): dense fp32 scores sc and bf16
+// probabilities p, both [S, H, Lq, Lv]; vt as for the bf16 query kernels.
+hipError_t launch_naive_scores(const void* q, const void* k, float* sc, const Dims& d,
+                               hipStream_t st);
+hipError_t launch_naive_softmax(const float* sc, const int32_t* sel, void* p, const Dims& d,
+                                hipStream_t st);
+hipError_t launch_naive_pv(const void* p, const void* vt, void* out, const Dims& d,
+                           hipStream_t st);
+
 }  // namespace moba

@@ -229,6 +229,26 @@ moba_status moba_backward_varlen(const moba_varlen_args* a);
 /* backward = 0: workspace of moba_forward_varlen; 1: of moba_backward_varlen. */
 size_t moba_varlen_workspace_size(const moba_varlen_args* a, int32_t backward);
 
+/*
+ * Mask-based MoBA, the "naive" form the pages set beside the efficient one
+ * ("MoBA" project card, "Highlighted Details" and "Limitations & Caveats":
+ * for understanding and visualising the masks; the baseline of the quoted
+ * efficient-vs-naive speedup at 32K tokens, 1 head, block 2048, top-k 3).
+ * Same arguments, gate and selection as moba_forward_ex, then ordinary
+ * attention over the dense score matrix: s = c q.k for EVERY (query, key)
+ * pair (c = 1/sqrt(head_dim)), keys outside the query's selected blocks or
+ * after the query masked out, row softmax, P V.  The output equals
+ * moba_forward_ex's up to rounding.  bf16 only (fp32 is UNSUPPORTED);
+ * lse_out is ignored.  A comparison baseline, deliberately dense: the
+ * workspace holds fp32 scores and bf16 probabilities for every pair,
+ * 6 * batch * n_heads * q_len * kv_len bytes (kv_len rounded up to 64) on top
+ * of the block means, the selection, V^T and the K tail tile;
+ * batch * n_heads * q_len must stay below 2^31.  Workspace bytes from
+ * moba_naive_workspace_size (0 for an invalid argument set).
+ */
+moba_status moba_naive_ex(const moba_args* a);
+size_t moba_naive_workspace_size(const moba_args* a);
+
 /* Workspace bytes moba_forward_ex / moba_full_attention_ex need for `a`
  * (0 for an invalid argument set; read moba_last_error()). */
 size_t moba_workspace_size(const moba_args* a);
@@ -267,7 +287,8 @@ int32_t moba_abi_version(void);
  * "attn_own_merge", "attn_full", "decode_plan", "decode_attn",
  * "decode_merge", "merge_partials", "pool_transpose", "block_mean_finalize",
  * "route_scan_small", and for the backward "bwd_dot", "bwd_transform",
- * "bwd_dq_routed", "bwd_dq_own", "bwd_dkdv".  Unknown names give
+ * "bwd_dq_routed", "bwd_dq_own", "bwd_dkdv", and for moba_naive_ex
+ * "naive_scores", "naive_softmax", "naive_pv".  Unknown names give
  * MOBA_ERR_INVALID_ARGUMENT.  (bf16 prefill runs the own-block attention,
  * "attn_own_merge", on an internal stream of the same device, forked from
  * and joined back into the caller's stream.)

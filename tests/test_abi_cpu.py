@@ -119,6 +119,28 @@ def test_full_workspace_sizes():
     assert vt <= n <= vt * 1.01, n
 
 
+def test_naive_workspace_and_validation():
+    """Mask-based form: the workspace holds fp32 scores and bf16
+    probabilities for every (query, key) pair (kv_len rounded up to 64) on top
+    of V^T; fp32 is refused, and so is a score matrix with 2^31 rows."""
+    import block_sparse_attention_gate_amd as moba
+    L = 1 << 15
+    a = _args(n_heads=1, n_kv_heads=1, block_size=2048, topk=3, q_len=L, kv_len=L)
+    n = moba._lib.moba_naive_workspace_size(ctypes.byref(a))
+    expect_min = 6 * L * L + L * 128 * 2
+    assert expect_min <= n <= expect_min * 1.01, (n, expect_min)
+    ragged = _args(n_heads=2, n_kv_heads=1, block_size=128, topk=3, q_len=1000, kv_len=1000)
+    n = moba._lib.moba_naive_workspace_size(ctypes.byref(ragged))
+    assert n >= 6 * 2 * 1000 * 1024, n
+    f32 = _args(n_heads=1, n_kv_heads=1, dtype=moba.MOBA_DTYPE_F32)
+    assert moba._lib.moba_naive_workspace_size(ctypes.byref(f32)) == 0
+    assert "bf16" in moba.moba_last_error()
+    assert moba._lib.moba_naive_ex(ctypes.byref(f32)) == 2   # UNSUPPORTED, nothing enqueued
+    rows = _args(n_heads=2048, n_kv_heads=1, topk=1, q_len=1 << 20, kv_len=1 << 20)
+    assert moba._lib.moba_naive_workspace_size(ctypes.byref(rows)) == 0
+    assert "too large" in moba.moba_last_error()
+
+
 def test_ragged_lengths_are_accepted():
     """kv_len need not be a multiple of the block size or of 64: the bf16
     workspace then holds V^T padded to a multiple of 64 keys and the last,

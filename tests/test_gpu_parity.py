@@ -19,13 +19,14 @@ def _moba():
     return moba
 
 
-def _run_case(w, n_uniform=None, seed=0):
+def _run_case(w, n_uniform=None, seed=0, entry="moba_forward_ex"):
     """Parity run of one workload: every row when n_uniform is None, else a
-    sample of rows (block edges + n_uniform uniform rows) for outputs."""
+    sample of rows (block edges + n_uniform uniform rows) for outputs.
+    `entry` names the forward under test (moba_forward_ex or moba_naive_ex)."""
     moba = _moba()
-    print(f"case {w}", flush=True)
+    print(f"case {w} via {entry}", flush=True)
     q, k, v = moba_inputs.make_inputs(w, device=DEV)
-    out, sel = moba.moba_forward_ex(q, k, v, w.block_size, w.topk, return_selection=True)
+    out, sel = getattr(moba, entry)(q, k, v, w.block_size, w.topk, return_selection=True)
     torch.cuda.synchronize()
     batched = q.dim() == 4
     qs = [q] if not batched else list(q)
@@ -284,6 +285,39 @@ def test_micro_32k_parity():
     """The 32K single-head shape (block 2048, top-k 3): every selection, and
     outputs for block-edge and uniform rows."""
     _run_case(moba_inputs.WORKLOADS["micro_32k"], n_uniform=2048)
+
+
+NAIVE = [
+    moba_inputs.custom("naive_h1_1k", "bf16", 1, 1024, None, 1, 1, 128, 64, 3, 41),
+    moba_inputs.custom("naive_gqa_ragged", "bf16", 1, 1000, None, 4, 2, 128, 128, 3, 42),
+    moba_inputs.custom("naive_d64", "bf16", 1, 512, None, 2, 2, 64, 128, 2, 43),
+    moba_inputs.custom("naive_chunked_batch", "bf16", 2, 300, 1100, 4, 1, 128, 128, 4, 44),
+    moba_inputs.custom("naive_k1", "bf16", 1, 640, None, 2, 1, 128, 64, 1, 45),
+]
+
+
+@pytest.mark.parametrize("w", NAIVE, ids=[w.name for w in NAIVE])
+def test_naive_parity(w):
+    """The mask-based form against the oracle: every selection and every
+    output row (ragged length, GQA, head_dim 64, batch with q_len < kv_len,
+    top-k 1)."""
+    _run_case(w, entry="moba_naive_ex")
+
+
+def test_naive_32k_matches_the_oracle_and_the_efficient_path():
+    """The 32K single-head shape the benchmark times the mask-based form on:
+    its selection is the efficient path's (same gate kernel, bit for bit),
+    outputs match the oracle on block-edge and uniform rows, and the two
+    forwards agree within the bf16 bar."""
+    moba = _moba()
+    w = moba_inputs.WORKLOADS["micro_32k"]
+    q, k, v, out_naive, sel_naive = _run_case(w, n_uniform=1024, entry="moba_naive_ex")
+    out, sel = moba.moba_forward_ex(q, k, v, w.block_size, w.topk, return_selection=True)
+    torch.cuda.synchronize()
+    assert torch.equal(sel, sel_naive)
+    diff = (out.float() - out_naive.float()).abs()
+    print(f"  naive vs efficient: max {diff.max().item():.2e} mean {diff.mean().item():.2e}")
+    assert diff.max().item() <= 2e-2 and diff.mean().item() <= 2e-3
 
 
 def test_error_paths_enqueue_nothing():
