@@ -213,8 +213,24 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_routed(
     float sl2, uint32_t nslots) {
   using T = Tiles<D, NW>;
   constexpr int TM = 32 * NW;  // routed entries per tile
+  // Eight-wave tiles (one workgroup per CU) copy the tile and bucket offsets
+  // into LDS with parallel loads and search them there, instead of a chain of
+  // dependent global loads before the first K/V tile can be requested.
+  constexpr int RL = NW == 8 ? kRoutedLdsRows : 0;
   __shared__ __attribute__((aligned(16))) bf16_t lds[2 * T::BUF];
-  const uint32_t ntiles = tile_off[nrows];
+  __shared__ uint32_t offs[RL > 0 ? 2 * (RL + 1) : 1];
+  const int tid = threadIdx.x;
+  const bool in_lds = RL > 0 && nrows <= RL;
+  if (in_lds) {
+    for (int i = tid; i <= nrows; i += T::NT) {
+      offs[i] = tile_off[i];
+      offs[RL + 1 + i] = bucket_off[i];
+    }
+    __syncthreads();
+  }
+  auto tile_at = [&](int i) { return in_lds ? offs[i] : tile_off[i]; };
+  auto bucket_at = [&](int i) { return in_lds ? offs[RL + 1 + i] : bucket_off[i]; };
+  const uint32_t ntiles = tile_at(nrows);
   const uint32_t per = (ntiles + 7) / 8;
   const uint32_t bid = blockIdx.x;
   if (bid / 8 >= per) return;
@@ -223,20 +239,21 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_routed(
   int lo = 0, hi = nrows;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (tile_off[mid] <= tile) lo = mid; else hi = mid;
+    if (tile_at(mid) <= tile) lo = mid; else hi = mid;
   }
   const int row = lo;
-  const uint32_t start = (tile - tile_off[row]) * TM;
-  const uint32_t avail = bucket_off[row + 1] - bucket_off[row] - start;
+  const uint32_t start = (tile - tile_at(row)) * TM;
+  const uint32_t b0 = bucket_at(row);
+  const uint32_t avail = bucket_at(row + 1) - b0 - start;
   const int cnt = avail < (uint32_t)TM ? (int)avail : TM;
   const int j = row % nb;
   const int sg = row / nb, g = sg % Hkv, s = sg / Hkv;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int lane = tid & 63, w = tid >> 6;
   const int n = lane & 31, hh = lane >> 5;
   const int e = 32 * w + n;
   const bool wave_on = 32 * w < cnt;
-  const uint32_t slot_raw = (e < cnt) ? list[bucket_off[row] + start + e] : 0u;
+  const uint32_t slot_raw = (e < cnt) ? list[b0 + start + e] : 0u;
   const bool valid = e < cnt && slot_raw < nslots;  // never write outside the partials
   const uint32_t slot = valid ? slot_raw : 0u;
   const uint32_t qh = slot / (uint32_t)kp;

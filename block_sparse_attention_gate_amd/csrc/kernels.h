@@ -12,6 +12,7 @@ constexpr int kOwnSplitSteps = 8;      // own-block tiles longer than this (64-k
 constexpr int kFullChunkTiles = 64;    // key chunk (64-key tiles) of split full attention
 constexpr int kFullMaxParts = 64;      // at most this many chunks per row
 constexpr int kMaxTopk = 17;           // largest supported topk (16 routed blocks + own)
+constexpr int kRoutedLdsRows = 4096;   // buckets whose offsets the routed kernel keeps in LDS
 
 // Problem dimensions shared by every launch of one call.
 struct Dims {
