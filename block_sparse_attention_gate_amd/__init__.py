@@ -378,7 +378,7 @@ def _bwd_args(q, k, v, out, dout, lse, sel, dq, dk, dv, block_size, topk) -> Mob
 
 def moba_backward_ex(q, k, v, out, dout, lse, sel, block_size, topk, *, dq=None, dk=None,
                      dv=None, workspace=None):
-    """Gradients ``(dq, dk, dv)`` of ``sum(out * dout)`` for a bf16 MoBA forward
+    """Gradients ``(dq, dk, dv)`` of ``sum(out * dout)`` for a MoBA forward (bf16 or fp32)
     (C ``moba_backward_ex``); ``lse`` and ``sel`` are the forward's
     ``return_lse`` / ``return_selection`` outputs for the same q, k, v."""
     dq = torch.empty_like(q) if dq is None else dq

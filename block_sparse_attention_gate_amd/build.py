@@ -15,7 +15,7 @@ BUILD_DIR = os.path.join(ROOT, "_build", "moba")
 LIB_PATH = os.path.join(PKG, "libmoba.so")
 
 SOURCES = ["api.cpp", "pool.hip", "gate.hip", "route.hip", "attn_bf16.hip", "attn_bwd.hip",
-           "attn_f32.hip",
+           "attn_f32.hip", "attn_bwd_f32.hip",
            "decode.hip", "naive.hip"]
 
 HIPCC_FLAGS = [

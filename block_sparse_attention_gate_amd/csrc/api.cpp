@@ -693,9 +693,8 @@ moba_status plan_backward(const moba_bwd_args* b, BwdPlan* bp) {
   moba_status st = forward_dims(&a, &bp->f);
   if (st != MOBA_OK) return st;
   Dims& d = bp->f.d;
-  if (!d.bf16) return fail(MOBA_ERR_UNSUPPORTED, "the backward supports bf16 only");
   d.tile_m = 128;  // four-wave routed dq tiles (eight waves would spill)
-  if (d.Lv * d.D >= ((int64_t)1 << 31))
+  if (d.bf16 && d.Lv * d.D >= ((int64_t)1 << 31))
     return fail(MOBA_ERR_UNSUPPORTED, "kv_len * head_dim >= 2^31");
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -705,8 +704,9 @@ moba_status plan_backward(const moba_bwd_args* b, BwdPlan* bp) {
   };
   Plan& p = bp->f;
   bp->off_dvec = take((size_t)d.S * d.H * d.Lq * 4);
-  bp->off_kt = take((size_t)d.S * d.Hkv * d.D * d.Lv * 2);
-  bp->need_tail = d.L % 64 != 0;
+  // fp32 reads K and V as given (no K^T, no tail tiles)
+  if (d.bf16) bp->off_kt = take((size_t)d.S * d.Hkv * d.D * d.Lv * 2);
+  bp->need_tail = d.bf16 && d.L % 64 != 0;
   if (bp->need_tail) {
     bp->off_ktail = take((size_t)d.S * 64 * d.Hkv * d.D * 2);
     bp->off_vtail = take((size_t)d.S * 64 * d.Hkv * d.D * 2);
@@ -718,9 +718,9 @@ moba_status plan_backward(const moba_bwd_args* b, BwdPlan* bp) {
     p.off_boff = take((size_t)(d.nrows + 1) * 4);
     p.off_toff = take((size_t)(d.nrows + 1) * 4);
     p.off_list = take((size_t)d.slots * 4);
-    bp->off_dqp = take((size_t)d.slots * d.D * 2);
+    bp->off_dqp = take((size_t)d.slots * d.D * (d.bf16 ? 2 : 4));
   }
-  const size_t kvp = moba::bwd_dkdv_partial_floats(d);
+  const size_t kvp = d.bf16 ? moba::bwd_dkdv_partial_floats(d) : 0;
   bp->need_kvpart = kvp > 0;
   if (bp->need_kvpart) bp->off_kvpart = take(kvp * 4);
   bp->total = off;
@@ -766,9 +766,13 @@ moba_status backward_impl(const moba_bwd_args* b) {
   void* dqp = bp.routed ? (void*)(w + bp.off_dqp) : nullptr;
 
   Launch l{ws.st};
-  l.run(K_BWD_DOT, [&] { return moba::launch_bwd_dot(b->out, b->dout, dvec, d, l.st); });
-  l.run(K_BWD_TRANSFORM,
-        [&] { return moba::launch_bwd_transform(b->k, b->v, kt, ktail, vtail, d, l.st); });
+  l.run(K_BWD_DOT, [&] {
+    return d.bf16 ? moba::launch_bwd_dot(b->out, b->dout, dvec, d, l.st)
+                  : moba::launch_bwd_dot_f32(b->out, b->dout, dvec, d, l.st);
+  });
+  if (d.bf16)
+    l.run(K_BWD_TRANSFORM,
+          [&] { return moba::launch_bwd_transform(b->k, b->v, kt, ktail, vtail, d, l.st); });
   if (bp.routed) {
     l.run(K_RCOUNT, [&] { return moba::launch_route_count(b->sel, counts, d, l.st); });
     const bool small_scan = moba::route_scan_small_fits(d);
@@ -784,15 +788,22 @@ moba_status backward_impl(const moba_bwd_args* b) {
       return moba::launch_route_scatter(b->sel, counts, boff, list, d, l.st, small_scan);
     });
     l.run(K_BWD_DQ_ROUTED, [&] {
-      return moba::launch_bwd_dq_routed(b->q, b->dout, b->k, b->v, kt, b->lse, dvec, list, boff,
-                                        toff, dqp, d, l.st);
+      return d.bf16 ? moba::launch_bwd_dq_routed(b->q, b->dout, b->k, b->v, kt, b->lse, dvec,
+                                                 list, boff, toff, dqp, d, l.st)
+                    : moba::launch_bwd_dq_routed_f32(b->q, b->dout, b->k, b->v, b->lse, dvec,
+                                                     list, boff, toff, (float*)dqp, d, l.st);
     });
   }
   l.run(K_BWD_DQ_OWN, [&] {
-    return moba::launch_bwd_dq_own(b->q, b->dout, b->k, b->v, kt, ktail, vtail, b->lse, dvec,
-                                   dqp, b->dq, d, l.st);
+    return d.bf16 ? moba::launch_bwd_dq_own(b->q, b->dout, b->k, b->v, kt, ktail, vtail, b->lse,
+                                            dvec, dqp, b->dq, d, l.st)
+                  : moba::launch_bwd_dq_own_f32(b->q, b->dout, b->k, b->v, b->lse, dvec,
+                                                (const float*)dqp, b->dq, d, l.st);
   });
   l.run(K_BWD_DKDV, [&] {
+    if (!d.bf16)
+      return moba::launch_bwd_dkdv_f32(b->q, b->dout, b->k, b->v, b->lse, dvec, list, boff,
+                                       b->dk, b->dv, d, l.st);
     float* kvpart = bp.need_kvpart ? (float*)(w + bp.off_kvpart) : nullptr;
     return moba::launch_bwd_dkdv(b->q, b->dout, b->k, b->v, b->lse, dvec, list, boff, b->dk,
                                  b->dv, kvpart, d, l.st);

@@ -155,6 +155,23 @@ hipError_t launch_bwd_dkdv(const void* q, const void* dout, const void* k, const
                            const uint32_t* bucket_off, void* dk, void* dv, float* kvpart,
                            const Dims& d, hipStream_t st);
 
+// fp32 backward (see attn_bwd_f32.hip): no K^T; dqp one fp32 row per routed
+// slot; list / bucket_off NULL when there are no routed entries.
+hipError_t launch_bwd_dot_f32(const void* out, const void* dout, float* dvec, const Dims& d,
+                              hipStream_t st);
+hipError_t launch_bwd_dq_routed_f32(const void* q, const void* dout, const void* k,
+                                    const void* v, const float* lse, const float* dvec,
+                                    const uint32_t* list, const uint32_t* bucket_off,
+                                    const uint32_t* tile_off, float* dqp, const Dims& d,
+                                    hipStream_t st);
+hipError_t launch_bwd_dq_own_f32(const void* q, const void* dout, const void* k, const void* v,
+                                 const float* lse, const float* dvec, const float* dqp,
+                                 void* dq, const Dims& d, hipStream_t st);
+hipError_t launch_bwd_dkdv_f32(const void* q, const void* dout, const void* k, const void* v,
+                               const float* lse, const float* dvec, const uint32_t* list,
+                               const uint32_t* bucket_off, void* dk, void* dv, const Dims& d,
+                               hipStream_t st);
+
 // Mask-based form (see naive.hip): dense fp32 scores sc and bf16
 // probabilities p, both [S, H, Lq, Lv]; vt as for the bf16 query kernels.
 hipError_t launch_naive_scores(const void* q, const void* k, float* sc, const Dims& d,

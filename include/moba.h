@@ -150,13 +150,13 @@ moba_status moba_full_attention_ex(const moba_args* a);
  * p = softmax(c K_T q), c = 1/sqrt(head_dim):
  *   dv_t += p_t dO,  ds_t = p_t (dO.v_t - dO.o),  dq = c sum_t ds_t k_t,
  *   dk_t += c ds_t q   (GQA: a KV head sums over its group's query heads).
- * bf16 only (fp32 is UNSUPPORTED); the other limits are the forward's, and
- * kv_len * head_dim (kv_len rounded up to 64) must stay below 2^31.
+ * bf16 (MFMA) or fp32 (VALU); the other limits are the forward's, and for
+ * bf16 kv_len * head_dim (kv_len rounded up to 64) must stay below 2^31.
  * sel and lse are what moba_forward_ex wrote to sel_out and lse_out for the
  * same q, k, v.  dq, dk, dv are fully overwritten (keys no query attends get
  * zero gradients).  Workspace (stream-ordered when NULL): dO.o per
- * query-head, K^T, the routing tables rebuilt from sel and one bf16 dq
- * partial per routed slot.
+ * query-head, the routing tables rebuilt from sel, one dq partial per routed
+ * slot (in the input dtype) and, for bf16, K^T.
  */
 typedef struct moba_bwd_args {
   size_t struct_size;          /* = sizeof(moba_bwd_args) */
