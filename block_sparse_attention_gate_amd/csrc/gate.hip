@@ -166,26 +166,51 @@ __device__ __forceinline__ void wave_best_pair(float& s, int& i) {
   }
 }
 
-// Decode (one query per head, bf16): one wave per (sequence, head).  Lane l
-// scores the past blocks j = l, l + 64, ... with fp32 dot products (the block
-// mean in fp32, the query widened from bf16), two blocks at a time, and keeps
-// its own top list; the wave then takes the k-1 best of the 64 lists one at a
-// time (wave_best_pair on the list heads, after which the winning lane drops
-// its head).  grid ceil(S*H/4), 256 threads.
+// Decode (one query per head, bf16): one workgroup of four waves per
+// (sequence, head).  Lane l of wave w scores the past blocks
+// j = 64 w + l, + 256, ... with fp32 dot products (the block mean in fp32,
+// the query widened from bf16) and keeps its own top list; each wave takes
+// the k-1 best of its 64 lists one at a time (wave_best_pair on the list
+// heads, after which the winning lane drops its head), and wave 0 takes the
+// k-1 best of the four waves' candidates the same way.  The order is total
+// (score descending, block index ascending), so the result is that of one
+// list over all blocks.  grid S*H, 256 threads.
 template <int D, int KM>
 __global__ __launch_bounds__(256) void k_gate_topk_decode_bf16(
     const bf16_t* __restrict__ q, const float* __restrict__ kbar, int32_t* __restrict__ sel,
-    int64_t L, int H, int Hkv, int B, int nb, int topk, int nsh) {
-  const int lane = threadIdx.x & 63;
-  const int sh = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (sh >= nsh) return;
+    int64_t L, int H, int Hkv, int B, int nb, int topk) {
+  __shared__ float cand_s[4][KM];
+  __shared__ int cand_i[4][KM];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int sh = blockIdx.x;
   const int s = sh / H, h = sh % H, g = h / (H / Hkv);
   const int b = (int)((L - 1) / B);  // own block of the query at the last position
   const int kp = topk - 1;
   const int nkeep = kp < b ? kp : b;
-  int kept[KM];
+  // the k-1 best of the wave's lane lists, best first, into (bs, bi)[t]
+  auto wave_take = [&](TopList<KM>& top, float (&bs)[KM], int (&bi)[KM]) {
 #pragma unroll
-  for (int t = 0; t < KM; ++t) kept[t] = 0x7fffffff;
+    for (int t = 0; t < KM; ++t) {
+      bs[t] = -__builtin_inff();
+      bi[t] = 0x7fffffff;
+      if (t < nkeep) {
+        float xs = top.s[0];
+        int xi = top.i[0];
+        wave_best_pair(xs, xi);
+        bs[t] = xs;
+        bi[t] = xi;
+        if (top.i[0] == xi) {  // exactly one lane holds block xi
+#pragma unroll
+          for (int u = 0; u + 1 < KM; ++u) {
+            top.s[u] = top.s[u + 1];
+            top.i[u] = top.i[u + 1];
+          }
+          top.s[KM - 1] = -__builtin_inff();
+          top.i[KM - 1] = 0x7fffffff;
+        }
+      }
+    }
+  };
   if (nkeep > 0) {
     float qr[D];
     const bf16_t* qrow = q + ((int64_t)s * H + h) * D;
@@ -201,46 +226,45 @@ __global__ __launch_bounds__(256) void k_gate_topk_decode_bf16(
     TopList<KM> top;
     top.init();
     const float* kb = kbar + ((int64_t)s * Hkv + g) * nb * D;
-    for (int j0 = lane; j0 < b; j0 += 128) {
-      // blocks j0 and j0 + 64 (the second may be past b: it reads block j0
-      // again and is not inserted)
-      const float* kr0 = kb + (int64_t)j0 * D;
-      const float* kr1 = kb + (int64_t)(j0 + 64 < b ? j0 + 64 : j0) * D;
-      float a0 = 0.f, a1 = 0.f;
+    for (int j = 64 * w + lane; j < b; j += 256) {
+      const float* kr = kb + (int64_t)j * D;
+      float a = 0.f;
 #pragma unroll
       for (int dd = 0; dd < D; dd += 4) {
-        const float4 x = *reinterpret_cast<const float4*>(kr0 + dd);
-        const float4 y = *reinterpret_cast<const float4*>(kr1 + dd);
-        a0 = fmaf(qr[dd], x.x, a0);
-        a0 = fmaf(qr[dd + 1], x.y, a0);
-        a0 = fmaf(qr[dd + 2], x.z, a0);
-        a0 = fmaf(qr[dd + 3], x.w, a0);
-        a1 = fmaf(qr[dd], y.x, a1);
-        a1 = fmaf(qr[dd + 1], y.y, a1);
-        a1 = fmaf(qr[dd + 2], y.z, a1);
-        a1 = fmaf(qr[dd + 3], y.w, a1);
+        const float4 x = *reinterpret_cast<const float4*>(kr + dd);
+        a = fmaf(qr[dd], x.x, a);
+        a = fmaf(qr[dd + 1], x.y, a);
+        a = fmaf(qr[dd + 2], x.z, a);
+        a = fmaf(qr[dd + 3], x.w, a);
       }
-      top.insert_ascending(a0, j0);
-      if (j0 + 64 < b) top.insert_ascending(a1, j0 + 64);
+      top.insert_ascending(a, j);
     }
+    float bs[KM];
+    int bi[KM];
+    wave_take(top, bs, bi);
+    if (lane == 0) {
 #pragma unroll
-    for (int t = 0; t < KM; ++t) {
-      if (t < nkeep) {
-        float bs = top.s[0];
-        int bi = top.i[0];
-        wave_best_pair(bs, bi);
-        kept[t] = bi;
-        if (top.i[0] == bi) {  // exactly one lane holds block bi
-#pragma unroll
-          for (int u = 0; u + 1 < KM; ++u) {
-            top.s[u] = top.s[u + 1];
-            top.i[u] = top.i[u + 1];
-          }
-          top.s[KM - 1] = -__builtin_inff();
-          top.i[KM - 1] = 0x7fffffff;
-        }
+      for (int t = 0; t < KM; ++t) {
+        cand_s[w][t] = bs[t];
+        cand_i[w][t] = bi[t];
       }
     }
+  }
+  __syncthreads();
+  if (w != 0) return;
+  int kept[KM];
+#pragma unroll
+  for (int t = 0; t < KM; ++t) kept[t] = 0x7fffffff;
+  if (nkeep > 0) {
+    // one candidate per lane (4 * KM <= 64), then the same extraction
+    TopList<KM> top;
+    top.init();
+    if (lane < 4 * KM) {
+      top.s[0] = cand_s[lane / KM][lane % KM];
+      top.i[0] = cand_i[lane / KM][lane % KM];
+    }
+    float bs[KM];
+    wave_take(top, bs, kept);
   }
   if (lane != 0) return;
   // ascending order (unused slots hold INT_MAX and stay last)
@@ -320,9 +344,9 @@ static hipError_t gate_dispatch_d(const void* q, const float* kbar, int32_t* sel
 #define MOBA_GATE_CASE(KMV)                                                                  \
   if (kp <= KMV) {                                                                           \
     if (d.bf16 && d.Lq == 1) {                                                  \
-      hipLaunchKernelGGL((k_gate_topk_decode_bf16<D, KMV>), dim3((d.S * d.H + 3) / 4),      \
-                         dim3(256), 0, st, static_cast<const bf16_t*>(q), kbar, sel, d.L, d.H, \
-                         d.Hkv, d.B, d.nb, d.topk, d.S * d.H);                               \
+      hipLaunchKernelGGL((k_gate_topk_decode_bf16<D, KMV>), dim3(d.S * d.H), dim3(256), 0,  \
+                         st, static_cast<const bf16_t*>(q), kbar, sel, d.L, d.H, d.Hkv, d.B,  \
+                         d.nb, d.topk);                                                      \
     } else if (d.bf16) {                                                                     \
       dim3 grid((unsigned)((d.Lq + 127) / 128), d.S * d.H);                                  \
       hipLaunchKernelGGL((k_gate_topk_bf16<D, KMV>), grid, dim3(256),                        \
