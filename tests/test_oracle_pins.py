@@ -158,6 +158,52 @@ def test_p4_gather_equals_mask_form_equals_sdpa(seed, L, B, topk, H, Hkv):
     np.testing.assert_allclose(out, _sdpa(q, k, v, mask=mask), atol=1e-12, rtol=0)
 
 
+# ------------------------------------------- property tests (hypothesis) ---
+try:
+    from hypothesis import given, settings, strategies as st
+except ImportError:  # pragma: no cover - hypothesis is part of the test image
+    given = None
+
+if given is not None:
+    _shapes = st.tuples(
+        st.integers(0, 2**31 - 1),                       # seed
+        st.integers(1, 256),                             # L
+        st.sampled_from([1, 2, 4, 8, 16, 32, 64]),       # B
+        st.sampled_from([(1, 1), (2, 1), (4, 2)]),       # (H, Hkv)
+        st.integers(1, 8),                               # head dim
+    )
+
+    @settings(max_examples=60, deadline=None)
+    @given(_shapes, st.data())
+    def test_property_selection_invariants_and_forms(shape, data):
+        """Random small shapes (L <= 256, B in 1..64, topk 1..nb+1, GQA):
+        the selection keeps its invariants (own block present and largest,
+        nothing from the future, min(k, b+1) blocks, ascending, -1 padding;
+        readings R2, R3), and the gathered form equals the mask form (Dev
+        Tutorial step 1; MoBA card 'Limitations & Caveats') and torch's
+        float64 SDPA with the boolean mask built from the selection."""
+        seed, L, B, (H, Hkv), D = shape
+        nb = -(-L // B)
+        topk = data.draw(st.integers(1, nb + 1), label="topk")
+        q, k, v = _case(seed, L, H, Hkv, D, B)
+        out, sel, _ = O.moba_reference(q, k, v, B, topk)
+        t = np.arange(L)
+        mask = np.zeros((H, L, L), dtype=bool)
+        for h in range(H):
+            for i in range(L):
+                b = i // B
+                row = sel[h, i].tolist()
+                valid = [x for x in row if x >= 0]
+                assert row == valid + [-1] * (topk - len(valid))
+                assert b in valid and max(valid) == b
+                assert len(valid) == min(topk, b + 1)
+                assert valid == sorted(set(valid))
+                mask[h, i] = np.isin(t // B, valid) & (t <= i)
+        np.testing.assert_allclose(out, O.naive_mask_reference(q, k, v, B, topk),
+                                   atol=1e-12, rtol=0)
+        np.testing.assert_allclose(out, _sdpa(q, k, v, mask=mask), atol=1e-12, rtol=0)
+
+
 # -------------------------------------------------- P5 local attention -----
 def test_p5_topk_one_is_block_diagonal_causal():
     """k = 1 keeps only the own block with its causal mask: block-diagonal
