@@ -43,48 +43,97 @@ __global__ __launch_bounds__(256) void k_gate_topk_bf16(
   const int nkeep = kp < b ? kp : b;
   TopList<KM> top;
   top.init();
-  if (wave_on) {
-    bf16x8 qf[D / 16];
+  // The workgroup stages each 32-block tile of the block means once, split
+  // into the three bf16 terms (hi, mid, lo: x = hi + mid + lo exactly to
+  // within the last term's rounding), in LDS; the four waves read their MFMA
+  // A operands from there instead of each re-reading and re-splitting the
+  // fp32 rows.  Tiles run up to the workgroup's last query block; a wave
+  // computes only the tiles below its own last query block.
+  constexpr int KS = D + 8;                     // padded LDS row (elements)
+  constexpr int CH = 32 * D / 4 / 256;          // float4 chunks per thread per tile
+  __shared__ __attribute__((aligned(16))) bf16_t ktile[3][32 * KS];
+  const int tid = threadIdx.x;
+  const int64_t rw0 = (int64_t)blockIdx.x * 128;
+  const int64_t rwl = rw0 + 127 < Lq ? rw0 + 127 : Lq - 1;
+  const int ntile = kp > 0 ? ((int)((q_off + rwl) / B) + 31) / 32 : 0;
+  const int64_t rlast = wave_on ? (rbase + 31 < Lq ? rbase + 31 : Lq - 1) : 0;
+  const int bmax = wave_on ? (int)((q_off + rlast) / B) : 0;
+  const float* kb = kbar + ((int64_t)s * Hkv + g) * nb * D;
+  bf16x8 qf[D / 16];
+  {
     const bf16_t* qrow = q + (((int64_t)s * Lq + (valid ? r : 0)) * H + h) * D;
 #pragma unroll
     for (int t = 0; t < D / 16; ++t) {
       qf[t] = ld_bf16x8(qrow + 16 * t + 8 * hh);
       if (!valid) qf[t] = bf16x8{};
     }
-    const int64_t rlast = (rbase + 31 < Lq ? rbase + 31 : Lq - 1);
-    const int bmax = (int)((q_off + rlast) / B);
-    const float* kb = kbar + ((int64_t)s * Hkv + g) * nb * D;
-    if (kp > 0) {
-      for (int jt = 0; jt * 32 < bmax; ++jt) {
-        const int jrow = (jt * 32 + n < nb) ? jt * 32 + n : nb - 1;
-        const float* arow = kb + (int64_t)jrow * D + 8 * hh;
-        f32x16 acc = {};
+  }
+  float4 xr[CH];
+  auto fetch = [&](int jt) {
 #pragma unroll
-        for (int t = 0; t < D / 16; ++t) {
-          const float4 x0 = *reinterpret_cast<const float4*>(arow + 16 * t);
-          const float4 x1 = *reinterpret_cast<const float4*>(arow + 16 * t + 4);
-          const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-          bf16x8 a0, a1, a2;
+    for (int i = 0; i < CH; ++i) {
+      const int c = tid + 256 * i, row = c / (D / 4), cc = c % (D / 4);
+      const int jrow = jt * 32 + row < nb ? jt * 32 + row : nb - 1;
+      xr[i] = *reinterpret_cast<const float4*>(kb + (int64_t)jrow * D + cc * 4);
+    }
+  };
+  auto split_store = [&]() {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const __bf16 hi = static_cast<__bf16>(xs[e]);
-            const float r1 = xs[e] - static_cast<float>(hi);
-            const __bf16 mid = static_cast<__bf16>(r1);
-            const float r2 = r1 - static_cast<float>(mid);
-            a0[e] = hi;
-            a1[e] = mid;
-            a2[e] = static_cast<__bf16>(r2);
-          }
-          acc = mfma32(a0, qf[t], acc);
-          acc = mfma32(a1, qf[t], acc);
-          acc = mfma32(a2, qf[t], acc);
-        }
+    for (int i = 0; i < CH; ++i) {
+      const int c = tid + 256 * i, row = c / (D / 4), cc = c % (D / 4);
+      const float xs[4] = {xr[i].x, xr[i].y, xr[i].z, xr[i].w};
+      uint16_t p0[4], p1[4], p2[4];
 #pragma unroll
-        for (int reg = 0; reg < 16; ++reg) {
-          const int j = jt * 32 + 8 * (reg >> 2) + 4 * hh + (reg & 3);
+      for (int e = 0; e < 4; ++e) {
+        const __bf16 hi = static_cast<__bf16>(xs[e]);
+        const float r1 = xs[e] - static_cast<float>(hi);
+        const __bf16 mid = static_cast<__bf16>(r1);
+        const float r2 = r1 - static_cast<float>(mid);
+        const __bf16 lo = static_cast<__bf16>(r2);
+        p0[e] = __builtin_bit_cast(uint16_t, hi);
+        p1[e] = __builtin_bit_cast(uint16_t, mid);
+        p2[e] = __builtin_bit_cast(uint16_t, lo);
+      }
+      const int off = row * KS + cc * 4;
+      *reinterpret_cast<uint2*>(&ktile[0][off]) =
+          make_uint2(p0[0] | ((uint32_t)p0[1] << 16), p0[2] | ((uint32_t)p0[3] << 16));
+      *reinterpret_cast<uint2*>(&ktile[1][off]) =
+          make_uint2(p1[0] | ((uint32_t)p1[1] << 16), p1[2] | ((uint32_t)p1[3] << 16));
+      *reinterpret_cast<uint2*>(&ktile[2][off]) =
+          make_uint2(p2[0] | ((uint32_t)p2[1] << 16), p2[2] | ((uint32_t)p2[3] << 16));
+    }
+  };
+  if (ntile > 0) fetch(0);
+  for (int jt = 0; jt < ntile; ++jt) {
+    __syncthreads();  // the previous tile is no longer read
+    split_store();
+    __syncthreads();
+    if (jt + 1 < ntile) fetch(jt + 1);
+    if (wave_on && jt * 32 < bmax) {
+      f32x16 acc = {};
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t) {
+        const int off = n * KS + 16 * t + 8 * hh;
+        acc = mfma32(ld_bf16x8(&ktile[0][off]), qf[t], acc);
+        acc = mfma32(ld_bf16x8(&ktile[1][off]), qf[t], acc);
+        acc = mfma32(ld_bf16x8(&ktile[2][off]), qf[t], acc);
+      }
+      // A candidate at or below a lane's last list entry leaves its list
+      // unchanged, so the insertion (a compare-and-shift over the whole
+      // list) is skipped when no lane of the wave has a better one: exact,
+      // and once the lists fill (long contexts) most candidates skip.
+#pragma unroll
+      for (int reg = 0; reg < 16; ++reg) {
+        const int j = jt * 32 + 8 * (reg >> 2) + 4 * hh + (reg & 3);
+        const bool better = j < b && acc[reg] > top.s[KM - 1];
+        if (__any(better)) {
           if (j < b) top.insert_ascending(acc[reg], j);
         }
       }
+    }
+  }
+  if (wave_on) {
+    if (kp > 0) {
       // Merge the other lane half's list: snapshot it first, since both halves
       // rewrite their own lists while merging.
       float os[KM];
