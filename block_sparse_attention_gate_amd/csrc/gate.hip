@@ -21,7 +21,7 @@ namespace moba {
 // With `counts` the workgroup (128 rows of one head = one routing chunk) also
 // writes the routing histogram of its kept past blocks: counts[bucket][col]
 // with col = (h - g*G) * nchunk_r + chunk (see route.hip).
-template <int D, int KM>
+template <int D, int KM, bool STAGE>
 __global__ __launch_bounds__(256) void k_gate_topk_bf16(
     const bf16_t* __restrict__ q, const float* __restrict__ kbar, int32_t* __restrict__ sel,
     int64_t Lq, int64_t q_off, int H, int Hkv, int B, int nb, int topk,
@@ -43,15 +43,6 @@ __global__ __launch_bounds__(256) void k_gate_topk_bf16(
   const int nkeep = kp < b ? kp : b;
   TopList<KM> top;
   top.init();
-  // The workgroup stages each 32-block tile of the block means once, split
-  // into the three bf16 terms (hi, mid, lo: x = hi + mid + lo exactly to
-  // within the last term's rounding), in LDS; the four waves read their MFMA
-  // A operands from there instead of each re-reading and re-splitting the
-  // fp32 rows.  Tiles run up to the workgroup's last query block; a wave
-  // computes only the tiles below its own last query block.
-  constexpr int KS = D + 8;                     // padded LDS row (elements)
-  constexpr int CH = 32 * D / 4 / 256;          // float4 chunks per thread per tile
-  __shared__ __attribute__((aligned(16))) bf16_t ktile[3][32 * KS];
   const int tid = threadIdx.x;
   const int64_t rw0 = (int64_t)blockIdx.x * 128;
   const int64_t rwl = rw0 + 127 < Lq ? rw0 + 127 : Lq - 1;
@@ -68,66 +59,116 @@ __global__ __launch_bounds__(256) void k_gate_topk_bf16(
       if (!valid) qf[t] = bf16x8{};
     }
   }
-  float4 xr[CH];
-  auto fetch = [&](int jt) {
+  // Many blocks (STAGE): the workgroup stages each 32-block tile of the block
+  // means once, split into the three bf16 terms (hi, mid, lo: x = hi + mid +
+  // lo exactly to within the last term's rounding), in LDS; the four waves
+  // read their MFMA A operands from there instead of each re-reading and
+  // re-splitting the fp32 rows.  Tiles run up to the workgroup's last query
+  // block; a wave computes only the tiles below its own last query block.
+  if constexpr (STAGE) {
+    constexpr int KS = D + 8;                     // padded LDS row (elements)
+    constexpr int CH = 32 * D / 4 / 256;          // float4 chunks per thread per tile
+    __shared__ __attribute__((aligned(16))) bf16_t ktile[3][32 * KS];
+    float4 xr[CH];
+    auto fetch = [&](int jt) {
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int c = tid + 256 * i, row = c / (D / 4), cc = c % (D / 4);
-      const int jrow = jt * 32 + row < nb ? jt * 32 + row : nb - 1;
-      xr[i] = *reinterpret_cast<const float4*>(kb + (int64_t)jrow * D + cc * 4);
-    }
-  };
-  auto split_store = [&]() {
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int c = tid + 256 * i, row = c / (D / 4), cc = c % (D / 4);
-      const float xs[4] = {xr[i].x, xr[i].y, xr[i].z, xr[i].w};
-      uint16_t p0[4], p1[4], p2[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const __bf16 hi = static_cast<__bf16>(xs[e]);
-        const float r1 = xs[e] - static_cast<float>(hi);
-        const __bf16 mid = static_cast<__bf16>(r1);
-        const float r2 = r1 - static_cast<float>(mid);
-        const __bf16 lo = static_cast<__bf16>(r2);
-        p0[e] = __builtin_bit_cast(uint16_t, hi);
-        p1[e] = __builtin_bit_cast(uint16_t, mid);
-        p2[e] = __builtin_bit_cast(uint16_t, lo);
+      for (int i = 0; i < CH; ++i) {
+        const int c = tid + 256 * i, row = c / (D / 4), cc = c % (D / 4);
+        const int jrow = jt * 32 + row < nb ? jt * 32 + row : nb - 1;
+        xr[i] = *reinterpret_cast<const float4*>(kb + (int64_t)jrow * D + cc * 4);
       }
-      const int off = row * KS + cc * 4;
-      *reinterpret_cast<uint2*>(&ktile[0][off]) =
-          make_uint2(p0[0] | ((uint32_t)p0[1] << 16), p0[2] | ((uint32_t)p0[3] << 16));
-      *reinterpret_cast<uint2*>(&ktile[1][off]) =
-          make_uint2(p1[0] | ((uint32_t)p1[1] << 16), p1[2] | ((uint32_t)p1[3] << 16));
-      *reinterpret_cast<uint2*>(&ktile[2][off]) =
-          make_uint2(p2[0] | ((uint32_t)p2[1] << 16), p2[2] | ((uint32_t)p2[3] << 16));
-    }
-  };
-  if (ntile > 0) fetch(0);
-  for (int jt = 0; jt < ntile; ++jt) {
-    __syncthreads();  // the previous tile is no longer read
-    split_store();
-    __syncthreads();
-    if (jt + 1 < ntile) fetch(jt + 1);
-    if (wave_on && jt * 32 < bmax) {
-      f32x16 acc = {};
+    };
+    auto split_store = [&]() {
 #pragma unroll
-      for (int t = 0; t < D / 16; ++t) {
-        const int off = n * KS + 16 * t + 8 * hh;
-        acc = mfma32(ld_bf16x8(&ktile[0][off]), qf[t], acc);
-        acc = mfma32(ld_bf16x8(&ktile[1][off]), qf[t], acc);
-        acc = mfma32(ld_bf16x8(&ktile[2][off]), qf[t], acc);
+      for (int i = 0; i < CH; ++i) {
+        const int c = tid + 256 * i, row = c / (D / 4), cc = c % (D / 4);
+        const float xs[4] = {xr[i].x, xr[i].y, xr[i].z, xr[i].w};
+        uint16_t p0[4], p1[4], p2[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const __bf16 hi = static_cast<__bf16>(xs[e]);
+          const float r1 = xs[e] - static_cast<float>(hi);
+          const __bf16 mid = static_cast<__bf16>(r1);
+          const float r2 = r1 - static_cast<float>(mid);
+          const __bf16 lo = static_cast<__bf16>(r2);
+          p0[e] = __builtin_bit_cast(uint16_t, hi);
+          p1[e] = __builtin_bit_cast(uint16_t, mid);
+          p2[e] = __builtin_bit_cast(uint16_t, lo);
+        }
+        const int off = row * KS + cc * 4;
+        *reinterpret_cast<uint2*>(&ktile[0][off]) =
+            make_uint2(p0[0] | ((uint32_t)p0[1] << 16), p0[2] | ((uint32_t)p0[3] << 16));
+        *reinterpret_cast<uint2*>(&ktile[1][off]) =
+            make_uint2(p1[0] | ((uint32_t)p1[1] << 16), p1[2] | ((uint32_t)p1[3] << 16));
+        *reinterpret_cast<uint2*>(&ktile[2][off]) =
+            make_uint2(p2[0] | ((uint32_t)p2[1] << 16), p2[2] | ((uint32_t)p2[3] << 16));
       }
-      // A candidate at or below a lane's last list entry leaves its list
-      // unchanged, so the insertion (a compare-and-shift over the whole
-      // list) is skipped when no lane of the wave has a better one: exact,
-      // and once the lists fill (long contexts) most candidates skip.
+    };
+    if (ntile > 0) fetch(0);
+    for (int jt = 0; jt < ntile; ++jt) {
+      __syncthreads();  // the previous tile is no longer read
+      split_store();
+      __syncthreads();
+      if (jt + 1 < ntile) fetch(jt + 1);
+      if (wave_on && jt * 32 < bmax) {
+        f32x16 acc = {};
 #pragma unroll
-      for (int reg = 0; reg < 16; ++reg) {
-        const int j = jt * 32 + 8 * (reg >> 2) + 4 * hh + (reg & 3);
-        const bool better = j < b && acc[reg] > top.s[KM - 1];
-        if (__any(better)) {
-          if (j < b) top.insert_ascending(acc[reg], j);
+        for (int t = 0; t < D / 16; ++t) {
+          const int off = n * KS + 16 * t + 8 * hh;
+          acc = mfma32(ld_bf16x8(&ktile[0][off]), qf[t], acc);
+          acc = mfma32(ld_bf16x8(&ktile[1][off]), qf[t], acc);
+          acc = mfma32(ld_bf16x8(&ktile[2][off]), qf[t], acc);
+        }
+        // A candidate at or below a lane's last list entry leaves its list
+        // unchanged, so the insertion (a compare-and-shift over the whole
+        // list) is skipped when no lane of the wave has a better one: exact,
+        // and once the lists fill (long contexts) most candidates skip.
+#pragma unroll
+        for (int reg = 0; reg < 16; ++reg) {
+          const int j = jt * 32 + 8 * (reg >> 2) + 4 * hh + (reg & 3);
+          const bool better = j < b && acc[reg] > top.s[KM - 1];
+          if (__any(better)) {
+            if (j < b) top.insert_ascending(acc[reg], j);
+          }
+        }
+      }
+    }
+  } else {
+    // few blocks (at most two tiles of 32): each wave reads and splits the
+    // fp32 rows itself, and the kernel holds no LDS tile (it then shares CUs
+    // with concurrent kernels more readily)
+    if (wave_on && kp > 0) {
+      for (int jt = 0; jt * 32 < bmax; ++jt) {
+        const int jrow = (jt * 32 + n < nb) ? jt * 32 + n : nb - 1;
+        const float* arow = kb + (int64_t)jrow * D + 8 * hh;
+        f32x16 acc = {};
+#pragma unroll
+        for (int t = 0; t < D / 16; ++t) {
+          const float4 x0 = *reinterpret_cast<const float4*>(arow + 16 * t);
+          const float4 x1 = *reinterpret_cast<const float4*>(arow + 16 * t + 4);
+          const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+          bf16x8 a0, a1, a2;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const __bf16 hi = static_cast<__bf16>(xs[e]);
+            const float r1 = xs[e] - static_cast<float>(hi);
+            const __bf16 mid = static_cast<__bf16>(r1);
+            const float r2 = r1 - static_cast<float>(mid);
+            a0[e] = hi;
+            a1[e] = mid;
+            a2[e] = static_cast<__bf16>(r2);
+          }
+          acc = mfma32(a0, qf[t], acc);
+          acc = mfma32(a1, qf[t], acc);
+          acc = mfma32(a2, qf[t], acc);
+        }
+#pragma unroll
+        for (int reg = 0; reg < 16; ++reg) {
+          const int j = jt * 32 + 8 * (reg >> 2) + 4 * hh + (reg & 3);
+          const bool better = j < b && acc[reg] > top.s[KM - 1];
+          if (__any(better)) {
+            if (j < b) top.insert_ascending(acc[reg], j);
+          }
         }
       }
     }
@@ -398,10 +439,16 @@ static hipError_t gate_dispatch_d(const void* q, const float* kbar, int32_t* sel
                          d.nb, d.topk);                                                      \
     } else if (d.bf16) {                                                                     \
       dim3 grid((unsigned)((d.Lq + 127) / 128), d.S * d.H);                                  \
-      hipLaunchKernelGGL((k_gate_topk_bf16<D, KMV>), grid, dim3(256),                        \
-                         counts ? d.nb * sizeof(uint32_t) : 0, st,                           \
-                         static_cast<const bf16_t*>(q), kbar, sel, d.Lq, d.q_off, d.H, d.Hkv, \
-                         d.B, d.nb, d.topk, counts, d.nchunk_r, d.ncols);                    \
+      if (d.nb > 64)                                                                         \
+        hipLaunchKernelGGL((k_gate_topk_bf16<D, KMV, true>), grid, dim3(256),                \
+                           counts ? d.nb * sizeof(uint32_t) : 0, st,                         \
+                           static_cast<const bf16_t*>(q), kbar, sel, d.Lq, d.q_off, d.H,     \
+                           d.Hkv, d.B, d.nb, d.topk, counts, d.nchunk_r, d.ncols);           \
+      else                                                                                   \
+        hipLaunchKernelGGL((k_gate_topk_bf16<D, KMV, false>), grid, dim3(256),               \
+                           counts ? d.nb * sizeof(uint32_t) : 0, st,                         \
+                           static_cast<const bf16_t*>(q), kbar, sel, d.Lq, d.q_off, d.H,     \
+                           d.Hkv, d.B, d.nb, d.topk, counts, d.nchunk_r, d.ncols);           \
     } else {                                                                                 \
       dim3 grid((unsigned)((d.Lq + 255) / 256), d.S * d.H);                                  \
       hipLaunchKernelGGL((k_gate_topk_f32<D, KMV>), grid, dim3(256), 0, st,                  \

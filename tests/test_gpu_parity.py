@@ -99,6 +99,9 @@ SMALL = [
     # group sizes 3 (one head per query-kernel tile) and 16
     moba_inputs.custom("g3", "bf16", 1, 640, None, 6, 2, 128, 64, 3, 29),
     moba_inputs.custom("g16", "bf16", 1, 512, None, 16, 1, 64, 128, 4, 30),
+    # more than 64 blocks: the gate stages its block-mean tiles in LDS
+    moba_inputs.custom("nb130_staged_gate", "bf16", 1, 8300, None, 4, 2, 64, 64, 6, 31),
+    moba_inputs.custom("nb97_staged_gate_d128", "bf16", 1, 6200, None, 2, 1, 128, 64, 12, 32),
 ]
 
 
