@@ -102,6 +102,8 @@ SMALL = [
     # more than 64 blocks: the gate stages its block-mean tiles in LDS
     moba_inputs.custom("nb130_staged_gate", "bf16", 1, 8300, None, 4, 2, 64, 64, 6, 31),
     moba_inputs.custom("nb97_staged_gate_d128", "bf16", 1, 6200, None, 2, 1, 128, 64, 12, 32),
+    # the staged gate with batched, chunked queries at the end of a longer cache
+    moba_inputs.custom("nb132_staged_gate_chunked", "bf16", 2, 500, 8400, 4, 2, 128, 64, 5, 33),
 ]
 
 
