@@ -332,6 +332,37 @@ def run_decode(moba, w, steps, warmup, with_full=True):
         res["full_frac_of_hbm_peak"] = res["full_gbs"] / PEAK_HBM_GBS
         res["speedup_vs_full"] = fms / ms
         del fout, fws
+    if with_full:
+        # A batch whose sequences hold different numbers of tokens in the same
+        # padded cache: one call with per-sequence cache lengths (kv_lens)
+        # against one call per sequence on its own rows (same block means).
+        gen = torch.Generator().manual_seed(w.seed + 1)
+        lens = torch.randint(L // 4, L + 1, (S,), generator=gen, dtype=torch.int32)
+        kv = lens.to(q.device)
+        kws = torch.empty(max(moba.moba_workspace_size(q, k, v, w.block_size, w.topk, kbar, sel),
+                              1), dtype=torch.uint8, device=q.device)
+        kfn = lambda: moba.moba_forward_ex(q, k, v, w.block_size, w.topk, out=out,
+                                           k_block_mean=kbar, sel_out=sel, workspace=kws,
+                                           kv_lens=kv)
+        per = []
+        for s_ in range(S):
+            Ls = int(lens[s_])
+            nbs = -(-Ls // w.block_size)
+            per.append((q[s_:s_ + 1], k[s_:s_ + 1, :Ls], v[s_:s_ + 1, :Ls],
+                        kbar[s_:s_ + 1, :, :nbs].contiguous(), out[s_:s_ + 1]))
+        # one workspace for every per-sequence call (they run in stream order)
+        pws = torch.empty(max(max(moba.moba_workspace_size(a, b, c, w.block_size, w.topk, kb)
+                                  for a, b, c, kb, _ in per), 1),
+                          dtype=torch.uint8, device=q.device)
+        pfn = lambda: [moba.moba_forward_ex(a, b, c, w.block_size, w.topk, out=o,
+                                            k_block_mean=kb, workspace=pws)
+                       for a, b, c, kb, o in per]
+        log(f"[bench] {w.name}: timing per-sequence cache lengths (one call vs one per sequence)")
+        kms, _ = time_region(kfn, steps, warmup)
+        pms, _ = time_region(pfn, steps, warmup)
+        res["kv_lens"] = {"lengths": [int(x) for x in lens], "one_call_ms": kms,
+                          "per_sequence_calls_ms": pms, "speedup": pms / kms}
+        del kws, per, pws
     del q, k, v, out, ws, kbar
     torch.cuda.empty_cache()
     return res

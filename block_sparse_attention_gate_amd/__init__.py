@@ -60,6 +60,7 @@ class MobaArgs(ctypes.Structure):
         ("workspace_bytes", ctypes.c_size_t),
         ("stream", ctypes.c_void_p),
         ("lse_out", ctypes.c_void_p),
+        ("kv_lens", ctypes.c_void_p),
     ]
 
 
@@ -310,14 +311,27 @@ def _workspace_tensor(nbytes: int, device, workspace):
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
+def _kv_lens_ptr(kv_lens, S):
+    if kv_lens is None:
+        return None
+    _dev_tensor(kv_lens, "kv_lens", torch.int32)
+    if kv_lens.numel() != S:
+        raise ValueError(f"kv_lens must be int32 [{S}] (one cache length per sequence)")
+    return kv_lens.data_ptr()
+
+
 def moba_forward_ex(q, k, v, block_size, topk, *, out=None, k_block_mean=None, sel_out=None,
-                    return_selection=False, workspace=None, lse_out=None, return_lse=False):
+                    return_selection=False, workspace=None, lse_out=None, return_lse=False,
+                    kv_lens=None):
     """General MoBA forward (C ``moba_forward_ex``): batches, q_len <= kv_len,
     optional precomputed block means, optional selection and log-sum-exp
     outputs (what moba_backward_ex needs).  The workspace is a torch
     allocation (or the given uint8 tensor).  Returns ``out``, then the
     selection ``[S, H, Lq, topk]`` if asked, then the log-sum-exp
-    ``[S, H, Lq]`` if asked (``[H, ...]`` without the batch axis for 3-D q)."""
+    ``[S, H, Lq]`` if asked (``[H, ...]`` without the batch axis for 3-D q).
+    ``kv_lens`` (int32 ``[S]`` on the device, decode batches with q_len 1):
+    the cache length of each sequence; ``k``/``v`` then hold ``kv_len`` rows
+    per sequence of which sequence s uses the first ``kv_lens[s]``."""
     out = torch.empty_like(q) if out is None else out
     S, Lq, H, D, L, Hkv = _shape4(q, k, v)
     if return_selection and sel_out is None:
@@ -331,6 +345,7 @@ def moba_forward_ex(q, k, v, block_size, topk, *, out=None, k_block_mean=None, s
     a = _args(q, k, v, out, block_size, topk, k_block_mean, sel_out)
     if lse_out is not None:
         a.lse_out = lse_out.data_ptr()
+    a.kv_lens = _kv_lens_ptr(kv_lens, S)
     need = int(_lib.moba_workspace_size(ctypes.byref(a)))
     if need == 0 and _lib.moba_last_error():
         _check(_lib.moba_forward_ex(ctypes.byref(a)), "moba_forward_ex")  # raises the error
@@ -514,9 +529,12 @@ def moba_varlen_workspace_size(q, k, v, cu_seqlens_q, cu_seqlens_k, block_size, 
     return int(_lib.moba_varlen_workspace_size(ctypes.byref(a), int(bool(backward))))
 
 
-def moba_full_attention_ex(q, k, v, *, out=None, workspace=None):
+def moba_full_attention_ex(q, k, v, *, out=None, workspace=None, kv_lens=None):
+    """Full causal attention in the general form (C ``moba_full_attention_ex``);
+    ``kv_lens`` as for moba_forward_ex."""
     out = torch.empty_like(q) if out is None else out
     a = _args(q, k, v, out)
+    a.kv_lens = _kv_lens_ptr(kv_lens, _shape4(q, k, v)[0])
     need = int(_lib.moba_full_workspace_size(ctypes.byref(a)))
     if need == 0 and _lib.moba_last_error():
         _check(_lib.moba_full_attention_ex(ctypes.byref(a)), "moba_full_attention_ex")

@@ -20,17 +20,19 @@ namespace {
 
 thread_local std::string g_last_error;
 
-// Size of the version-1 moba_args (without lse_out), still accepted.
+// Sizes of the version-1 moba_args (without lse_out and kv_lens) and of the
+// version-2 one (without kv_lens), still accepted.
 constexpr size_t kArgsV1Size = offsetof(moba_args, lse_out);
+constexpr size_t kArgsV2Size = offsetof(moba_args, kv_lens);
 
-// Copies the caller's struct (either version) into a full one, so that no
-// field past the caller's struct_size is read; lse_out defaults to NULL.
+// Copies the caller's struct (any version) into a full one, so that no field
+// past the caller's struct_size is read; later fields default to NULL.
 moba_args load_args(const moba_args* a) {
   moba_args b;
   std::memset(&b, 0, sizeof(b));
   size_t n = 0;
   std::memcpy(&n, a, sizeof(size_t));   // struct_size comes first in every version
-  if (n == sizeof(moba_args) || n == kArgsV1Size) std::memcpy(&b, a, n);
+  if (n == sizeof(moba_args) || n == kArgsV1Size || n == kArgsV2Size) std::memcpy(&b, a, n);
   else b.struct_size = n;               // rejected by check_common
   return b;
 }
@@ -159,7 +161,8 @@ struct Plan {
 
 moba_status check_common(const moba_args* a, bool full, Plan* p) {
   if (!a) return fail(MOBA_ERR_INVALID_ARGUMENT, "args is NULL");
-  if (a->struct_size != sizeof(moba_args) && a->struct_size != kArgsV1Size)
+  if (a->struct_size != sizeof(moba_args) && a->struct_size != kArgsV1Size &&
+      a->struct_size != kArgsV2Size)
     return fail(MOBA_ERR_INVALID_ARGUMENT, "struct_size %zu != sizeof(moba_args) %zu",
                 a->struct_size, sizeof(moba_args));
   if (!a->q || !a->k || !a->v || !a->out)
@@ -184,10 +187,15 @@ moba_status check_common(const moba_args* a, bool full, Plan* p) {
     return fail(MOBA_ERR_INVALID_ARGUMENT, "sel_out must be 4-byte aligned");
   if (a->lse_out && ((uintptr_t)a->lse_out & 3))
     return fail(MOBA_ERR_INVALID_ARGUMENT, "lse_out must be 4-byte aligned");
+  if (a->kv_lens && ((uintptr_t)a->kv_lens & 3))
+    return fail(MOBA_ERR_INVALID_ARGUMENT, "kv_lens must be 4-byte aligned");
+  if (a->kv_lens && a->q_len != 1)
+    return fail(MOBA_ERR_UNSUPPORTED, "kv_lens needs q_len 1 (a decode batch)");
 
   Dims& d = p->d;
   d.S = a->batch; d.H = a->n_heads; d.Hkv = a->n_kv_heads; d.G = d.H / d.Hkv; d.D = a->head_dim;
   d.Lq = a->q_len; d.L = a->kv_len; d.q_off = d.L - d.Lq; d.bf16 = a->dtype == MOBA_DTYPE_BF16;
+  d.kv_lens = a->kv_lens;
   int64_t t = 0;
   if (!mul_ok(d.S, d.Lq, &t) || !mul_ok(t, d.H, &t) || !mul_ok(t, d.D, &t) ||
       !mul_ok(d.S, d.L, &t) || !mul_ok(t, d.Hkv, &t) || !mul_ok(t, d.D, &t) ||
@@ -244,6 +252,10 @@ moba_status plan_forward(const moba_args* a, Plan* p) {
   p->need_kbar = a->k_block_mean == nullptr;
   p->need_sel = a->sel_out == nullptr;
   p->decode = moba::decode_supported(d);
+  if (d.kv_lens && !p->decode)
+    return fail(MOBA_ERR_UNSUPPORTED,
+                "kv_lens needs the decode kernels (block_size a multiple of 512, at most 8 "
+                "query heads per KV head)");
   p->need_vt = d.bf16 && !p->decode;
   p->routed = !p->decode && d.kp > 0 && d.nb > 1;
   size_t off = 0;
@@ -301,6 +313,7 @@ moba_status plan_naive(const moba_args* a, Plan* p) {
   if (st != MOBA_OK) return st;
   Dims& d = p->d;
   if (!d.bf16) return fail(MOBA_ERR_UNSUPPORTED, "moba_naive_ex: bf16 only");
+  if (d.kv_lens) return fail(MOBA_ERR_UNSUPPORTED, "moba_naive_ex: no kv_lens");
   int64_t pairs = 0;
   if (!mul_ok((int64_t)d.S * d.H, d.Lq, &pairs) || pairs >= ((int64_t)1 << 31) ||
       !mul_ok(pairs, d.Lv, &pairs) || !mul_ok(pairs, 6, &pairs))
@@ -347,6 +360,9 @@ moba_status plan_full(const moba_args* a, Plan* p) {
   dd.B = moba::decode_chunk();
   dd.nb = (int)((d.L + dd.B - 1) / dd.B);
   dd.topk = dd.nb;
+  if (d.kv_lens && !(dd.nb <= moba::kMaxBlocks && moba::decode_supported(dd)))
+    return fail(MOBA_ERR_UNSUPPORTED, "kv_lens needs the decode kernels (at most 8 query "
+                "heads per KV head)");
   if (dd.nb <= moba::kMaxBlocks && moba::decode_supported(dd)) {
     d = dd;
     d.kp = 0;

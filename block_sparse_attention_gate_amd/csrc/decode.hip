@@ -70,7 +70,7 @@ __global__ __launch_bounds__(256) void k_decode_attn(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const int32_t* __restrict__ ublk, const uint32_t* __restrict__ umask,
     const int32_t* __restrict__ ucount, float* __restrict__ part, int64_t L, int H, int Hkv,
-    int B, int umax, float scale_log2, int nsg) {
+    int B, int umax, float scale_log2, int nsg, const int32_t* __restrict__ kv_lens) {
   constexpr int DG = D / 8;             // d-groups of 8 (score and P.V phases)
   constexpr int KG = 256 / DG;          // key groups
   __shared__ float qs[GM][D];
@@ -91,8 +91,15 @@ __global__ __launch_bounds__(256) void k_decode_attn(
   const int64_t key0 = (int64_t)j * B + (int64_t)c * kDecChunk;
   const int64_t item = ((int64_t)sg * umax + u) * (B / kDecChunk) + c;
   // keys of this chunk that exist: a chunk of a partial last block may hold
-  // fewer than kDecChunk, or none (then its partial is empty: max -inf)
-  const int nkey = L - key0 >= kDecChunk ? kDecChunk : (L > key0 ? (int)(L - key0) : 0);
+  // fewer than kDecChunk, or none (then its partial is empty: max -inf).
+  // With kv_lens the sequence's cache ends at its own length (clamped to
+  // [1, L]); L stays the row count of the cache.
+  int64_t Ls = L;
+  if (kv_lens != nullptr) {
+    const int64_t x = kv_lens[s];
+    Ls = x < 1 ? 1 : (x > L ? L : x);
+  }
+  const int nkey = Ls - key0 >= kDecChunk ? kDecChunk : (Ls > key0 ? (int)(Ls - key0) : 0);
   if (nkey == 0) {
     for (int hl = 0; hl < G && hl < GM; ++hl) {
       if (!((mask >> hl) & 1u)) continue;
@@ -377,7 +384,7 @@ static hipError_t decode_attn_gm(const void* q, const void* k, const void* v,
   hipLaunchKernelGGL((k_decode_attn<T, D, GMV>), dim3((unsigned)nwg), dim3(256), 0, st,    \
                      static_cast<const T*>(q), static_cast<const T*>(k),                   \
                      static_cast<const T*>(v), ublk, umask, ucount, part, d.L, d.H, d.Hkv, \
-                     d.B, umax, sl2, nsg)
+                     d.B, umax, sl2, nsg, d.kv_lens)
   switch (decode_gm(d)) {
     case 1: MOBA_DEC(1); break;
     case 2: MOBA_DEC(2); break;

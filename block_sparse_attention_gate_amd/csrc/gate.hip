@@ -268,13 +268,19 @@ __device__ __forceinline__ void wave_best_pair(float& s, int& i) {
 template <int D, int KM>
 __global__ __launch_bounds__(256) void k_gate_topk_decode_bf16(
     const bf16_t* __restrict__ q, const float* __restrict__ kbar, int32_t* __restrict__ sel,
-    int64_t L, int H, int Hkv, int B, int nb, int topk) {
+    int64_t L, int H, int Hkv, int B, int nb, int topk, const int32_t* __restrict__ kv_lens) {
   __shared__ float cand_s[4][KM];
   __shared__ int cand_i[4][KM];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int sh = blockIdx.x;
   const int s = sh / H, h = sh % H, g = h / (H / Hkv);
-  const int b = (int)((L - 1) / B);  // own block of the query at the last position
+  // the sequence's cache length (kv_lens: per sequence, clamped to [1, L])
+  int64_t Ls = L;
+  if (kv_lens != nullptr) {
+    const int64_t x = kv_lens[s];
+    Ls = x < 1 ? 1 : (x > L ? L : x);
+  }
+  const int b = (int)((Ls - 1) / B);  // own block of the query at the last position
   const int kp = topk - 1;
   const int nkeep = kp < b ? kp : b;
   // the k-1 best of the wave's lane lists, best first, into (bs, bi)[t]
@@ -382,11 +388,19 @@ __global__ __launch_bounds__(256) void k_gate_topk_decode_bf16(
 template <int D, int KM>
 __global__ __launch_bounds__(256) void k_gate_topk_f32(
     const float* __restrict__ q, const float* __restrict__ kbar, int32_t* __restrict__ sel,
-    int64_t Lq, int64_t q_off, int H, int Hkv, int B, int nb, int topk) {
+    int64_t Lq, int64_t q_off, int H, int Hkv, int B, int nb, int topk,
+    const int32_t* __restrict__ kv_lens) {
   const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (r >= Lq) return;
   const int sh = blockIdx.y, s = sh / H, h = sh % H, g = h / (H / Hkv);
-  const int b = (int)((q_off + r) / B);
+  // kv_lens (decode batches, q_len 1): the query sits at the sequence's last
+  // cache position, clamped to [0, kv_len)
+  int64_t pos = q_off + r;
+  if (kv_lens != nullptr) {
+    const int64_t x = kv_lens[s];
+    pos = (x < 1 ? 1 : (x > q_off + Lq ? q_off + Lq : x)) - 1;
+  }
+  const int b = (int)(pos / B);
   const int kp = topk - 1;
   const int nkeep = kp < b ? kp : b;
   TopList<KM> top;
@@ -436,7 +450,7 @@ static hipError_t gate_dispatch_d(const void* q, const float* kbar, int32_t* sel
     if (d.bf16 && d.Lq == 1) {                                                  \
       hipLaunchKernelGGL((k_gate_topk_decode_bf16<D, KMV>), dim3(d.S * d.H), dim3(256), 0,  \
                          st, static_cast<const bf16_t*>(q), kbar, sel, d.L, d.H, d.Hkv, d.B,  \
-                         d.nb, d.topk);                                                      \
+                         d.nb, d.topk, d.kv_lens);                                           \
     } else if (d.bf16) {                                                                     \
       dim3 grid((unsigned)((d.Lq + 127) / 128), d.S * d.H);                                  \
       if (d.nb > 64)                                                                         \
@@ -453,7 +467,7 @@ static hipError_t gate_dispatch_d(const void* q, const float* kbar, int32_t* sel
       dim3 grid((unsigned)((d.Lq + 255) / 256), d.S * d.H);                                  \
       hipLaunchKernelGGL((k_gate_topk_f32<D, KMV>), grid, dim3(256), 0, st,                  \
                          static_cast<const float*>(q), kbar, sel, d.Lq, d.q_off, d.H, d.Hkv,  \
-                         d.B, d.nb, d.topk);                                                 \
+                         d.B, d.nb, d.topk, d.kv_lens);                                      \
     }                                                                                        \
     return hipGetLastError();                                                                \
   }

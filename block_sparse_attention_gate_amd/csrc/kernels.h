@@ -36,6 +36,10 @@ struct Dims {
   int nrows = 1;      // S * Hkv * nb buckets
   int64_t slots = 0;  // S * H * Lq * kp routed slots
   int tile_m = 128;   // routed entries per attention tile (128 or 256)
+  // decode batches: per-sequence cache lengths (device int32 [S], nullable);
+  // sequence s then attends keys [0, clamp(kv_lens[s], 1, L)) and L is the
+  // cache's row count
+  const int32_t* kv_lens = nullptr;
 };
 
 // Block means; `partial` holds block_mean_partial_floats(d) floats (may be

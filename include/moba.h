@@ -71,8 +71,10 @@ extern "C" {
 
 /* 2: moba_args gained lse_out (a version-1 struct, without it, is still
  * accepted); moba_backward_ex, moba_block_mean_update and the packed
- * variable-length calls were added. */
-#define MOBA_ABI_VERSION 2
+ * variable-length calls were added.
+ * 3: moba_args gained kv_lens (per-sequence cache lengths for decode; the
+ * version-1 and version-2 structs are still accepted); moba_naive_ex. */
+#define MOBA_ABI_VERSION 3
 
 typedef enum { MOBA_DTYPE_F32 = 0, MOBA_DTYPE_BF16 = 1 } moba_dtype;
 
@@ -132,9 +134,26 @@ typedef struct moba_args {
                                   normaliser over its selected keys (scaled
                                   logits), kept for moba_backward_ex; ignored
                                   by the full-attention calls */
+  const int32_t* kv_lens;      /* nullable: int32 [batch] on the device, the
+                                  cache length of each sequence for a decode
+                                  batch (q_len 1): sequence s attends keys
+                                  [0, kv_lens[s]) of its cache rows and its
+                                  query sits at position kv_lens[s] - 1;
+                                  kv_len is then the cache's row count (the
+                                  row stride of k and v), values are clamped
+                                  to [1, kv_len].  Block means passed in may
+                                  be those of the padded cache
+                                  (moba_block_mean over kv_len rows): the gate
+                                  reads only complete past blocks.  Supported
+                                  where q_len 1 takes the decode kernels
+                                  (block_size a multiple of 512, at most 8
+                                  query heads per KV head), for
+                                  moba_forward_ex and moba_full_attention_ex;
+                                  else UNSUPPORTED */
 } moba_args;
 /* struct_size may also be that of the version-1 struct (up to and including
- * `stream`); lse_out is then taken as NULL. */
+ * `stream`; lse_out and kv_lens are then NULL) or of the version-2 struct (up
+ * to and including `lse_out`; kv_lens is then NULL). */
 
 moba_status moba_forward_ex(const moba_args* a);
 /* Full attention in the general form; block_size, topk, k_block_mean and

@@ -39,7 +39,7 @@ def test_binding_covers_the_header():
 
 def test_version_and_status_strings():
     import block_sparse_attention_gate_amd as moba
-    assert moba.moba_abi_version() == 2
+    assert moba.moba_abi_version() == 3
     assert moba.moba_status_string(0) == "MOBA_OK"
     assert moba.moba_status_string(2) == "MOBA_ERR_UNSUPPORTED"
     assert moba.moba_status_string(99) == "MOBA_STATUS_UNKNOWN"
@@ -198,6 +198,37 @@ def test_version_one_struct_is_accepted():
     a.struct_size = v1 + 4
     assert moba._lib.moba_workspace_size(ctypes.byref(a)) == 0
     assert "struct_size" in moba.moba_last_error()
+
+
+def test_version_two_struct_and_kv_lens_validation():
+    """A version-2 struct (up to lse_out) is accepted with kv_lens taken as
+    NULL; kv_lens is refused off the decode path (q_len > 1, block size not
+    a multiple of 512, the mask-based form) before any launch."""
+    import block_sparse_attention_gate_amd as moba
+    fake = 1 << 40
+    a = _args(batch=8, q_len=1, kv_len=1 << 20)
+    a.struct_size = moba.MobaArgs.kv_lens.offset
+    a.kv_lens = 3   # past the version-2 struct: never read
+    assert moba._lib.moba_workspace_size(ctypes.byref(a)) > 0, moba.moba_last_error()
+    a.struct_size = ctypes.sizeof(moba.MobaArgs)
+    a.kv_lens = fake
+    assert moba._lib.moba_workspace_size(ctypes.byref(a)) > 0, moba.moba_last_error()
+    a.kv_lens = fake + 2
+    assert moba._lib.moba_workspace_size(ctypes.byref(a)) == 0
+    assert "aligned" in moba.moba_last_error()
+    a.kv_lens = fake
+    a.q_len = 2
+    assert moba._lib.moba_forward_ex(ctypes.byref(a)) == moba.MOBA_ERR_UNSUPPORTED
+    assert "q_len 1" in moba.moba_last_error()
+    a.q_len, a.block_size = 1, 256
+    assert moba._lib.moba_forward_ex(ctypes.byref(a)) == moba.MOBA_ERR_UNSUPPORTED
+    assert "decode kernels" in moba.moba_last_error()
+    a.block_size = 4096
+    assert moba._lib.moba_naive_workspace_size(ctypes.byref(a)) == 0
+    assert "kv_lens" in moba.moba_last_error()
+    full = _args(batch=8, q_len=1, kv_len=1 << 20, n_heads=64, n_kv_heads=2)
+    full.kv_lens = fake
+    assert moba._lib.moba_full_attention_ex(ctypes.byref(full)) == moba.MOBA_ERR_UNSUPPORTED
 
 
 def test_plain_c_consumer_host_checks():

@@ -431,6 +431,52 @@ def test_decode_kernels_parity(w):
         print(f"  seq {s}: tie {ntie} max|err| {emax:.2e} mean|err| {emean:.2e}")
 
 
+KV_LENS = [9000, 6001, 4097, 513, 1]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_decode_batch_with_per_sequence_cache_lengths(dtype):
+    """One decode call over sequences whose caches hold different numbers of
+    tokens (kv_lens; the cache tensor is padded to the longest): every
+    sequence gets the bits of its own call on its own cache with the same
+    block means, the selection and outputs match the oracle, and full
+    attention with kv_lens equals per-sequence full attention.  Lengths: the
+    whole cache, ragged, one key into a new block, one key past the first
+    block, a single key."""
+    moba = _moba()
+    S, Lmax, B, topk = len(KV_LENS), max(KV_LENS), 512, 5
+    w = moba_inputs.custom("kv_lens", dtype, S, 1, Lmax, 8, 2, 128, B, topk, 51)
+    print(f"case {w} kv_lens {KV_LENS}", flush=True)
+    q, k, v = moba_inputs.make_inputs(w, device=DEV)
+    kv = torch.tensor(KV_LENS, dtype=torch.int32, device=DEV)
+    kbar = moba.moba_block_mean(k, B)                    # over the padded cache
+    out, sel = moba.moba_forward_ex(q, k, v, B, topk, k_block_mean=kbar, kv_lens=kv,
+                                    return_selection=True)
+    fout = moba.moba_full_attention_ex(q, k, v, kv_lens=kv)
+    torch.cuda.synchronize()
+    bits = torch.int16 if dtype == "bf16" else torch.int32
+    for s, Ls in enumerate(KV_LENS):
+        qs = q[s:s + 1]
+        ks, vs = k[s:s + 1, :Ls].contiguous(), v[s:s + 1, :Ls].contiguous()
+        kbs = kbar[s:s + 1, :, :-(-Ls // B)].contiguous()
+        o1, s1 = moba.moba_forward_ex(qs, ks, vs, B, topk, k_block_mean=kbs,
+                                      return_selection=True)
+        f1 = moba.moba_full_attention_ex(qs, ks, vs)
+        torch.cuda.synchronize()
+        assert torch.equal(sel[s], s1[0]), s
+        assert torch.equal(out[s].view(bits), o1[0].view(bits)), s
+        assert torch.equal(fout[s].view(bits), f1[0].view(bits)), s
+        qh, kh, vh = to64(qs[0]), to64(ks[0]), to64(vs[0])
+        positions = np.array([Ls - 1])
+        kb = O.block_mean(kh, B)
+        sel_np = sel[s].cpu().numpy()
+        ntie, _ = check_selection(qh, positions, kb, sel_np, B, topk)
+        pairs = [(h, 0) for h in range(qh.shape[1])]
+        emax, emean = check_outputs(to64(out[s]), qh, positions, sel_np, B, Ls, dtype, pairs,
+                                    host_fetch(kh, vh), kh.shape[1])
+        print(f"  seq {s} (kv_len {Ls}): tie {ntie} max|err| {emax:.2e} mean|err| {emean:.2e}")
+
+
 @pytest.mark.parametrize("dtype,L", [("bf16", 8192), ("f32", 8192), ("bf16", 8192 + 77)])
 def test_full_attention_decode_parity(dtype, L):
     """Full causal attention with q_len = 1 (split-K over the whole cache,
