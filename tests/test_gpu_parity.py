@@ -434,8 +434,10 @@ def test_decode_kernels_parity(w):
 KV_LENS = [9000, 6001, 4097, 513, 1]
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_decode_batch_with_per_sequence_cache_lengths(dtype):
+@pytest.mark.parametrize("dtype,H,Hkv,D,B,topk", [("bf16", 8, 2, 128, 512, 5),
+                                                   ("f32", 8, 2, 128, 512, 5),
+                                                   ("bf16", 8, 1, 64, 1024, 3)])
+def test_decode_batch_with_per_sequence_cache_lengths(dtype, H, Hkv, D, B, topk):
     """One decode call over sequences whose caches hold different numbers of
     tokens (kv_lens; the cache tensor is padded to the longest): every
     sequence gets the bits of its own call on its own cache with the same
@@ -444,8 +446,8 @@ def test_decode_batch_with_per_sequence_cache_lengths(dtype):
     whole cache, ragged, one key into a new block, one key past the first
     block, a single key."""
     moba = _moba()
-    S, Lmax, B, topk = len(KV_LENS), max(KV_LENS), 512, 5
-    w = moba_inputs.custom("kv_lens", dtype, S, 1, Lmax, 8, 2, 128, B, topk, 51)
+    S, Lmax = len(KV_LENS), max(KV_LENS)
+    w = moba_inputs.custom("kv_lens", dtype, S, 1, Lmax, H, Hkv, D, B, topk, 51)
     print(f"case {w} kv_lens {KV_LENS}", flush=True)
     q, k, v = moba_inputs.make_inputs(w, device=DEV)
     kv = torch.tensor(KV_LENS, dtype=torch.int32, device=DEV)
