@@ -447,7 +447,7 @@ static hipError_t gate_dispatch_d(const void* q, const float* kbar, int32_t* sel
   const int kp = d.topk - 1;
 #define MOBA_GATE_CASE(KMV)                                                                  \
   if (kp <= KMV) {                                                                           \
-    if (d.bf16 && d.Lq == 1) {                                                  \
+    if (gate_uses_decode_kernel(d)) {                                                        \
       hipLaunchKernelGGL((k_gate_topk_decode_bf16<D, KMV>), dim3(d.S * d.H), dim3(256), 0,  \
                          st, static_cast<const bf16_t*>(q), kbar, sel, d.L, d.H, d.Hkv, d.B,  \
                          d.nb, d.topk, d.kv_lens);                                           \
@@ -481,8 +481,15 @@ static hipError_t gate_dispatch_d(const void* q, const float* kbar, int32_t* sel
   return hipErrorInvalidValue;
 }
 
+// bf16 with one query row per (sequence, head): the decode gate (one
+// workgroup per query-head), whatever the group size.  It writes no routing
+// histogram, so the route_count step must run after it when the call routes.
+bool gate_uses_decode_kernel(const Dims& d) { return d.bf16 && d.Lq == 1; }
+
+// The routing histogram comes from the same predicate as the dispatch above:
+// only the 128-row bf16 gate writes it.
 bool gate_writes_counts(const Dims& d) {
-  return d.bf16 && !(d.Lq == 1 && d.G <= 32) && kRouteChunkRows == 128;
+  return d.bf16 && !gate_uses_decode_kernel(d) && kRouteChunkRows == 128;
 }
 
 hipError_t launch_gate_topk(const void* q, const float* kbar, int32_t* sel, const Dims& d,

@@ -68,8 +68,10 @@ hipError_t launch_transpose_v(const void* k, const void* v, void* vt, void* ktai
 // histogram of its 128-row chunk (the route_count step), see route.hip.
 hipError_t launch_gate_topk(const void* q, const float* kbar, int32_t* sel, const Dims& d,
                             hipStream_t st, uint32_t* counts = nullptr);
-// True when launch_gate_topk can produce the routing counts itself.
+// True when launch_gate_topk can produce the routing counts itself (never
+// when it runs the decode gate, see gate_uses_decode_kernel).
 bool gate_writes_counts(const Dims& d);
+bool gate_uses_decode_kernel(const Dims& d);
 hipError_t launch_route_count(const int32_t* sel, uint32_t* counts, const Dims& d,
                               hipStream_t st);
 hipError_t launch_route_scan_rows(uint32_t* counts, uint32_t* bucket_total, const Dims& d,

@@ -6,8 +6,8 @@ import torch
 
 import moba_inputs
 from oracle import moba_oracle as O
-from tests.parity import (check_outputs, check_selection, device_fetch, host_fetch,
-                          sample_rows, to64)
+from tests.parity import (check_outputs, check_selection, check_selection_all_rows,
+                          device_fetch, host_fetch, sample_rows, to64)
 
 pytestmark = pytest.mark.gpu
 
@@ -53,10 +53,11 @@ def _run_case(w, n_uniform=None, seed=0, entry="moba_forward_ex"):
     return q, k, v, out, sel
 
 
-def _run_large(w, n_sel_rows, n_out_rows, heads_out, n_edge_rows=32, seed=0):
+def _run_large(w, n_sel_rows, n_out_rows, heads_out, n_edge_rows=32, seed=0, all_rows=False):
     """Full-size workload in the launch configuration the benchmark times:
-    selection checked on a row sample for every head, outputs on block-edge
-    and uniform rows of a few heads; K and V rows are fetched per query."""
+    selection checked on a row sample for every head (and, with all_rows, on
+    every row of every head), outputs on block-edge and uniform rows of a few
+    heads; K and V rows are fetched per query."""
     moba = _moba()
     print(f"case {w}", flush=True)
     q, k, v = moba_inputs.make_inputs(w, device=DEV)
@@ -72,6 +73,17 @@ def _run_large(w, n_sel_rows, n_out_rows, heads_out, n_edge_rows=32, seed=0):
         rng.choice(edges, size=min(n_edge_rows, edges.size), replace=False),
         rng.integers(0, L, size=n_out_rows), [L - 1]]))
     rows = np.unique(np.concatenate([edges, out_pick, rng.integers(0, L, size=n_sel_rows)]))
+    if all_rows:
+        # every query row of every head: the oracle's fp64 gate scores per
+        # block of rows (check_selection_all_rows)
+        G = q.shape[1] // k.shape[1]
+        nties = 0
+        for h in range(q.shape[1]):
+            ties, _ = check_selection_all_rows(to64(q[:, h]), kbar[h // G],
+                                               sel[h].cpu().numpy(), w.block_size, w.topk)
+            nties += ties
+        print(f"  selection ok on every row: {L} rows x {q.shape[1]} heads, tie-window "
+              f"{nties}", flush=True)
     idx = torch.from_numpy(rows).to(DEV)
     q_rows = to64(q.index_select(0, idx))
     sel_rows = sel.index_select(1, idx).cpu().numpy()
@@ -340,16 +352,18 @@ def test_error_paths_enqueue_nothing():
                              workspace=torch.empty(16, dtype=torch.uint8, device=DEV))
 
 
-def test_llama8b_128k_parity_sampled():
-    """Llama-3.1-8B layer shape at 128K (32/8 heads, block 4096, top-k 12)."""
+def test_llama8b_128k_parity():
+    """Llama-3.1-8B layer shape at 128K (32/8 heads, block 4096, top-k 12):
+    the selection of every query row of every head, outputs sampled."""
     _run_large(moba_inputs.WORKLOADS["llama8b_128k"], n_sel_rows=8192, n_out_rows=32,
-               heads_out=(0, 5, 31), n_edge_rows=32)
+               heads_out=(0, 5, 31), n_edge_rows=32, all_rows=True)
 
 
-def test_prefill_1m_parity_sampled():
-    """The 1M-token prefill (32/8 heads, block 4096, top-k 12), sampled."""
+def test_prefill_1m_parity():
+    """The 1M-token prefill (32/8 heads, block 4096, top-k 12): the selection
+    of every query row of every head (33.6M query-heads), outputs sampled."""
     _run_large(moba_inputs.WORKLOADS["prefill_1m"], n_sel_rows=4096, n_out_rows=24,
-               heads_out=(0, 17), n_edge_rows=24)
+               heads_out=(0, 17), n_edge_rows=24, all_rows=True)
 
 
 def test_prefill_10m_parity_sampled():
@@ -400,6 +414,10 @@ DECODE = [
     # take: the general path)
     moba_inputs.custom("dec_g3", "bf16", 2, 1, 4096, 6, 2, 128, 512, 3, 49),
     moba_inputs.custom("dec_g16", "bf16", 1, 1, 4096, 16, 1, 128, 512, 3, 50),
+    # group of 64 at q_len 1: the bf16 decode gate, which writes no routing
+    # histogram, ahead of the routed path (the route_count step must run)
+    moba_inputs.custom("dec_g64", "bf16", 2, 1, 4096, 64, 1, 128, 512, 4, 56),
+    moba_inputs.custom("dec_g64_b64_d64", "bf16", 1, 1, 2000, 64, 1, 64, 64, 5, 57),
 ]
 
 
@@ -834,11 +852,12 @@ def test_plain_c_consumer_on_the_gpu():
 VARLEN_LENS = [(300, 300), (0, 0), (77, 1234), (1000, 1000), (0, 50), (1, 700), (129, 129)]
 
 
-def _packed(dtype, seed, H=4, Hkv=2, D=128, B=128):
-    """Packed q/k/v of the VARLEN_LENS sequences, each drawn like a workload of
-    its own shape (offset per block of its keys)."""
+def _packed(dtype, seed, H=4, Hkv=2, D=128, B=128, lens=None):
+    """Packed q/k/v of the VARLEN_LENS sequences (or `lens`), each drawn like a
+    workload of its own shape (offset per block of its keys)."""
+    lens = VARLEN_LENS if lens is None else lens
     qs, ks, vs = [], [], []
-    for i, (qn, kn) in enumerate(VARLEN_LENS):
+    for i, (qn, kn) in enumerate(lens):
         if kn == 0:
             continue
         w = moba_inputs.custom("varlen", dtype, 1, max(qn, 1), kn, H, Hkv, D, B, 3, seed + i)
@@ -849,8 +868,8 @@ def _packed(dtype, seed, H=4, Hkv=2, D=128, B=128):
         qs.append(q4[0, :qn])
         ks.append(k4[0])
         vs.append(v4[0])
-    cu_q = np.concatenate([[0], np.cumsum([qn for qn, _ in VARLEN_LENS])])
-    cu_k = np.concatenate([[0], np.cumsum([kn for _, kn in VARLEN_LENS])])
+    cu_q = np.concatenate([[0], np.cumsum([qn for qn, _ in lens])])
+    cu_k = np.concatenate([[0], np.cumsum([kn for _, kn in lens])])
     return (torch.cat(qs).contiguous(), torch.cat(ks).contiguous(), torch.cat(vs).contiguous(),
             cu_q, cu_k)
 
@@ -889,6 +908,32 @@ def test_varlen_forward_equals_per_sequence_calls(dtype):
         check_outputs(to64(o_v), qh, positions, sel_np, B, kn, dtype,
                       [(h, r) for h in range(H) for r in range(qn)], host_fetch(kh, vh),
                       kh.shape[1])
+
+
+ONE_TOKEN_LENS = [(1, 700), (1, 1300), (1, 129), (1, 2000)]
+
+
+def test_varlen_one_token_sequences_group_64():
+    """A packed batch of one-token sequences with 64 query heads on one KV
+    head (bf16): every sequence runs the decode gate ahead of the routed
+    path, which must then count its routing histogram itself.  Outputs and
+    selections against the oracle."""
+    moba = _moba()
+    H, Hkv, D, B, topk = 64, 1, 128, 64, 4
+    q, k, v, cu_q, cu_k = _packed("bf16", 160, H, Hkv, D, B, ONE_TOKEN_LENS)
+    out, sel = moba.moba_forward_varlen(q, k, v, cu_q, cu_k, B, topk, return_selection=True)
+    torch.cuda.synchronize()
+    for s, (qn, kn) in enumerate(ONE_TOKEN_LENS):
+        qs = q[cu_q[s]:cu_q[s + 1]]
+        ks, vs = k[cu_k[s]:cu_k[s + 1]], v[cu_k[s]:cu_k[s + 1]]
+        qh, kh, vh = to64(qs), to64(ks), to64(vs)
+        positions = np.array([kn - 1])
+        sel_np = sel[H * cu_q[s] * topk:H * cu_q[s + 1] * topk].view(H, qn, topk).cpu().numpy()
+        ntie, _ = check_selection(qh, positions, O.block_mean(kh, B), sel_np, B, topk)
+        emax, emean = check_outputs(to64(out[cu_q[s]:cu_q[s + 1]]), qh, positions, sel_np, B,
+                                    kn, "bf16", [(h, 0) for h in range(H)], host_fetch(kh, vh),
+                                    Hkv)
+        print(f"  seq {s} (kv {kn}): tie {ntie} max|err| {emax:.2e} mean|err| {emean:.2e}")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])

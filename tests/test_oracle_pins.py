@@ -60,6 +60,61 @@ def test_golden_hand_worked_example():
     assert [float(x) for x in g["gap"]] == gap[0].tolist()
 
 
+def test_golden_hand_worked_head_dim_4():
+    """Hand-derived selections, gate gaps and outputs at head_dim 4
+    (tests/golden/): integer block means and queries, so the gaps are exact
+    integers of the UNSCALED gate (reading R1), while the attention logits
+    carry the 1/sqrt(4) scale (R7).  A gate scaled by 1/sqrt(D), a gap taken
+    at the wrong rank or a tie broken towards the higher index each change a
+    value here."""
+    g = json.load(open(os.path.join(GOLDEN, "hand_worked_8tok_d4.json")))
+    L, D, B = g["seq_len"], g["head_dim"], g["block_size"]
+    q = np.array(g["q"], float).reshape(L, 1, D)
+    k = np.array(g["k"], float).reshape(L, 1, D)
+    v = np.array(g["v"], float).reshape(L, 1, D)
+    kb = O.block_mean(k, B)
+    np.testing.assert_array_equal(kb[0], np.array(g["kbar"], float))
+    np.testing.assert_array_equal(O.gate_scores(q[6, 0], kb[0], 3), [1.0, 4.0, -1.0])
+    np.testing.assert_array_equal(O.gate_scores(q[7, 0], kb[0], 3), [0.0, 0.0, 1.0])
+    assert O.select_blocks(O.gate_scores(q[7, 0], kb[0], 3), 3, 3) == ((0, 2, 3), 0.0)
+    assert O.select_blocks(O.gate_scores(q[6, 0], kb[0], 3), 3, 2) == ((1, 3), 3.0)
+    env = {"e": math.e, "exp": math.exp}
+    for topk_s, case in g["cases"].items():
+        topk = int(topk_s)
+        out, sel, gap = O.moba_reference(q, k, v, B, topk)
+        assert sel[0].tolist() == case["sel"], topk
+        assert gap[0].tolist() == [float(x) for x in case["gap"]], topk
+        sel2, gap2 = O.select_all(q, kb, B, topk)
+        assert sel2[0].tolist() == case["sel"] and gap2[0].tolist() == gap[0].tolist()
+        if "out0_closed_form" in case:
+            want = np.array([eval(x, {}, env) for x in case["out0_closed_form"]])
+            np.testing.assert_allclose(out[:, 0, 0], want, rtol=0, atol=1e-14)
+            np.testing.assert_allclose(out[:, 0, 1], 1.0, rtol=0, atol=1e-14)
+            np.testing.assert_array_equal(out[:, 0, 2:], 0.0)
+
+
+def test_gap_is_the_boundary_difference_of_the_raw_scores_at_d128():
+    """At head_dim 128 the gate gap equals the (k-1)-th minus the k-th largest
+    past score of kbar @ q (no 1/sqrt(D) factor), taken from a full sort of
+    the raw dot products of every query."""
+    rng = np.random.default_rng(77)
+    L, B, D, topk = 512, 32, 128, 4
+    q = rng.standard_normal((L, 2, D))
+    kb = rng.standard_normal((1, L // B, D)) * 0.5
+    sel, gap = O.select_all(q, kb, B, topk)
+    checked = 0
+    for h in range(2):
+        for i in range(L):
+            b = i // B
+            s = np.sort(np.array([np.dot(kb[0, j], q[i, h]) for j in range(b)]))[::-1]
+            if b > topk - 1:
+                assert gap[h, i] == pytest.approx(s[topk - 2] - s[topk - 1], abs=1e-12)
+                checked += 1
+            else:
+                assert gap[h, i] == math.inf
+    assert checked > 0
+
+
 # ------------------------------------------------------------- pooling -----
 def test_block_mean_ramp_and_partial_block():
     """Mean of a ramp K[t] = t is the block midpoint; a partial last block is
