@@ -61,6 +61,7 @@ class MobaArgs(ctypes.Structure):
         ("stream", ctypes.c_void_p),
         ("lse_out", ctypes.c_void_p),
         ("kv_lens", ctypes.c_void_p),
+        ("routed_bytes_limit", ctypes.c_size_t),
     ]
 
 
@@ -284,9 +285,11 @@ def moba_full_attention(q, k, v, out=None):
     return out
 
 
-def moba_workspace_size(q, k, v, block_size, topk, k_block_mean=None, sel_out=None) -> int:
+def moba_workspace_size(q, k, v, block_size, topk, k_block_mean=None, sel_out=None,
+                        routed_bytes_limit=0) -> int:
     """Workspace bytes moba_forward_ex needs (C ``moba_workspace_size``)."""
     a = _args(q, k, v, q, block_size, topk, k_block_mean, sel_out)
+    a.routed_bytes_limit = int(routed_bytes_limit)
     n = int(_lib.moba_workspace_size(ctypes.byref(a)))
     if n == 0 and _lib.moba_last_error():
         raise ValueError(f"moba_workspace_size: {_lib.moba_last_error().decode()}")
@@ -322,7 +325,7 @@ def _kv_lens_ptr(kv_lens, S):
 
 def moba_forward_ex(q, k, v, block_size, topk, *, out=None, k_block_mean=None, sel_out=None,
                     return_selection=False, workspace=None, lse_out=None, return_lse=False,
-                    kv_lens=None):
+                    kv_lens=None, routed_bytes_limit=0):
     """General MoBA forward (C ``moba_forward_ex``): batches, q_len <= kv_len,
     optional precomputed block means, optional selection and log-sum-exp
     outputs (what moba_backward_ex needs).  The workspace is a torch
@@ -331,7 +334,10 @@ def moba_forward_ex(q, k, v, block_size, topk, *, out=None, k_block_mean=None, s
     ``[S, H, Lq]`` if asked (``[H, ...]`` without the batch axis for 3-D q).
     ``kv_lens`` (int32 ``[S]`` on the device, decode batches with q_len 1):
     the cache length of each sequence; ``k``/``v`` then hold ``kv_len`` rows
-    per sequence of which sequence s uses the first ``kv_lens[s]``."""
+    per sequence of which sequence s uses the first ``kv_lens[s]``.
+    ``routed_bytes_limit`` (bytes, 0 = the library's 12 GiB): above it large
+    bf16 problems route a few KV heads of one sequence at a time, which
+    bounds the workspace; the output is the same bits."""
     out = torch.empty_like(q) if out is None else out
     S, Lq, H, D, L, Hkv = _shape4(q, k, v)
     if return_selection and sel_out is None:
@@ -346,6 +352,7 @@ def moba_forward_ex(q, k, v, block_size, topk, *, out=None, k_block_mean=None, s
     if lse_out is not None:
         a.lse_out = lse_out.data_ptr()
     a.kv_lens = _kv_lens_ptr(kv_lens, S)
+    a.routed_bytes_limit = int(routed_bytes_limit)
     need = int(_lib.moba_workspace_size(ctypes.byref(a)))
     if need == 0 and _lib.moba_last_error():
         _check(_lib.moba_forward_ex(ctypes.byref(a)), "moba_forward_ex")  # raises the error

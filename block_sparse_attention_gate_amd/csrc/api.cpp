@@ -24,6 +24,11 @@ thread_local std::string g_last_error;
 // version-2 one (without kv_lens), still accepted.
 constexpr size_t kArgsV1Size = offsetof(moba_args, lse_out);
 constexpr size_t kArgsV2Size = offsetof(moba_args, kv_lens);
+constexpr size_t kArgsV3Size = offsetof(moba_args, routed_bytes_limit);
+// Routed partial outputs (with their log-sum-exps and list entries) a bf16
+// prefill holds at once unless moba_args.routed_bytes_limit says otherwise;
+// above it the routing runs one (sequence, KV head) at a time.
+constexpr size_t kDefaultRoutedBytes = (size_t)12 << 30;
 
 // Copies the caller's struct (any version) into a full one, so that no field
 // past the caller's struct_size is read; later fields default to NULL.
@@ -32,7 +37,8 @@ moba_args load_args(const moba_args* a) {
   std::memset(&b, 0, sizeof(b));
   size_t n = 0;
   std::memcpy(&n, a, sizeof(size_t));   // struct_size comes first in every version
-  if (n == sizeof(moba_args) || n == kArgsV1Size || n == kArgsV2Size) std::memcpy(&b, a, n);
+  if (n == sizeof(moba_args) || n == kArgsV1Size || n == kArgsV2Size || n == kArgsV3Size)
+    std::memcpy(&b, a, n);
   else b.struct_size = n;               // rejected by check_common
   return b;
 }
@@ -157,12 +163,14 @@ struct Plan {
   bool need_ktail = false;
   bool split_own = false;  // own block on the side stream + separate merge
   int full_parts = 0;      // split full attention: key chunks per row (0: whole rows)
+  bool grouped = false;    // routing pass by pass: group_kv KV heads of one sequence each
+  int group_kv = 0;
 };
 
 moba_status check_common(const moba_args* a, bool full, Plan* p) {
   if (!a) return fail(MOBA_ERR_INVALID_ARGUMENT, "args is NULL");
   if (a->struct_size != sizeof(moba_args) && a->struct_size != kArgsV1Size &&
-      a->struct_size != kArgsV2Size)
+      a->struct_size != kArgsV2Size && a->struct_size != kArgsV3Size)
     return fail(MOBA_ERR_INVALID_ARGUMENT, "struct_size %zu != sizeof(moba_args) %zu",
                 a->struct_size, sizeof(moba_args));
   if (!a->q || !a->k || !a->v || !a->out)
@@ -196,6 +204,7 @@ moba_status check_common(const moba_args* a, bool full, Plan* p) {
   d.S = a->batch; d.H = a->n_heads; d.Hkv = a->n_kv_heads; d.G = d.H / d.Hkv; d.D = a->head_dim;
   d.Lq = a->q_len; d.L = a->kv_len; d.q_off = d.L - d.Lq; d.bf16 = a->dtype == MOBA_DTYPE_BF16;
   d.kv_lens = a->kv_lens;
+  moba::whole_pass(d);
   int64_t t = 0;
   if (!mul_ok(d.S, d.Lq, &t) || !mul_ok(t, d.H, &t) || !mul_ok(t, d.D, &t) ||
       !mul_ok(d.S, d.L, &t) || !mul_ok(t, d.Hkv, &t) || !mul_ok(t, d.D, &t) ||
@@ -239,6 +248,7 @@ moba_status forward_dims(const moba_args* a, Plan* p) {
   // work per K/V tile load) unless there would be too few of them to spread
   // over the chip; the fp32 path always uses 128.
   d.tile_m = (d.bf16 && slots / 256 >= 128) ? 256 : 128;
+  moba::whole_pass(d);
   if ((int64_t)d.S * d.H * d.nchunk_r >= ((int64_t)1 << 31))
     return fail(MOBA_ERR_UNSUPPORTED, "too many routing chunks");
   return MOBA_OK;
@@ -280,13 +290,29 @@ moba_status plan_forward(const moba_args* a, Plan* p) {
   if (p->need_ktail) p->off_ktail = take((size_t)d.S * 64 * d.Hkv * d.D * 2);
   if (p->need_sel) p->off_sel = take((size_t)d.S * d.H * d.Lq * d.topk * 4);
   if (p->routed) {
+    // Large bf16 problems whose routed partials pass the limit route one
+    // (sequence, KV head) at a time: list and partials then hold one pass.
+    const size_t limit = a->routed_bytes_limit ? a->routed_bytes_limit : kDefaultRoutedBytes;
+    const bool small = d.bf16 && (int64_t)d.S * d.H * d.Lq <= ((int64_t)1 << 20);
+    const size_t routed_bytes = (size_t)d.slots * (d.D * esz + 8);
+    p->grouped = d.bf16 && !small && d.S * d.Hkv > 1 && routed_bytes > limit;
+    Dims dp = d;
+    if (p->grouped) {
+      // as many KV heads of one sequence per pass as fit the limit (at least one)
+      const size_t per_kv = (size_t)d.G * d.Lq * d.kp * (d.D * esz + 8);
+      size_t ng = limit / per_kv;
+      if (ng < 1) ng = 1;
+      if (ng > (size_t)d.Hkv) ng = d.Hkv;
+      p->group_kv = (int)ng;
+      moba::group_pass(dp, 0, 0, p->group_kv);
+    }
     p->off_counts = take((size_t)d.nrows * d.ncols * 4);
     p->off_btotal = take((size_t)d.nrows * 4);
-    p->off_boff = take((size_t)(d.nrows + 1) * 4);
-    p->off_toff = take((size_t)(d.nrows + 1) * 4);
-    p->off_list = take((size_t)d.slots * 4);
-    p->off_po = take((size_t)d.slots * d.D * esz);
-    p->off_plse = take((size_t)d.slots * 4);
+    p->off_boff = take((size_t)(dp.pnrows + 1) * 4);
+    p->off_toff = take((size_t)(dp.pnrows + 1) * 4);
+    p->off_list = take((size_t)dp.pslots * 4);
+    p->off_po = take((size_t)dp.pslots * d.D * esz);
+    p->off_plse = take((size_t)dp.pslots * 4);
     // Small problems: run the own block concurrently with the routing (its
     // workgroups alone do not fill the chip).  Large ones fill the chip with
     // the routed attention already, and the fused own-block + merge is cheaper.
@@ -547,27 +573,55 @@ moba_status forward_impl(const moba_args* a) {
     if (l.err != hipSuccess) return hip_fail(l);
     return MOBA_OK;
   }
+  // One routed pass (the whole problem, or one (sequence, KV head) when
+  // grouped): scans of the pass's buckets, its scatter and routed tiles;
+  // with `own`, the own block and the merge of the pass's heads follow.
+  // (grouped passes scan with route_scan_buckets: the column scans of every
+  // bucket run once before the passes)
+  const bool small_scan = p.routed && !p.grouped && moba::route_scan_small_fits(d);
+  auto routed_pass = [&](const Dims& dp, bool own) {
+    if (small_scan) {
+      l.run(K_RSCAN_SMALL,
+            [&] { return moba::launch_route_scan_small(counts, boff, toff, dp, l.st); });
+    } else {
+      l.run(K_RSCAN_BUCKETS,
+            [&] { return moba::launch_route_scan_buckets(btotal, boff, toff, dp, l.st); });
+    }
+    l.run(K_RSCATTER, [&] {
+      return moba::launch_route_scatter(sel, counts, boff, list, dp, l.st, small_scan);
+    });
+    l.run(K_ATTN_ROUTED, [&] {
+      return dp.bf16 ? moba::launch_attn_routed_bf16(a->q, a->k, vt, list, boff, toff, po, plse,
+                                                     dp, l.st)
+                     : moba::launch_attn_routed_f32(a->q, a->k, a->v, list, boff, toff, po,
+                                                    plse, dp, l.st);
+    });
+    if (own)
+      l.run(K_ATTN_OWN, [&] {
+        return dp.bf16 ? moba::launch_attn_query_bf16(a->q, a->k, vt, ktail, po, plse, a->out, 0,
+                                                      dp, l.st, 0, a->lse_out)
+                       : moba::launch_attn_query_f32(a->q, a->k, a->v, po, plse, a->out, 0, dp,
+                                                     l.st, a->lse_out);
+      });
+  };
   if (p.routed) {
     if (!gate_counts)
       l.run(K_RCOUNT, [&] { return moba::launch_route_count(sel, counts, d, l.st); });
-    const bool small_scan = moba::route_scan_small_fits(d);
-    if (small_scan) {
-      l.run(K_RSCAN_SMALL,
-            [&] { return moba::launch_route_scan_small(counts, boff, toff, d, l.st); });
-    } else {
+    // per-bucket column scans of every bucket at once (the small scan does
+    // them itself, pass by pass)
+    if (!small_scan)
       l.run(K_RSCAN_ROWS, [&] { return moba::launch_route_scan_rows(counts, btotal, d, l.st); });
-      l.run(K_RSCAN_BUCKETS,
-            [&] { return moba::launch_route_scan_buckets(btotal, boff, toff, d, l.st); });
+    if (p.grouped) {
+      for (int s = 0; s < d.S && l.err == hipSuccess; ++s)
+        for (int g = 0; g < d.Hkv && l.err == hipSuccess; g += p.group_kv) {
+          Dims dp = d;
+          moba::group_pass(dp, s, g, g + p.group_kv <= d.Hkv ? p.group_kv : d.Hkv - g);
+          routed_pass(dp, true);
+        }
+      if (l.err != hipSuccess) return hip_fail(l);
+      return MOBA_OK;
     }
-    l.run(K_RSCATTER, [&] {
-      return moba::launch_route_scatter(sel, counts, boff, list, d, l.st, small_scan);
-    });
-    l.run(K_ATTN_ROUTED, [&] {
-      return d.bf16 ? moba::launch_attn_routed_bf16(a->q, a->k, vt, list, boff, toff, po, plse,
-                                                    d, l.st)
-                    : moba::launch_attn_routed_f32(a->q, a->k, a->v, list, boff, toff, po, plse,
-                                                   d, l.st);
-    });
+    routed_pass(d, false);
   }
   if (p.split_own) {
     if (l.err == hipSuccess) {

@@ -210,7 +210,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_routed(
     const uint32_t* __restrict__ list, const uint32_t* __restrict__ bucket_off,
     const uint32_t* __restrict__ tile_off, bf16_t* __restrict__ po, float* __restrict__ plse,
     int64_t Lq, int64_t L, int64_t Lv, int H, int Hkv, int kp, int B, int nb, int nrows,
-    float sl2, uint32_t nslots) {
+    float sl2, uint32_t nslots, int64_t prow0, int ph0, int pH) {
   using T = Tiles<D, NW>;
   constexpr int TM = 32 * NW;  // routed entries per tile
   // Eight-wave tiles (one workgroup per CU) copy the tile and bucket offsets
@@ -246,8 +246,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_routed(
   const uint32_t b0 = bucket_at(row);
   const uint32_t avail = bucket_at(row + 1) - b0 - start;
   const int cnt = avail < (uint32_t)TM ? (int)avail : TM;
-  const int j = row % nb;
-  const int sg = row / nb, g = sg % Hkv, s = sg / Hkv;
+  // bucket rows and slots are the pass's (prow0, ph0, pH: see Dims)
+  const int64_t grow = prow0 + row;
+  const int j = (int)(grow % nb);
+  const int sg = (int)(grow / nb), g = sg % Hkv, s = sg / Hkv;
 
   const int lane = tid & 63, w = tid >> 6;
   const int n = lane & 31, hh = lane >> 5;
@@ -258,7 +260,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_routed(
   const uint32_t slot = valid ? slot_raw : 0u;
   const uint32_t qh = slot / (uint32_t)kp;
   const int64_t r = qh % Lq;
-  const int h = (int)((qh / Lq) % H);
+  const int h = ph0 + (int)((qh / Lq) % pH);
   bf16x8 qf[D / 16];
   load_q<D>(q + (((int64_t)s * Lq + r) * H + h) * D, valid, hh, qf);
 
@@ -329,7 +331,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_query(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ vt,
     const bf16_t* __restrict__ po, const float* __restrict__ plse, bf16_t* __restrict__ out,
     const bf16_t* __restrict__ ktail, float* __restrict__ lse_out, int Lq, int L, int Lv,
-    int q_off, int H, int Hkv, int kp, int B, int HW, float sl2, int nparts, int chunk_tiles) {
+    int q_off, int H, int Hkv, int kp, int B, int HW, float sl2, int nparts, int chunk_tiles,
+    int ps0, int ph0, int pH) {
   using T = Tiles<D, NW>;
   __shared__ __attribute__((aligned(16))) bf16_t lds[2 * T::BUF];
   const int RW = 32 * NW / HW;
@@ -350,9 +353,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_query(
   } else {
     rt = item;
   }
-  const int hgroups = H / HW;
-  const int s = blockIdx.y / hgroups;
-  const int h0 = (blockIdx.y % hgroups) * HW;
+  // blockIdx.y: (sequence, head group) of the pass's heads [ph0, ph0 + pH)
+  // of sequences ps0.. (the whole problem without passes)
+  const int hgroups = pH / HW;
+  const int s = ps0 + (int)blockIdx.y / hgroups;
+  const int h0 = ph0 + ((int)blockIdx.y % hgroups) * HW;
   const int g = h0 / (H / Hkv);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int n = lane & 31, hh = lane >> 5;
@@ -492,7 +497,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_query(
     const int npast = kp < own ? kp : own;
     const float lse_own = acc.m + __log2f(ltot);
     float M = lse_own;
-    const int64_t sbase = (((int64_t)s * H + h) * Lq + r) * kp;
+    const int64_t sbase = (((int64_t)(s - ps0) * pH + (h - ph0)) * Lq + r) * kp;
     // all routed log-sum-exps first (independent loads), then the partial
     // rows four at a time (four loads in flight per lane instead of one)
     float lsv[kMaxTopk - 1];
@@ -666,7 +671,7 @@ hipError_t launch_attn_routed_bf16(const void* q, const void* k, const void* vt,
                      static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),           \
                      static_cast<const bf16_t*>(vt), list, bucket_off, tile_off,             \
                      static_cast<bf16_t*>(part_o), part_lse, d.Lq, d.L, d.Lv, d.H, d.Hkv,    \
-                     d.kp, d.B, d.nb, d.nrows, sl2, (uint32_t)d.slots)
+                     d.kp, d.B, d.nb, d.pnrows, sl2, (uint32_t)d.pslots, d.prow0, d.ph0, d.pH)
   if (d.tile_m == 256) {
     if (d.D == 128) MOBA_ROUTED(128, 8); else MOBA_ROUTED(64, 8);
   } else {
@@ -705,7 +710,7 @@ hipError_t launch_attn_query_bf16(const void* q, const void* k, const void* vt,
   if (mode == 3) NW = 8;
   const int RW = 32 * NW / HW;
   const int per = mode == 2 ? 2 : (mode == 3 ? nparts : 1);
-  dim3 grid((unsigned)((d.Lq + RW - 1) / RW * per), d.S * d.H / HW);
+  dim3 grid((unsigned)((d.Lq + RW - 1) / RW * per), d.pS * d.pH / HW);
   const float sl2 = kLog2e / sqrtf((float)d.D);
 #define MOBA_QUERY(DV, MV, NWV)                                                              \
   hipLaunchKernelGGL((k_attn_query<DV, MV, NWV>), grid, dim3(64 * NWV), 0, st,               \
@@ -713,7 +718,8 @@ hipError_t launch_attn_query_bf16(const void* q, const void* k, const void* vt,
                      static_cast<const bf16_t*>(vt), static_cast<const bf16_t*>(part_o),     \
                      part_lse, static_cast<bf16_t*>(out), static_cast<const bf16_t*>(ktail), \
                      mode == 0 ? lse_out : nullptr, (int)d.Lq, (int)d.L, (int)d.Lv,            \
-                     (int)d.q_off, d.H, d.Hkv, d.kp, d.B, HW, sl2, nparts, kFullChunkTiles)
+                     (int)d.q_off, d.H, d.Hkv, d.kp, d.B, HW, sl2, nparts, kFullChunkTiles, \
+                     d.ps0, d.ph0, d.pH)
 #define MOBA_QUERY_NW(DV, MV) \
   if (NW == 8) MOBA_QUERY(DV, MV, 8); else MOBA_QUERY(DV, MV, 4);
   if (d.D == 128) {

@@ -36,11 +36,35 @@ struct Dims {
   int nrows = 1;      // S * Hkv * nb buckets
   int64_t slots = 0;  // S * H * Lq * kp routed slots
   int tile_m = 128;   // routed entries per attention tile (128 or 256)
+  // routed pass: a forward may route one (sequence, KV head) at a time to
+  // bound the partial outputs it holds.  The pass covers query heads
+  // [ph0, ph0 + pH) of sequences [ps0, ps0 + pS) and the buckets
+  // [prow0, prow0 + pnrows) (bucket row (s * Hkv + g) * nb + j); its routed
+  // slots are numbered (((s - ps0) * pH + h - ph0) * Lq + r) * kp + t, pslots
+  // of them.  Without passes: ps0 = 0, pS = S, ph0 = 0, pH = H, prow0 = 0,
+  // pnrows = nrows, pslots = slots (see whole_pass).
+  int ps0 = 0, pS = 1, ph0 = 0, pH = 1;
+  int64_t prow0 = 0;
+  int pnrows = 1;
+  int64_t pslots = 0;
   // decode batches: per-sequence cache lengths (device int32 [S], nullable);
   // sequence s then attends keys [0, clamp(kv_lens[s], 1, L)) and L is the
   // cache's row count
   const int32_t* kv_lens = nullptr;
 };
+
+// Pass fields covering the whole problem.
+inline void whole_pass(Dims& d) {
+  d.ps0 = 0; d.pS = d.S; d.ph0 = 0; d.pH = d.H;
+  d.prow0 = 0; d.pnrows = d.nrows; d.pslots = d.slots;
+}
+// Pass fields for KV heads [g, g + ng) of sequence s (their ng * G query
+// heads).
+inline void group_pass(Dims& d, int s, int g, int ng) {
+  d.ps0 = s; d.pS = 1; d.ph0 = g * d.G; d.pH = ng * d.G;
+  d.prow0 = ((int64_t)s * d.Hkv + g) * d.nb; d.pnrows = ng * d.nb;
+  d.pslots = (int64_t)ng * d.G * d.Lq * d.kp;
+}
 
 // Block means; `partial` holds block_mean_partial_floats(d) floats (may be
 // NULL when that is 0).
@@ -78,8 +102,12 @@ hipError_t launch_route_scan_rows(uint32_t* counts, uint32_t* bucket_total, cons
                                   hipStream_t st);
 hipError_t launch_route_scan_buckets(const uint32_t* bucket_total, uint32_t* bucket_off,
                                      uint32_t* tile_off, const Dims& d, hipStream_t st);
+// The scans, the scatter and the routed attention work on the pass's buckets
+// (d.prow0 .. + d.pnrows): bucket_total, bucket_off and tile_off are indexed
+// from the pass's first bucket, counts globally; list and the partials hold
+// the pass's slots only.
 // Small problems (nrows * ncols <= 16K): both scans in one workgroup; counts
-// then hold global list positions (scatter with counts_global).
+// then hold list positions within the pass (scatter with counts_global).
 bool route_scan_small_fits(const Dims& d);
 hipError_t launch_route_scan_small(uint32_t* counts, uint32_t* bucket_off, uint32_t* tile_off,
                                    const Dims& d, hipStream_t st);

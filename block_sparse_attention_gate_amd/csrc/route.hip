@@ -26,15 +26,22 @@
 namespace moba {
 
 struct RouteArgs {
-  int64_t Lq, q_off;
+  int64_t Lq, q_off, prow0;
   int H, Hkv, G, B, nb, topk, kp, nchunk_r, ncols, nchunks, nbits;
+  int ps0, ph0, pH;   // the pass's first sequence and head, heads per sequence
 };
 
-static RouteArgs route_args(const Dims& d) {
+// pass = false: every chunk of the problem (route_count); else the chunks of
+// the pass's heads (route_scatter).
+static RouteArgs route_args(const Dims& d, bool pass) {
   RouteArgs a;
   a.Lq = d.Lq; a.q_off = d.q_off; a.H = d.H; a.Hkv = d.Hkv; a.G = d.G; a.B = d.B;
   a.nb = d.nb; a.topk = d.topk; a.kp = d.kp; a.nchunk_r = d.nchunk_r; a.ncols = d.ncols;
-  a.nchunks = d.S * d.H * d.nchunk_r;
+  a.ps0 = pass ? d.ps0 : 0;
+  a.ph0 = pass ? d.ph0 : 0;
+  a.pH = pass ? d.pH : d.H;
+  a.prow0 = pass ? d.prow0 : 0;
+  a.nchunks = (pass ? d.pS * d.pH : d.S * d.H) * d.nchunk_r;
   int bits = 0;
   while ((1 << bits) < d.nb) ++bits;
   a.nbits = bits;
@@ -45,8 +52,8 @@ static RouteArgs route_args(const Dims& d) {
 __device__ __forceinline__ void chunk_coords(const RouteArgs& a, int ci, int& s, int& h, int& c) {
   c = ci % a.nchunk_r;
   const int sh = ci / a.nchunk_r;
-  h = sh % a.H;
-  s = sh / a.H;
+  h = a.ph0 + sh % a.pH;
+  s = a.ps0 + sh / a.pH;
 }
 
 __global__ __launch_bounds__(256) void k_route_count(const int32_t* __restrict__ sel,
@@ -165,13 +172,15 @@ __global__ __launch_bounds__(256) void k_route_scatter(const int32_t* __restrict
   const int col = (h - g * a.G) * a.nchunk_r + c;
   for (int j = lane; j < a.nb; j += 64) {
     const int64_t row = ((int64_t)s * a.Hkv + g) * a.nb + j;
-    cur[j] = (counts_global ? 0u : bucket_off[row]) + counts[row * a.ncols + col];
+    cur[j] = (counts_global ? 0u : bucket_off[row - a.prow0]) + counts[row * a.ncols + col];
   }
   const int64_t r0 = (int64_t)c * kRouteChunkRows;
   const int64_t rows = (a.Lq - r0 < kRouteChunkRows) ? a.Lq - r0 : kRouteChunkRows;
   const int total = (int)rows * a.kp;
   const int32_t* selh = sel + ((int64_t)s * a.H + h) * a.Lq * a.topk;
-  const uint64_t slot_base = (((uint64_t)s * a.H + h) * a.Lq + r0) * a.kp;
+  // slot ids of the pass: (((s - ps0) * pH + h - ph0) * Lq + r) * kp + t
+  const uint64_t slot_base =
+      (((uint64_t)(s - a.ps0) * a.pH + (h - a.ph0)) * a.Lq + r0) * a.kp;
   const uint64_t lt_mask = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
   for (int base = 0; base < total; base += 64) {
     const int e = base + lane;
@@ -202,7 +211,7 @@ __global__ __launch_bounds__(256) void k_route_scatter(const int32_t* __restrict
 
 hipError_t launch_route_count(const int32_t* sel, uint32_t* counts, const Dims& d,
                               hipStream_t st) {
-  const RouteArgs a = route_args(d);
+  const RouteArgs a = route_args(d, false);
   const unsigned grid = (unsigned)((a.nchunks + 3) / 4);
   hipLaunchKernelGGL(k_route_count, dim3(grid), dim3(256), 4 * d.nb * sizeof(uint32_t), st, sel,
                      counts, a);
@@ -218,15 +227,15 @@ hipError_t launch_route_scan_rows(uint32_t* counts, uint32_t* bucket_total, cons
 
 hipError_t launch_route_scan_buckets(const uint32_t* bucket_total, uint32_t* bucket_off,
                                      uint32_t* tile_off, const Dims& d, hipStream_t st) {
-  hipLaunchKernelGGL(k_route_scan_buckets, dim3(1), dim3(256), 0, st, bucket_total, bucket_off,
-                     tile_off, d.nrows, d.tile_m);
+  hipLaunchKernelGGL(k_route_scan_buckets, dim3(1), dim3(256), 0, st, bucket_total + d.prow0,
+                     bucket_off, tile_off, d.pnrows, d.tile_m);
   return hipGetLastError();
 }
 
 hipError_t launch_route_scatter(const int32_t* sel, const uint32_t* counts,
                                 const uint32_t* bucket_off, uint32_t* list, const Dims& d,
                                 hipStream_t st, bool counts_global) {
-  const RouteArgs a = route_args(d);
+  const RouteArgs a = route_args(d, true);
   const unsigned grid = (unsigned)((a.nchunks + 3) / 4);
   hipLaunchKernelGGL(k_route_scatter, dim3(grid), dim3(256), 4 * d.nb * sizeof(uint32_t), st,
                      sel, counts, bucket_off, list, a, counts_global ? 1 : 0);
@@ -334,18 +343,19 @@ __global__ __launch_bounds__(kScanSmallThreads) void k_route_scan_small(
 }
 
 bool route_scan_small_fits(const Dims& d) {
-  return (int64_t)d.nrows * d.ncols <= kScanSmallMax;
+  return (int64_t)d.pnrows * d.ncols <= kScanSmallMax;
 }
 
 hipError_t launch_route_scan_small(uint32_t* counts, uint32_t* bucket_off, uint32_t* tile_off,
                                    const Dims& d, hipStream_t st) {
-  hipLaunchKernelGGL(k_route_scan_small, dim3(1), dim3(kScanSmallThreads), 0, st, counts,
-                     bucket_off, tile_off, d.nrows, d.ncols, d.tile_m);
+  hipLaunchKernelGGL(k_route_scan_small, dim3(1), dim3(kScanSmallThreads), 0, st,
+                     counts + d.prow0 * d.ncols, bucket_off, tile_off, d.pnrows, d.ncols,
+                     d.tile_m);
   return hipGetLastError();
 }
 
 int64_t routed_tile_bound(const Dims& d) {
-  return (d.slots + d.tile_m - 1) / d.tile_m + d.nrows;
+  return (d.pslots + d.tile_m - 1) / d.tile_m + d.pnrows;
 }
 
 }  // namespace moba

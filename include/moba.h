@@ -73,8 +73,9 @@ extern "C" {
  * accepted); moba_backward_ex, moba_block_mean_update and the packed
  * variable-length calls were added.
  * 3: moba_args gained kv_lens (per-sequence cache lengths for decode; the
- * version-1 and version-2 structs are still accepted); moba_naive_ex. */
-#define MOBA_ABI_VERSION 3
+ * version-1 and version-2 structs are still accepted); moba_naive_ex.
+ * 4: moba_args gained routed_bytes_limit (earlier structs still accepted). */
+#define MOBA_ABI_VERSION 4
 
 typedef enum { MOBA_DTYPE_F32 = 0, MOBA_DTYPE_BF16 = 1 } moba_dtype;
 
@@ -150,10 +151,23 @@ typedef struct moba_args {
                                   query heads per KV head), for
                                   moba_forward_ex and moba_full_attention_ex;
                                   else UNSUPPORTED */
+  size_t routed_bytes_limit;   /* bytes of routed partial outputs (bf16 rows
+                                  of head_dim values plus an fp32 log-sum-exp
+                                  and a list entry each, one per (query,
+                                  selected past block) pair) the bf16 forward
+                                  may hold at once; 0 = 12 GiB.  Above it,
+                                  problems with more than 2^20 query rows x
+                                  heads and more than one (sequence, KV head)
+                                  route in passes of as many KV heads of one
+                                  sequence as fit the limit (at least one):
+                                  the workspace then holds one pass, and the
+                                  output is bitwise the same.  Ignored by the
+                                  other calls */
 } moba_args;
 /* struct_size may also be that of the version-1 struct (up to and including
- * `stream`; lse_out and kv_lens are then NULL) or of the version-2 struct (up
- * to and including `lse_out`; kv_lens is then NULL). */
+ * `stream`; lse_out and kv_lens are then NULL), of the version-2 struct (up
+ * to and including `lse_out`; kv_lens is then NULL) or of the version-3 struct
+ * (up to and including `kv_lens`; routed_bytes_limit is then 0). */
 
 moba_status moba_forward_ex(const moba_args* a);
 /* Full attention in the general form; block_size, topk, k_block_mean and

@@ -39,7 +39,7 @@ def test_binding_covers_the_header():
 
 def test_version_and_status_strings():
     import block_sparse_attention_gate_amd as moba
-    assert moba.moba_abi_version() == 3
+    assert moba.moba_abi_version() == 4
     assert moba.moba_status_string(0) == "MOBA_OK"
     assert moba.moba_status_string(2) == "MOBA_ERR_UNSUPPORTED"
     assert moba.moba_status_string(99) == "MOBA_STATUS_UNKNOWN"
@@ -78,13 +78,24 @@ def test_validation_rejects_before_any_launch(field, value, status):
 def test_workspace_size_of_the_1m_prefill():
     """Workspace for 1M tokens, 32/8 heads, block 4096, top-k 12: V^T, block
     means, selection, routing tables and the routed partials (bf16 o + fp32
-    lse per slot) -- about 100 GB, within one GPU's 288 GB."""
+    lse + list entry per slot).  All 32 heads' partials would be ~94 GB, past
+    the default 12 GiB routed limit, so the forward routes one KV head (four
+    query heads, 11.9 GB of partials) at a time: the workspace holds one
+    pass, under 16 GiB.  A limit above the whole problem's partials keeps
+    them all."""
     import block_sparse_attention_gate_amd as moba
+    L, slots_all = 1 << 20, 32 * (1 << 20) * 11
+    vt, sel, counts = L * 8 * 128 * 2, 32 * L * 12 * 4, 8 * 256 * (4 * L // 128) * 4
+    per_slot = 128 * 2 + 4 + 4
     a = _args()
     n = moba._lib.moba_workspace_size(ctypes.byref(a))
-    slots = 32 * (1 << 20) * 11
-    expect_min = (1 << 20) * 8 * 128 * 2 + slots * (128 * 2 + 4 + 4)
-    assert expect_min <= n <= expect_min * 1.1, n
+    expect_min = vt + sel + counts + (slots_all // 8) * per_slot
+    assert expect_min <= n <= expect_min * 1.05, (n, expect_min)
+    assert n < 16 << 30
+    a.routed_bytes_limit = 128 << 30
+    n_all = moba._lib.moba_workspace_size(ctypes.byref(a))
+    expect_all = vt + sel + counts + slots_all * per_slot
+    assert expect_all <= n_all <= expect_all * 1.05, (n_all, expect_all)
     bad = _args(head_dim=96)
     assert moba._lib.moba_workspace_size(ctypes.byref(bad)) == 0
     assert "head_dim" in moba.moba_last_error()
@@ -198,6 +209,34 @@ def test_version_one_struct_is_accepted():
     a.struct_size = v1 + 4
     assert moba._lib.moba_workspace_size(ctypes.byref(a)) == 0
     assert "struct_size" in moba.moba_last_error()
+
+
+def test_grouped_workspace_of_the_128k_prefill():
+    """128K tokens, 32/8 heads, block 4096, top-k 12: the routed partials of
+    all heads (9.9 GB) fit the default limit (one pass); a 3 GiB limit gives
+    passes of two KV heads (2.5 GB each), a 1-byte limit passes of one."""
+    import block_sparse_attention_gate_amd as moba
+    L = 1 << 17
+    slots_kv = 4 * L * 11
+    per_slot = 128 * 2 + 4 + 4
+    a = _args(q_len=L, kv_len=L)
+    sizes = []
+    for limit in (0, 3 << 30, 1):
+        a.routed_bytes_limit = limit
+        sizes.append(moba._lib.moba_workspace_size(ctypes.byref(a)))
+    assert sizes[0] - sizes[1] == pytest.approx(6 * slots_kv * per_slot, rel=0.01), sizes
+    assert sizes[1] - sizes[2] == pytest.approx(slots_kv * per_slot, rel=0.01), sizes
+
+
+def test_version_three_struct_is_accepted():
+    """A version-3 struct (up to kv_lens) is accepted with routed_bytes_limit
+    taken as 0 (the default limit); bytes past it are never read."""
+    import block_sparse_attention_gate_amd as moba
+    a = _args()
+    n4 = moba._lib.moba_workspace_size(ctypes.byref(a))
+    a.struct_size = moba.MobaArgs.routed_bytes_limit.offset
+    a.routed_bytes_limit = 1 << 50      # past the version-3 struct: never read
+    assert moba._lib.moba_workspace_size(ctypes.byref(a)) == n4, moba.moba_last_error()
 
 
 def test_version_two_struct_and_kv_lens_validation():

@@ -359,6 +359,52 @@ def test_llama8b_128k_parity():
                heads_out=(0, 5, 31), n_edge_rows=32, all_rows=True)
 
 
+def test_grouped_routing_is_bitwise_the_ungrouped_forward():
+    """A bf16 problem past 2^20 query rows x heads whose routed partials pass
+    moba_args.routed_bytes_limit routes one (sequence, KV head) at a time; the
+    buckets, their entry order and every partial are the same, so the output,
+    selection and log-sum-exp equal the single-pass forward's bits.  Batch 2,
+    a ragged length, GQA 4:1 (16 passes); sampled rows against the oracle."""
+    moba = _moba()
+    w = moba_inputs.custom("grouped", "bf16", 2, 20000, None, 32, 8, 128, 1024, 5, 61)
+    q, k, v = moba_inputs.make_inputs(w, device=DEV)
+    one = moba.moba_workspace_size(q, k, v, w.block_size, w.topk, routed_bytes_limit=1 << 40)
+    grp = moba.moba_workspace_size(q, k, v, w.block_size, w.topk, routed_bytes_limit=1)
+    print(f"  workspace: single pass {one / 2**20:.0f} MiB, grouped {grp / 2**20:.0f} MiB")
+    assert grp < one
+    o1, s1, l1 = moba.moba_forward_ex(q, k, v, w.block_size, w.topk, return_selection=True,
+                                      return_lse=True, routed_bytes_limit=1 << 40)
+    o2, s2, l2 = moba.moba_forward_ex(q, k, v, w.block_size, w.topk, return_selection=True,
+                                      return_lse=True, routed_bytes_limit=1)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(s1, s2) and torch.equal(l1, l2)
+    rng = np.random.default_rng(62)
+    for sq in range(2):
+        qh, kh, vh = to64(q[sq]), to64(k[sq]), to64(v[sq])
+        positions = np.arange(qh.shape[0])
+        rows = sample_rows(qh.shape[0], w.block_size, 0, 64, rng)
+        sel_np = s2[sq].cpu().numpy()
+        kbar = O.block_mean(kh, w.block_size)
+        check_selection(qh[rows], rows, kbar, sel_np[:, rows], w.block_size, w.topk)
+        pairs = [(h, n) for h in (0, 13, 31) for n in range(rows.size)]
+        check_outputs(to64(o2[sq])[rows], qh[rows], rows, sel_np[:, rows], w.block_size,
+                      kh.shape[0], "bf16", pairs, host_fetch(kh, vh), 8)
+
+
+def test_grouped_routing_128k_bitwise():
+    """The 128K Llama-layer shape in one pass (the default: 9.9 GB of routed
+    partials) and in passes of three KV heads (a 4 GiB limit: 3, 3 and 2 KV
+    heads): the same bits."""
+    moba = _moba()
+    w = moba_inputs.WORKLOADS["llama8b_128k"]
+    q, k, v = moba_inputs.make_inputs(w, device=DEV)
+    o1 = moba.moba_forward_ex(q, k, v, w.block_size, w.topk)
+    o2 = moba.moba_forward_ex(q, k, v, w.block_size, w.topk, routed_bytes_limit=4 << 30)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
 def test_prefill_1m_parity():
     """The 1M-token prefill (32/8 heads, block 4096, top-k 12): the selection
     of every query row of every head (33.6M query-heads), outputs sampled."""
