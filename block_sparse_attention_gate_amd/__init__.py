@@ -133,6 +133,7 @@ _SIGNATURES = {
     "moba_forward": (_ST, [_P, _P, _P, _I64, _I32, _I32, _I32, _I32, _I32, _P, ctypes.c_int, _P]),
     "moba_full_attention": (_ST, [_P, _P, _P, _I64, _I32, _I32, _I32, _P, ctypes.c_int, _P]),
     "moba_forward_ex": (_ST, [ctypes.POINTER(MobaArgs)]),
+    "moba_forward_noalloc": (_ST, [ctypes.POINTER(MobaArgs)]),
     "moba_full_attention_ex": (_ST, [ctypes.POINTER(MobaArgs)]),
     "moba_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(MobaArgs)]),
     "moba_full_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(MobaArgs)]),
@@ -367,6 +368,27 @@ def moba_forward_ex(q, k, v, block_size, topk, *, out=None, k_block_mean=None, s
     if return_lse:
         res.append(lse_out.view(S, H, Lq)[0] if q.dim() == 3 else lse_out.view(S, H, Lq))
     return res[0] if len(res) == 1 else tuple(res)
+
+
+def moba_forward_noalloc(q, k, v, block_size, topk, *, out=None, k_block_mean=None,
+                         sel_out=None, lse_out=None, kv_lens=None):
+    """moba_forward_ex without any device allocation (C ``moba_forward_noalloc``):
+    the library's static per-GPU scratch array (64 MiB) is the workspace;
+    larger problems raise ValueError.  ``out``, ``sel_out`` and ``lse_out``
+    are written when given (allocate them beforehand to stay allocation-free);
+    returns ``out``."""
+    if out is None:
+        out = torch.empty_like(q)
+    S, Lq, H, D, L, Hkv = _shape4(q, k, v)
+    a = _args(q, k, v, out, block_size, topk, k_block_mean, sel_out)
+    if lse_out is not None:
+        _dev_tensor(lse_out, "lse_out", torch.float32)
+        if lse_out.numel() != S * H * Lq:
+            raise ValueError(f"lse_out must be float32 [{S}, {H}, {Lq}]")
+        a.lse_out = lse_out.data_ptr()
+    a.kv_lens = _kv_lens_ptr(kv_lens, S)
+    _check(_lib.moba_forward_noalloc(ctypes.byref(a)), "moba_forward_noalloc")
+    return out
 
 
 def _bwd_args(q, k, v, out, dout, lse, sel, dq, dk, dv, block_size, topk) -> MobaBwdArgs:

@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(PKG, "libmoba.so")
 
 SOURCES = ["api.cpp", "pool.hip", "gate.hip", "route.hip", "attn_bf16.hip", "attn_bwd.hip",
            "attn_f32.hip", "attn_bwd_f32.hip",
-           "decode.hip", "naive.hip"]
+           "decode.hip", "naive.hip", "scratch.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

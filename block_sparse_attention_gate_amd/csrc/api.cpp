@@ -469,13 +469,26 @@ moba_status hip_fail(const Launch& l) {
               hipGetErrorString(l.err));
 }
 
-moba_status forward_impl(const moba_args* a) {
+// fixed_ws (nullable): device memory of fixed_bytes used as the workspace
+// instead of the caller's or an allocation; the call then also keeps off the
+// internal stream (no stream or event is created) and allocates nothing.
+moba_status forward_impl(const moba_args* a, void* fixed_ws = nullptr, size_t fixed_bytes = 0) {
   Plan p;
   moba_status st = plan_forward(a, &p);
   if (st != MOBA_OK) return st;
   Workspace ws;
-  st = get_workspace(a, p, &ws);
-  if (st != MOBA_OK) return st;
+  if (fixed_ws) {
+    if (p.total > fixed_bytes)
+      return fail(MOBA_ERR_UNSUPPORTED,
+                  "the problem needs %zu bytes of scratch; the entry point that allocates "
+                  "nothing holds at most %zu (use moba_forward_ex with a workspace)",
+                  p.total, fixed_bytes);
+    ws.base = (char*)fixed_ws;
+    ws.st = (hipStream_t)a->stream;
+  } else {
+    st = get_workspace(a, p, &ws);
+    if (st != MOBA_OK) return st;
+  }
   const Dims& d = p.d;
   char* w = ws.base;
   float* kbar = p.need_kbar ? (float*)(w + p.off_kbar) : const_cast<float*>(a->k_block_mean);
@@ -509,29 +522,38 @@ moba_status forward_impl(const moba_args* a) {
       l.run(K_TRANSPOSE_V,
             [&] { return moba::launch_transpose_v(a->k, a->v, vt, ktail, d, l.st); });
     if (l.err != hipSuccess) return hip_fail(l);
-    hipStream_t side = nullptr;
-    hipEvent_t fork = nullptr;
-    hipError_t e = side_stream(&side);
-    // device-scope release: the events only order work on this device
-    const unsigned evf = hipEventDisableTiming | hipEventReleaseToDevice;
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&fork, evf);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&join.done, evf);
-    if (e == hipSuccess) e = hipEventRecord(fork, l.st);
-    if (e == hipSuccess) e = hipStreamWaitEvent(side, fork, 0);
-    if (fork) (void)hipEventDestroy(fork);
-    if (e != hipSuccess) {
-      if (join.done) (void)hipEventDestroy(join.done);
-      join.done = nullptr;
-      return fail(MOBA_ERR_HIP, "side stream setup failed: %s", hipGetErrorString(e));
+    if (fixed_ws) {
+      // no internal stream: the own block runs here, ahead of the gate (the
+      // same kernels and partials, so the same output bits)
+      l.run(K_ATTN_OWN, [&] {
+        return moba::launch_attn_query_bf16(a->q, a->k, vt, ktail, own_o, own_lse, nullptr, 2,
+                                            d, l.st);
+      });
+    } else {
+      hipStream_t side = nullptr;
+      hipEvent_t fork = nullptr;
+      hipError_t e = side_stream(&side);
+      // device-scope release: the events only order work on this device
+      const unsigned evf = hipEventDisableTiming | hipEventReleaseToDevice;
+      if (e == hipSuccess) e = hipEventCreateWithFlags(&fork, evf);
+      if (e == hipSuccess) e = hipEventCreateWithFlags(&join.done, evf);
+      if (e == hipSuccess) e = hipEventRecord(fork, l.st);
+      if (e == hipSuccess) e = hipStreamWaitEvent(side, fork, 0);
+      if (fork) (void)hipEventDestroy(fork);
+      if (e != hipSuccess) {
+        if (join.done) (void)hipEventDestroy(join.done);
+        join.done = nullptr;
+        return fail(MOBA_ERR_HIP, "side stream setup failed: %s", hipGetErrorString(e));
+      }
+      Launch ls{side};
+      ls.run(K_ATTN_OWN, [&] {
+        return moba::launch_attn_query_bf16(a->q, a->k, vt, ktail, own_o, own_lse, nullptr, 2,
+                                            d, side);
+      });
+      const hipError_t ed = hipEventRecord(join.done, side);
+      if (ls.err == hipSuccess) ls.err = ed;
+      if (ls.err != hipSuccess) return hip_fail(ls);
     }
-    Launch ls{side};
-    ls.run(K_ATTN_OWN, [&] {
-      return moba::launch_attn_query_bf16(a->q, a->k, vt, ktail, own_o, own_lse, nullptr, 2, d,
-                                          side);
-    });
-    const hipError_t ed = hipEventRecord(join.done, side);
-    if (ls.err == hipSuccess) ls.err = ed;
-    if (ls.err != hipSuccess) return hip_fail(ls);
     if (p.need_kbar)
       l.run(K_MEAN_FINALIZE,
             [&] { return moba::launch_block_mean_finalize(kbar, bm_partial, d, l.st); });
@@ -624,7 +646,7 @@ moba_status forward_impl(const moba_args* a) {
     routed_pass(d, false);
   }
   if (p.split_own) {
-    if (l.err == hipSuccess) {
+    if (l.err == hipSuccess && join.done) {
       l.err = hipStreamWaitEvent(l.st, join.done, 0);
       if (l.err == hipSuccess) {
         (void)hipEventDestroy(join.done);
@@ -1071,6 +1093,28 @@ moba_status moba_forward_ex(const moba_args* a) {
     if (!a) return fail(MOBA_ERR_INVALID_ARGUMENT, "args is NULL");
     const moba_args b = load_args(a);
     return forward_impl(&b);
+  });
+}
+
+moba_status moba_forward_noalloc(const moba_args* a) {
+  return guarded([&]() -> moba_status {
+    if (!a) return fail(MOBA_ERR_INVALID_ARGUMENT, "args is NULL");
+    moba_args b = load_args(a);
+    b.workspace = nullptr;    // the scratch array replaces any workspace
+    b.workspace_bytes = 0;
+    Plan p;
+    moba_status st = plan_forward(&b, &p);   // every argument check first
+    if (st != MOBA_OK) return st;
+    if (p.total > moba::kNoAllocScratchBytes)
+      return fail(MOBA_ERR_UNSUPPORTED,
+                  "the problem needs %zu bytes of scratch; moba_forward_noalloc holds at most "
+                  "%zu (use moba_forward_ex with a workspace)",
+                  p.total, moba::kNoAllocScratchBytes);
+    void* scratch = nullptr;
+    const hipError_t e = moba::noalloc_scratch(&scratch);
+    if (e != hipSuccess)
+      return fail(MOBA_ERR_HIP, "scratch address lookup failed: %s", hipGetErrorString(e));
+    return forward_impl(&b, scratch, moba::kNoAllocScratchBytes);
   });
 }
 

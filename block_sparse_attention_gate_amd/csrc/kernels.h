@@ -13,6 +13,9 @@ constexpr int kFullChunkTiles = 64;    // key chunk (64-key tiles) of split full
 constexpr int kFullMaxParts = 64;      // at most this many chunks per row
 constexpr int kMaxTopk = 17;           // largest supported topk (16 routed blocks + own)
 constexpr int kRoutedLdsRows = 4096;   // buckets whose offsets the routed kernel keeps in LDS
+constexpr int kMaxGridCacheDevices = 64;  // devices whose per-device pointers are kept
+// Device scratch of moba_forward_noalloc (a static array per GPU).
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
 
 // Problem dimensions shared by every launch of one call.
 struct Dims {
@@ -65,6 +68,10 @@ inline void group_pass(Dims& d, int s, int g, int ng) {
   d.prow0 = ((int64_t)s * d.Hkv + g) * d.nb; d.pnrows = ng * d.nb;
   d.pslots = (int64_t)ng * d.G * d.Lq * d.kp;
 }
+
+// Device address of this device's scratch array (kNoAllocScratchBytes),
+// looked up once per device with hipGetSymbolAddress.
+hipError_t noalloc_scratch(void** out);
 
 // Block means; `partial` holds block_mean_partial_floats(d) floats (may be
 // NULL when that is 0).

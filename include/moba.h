@@ -170,6 +170,23 @@ typedef struct moba_args {
  * (up to and including `kv_lens`; routed_bytes_limit is then 0). */
 
 moba_status moba_forward_ex(const moba_args* a);
+
+/*
+ * moba_forward_ex for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation and the same output bits, with no allocation and no
+ * internal stream or event.  Its workspace is a static device array of 64
+ * MiB per GPU (kept until the process ends) instead of a.workspace (which is
+ * ignored, as is workspace_bytes); a problem whose workspace
+ * (moba_workspace_size) is larger is refused with MOBA_ERR_UNSUPPORTED
+ * before anything is enqueued (a 32K-token single-head prefill needs about
+ * 43 MB; a decode step with block means passed in, a few MB).  Every call on
+ * one GPU shares that GPU's array, and nothing in it needs to start at zero:
+ * calls that overlap on one GPU (concurrent streams, or threads) race and
+ * must be serialised by the caller.
+ */
+moba_status moba_forward_noalloc(const moba_args* a);
+
 /* Full attention in the general form; block_size, topk, k_block_mean and
  * sel_out are ignored. */
 moba_status moba_full_attention_ex(const moba_args* a);

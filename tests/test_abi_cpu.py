@@ -336,3 +336,17 @@ def test_block_count_limit():
     a.q_len = a.kv_len = 8192 * 64 + 1
     assert moba._lib.moba_workspace_size(ctypes.byref(a)) == 0
     assert "8192" in moba.moba_last_error()
+
+
+def test_noalloc_refuses_a_problem_past_its_scratch():
+    """moba_forward_noalloc holds a 64 MiB scratch array per GPU: a problem
+    whose workspace is larger is UNSUPPORTED, refused before any launch (no
+    GPU is touched), with the sizes in the message."""
+    import block_sparse_attention_gate_amd as moba
+    a = _args(q_len=1 << 17, kv_len=1 << 17)      # 128K tokens, 32/8 heads
+    assert moba._lib.moba_workspace_size(ctypes.byref(a)) > 64 << 20
+    assert moba._lib.moba_forward_noalloc(ctypes.byref(a)) == moba.MOBA_ERR_UNSUPPORTED
+    assert "moba_forward_noalloc holds at most" in moba.moba_last_error()
+    bad = _args(head_dim=96)
+    assert moba._lib.moba_forward_noalloc(ctypes.byref(bad)) == moba.MOBA_ERR_UNSUPPORTED
+    assert "head_dim" in moba.moba_last_error()
