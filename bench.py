@@ -161,7 +161,9 @@ def kernel_breakdown(moba, fn, steps):
     for name in moba.KERNEL_NAMES:
         ms, n = moba.moba_profile_read(name)
         if n:
-            out[name] = {"avg_ms": ms / n, "launches": n}
+            # per_step: launches of the kernel per call (a long prefill routes
+            # in passes of KV heads, one routed launch per pass)
+            out[name] = {"avg_ms": ms / n, "launches": n, "per_step": n / steps}
     moba.moba_profile_reset()
     return out
 
@@ -197,10 +199,11 @@ def run_prefill(moba, w, steps, warmup, full_steps, full_warmup, with_full=True,
         res["cold_effective_tflops"] = eff / (cold_ms * 1e-3) / 1e12
     if "attn_routed" in kern:
         t = kern["attn_routed"]["avg_ms"] * 1e-3
-        res["attn_routed_tflops"] = routed / t / 1e12
+        res["attn_routed_tflops"] = routed / (t * kern["attn_routed"]["per_step"]) / 1e12
+        res["attn_routed_launches_per_step"] = kern["attn_routed"]["per_step"]
     if "attn_own_merge" in kern:
         t = kern["attn_own_merge"]["avg_ms"] * 1e-3
-        res["attn_own_merge_tflops"] = own / t / 1e12
+        res["attn_own_merge_tflops"] = own / (t * kern["attn_own_merge"]["per_step"]) / 1e12
     if with_full:
         fout = torch.empty_like(q)
         fws = torch.empty(max(moba.moba_full_workspace_size(q, k, v), 1), dtype=torch.uint8,
@@ -373,7 +376,9 @@ def roofline(res):
     if "attn_routed" not in kern:
         return None
     t = kern["attn_routed"]["avg_ms"] * 1e-3
-    achieved = res["routed_flop"] / t / 1e12
+    # algorithmic FLOPs of one launch: 4 D B per routed entry, the entries of
+    # one pass (all of them when the call routes in one pass)
+    achieved = res["routed_flop"] / kern["attn_routed"]["per_step"] / t / 1e12
     return {"bound": "mfma", "kernel": "attn_routed", "achieved": achieved,
             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
             "traffic": measured_traffic(f"attn_routed_{res['workload']}_bytes"),
