@@ -147,6 +147,9 @@ _SIGNATURES = {
     "moba_block_mean": (_ST, [_P, _I32, _I64, _I32, _I32, _I32, _P, ctypes.c_int, _P]),
     "moba_block_mean_update": (_ST, [_P, _I32, _I64, _I32, _I32, _I32, _I32, _P, ctypes.c_int,
                                      _P]),
+    "moba_route": (_ST, [_P, _I32, _I32, _I32, _I64, _I64, _I32, _I32, _P, _P, _P,
+                         ctypes.c_size_t, _P]),
+    "moba_route_workspace_size": (ctypes.c_size_t, [_I32, _I32, _I32, _I64, _I64, _I32, _I32]),
     "moba_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "moba_last_error": (ctypes.c_char_p, []),
     "moba_abi_version": (_I32, []),
@@ -389,6 +392,46 @@ def moba_forward_noalloc(q, k, v, block_size, topk, *, out=None, k_block_mean=No
     a.kv_lens = _kv_lens_ptr(kv_lens, S)
     _check(_lib.moba_forward_noalloc(ctypes.byref(a)), "moba_forward_noalloc")
     return out
+
+
+def moba_route_workspace_size(batch, n_heads, n_kv_heads, q_len, kv_len, block_size,
+                              topk) -> int:
+    """Workspace bytes of moba_route (C ``moba_route_workspace_size``)."""
+    n = int(_lib.moba_route_workspace_size(int(batch), int(n_heads), int(n_kv_heads),
+                                           int(q_len), int(kv_len), int(block_size), int(topk)))
+    if n == 0:
+        raise ValueError(f"moba_route_workspace_size: {_lib.moba_last_error().decode()}")
+    return n
+
+
+def moba_route(sel, n_kv_heads, kv_len, block_size, *, workspace=None):
+    """The query -> block dispatch alone (C ``moba_route``): from a selection
+    ``sel`` int32 [S, H, Lq, topk] (or [H, Lq, topk]) on the GPU, returns
+    ``(bucket_off, list)``: uint32-valued int32 tensors, bucket_off
+    [S * Hkv * nb + 1] (entry offsets per (sequence, KV head, block) bucket)
+    and the slot ids of the routed entries bucket by bucket, ascending inside
+    each bucket (list holds bucket_off[-1] entries)."""
+    _dev_tensor(sel, "sel", torch.int32)
+    if sel.dim() == 3:
+        sel = sel.unsqueeze(0)
+    if sel.dim() != 4:
+        raise ValueError("sel must be [S, H, Lq, topk] or [H, Lq, topk]")
+    S, H, Lq, topk = (int(x) for x in sel.shape)
+    nb = -(-int(kv_len) // int(block_size))
+    args = (S, H, int(n_kv_heads), Lq, int(kv_len), int(block_size), topk)
+    need = int(_lib.moba_route_workspace_size(*args))
+    if need == 0:
+        raise ValueError(f"moba_route: {_lib.moba_last_error().decode()}")
+    ws = _workspace_tensor(need, sel.device, workspace)
+    boff = torch.empty(S * int(n_kv_heads) * nb + 1, dtype=torch.int32, device=sel.device)
+    lst = torch.empty(max(S * H * Lq * (topk - 1), 1), dtype=torch.int32, device=sel.device)
+    st = _lib.moba_route(sel.data_ptr(), *args, boff.data_ptr(), lst.data_ptr(),
+                         None if ws is None else ws.data_ptr(),
+                         0 if ws is None else ws.numel() * ws.element_size(),
+                         _stream_ptr(sel.device))
+    _check(st, "moba_route")
+    n = int(boff[-1].item())
+    return boff, lst[:n]
 
 
 def _bwd_args(q, k, v, out, dout, lse, sel, dq, dk, dv, block_size, topk) -> MobaBwdArgs:

@@ -1051,6 +1051,38 @@ moba_args simple_args(const void* q, const void* k, const void* v, int64_t seq_l
   return a;
 }
 
+// ------------------------------------------------------------ routing alone
+
+// Dims and workspace layout of moba_route (a moba_args view of its arguments
+// through forward_dims, so the limits are the forward's).
+moba_status plan_route(int32_t batch, int32_t n_heads, int32_t n_kv_heads, int64_t q_len,
+                       int64_t kv_len, int32_t block_size, int32_t topk, Plan* p) {
+  moba_args a;
+  std::memset(&a, 0, sizeof(a));
+  a.struct_size = sizeof(moba_args);
+  const uintptr_t fake = (uintptr_t)1 << 40;   // checked, never dereferenced
+  a.q = a.k = a.v = (const void*)fake;
+  a.out = (void*)fake;
+  a.batch = batch; a.n_heads = n_heads; a.n_kv_heads = n_kv_heads; a.head_dim = 128;
+  a.block_size = block_size; a.topk = topk; a.q_len = q_len; a.kv_len = kv_len;
+  a.dtype = MOBA_DTYPE_BF16;
+  moba_status st = forward_dims(&a, p);
+  if (st != MOBA_OK) return st;
+  const Dims& d = p->d;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  p->off_counts = take((size_t)d.nrows * d.ncols * 4);
+  p->off_btotal = take((size_t)d.nrows * 4);
+  p->off_toff = take((size_t)(d.nrows + 1) * 4);
+  p->total = off;
+  return MOBA_OK;
+}
+
+
 template <class F>
 moba_status guarded(F&& f) {
   g_last_error.clear();
@@ -1306,6 +1338,69 @@ moba_status moba_block_mean_update(const void* k, int32_t batch, int64_t kv_len,
                                    void* stream) {
   return block_mean_impl(k, batch, kv_len, n_kv_heads, head_dim, block_size, first_block,
                          k_block_mean, dtype, stream);
+}
+
+moba_status moba_route(const int32_t* sel, int32_t batch, int32_t n_heads, int32_t n_kv_heads,
+                       int64_t q_len, int64_t kv_len, int32_t block_size, int32_t topk,
+                       uint32_t* bucket_off, uint32_t* list, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  return guarded([&]() -> moba_status {
+    if (!sel || !bucket_off || !list)
+      return fail(MOBA_ERR_INVALID_ARGUMENT, "sel, bucket_off and list must be non-NULL");
+    if (((uintptr_t)sel | (uintptr_t)bucket_off | (uintptr_t)list) & 3)
+      return fail(MOBA_ERR_INVALID_ARGUMENT, "sel, bucket_off and list must be 4-byte aligned");
+    if ((uintptr_t)workspace & 15)
+      return fail(MOBA_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+    Plan p;
+    moba_status st = plan_route(batch, n_heads, n_kv_heads, q_len, kv_len, block_size, topk, &p);
+    if (st != MOBA_OK) return st;
+    if (workspace && workspace_bytes < p.total)
+      return fail(MOBA_ERR_INVALID_ARGUMENT, "workspace too small: %zu < %zu bytes",
+                  workspace_bytes, p.total);
+    Dims& d = p.d;
+    moba_args wa;
+    std::memset(&wa, 0, sizeof(wa));
+    wa.workspace = workspace;
+    wa.stream = stream;
+    Workspace ws;
+    st = get_workspace(&wa, p, &ws);
+    if (st != MOBA_OK) return st;
+    Launch l{(hipStream_t)stream};
+    char* w = ws.base;   // (topk 1: the counts are all zero, every bucket empty)
+    uint32_t* counts = (uint32_t*)(w + p.off_counts);
+    uint32_t* btotal = (uint32_t*)(w + p.off_btotal);
+    uint32_t* toff = (uint32_t*)(w + p.off_toff);
+    l.run(K_RCOUNT, [&] { return moba::launch_route_count(sel, counts, d, l.st); });
+    const bool small_scan = moba::route_scan_small_fits(d);
+    if (small_scan) {
+      l.run(K_RSCAN_SMALL,
+            [&] { return moba::launch_route_scan_small(counts, bucket_off, toff, d, l.st); });
+    } else {
+      l.run(K_RSCAN_ROWS, [&] { return moba::launch_route_scan_rows(counts, btotal, d, l.st); });
+      l.run(K_RSCAN_BUCKETS, [&] {
+        return moba::launch_route_scan_buckets(btotal, bucket_off, toff, d, l.st);
+      });
+    }
+    l.run(K_RSCATTER, [&] {
+      return moba::launch_route_scatter(sel, counts, bucket_off, list, d, l.st, small_scan);
+    });
+    if (l.err != hipSuccess) return hip_fail(l);
+    return MOBA_OK;
+  });
+}
+
+size_t moba_route_workspace_size(int32_t batch, int32_t n_heads, int32_t n_kv_heads,
+                                 int64_t q_len, int64_t kv_len, int32_t block_size,
+                                 int32_t topk) {
+  size_t n = 0;
+  (void)guarded([&]() -> moba_status {
+    Plan p;
+    const moba_status st =
+        plan_route(batch, n_heads, n_kv_heads, q_len, kv_len, block_size, topk, &p);
+    if (st == MOBA_OK) n = p.total;
+    return st;
+  });
+  return n;
 }
 
 const char* moba_status_string(moba_status s) {

@@ -323,6 +323,34 @@ moba_status moba_block_mean_update(const void* k, int32_t batch, int64_t kv_len,
                                    int32_t first_block, float* k_block_mean, moba_dtype dtype,
                                    void* stream);
 
+/*
+ * The query -> KV-block dispatch of the forward on its own (the pages liken
+ * the gate to an MoE router with the blocks as experts: "MoBA" project card,
+ * "How It Works"; AiBoss MoBA article, "MoBAの主な機能"): from a selection
+ * `sel` [batch, n_heads, q_len, topk] (sel_out of moba_forward_ex, device),
+ * every routed entry -- query row r of head h in sequence s with its t-th
+ * kept PAST block (t < topk - 1; the own block is not routed) -- is listed
+ * in the bucket of (s, h / (n_heads / n_kv_heads), block), buckets in that
+ * order:
+ *   bucket_off [batch * n_kv_heads * nb + 1] (uint32, device): entry
+ *     offsets, bucket_off[0] = 0 and the last one the number of entries;
+ *   list [batch * n_heads * q_len * (topk - 1)] (uint32, device; only the
+ *     first bucket_off[last] are written): slot ids
+ *     ((s * n_heads + h) * q_len + r) * (topk - 1) + t, ascending inside
+ *     each bucket (a stable counting sort: the same bits on every run).
+ * nb = ceil(kv_len / block_size); query row r sits at position
+ * kv_len - q_len + r; the limits and checks are moba_forward_ex's.  Entries
+ * whose block is not a kept past block (-1 padding) are skipped.
+ * Workspace: moba_route_workspace_size bytes (stream-ordered when NULL).
+ */
+moba_status moba_route(const int32_t* sel, int32_t batch, int32_t n_heads, int32_t n_kv_heads,
+                       int64_t q_len, int64_t kv_len, int32_t block_size, int32_t topk,
+                       uint32_t* bucket_off, uint32_t* list, void* workspace,
+                       size_t workspace_bytes, void* stream);
+size_t moba_route_workspace_size(int32_t batch, int32_t n_heads, int32_t n_kv_heads,
+                                 int64_t q_len, int64_t kv_len, int32_t block_size,
+                                 int32_t topk);
+
 const char* moba_status_string(moba_status s);
 const char* moba_last_error(void);
 int32_t moba_abi_version(void);

@@ -405,6 +405,33 @@ def test_grouped_routing_128k_bitwise():
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
 
 
+@pytest.mark.parametrize("w", [
+    moba_inputs.custom("route_gqa", "bf16", 2, 700, 1500, 6, 2, 128, 64, 5, 81),
+    moba_inputs.custom("route_small_scan", "bf16", 1, 1024, None, 4, 1, 64, 128, 3, 82),
+    moba_inputs.custom("route_large_scan", "bf16", 1, 20000, None, 8, 4, 64, 256, 6, 83),
+], ids=lambda w: w.name)
+def test_routing_table_equals_the_oracle(w):
+    """The GPU's query -> block dispatch (moba_route on the forward's own
+    selection) equals the oracle's routing table element by element: bucket
+    offsets and the slot ids in every bucket (a stable counting sort, so the
+    order inside a bucket is unique).  Chunked queries at the end of a longer
+    cache, the one-workgroup scan and the two-kernel scan."""
+    moba = _moba()
+    q, k, v = moba_inputs.make_inputs(w, device=DEV)
+    out, sel = moba.moba_forward_ex(q, k, v, w.block_size, w.topk, return_selection=True)
+    boff, lst = moba.moba_route(sel, w.n_kv_heads, w.kv_len, w.block_size)
+    torch.cuda.synchronize()
+    nb = -(-w.kv_len // w.block_size)
+    sel_np = sel.cpu().numpy()
+    counts, offsets, entries = O.routing_table(sel_np, w.n_kv_heads, nb, w.block_size,
+                                               w.kv_len - w.q_len)
+    got_off = boff.cpu().numpy().astype(np.int64)
+    got = lst.cpu().numpy().astype(np.int64) & 0xFFFFFFFF
+    print(f"  {w.name}: {entries.size} routed entries in {counts.size} buckets", flush=True)
+    np.testing.assert_array_equal(got_off, offsets)
+    np.testing.assert_array_equal(got, entries)
+
+
 def test_prefill_1m_parity():
     """The 1M-token prefill (32/8 heads, block 4096, top-k 12): the selection
     of every query row of every head (33.6M query-heads), outputs sampled."""
