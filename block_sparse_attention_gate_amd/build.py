@@ -14,7 +14,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build", "moba")
 LIB_PATH = os.path.join(PKG, "libmoba.so")
 
-SOURCES = ["api.cpp", "pool.hip", "gate.hip", "route.hip", "attn_bf16.hip", "attn_bwd.hip",
+SOURCES = ["api.cpp", "plan.cpp", "pool.hip", "gate.hip", "route.hip", "attn_bf16.hip", "attn_bwd.hip",
            "attn_f32.hip", "attn_bwd_f32.hip",
            "decode.hip", "naive.hip", "scratch.hip"]
 

@@ -689,17 +689,6 @@ static void query_shape(const Dims& d, int* HW, int* NW) {
   *NW = wgs8 >= 2048 ? 8 : 4;
 }
 
-int full_split_parts(const Dims& d) {
-  if (!d.bf16) return 0;
-  const int HW = gcd_int(d.G, 4);
-  const int RW = 256 / HW;  // eight-wave workgroups
-  const int64_t wgs = (d.Lq + RW - 1) / RW * (int64_t)(d.S * d.H / HW);
-  if (wgs >= 1024) return 0;  // whole row tiles already fill the chip
-  const int64_t tiles = (d.q_off + d.Lq + 63) / 64;  // key tiles of the longest row
-  const int64_t p = (tiles + kFullChunkTiles - 1) / kFullChunkTiles;
-  return p > 1 && p <= kFullMaxParts ? (int)p : 0;
-}
-
 hipError_t launch_attn_query_bf16(const void* q, const void* k, const void* vt,
                                   const void* ktail, const void* part_o, const float* part_lse,
                                   void* out, int mode, const Dims& d, hipStream_t st,

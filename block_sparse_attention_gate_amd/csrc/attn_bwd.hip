@@ -873,21 +873,7 @@ hipError_t launch_bwd_dq_own(const void* q, const void* dout, const void* k, con
   return hipGetLastError();
 }
 
-int bwd_dkdv_waves(const Dims& d) { return d.B % 128 == 0 ? 4 : 2; }
 constexpr int kDkdvNQ = 2;   // 64 queries per step
-
-int bwd_dkdv_segments(const Dims& d) {
-  const int KC = 32 * bwd_dkdv_waves(d);
-  const int64_t wgs = (int64_t)d.S * d.Hkv * d.nb * ((d.B + KC - 1) / KC);
-  if (wgs >= 1024) return 1;
-  const int64_t sgs = (1024 + wgs - 1) / wgs;
-  return sgs > 8 ? 8 : (int)sgs;
-}
-
-size_t bwd_dkdv_partial_floats(const Dims& d) {
-  const int nseg = bwd_dkdv_segments(d);
-  return nseg > 1 ? (size_t)nseg * 2 * d.S * d.L * d.Hkv * d.D : 0;
-}
 
 hipError_t launch_bwd_dkdv(const void* q, const void* dout, const void* k, const void* v,
                            const float* lse, const float* dvec, const uint32_t* list,

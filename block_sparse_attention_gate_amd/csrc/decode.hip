@@ -21,7 +21,6 @@
 
 namespace moba {
 
-constexpr int kDecChunk = 512;  // keys per decode work item
 
 // grid S*Hkv, 64 threads.
 // all_blocks = 1 selects every block for every head (split-K full attention).
@@ -256,7 +255,6 @@ __global__ __launch_bounds__(256) void k_decode_attn(
 // (union slot, then chunk); the max, the weights and the sum of the partials
 // are then workgroup reductions, and the weighted sum of the partial rows
 // keeps eight loads in flight (fixed order: deterministic).
-constexpr int kMergeMaxItems = 8192;
 template <typename T, int D, int GM>
 __global__ __launch_bounds__(D) void k_decode_merge(const float* __restrict__ part,
                                                     const int32_t* __restrict__ ublk,
@@ -340,27 +338,6 @@ __global__ __launch_bounds__(D) void k_decode_merge(const float* __restrict__ pa
     reinterpret_cast<bf16_t*>(orow)[tid] = f32_to_bf16(r);
   else
     reinterpret_cast<float*>(orow)[tid] = r;
-}
-
-int decode_umax(const Dims& d) {
-  const int u = d.G * d.topk;
-  return u < d.nb ? u : d.nb;
-}
-
-int decode_chunk() { return kDecChunk; }
-
-int decode_gm(const Dims& d) {
-  return d.G <= 1 ? 1 : d.G <= 2 ? 2 : d.G <= 4 ? 4 : 8;
-}
-
-size_t decode_part_floats(const Dims& d) {
-  return (size_t)d.S * d.Hkv * decode_umax(d) * (d.B / kDecChunk) * decode_gm(d) * (d.D + 2);
-}
-
-bool decode_supported(const Dims& d) {
-  // the merge lists at most kMergeMaxItems partials per head
-  return d.Lq == 1 && d.G <= 8 && d.B % kDecChunk == 0 &&
-         (int64_t)decode_umax(d) * (d.B / kDecChunk) <= kMergeMaxItems;
 }
 
 hipError_t launch_decode_plan(const int32_t* sel, int32_t* ublk, uint32_t* umask,

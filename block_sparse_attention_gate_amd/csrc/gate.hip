@@ -481,17 +481,6 @@ static hipError_t gate_dispatch_d(const void* q, const float* kbar, int32_t* sel
   return hipErrorInvalidValue;
 }
 
-// bf16 with one query row per (sequence, head): the decode gate (one
-// workgroup per query-head), whatever the group size.  It writes no routing
-// histogram, so the route_count step must run after it when the call routes.
-bool gate_uses_decode_kernel(const Dims& d) { return d.bf16 && d.Lq == 1; }
-
-// The routing histogram comes from the same predicate as the dispatch above:
-// only the 128-row bf16 gate writes it.
-bool gate_writes_counts(const Dims& d) {
-  return d.bf16 && !gate_uses_decode_kernel(d) && kRouteChunkRows == 128;
-}
-
 hipError_t launch_gate_topk(const void* q, const float* kbar, int32_t* sel, const Dims& d,
                             hipStream_t st, uint32_t* counts) {
   if (counts && !gate_writes_counts(d)) return hipErrorInvalidValue;

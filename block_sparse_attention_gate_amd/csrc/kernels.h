@@ -13,6 +13,9 @@ constexpr int kFullChunkTiles = 64;    // key chunk (64-key tiles) of split full
 constexpr int kFullMaxParts = 64;      // at most this many chunks per row
 constexpr int kMaxTopk = 17;           // largest supported topk (16 routed blocks + own)
 constexpr int kRoutedLdsRows = 4096;   // buckets whose offsets the routed kernel keeps in LDS
+constexpr int kScanSmallMax = 16 * 1024;  // count-matrix entries route_scan_small handles
+constexpr int kDecChunk = 512;         // keys per decode work item
+constexpr int kMergeMaxItems = 8192;   // decode partials the merge lists per head, at most
 constexpr int kMaxGridCacheDevices = 64;  // devices whose per-device pointers are kept
 // Device scratch of moba_forward_noalloc (a static array per GPU).
 constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
@@ -79,6 +82,7 @@ hipError_t noalloc_scratch(void** out);
 // launch_transpose_v (given the same partial / kbar) finishes the means.
 // j0 > 0 computes only blocks j0 .. nb-1 (partial then holds
 // block_mean_update_partial_floats(d, j0) floats; no defer_finalize).
+int block_mean_splits(const Dims& d);
 size_t block_mean_partial_floats(const Dims& d);
 size_t block_mean_update_partial_floats(const Dims& d, int j0);
 hipError_t launch_block_mean(const void* k, float* kbar, float* partial, const Dims& d,
@@ -161,6 +165,7 @@ hipError_t launch_attn_query_f32(const void* q, const void* k, const void* v, co
 bool decode_supported(const Dims& d);   // q_len 1, G <= 8, block_size % 512 == 0
 int decode_chunk();
 int decode_umax(const Dims& d);
+int decode_gm(const Dims& d);           // query heads per decode work item (1, 2, 4 or 8)
 size_t decode_part_floats(const Dims& d);
 hipError_t launch_decode_plan(const int32_t* sel, int32_t* ublk, uint32_t* umask,
                               int32_t* ucount, bool all_blocks, const Dims& d, hipStream_t st);
@@ -190,6 +195,8 @@ hipError_t launch_bwd_dq_own(const void* q, const void* dout, const void* k, con
 // list / bucket_off NULL: no routed entries (top-k 1 or a single block).
 // kvpart: bwd_dkdv_partial_floats(d) floats (small problems split every
 // bucket into segments whose fp32 partials are added afterwards; else NULL).
+int bwd_dkdv_waves(const Dims& d);
+int bwd_dkdv_segments(const Dims& d);
 size_t bwd_dkdv_partial_floats(const Dims& d);
 hipError_t launch_bwd_dkdv(const void* q, const void* dout, const void* k, const void* v,
                            const float* lse, const float* dvec, const uint32_t* list,

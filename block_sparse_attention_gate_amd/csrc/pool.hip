@@ -121,27 +121,6 @@ __global__ __launch_bounds__(256) void k_block_mean_finalize(const float* __rest
   }
 }
 
-int block_mean_splits(const Dims& d) {
-  // enough workgroups to cover the chip (>= 1024), at least 64 rows each
-  int splits = 1;
-  const int64_t wgs = (int64_t)d.nb * d.S;
-  while (wgs * splits < 1024 && d.B % (splits * 2) == 0 && d.B / (splits * 2) >= 64) splits *= 2;
-  return splits;
-}
-
-size_t block_mean_partial_floats(const Dims& d) {
-  const int sp = block_mean_splits(d);
-  return sp > 1 ? (size_t)d.S * d.nb * sp * d.Hkv * d.D : 0;
-}
-
-// The split count is that of the whole problem also when only blocks j0..
-// are computed, so that every block's sum is formed in the same order (the
-// same bits) as by the full computation.
-size_t block_mean_update_partial_floats(const Dims& d, int j0) {
-  const int sp = block_mean_splits(d);
-  return sp > 1 ? (size_t)d.S * (d.nb - j0) * sp * d.Hkv * d.D : 0;
-}
-
 hipError_t launch_block_mean(const void* k, float* kbar, float* partial, const Dims& d,
                              hipStream_t st, bool defer_finalize, int j0) {
   if (j0 < 0 || j0 >= d.nb || (defer_finalize && j0 != 0)) return hipErrorInvalidValue;

@@ -247,7 +247,6 @@ hipError_t launch_route_scatter(const int32_t* sel, const uint32_t* counts,
 // bucket order, then column order), and derives the bucket and tile offsets
 // from it.  Thread t scans the contiguous segment [t*seg, (t+1)*seg).
 constexpr int kScanSmallThreads = 1024;
-constexpr int kScanSmallMax = 16 * 1024;   // counts handled by route_scan_small
 
 __global__ __launch_bounds__(kScanSmallThreads) void k_route_scan_small(
     uint32_t* __restrict__ counts, uint32_t* __restrict__ bucket_off,
@@ -342,20 +341,12 @@ __global__ __launch_bounds__(kScanSmallThreads) void k_route_scan_small(
   }
 }
 
-bool route_scan_small_fits(const Dims& d) {
-  return (int64_t)d.pnrows * d.ncols <= kScanSmallMax;
-}
-
 hipError_t launch_route_scan_small(uint32_t* counts, uint32_t* bucket_off, uint32_t* tile_off,
                                    const Dims& d, hipStream_t st) {
   hipLaunchKernelGGL(k_route_scan_small, dim3(1), dim3(kScanSmallThreads), 0, st,
                      counts + d.prow0 * d.ncols, bucket_off, tile_off, d.pnrows, d.ncols,
                      d.tile_m);
   return hipGetLastError();
-}
-
-int64_t routed_tile_bound(const Dims& d) {
-  return (d.pslots + d.tile_m - 1) / d.tile_m + d.pnrows;
 }
 
 }  // namespace moba
