@@ -19,13 +19,16 @@
 //                    the query's routed dq partials -> dq.
 //   k_bwd_dkdv       per 32 * NW keys of one block (key-stationary, no
 //                    atomics): loops over the block's routed entries and its
-//                    own queries 32 at a time; S = Q K^T and dP = dO V^T with
+//                    own queries 64 at a time; S = Q K^T and dP = dO V^T with
 //                    the wave's K and V rows as register B operands, then
-//                    dV^T += dO^T P and dK^T += Q^T dS from transposed Q / dO
-//                    tiles in LDS.
+//                    dV^T += dO^T P and dK^T += Q^T dS with the A operands
+//                    read transposed (LDS transpose reads) from the same Q /
+//                    dO tiles.
 // Queries are loaded into the MFMA A rows in the kperm order (common.h), so
 // the accumulator of a product over 32 queries is directly the B operand of
 // the following product over those queries.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -470,28 +473,76 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_bwd_dq_own(
 }
 
 // ============================================================ dk, dv kernel
-// QN = 32 NQ queries per step.
-template <int D, int NW, int NQ>
+// Q and dO tiles of QN = 64 queries, row-major in LDS.  The A operands of
+// dV^T += dO^T P and dK^T += Q^T dS (rows d, contraction over queries) are
+// read from the same row-major tiles with the LDS transpose read.
+template <int D, int NW>
 struct KvTiles {
   static constexpr int NT = 64 * NW;
-  static constexpr int QN = 32 * NQ;
-  static constexpr int QS = D + 8;              // Q / dO tile row stride (QN rows)
-  static constexpr int TS = QN + 8;             // Q^T / dO^T tile row stride (D rows)
-  static constexpr int QE = QN * QS;
-  static constexpr int TE = D * TS;
-  static constexpr int BUF = 2 * QE + 2 * TE;   // Q, dO, Q^T, dO^T (bf16 elements)
-  static constexpr int CH = QN * (D / 8) / NT;  // 16-byte chunks per thread per tensor
+  static constexpr int QN = 64;
+  static constexpr int QE = QN * D;
+  static constexpr int BUF = 2 * QE;            // Q, dO (bf16 elements)
+  static constexpr int CH = D / 8 / NW;         // 16-byte chunks of a row per thread per tensor
 };
+
+// Q / dO tiles: QN rows of D bf16, unpadded, with the 16-byte chunks of row r
+// permuted by XOR with kv_swz(r).  The pattern makes both reads of the tiles
+// free of LDS bank conflicts: 16 consecutive rows at one chunk (the MFMA A
+// rows of S and dP), and 4 consecutive rows x 4 consecutive chunks (a
+// 32-lane half of a transpose read).
+template <int D>
+__device__ __forceinline__ int kv_swz(int r) {
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
+template <int D>
+__device__ __forceinline__ int kv_off(int r, int chunk) {
+  return r * D + ((chunk ^ kv_swz<D>(r)) << 3);
+}
+
+// A operand of a product over queries (rows d = 32 dt + lane % 32, k-slots =
+// queries 16 c2 + 8 (lane / 32) + [0, 8)) from a row-major [query][d] tile.
+// The LDS transpose read (16-bit elements, 64 bits per lane) hands lane i of
+// each 16-lane group element i % 4 of the values read by lanes i / 4 + 4e of
+// its group, e = 0..3; so lane 4e + f of a group reads dims 4f.. of query e,
+// and lane i receives dim i of four consecutive queries.  Two reads give the
+// eight queries.
+template <int D>
+__device__ __forceinline__ bf16x8 tr_frag(const bf16_t* tile, int dt, int c2, int lane) {
+  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+  const int grp = lane >> 4, e = (lane >> 2) & 3, f = lane & 3;
+  const int col = 32 * dt + 16 * (grp & 1) + 4 * f;
+  bf16x4 part[2];
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int r = 16 * c2 + 8 * (grp >> 1) + 4 * half + e;
+    const bf16_t* p = tile + kv_off<D>(r, col >> 3) + (col & 7);
+    part[half] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)const_cast<bf16_t*>(p));
+  }
+  return bf16x8{part[0][0], part[0][1], part[0][2], part[0][3],
+                part[1][0], part[1][1], part[1][2], part[1][3]};
+}
+
+// Calls f(std::integral_constant<int, K>) for K = B .. E-1 in order (a loop
+// whose index is a compile-time constant in the body).
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
 
 // Key-stationary: workgroup (s, g, block j, chunk c, segment) owns keys
 // [jB + c*32*NW, +32*NW) of the block (wave w the 32 from +32w) and loops over
 // its segment of the block's routed entries, then of its own queries (one
-// head at a time, QN positions per step, causal mask), QN = 32 NQ queries per
-// step.  With nseg = 1 it writes dk, dv; with more segments (small problems,
-// whose few long buckets would leave the chip idle) each segment writes fp32
-// partials [nseg][2][S, L, Hkv, D] that k_bwd_reduce_kv adds in segment order.
+// head at a time, 64 positions per step, causal mask).  With nseg = 1 it
+// writes dk, dv; with more segments (small problems, whose few long buckets
+// would leave the chip idle) each segment writes fp32 partials
+// [nseg][2][S, L, Hkv, D] that k_bwd_reduce_kv adds in segment order.
 // grid (S * Hkv * nb * ceil(B / (32 NW)) * nseg), 64*NW threads.
-template <int D, int NW, int NQ>
+template <int D, int NW>
 __global__ __launch_bounds__(64 * NW, 1) void k_bwd_dkdv(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ dout,
     const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, const float* __restrict__ lse,
@@ -499,7 +550,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_bwd_dkdv(
     const uint32_t* __restrict__ bucket_off, bf16_t* __restrict__ dk, bf16_t* __restrict__ dv,
     float* __restrict__ kvpart, int Lq, int L, int q_off, int H, int Hkv, int kp, int B, int nb,
     int nchunk, int nseg, FastDiv fd_kp, FastDiv fd_lq, float sl2, float scale) {
-  using T = KvTiles<D, NW, NQ>;
+  using T = KvTiles<D, NW>;
   constexpr int QN = T::QN;
   __shared__ __attribute__((aligned(16))) bf16_t lds[2 * T::BUF];
   __shared__ __attribute__((aligned(16))) float stat[2][2][QN];  // [buffer][lse2, Dv][query]
@@ -558,22 +609,19 @@ __global__ __launch_bounds__(64 * NW, 1) void k_bwd_dkdv(
   const int olo = (int)((int64_t)nown_all * seg / nseg);   // this segment's own steps
   const int nsteps = rsteps + (int)((int64_t)nown_all * (seg + 1) / nseg) - olo;
 
-  // Staging, three steps in flight: the entry ids of step it+2 (routed steps
-  // read them from the list), the Q / dO rows and the two statistics of step
+  // Staging, three steps in flight: the entry id of step it+2 (routed steps
+  // read it from the list), the Q / dO row and the two statistics of step
   // it+1 (requested once step it's first products are issued), and the LDS
-  // tiles of step it.
-  // Thread chunk i covers query qi = (tid + NT i) % QN, dims cc*8.. with
-  // cc = (tid + NT i) / QN: the lanes of a transposed store then write
-  // different queries of one row.
+  // tiles of step it.  Lane l stages query l of a step; wave w its 16-byte
+  // chunks w, w + NW, ... of the row.
   u32x4 qr[T::CH], dr[T::CH];
-  float st_l = 0.f, st_d = 0.f;      // threads < QN: lse2, Dv of query tid (step it+1)
-  uint32_t ida[T::CH];               // entry ids of step it+1, then it+2
-  uint32_t sida = 0u;                // threads < QN: the id of query tid
-  // query (row offset, query-head index) of query qi of a step, or false
-  auto query_at = [&](int step, int qi, uint32_t id, int64_t& qrow, int64_t& qhi) -> bool {
+  float st_l = 0.f, st_d = 0.f;      // wave 0: lse2, Dv of query `lane` (step it+1)
+  uint32_t ida = 0u;                 // entry id of query `lane` of step it+1, then it+2
+  // query `lane` of a step: row offset and query-head index, or false
+  auto query_at = [&](int step, uint32_t id, int64_t& qrow, int64_t& qhi) -> bool {
     int r, h;
     if (step < rsteps) {
-      if (step * QN + qi >= nrt) return false;
+      if (step * QN + lane >= nrt) return false;
       const uint32_t qhh = fdiv(id, fd_kp);             // (s*H + h)*Lq + r
       const uint32_t sh = fdiv(qhh, fd_lq);             // s*H + h
       r = (int)(qhh - sh * fd_lq.d);
@@ -582,7 +630,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_bwd_dkdv(
     } else {
       const int st = step - rsteps + olo;
       const int hl = st / psteps_h, pc = st - hl * psteps_h;
-      const int p = p0 + pc * QN + qi;
+      const int p = p0 + pc * QN + lane;
       if (p >= pend) return false;
       r = p - q_off;
       h = g * G + hl;
@@ -591,31 +639,22 @@ __global__ __launch_bounds__(64 * NW, 1) void k_bwd_dkdv(
     qhi = ((int64_t)s * H + h) * Lq + r;
     return true;
   };
-  auto fetch_ids = [&](int step) {
+  auto fetch_id = [&](int step) {
     if (step >= rsteps) return;  // own steps need no ids
-#pragma unroll
-    for (int i = 0; i < T::CH; ++i) {
-      const int e = step * QN + (tid + T::NT * i) % QN;
-      ida[i] = e < nrt ? list[rbase + e] : 0u;
-    }
-    if (tid < QN) {
-      const int e = step * QN + tid;
-      sida = e < nrt ? list[rbase + e] : 0u;
-    }
+    const int e = step * QN + lane;
+    ida = e < nrt ? list[rbase + e] : 0u;
   };
   auto fetch_rows = [&](int step) {
+    int64_t qrow = 0, qhi = 0;
+    const bool ok = query_at(step, ida, qrow, qhi);
+    const bf16_t* qp = q + qrow + 8 * w;
+    const bf16_t* dp = dout + qrow + 8 * w;
 #pragma unroll
     for (int i = 0; i < T::CH; ++i) {
-      const int cidx = tid + T::NT * i;
-      const int qi = cidx % QN, cc = cidx / QN;
-      int64_t qrow = 0, qhi = 0;
-      const bool ok = query_at(step, qi, ida[i], qrow, qhi);
-      qr[i] = ok ? *reinterpret_cast<const u32x4*>(q + qrow + cc * 8) : u32x4{0u, 0u, 0u, 0u};
-      dr[i] = ok ? *reinterpret_cast<const u32x4*>(dout + qrow + cc * 8) : u32x4{0u, 0u, 0u, 0u};
+      qr[i] = ok ? *reinterpret_cast<const u32x4*>(qp + 8 * NW * i) : u32x4{0u, 0u, 0u, 0u};
+      dr[i] = ok ? *reinterpret_cast<const u32x4*>(dp + 8 * NW * i) : u32x4{0u, 0u, 0u, 0u};
     }
-    if (tid < QN) {
-      int64_t qrow = 0, qhi = 0;
-      const bool ok = query_at(step, tid, sida, qrow, qhi);
+    if (w == 0) {
       // an invalid query gets lse2 = +inf, hence p = 0 (its rows are zero)
       st_l = ok ? lse[qhi] * kLog2e : __builtin_inff();
       st_d = ok ? dvec[qhi] : 0.f;
@@ -625,107 +664,147 @@ __global__ __launch_bounds__(64 * NW, 1) void k_bwd_dkdv(
     bf16_t* b = lds + buf * T::BUF;
 #pragma unroll
     for (int i = 0; i < T::CH; ++i) {
-      const int cidx = tid + T::NT * i;
-      const int qi = cidx % QN, cc = cidx / QN;
-      *reinterpret_cast<u32x4*>(b + qi * T::QS + cc * 8) = qr[i];
-      *reinterpret_cast<u32x4*>(b + T::QE + qi * T::QS + cc * 8) = dr[i];
-      const bf16_t* qe = reinterpret_cast<const bf16_t*>(&qr[i]);
-      const bf16_t* de = reinterpret_cast<const bf16_t*>(&dr[i]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        b[2 * T::QE + (cc * 8 + e) * T::TS + qi] = qe[e];
-        b[2 * T::QE + T::TE + (cc * 8 + e) * T::TS + qi] = de[e];
-      }
+      const int o = kv_off<D>(lane, w + NW * i);
+      *reinterpret_cast<u32x4*>(b + o) = qr[i];
+      *reinterpret_cast<u32x4*>(b + T::QE + o) = dr[i];
     }
-    if (tid < QN) {
-      stat[buf][0][tid] = st_l;
-      stat[buf][1][tid] = st_d;
+  };
+  auto stage_stats = [&](int buf) {
+    if (w == 0) {
+      stat[buf][0][lane] = st_l;
+      stat[buf][1][lane] = st_d;
     }
   };
 
-  // prologue: tiles of step 0, ids of step 1
+  // prologue: tiles of step 0, id of step 1
   if (nsteps > 0) {
-    fetch_ids(0);
+    fetch_id(0);
     fetch_rows(0);
     stage_store(0);
-    if (nsteps > 1) fetch_ids(1);
+    stage_stats(0);
+    if (nsteps > 1) fetch_id(1);
   }
   __syncthreads();
+  // One step is a fixed sequence of 4 NS MFMA slots (NS = D / 8), each with
+  // its A fragment read from LDS kPre slots ahead:
+  //   phase 0  S and dP of queries 0-31 (t = slot / 2; S on even slots)
+  //   phase 1  S and dP of queries 32-63, with the softmax of queries 0-31
+  //   phase 2  dV^T and dK^T over queries 0-31 (transpose reads), with the
+  //            softmax of queries 32-63
+  //   phase 3  dV^T and dK^T over queries 32-63, with the stores of the next
+  //            step's tiles in its last slots
+  // One wave runs per SIMD, so the softmax arithmetic and the LDS traffic
+  // have to issue between the MFMAs of the same wave; scheduling barriers
+  // keep each slot's instructions in place.  The products and their
+  // accumulation order are those of the plain loop nest (dV^T / dK^T over
+  // query groups 0..3 in order).
+  constexpr int NS = D / 8;          // slots per phase
+  constexpr int EPS = 16 / NS;       // softmax elements per slot
+  constexpr int GS = 4 / EPS;        // slots per group of four elements
+  constexpr int kPre = 4;
+  const int arow = kperm(n);
+  auto frag = [&](const bf16_t* b, int k) -> bf16x8 {
+    if (k < 2 * NS) {
+      const int qb = k / NS, t = (k % NS) >> 1, tensor = k & 1;
+      return ld_bf16x8(b + tensor * T::QE + kv_off<D>(32 * qb + arow, 2 * t + hh));
+    }
+    const int qb = (k - 2 * NS) / NS, idx = (k - 2 * NS) % NS;
+    const int dt = idx >> 2, c = (idx >> 1) & 1, tensor = idx & 1;   // 0: dO^T, 1: Q^T
+    return tr_frag<D>(b + (tensor ? 0 : T::QE), dt, 2 * qb + c, lane);
+  };
+  // P and dS: register reg of a half's S / dP accumulator (lane half hh)
+  // holds query 32 qb + acc_key(reg, hh); registers [8c, 8c + 8) are the
+  // queries 32 qb + 16 c + 8 hh + [0, 8) in order, the B operand layout of P
+  // and dS for the products over queries.  Queries at positions before the
+  // key (own steps) get p = 0.
+  auto soft = [&](int qb, int reg, int pos0, float s, float dp, const f32x4& l4,
+                  const f32x4& d4, bf16x8 (&pb)[2], bf16x8 (&dsb)[2]) {
+    const int jj = reg & 3;
+    const int qi = 32 * qb + acc_key(reg, hh);
+    float p = __builtin_amdgcn_exp2f(fmaf(s, sl2, -l4[jj]));
+    p = pos0 + qi < key ? 0.f : p;
+    const float ds = p * (dp - d4[jj]);
+    pb[reg >> 3][reg & 7] = static_cast<__bf16>(p);
+    dsb[reg >> 3][reg & 7] = static_cast<__bf16>(ds);
+  };
+
   for (int it = 0; it < nsteps; ++it) {
-    const int cb = it & 1;
-    const bool more = it + 1 < nsteps;
-    const bf16_t* b = lds + cb * T::BUF;
-    const bool own_step = it >= rsteps;
-    // S = Q K^T and dP = dO V^T (32 queries per block x the wave's 32 keys);
-    // A rows in the kperm order
-    f32x16 sacc[NQ], dpacc[NQ];
-#pragma unroll
-    for (int qb = 0; qb < NQ; ++qb) {
-      sacc[qb] = f32x16{};
-      dpacc[qb] = f32x16{};
+    const int CB = it & 1;
+    const bf16_t* b = lds + CB * T::BUF;
+    const float* st = &stat[CB][0][0];
+    // position of the step's first query (own steps); routed steps mask
+    // nothing
+    int pos0 = 0x3fffffff;
+    if (it >= rsteps) {
+      const int sidx = it - rsteps + olo;
+      pos0 = p0 + (sidx - (sidx / psteps_h) * psteps_h) * QN;
     }
-#pragma unroll
-    for (int qb = 0; qb < NQ; ++qb) {
-      const bf16_t* qa = b + (32 * qb + kperm(n)) * T::QS + 8 * hh;
-      const bf16_t* da = b + T::QE + (32 * qb + kperm(n)) * T::QS + 8 * hh;
-      bf16x8 fa[D / 16], fd[D / 16];
-#pragma unroll
-      for (int t = 0; t < D / 16; ++t) fa[t] = ld_bf16x8(qa + 16 * t);
-#pragma unroll
-      for (int t = 0; t < D / 16; ++t) fd[t] = ld_bf16x8(da + 16 * t);
-#pragma unroll
-      for (int t = 0; t < D / 16; ++t) {
-        sacc[qb] = mfma32(fa[t], kb[t], sacc[qb]);
-        dpacc[qb] = mfma32(fd[t], vb[t], dpacc[qb]);
-      }
-    }
-    // the next step's rows are requested while this step's math runs
-    if (more) {
+    // the next step's rows (and the id of the one after) are requested
+    // first; they are stored to the other buffer in the last slots
+    if (it + 1 < nsteps) {
       fetch_rows(it + 1);
-      if (it + 2 < nsteps) fetch_ids(it + 2);
+      if (it + 2 < nsteps) fetch_id(it + 2);
     }
-    // register 4i + jj of half hh of query block qb holds query
-    // 32 qb + acc_key(4i + jj, hh): four consecutive queries per i
-    int ppos0 = 0;
-    if (own_step) {
-      const int st = it - rsteps + olo;
-      const int hl = st / psteps_h;
-      ppos0 = p0 + (st - hl * psteps_h) * QN;
-    }
-    bf16x8 pb[2 * NQ], dsb[2 * NQ];
-#pragma unroll
-    for (int qb = 0; qb < NQ; ++qb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int qi0 = 32 * qb + acc_key(4 * i, hh);
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&stat[cb][0][qi0]);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&stat[cb][1][qi0]);
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int reg = 4 * i + jj;
-          float p = __builtin_amdgcn_exp2f(fmaf(sacc[qb][reg], sl2, -l4[jj]));
-          if (own_step && ppos0 + qi0 + jj < key) p = 0.f;   // causal: query before the key
-          const float ds = p * (dpacc[qb][reg] - d4[jj]);
-          pb[2 * qb + (reg >> 3)][reg & 7] = static_cast<__bf16>(p);
-          dsb[2 * qb + (reg >> 3)][reg & 7] = static_cast<__bf16>(ds);
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16 s0 = f32x16{}, d0 = f32x16{}, s1 = f32x16{}, d1 = f32x16{};
+    bf16x8 pb0[2], dsb0[2], pb1[2], dsb1[2];
+    f32x4 l4[2] = {f32x4{}, f32x4{}}, d4[2] = {f32x4{}, f32x4{}};
+    bf16x8 fr[4 * NS];
+    static_for<0, kPre>([&](auto kc) { fr[kc.value] = frag(b, kc.value); });
+    static_for<0, 4 * NS>([&](auto kc) {
+      constexpr int k = decltype(kc)::value;
+      constexpr int ph = k / NS, ks = k % NS;
+      // statistics of the four queries of softmax element group g (elements
+      // 4g..4g+3 of the two halves' 32): read GS slots before their first
+      // use (slot NS + g GS), after the last use of group g - 2 (the same
+      // registers)
+      if constexpr (k >= NS - GS && k < NS + 7 * GS && (k - NS + GS) % GS == 0) {
+        constexpr int g = (k - NS + GS) / GS;
+        const int qi0 = 32 * (g >> 2) + acc_key(4 * (g & 3), hh);
+        l4[g & 1] = *reinterpret_cast<const f32x4*>(st + qi0);
+        d4[g & 1] = *reinterpret_cast<const f32x4*>(st + QN + qi0);
+      }
+      if constexpr (ph == 0) {
+        constexpr int t = ks >> 1;
+        if constexpr (k & 1) d0 = mfma32(fr[k], vb[t], d0);
+        else s0 = mfma32(fr[k], kb[t], s0);
+      } else if constexpr (ph == 1) {
+        constexpr int t = ks >> 1;
+        if constexpr (k & 1) d1 = mfma32(fr[k], vb[t], d1);
+        else s1 = mfma32(fr[k], kb[t], s1);
+        static_for<0, EPS>([&](auto ec) {
+          constexpr int reg = ks * EPS + decltype(ec)::value, g = reg >> 2;
+          soft(0, reg, pos0, s0[reg], d0[reg], l4[g & 1], d4[g & 1], pb0, dsb0);
+        });
+      } else if constexpr (ph == 2) {
+        constexpr int dt = ks >> 2, c = (ks >> 1) & 1;
+        if constexpr (ks & 1) dka[dt] = mfma32(fr[k], dsb0[c], dka[dt]);
+        else dva[dt] = mfma32(fr[k], pb0[c], dva[dt]);
+        static_for<0, EPS>([&](auto ec) {
+          constexpr int reg = ks * EPS + decltype(ec)::value, g = 4 + (reg >> 2);
+          soft(1, reg, pos0, s1[reg], d1[reg], l4[g & 1], d4[g & 1], pb1, dsb1);
+        });
+      } else {
+        constexpr int dt = ks >> 2, c = (ks >> 1) & 1;
+        if constexpr (ks & 1) dka[dt] = mfma32(fr[k], dsb1[c], dka[dt]);
+        else dva[dt] = mfma32(fr[k], pb1[c], dva[dt]);
+        if constexpr (ks >= NS - 8) {
+          constexpr int i = ks - (NS - 8);   // tile chunk stores of the next step
+          if constexpr (i < T::CH) {
+            const int o = kv_off<D>(lane, w + NW * i);
+            *reinterpret_cast<u32x4*>(lds + (CB ^ 1) * T::BUF + o) = qr[i];
+            *reinterpret_cast<u32x4*>(lds + (CB ^ 1) * T::BUF + T::QE + o) = dr[i];
+          }
         }
       }
-    // dV^T += dO^T P, dK^T += Q^T dS: A = the transposed tiles (rows d,
-    // k-slots queries 16 c2 + 8 hh + [0, 8)), B = P / dS
-    {
-      const bf16_t* qt = b + 2 * T::QE + n * T::TS + 8 * hh;
-      const bf16_t* dtp = b + 2 * T::QE + T::TE + n * T::TS + 8 * hh;
+      if constexpr (k + kPre < 4 * NS) fr[k + kPre] = frag(b, k + kPre);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    stage_stats(CB ^ 1);
+    // the dK^T / dV^T accumulators stay in the accumulation registers across
+    // steps (no copies at the loop edge)
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-        for (int c2 = 0; c2 < 2 * NQ; ++c2) {
-          const bf16x8 ad = ld_bf16x8(dtp + 32 * dt * T::TS + 16 * c2);
-          const bf16x8 aq = ld_bf16x8(qt + 32 * dt * T::TS + 16 * c2);
-          dva[dt] = mfma32(ad, pb[c2], dva[dt]);
-          dka[dt] = mfma32(aq, dsb[c2], dka[dt]);
-        }
-    }
-    if (more) stage_store(cb ^ 1);
+    for (int dt = 0; dt < D / 32; ++dt) asm volatile("" : "+a"(dka[dt]), "+a"(dva[dt]));
     __syncthreads();
   }
   if (!key_ok) return;
@@ -873,8 +952,6 @@ hipError_t launch_bwd_dq_own(const void* q, const void* dout, const void* k, con
   return hipGetLastError();
 }
 
-constexpr int kDkdvNQ = 2;   // 64 queries per step
-
 hipError_t launch_bwd_dkdv(const void* q, const void* dout, const void* k, const void* v,
                            const float* lse, const float* dvec, const uint32_t* list,
                            const uint32_t* bucket_off, void* dk, void* dv, float* kvpart,
@@ -890,7 +967,7 @@ hipError_t launch_bwd_dkdv(const void* q, const void* dout, const void* k, const
   const FastDiv fkp = make_fastdiv((uint32_t)(d.kp > 0 ? d.kp : 1));
   const FastDiv flq = make_fastdiv((uint32_t)d.Lq);
 #define MOBA_BKV(DV, NWV)                                                                       \
-  hipLaunchKernelGGL((k_bwd_dkdv<DV, NWV, kDkdvNQ>), dim3((unsigned)grid), dim3(64 * NWV), 0, st, \
+  hipLaunchKernelGGL((k_bwd_dkdv<DV, NWV>), dim3((unsigned)grid), dim3(64 * NWV), 0, st, \
                      static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(dout),           \
                      static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v), lse, dvec,   \
                      list, bucket_off, static_cast<bf16_t*>(dk), static_cast<bf16_t*>(dv),      \
