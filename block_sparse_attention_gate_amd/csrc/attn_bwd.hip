@@ -615,7 +615,8 @@ __global__ __launch_bounds__(64 * NW, 1) void k_bwd_dkdv(
   // tiles of step it.  Lane l stages query l of a step; wave w its 16-byte
   // chunks w, w + NW, ... of the row.
   u32x4 qr[T::CH], dr[T::CH];
-  float st_l = 0.f, st_d = 0.f;      // wave 0: lse2, Dv of query `lane` (step it+1)
+  bool row_ok = false;               // query `lane` of step it+1 exists
+  float st_l = 0.f, st_d = 0.f;      // wave 0: lse, Dv of query `lane` (step it+1)
   uint32_t ida = 0u;                 // entry id of query `lane` of step it+1, then it+2
   // query `lane` of a step: row offset and query-head index, or false
   auto query_at = [&](int step, uint32_t id, int64_t& qrow, int64_t& qhi) -> bool {
@@ -639,40 +640,46 @@ __global__ __launch_bounds__(64 * NW, 1) void k_bwd_dkdv(
     qhi = ((int64_t)s * H + h) * Lq + r;
     return true;
   };
+  // The loads below go to valid addresses whatever the query (row 0 and
+  // entry rbase stand in for invalid ones) and are not selected on right
+  // away: a select on a loaded value would wait for the load there, at the
+  // start of the step.  Invalid rows are zeroed when the tiles are stored.
   auto fetch_id = [&](int step) {
-    if (step >= rsteps) return;  // own steps need no ids
+    if (step >= rsteps) return;  // own steps need no ids (and rsteps > 0 means nrt > 0)
     const int e = step * QN + lane;
-    ida = e < nrt ? list[rbase + e] : 0u;
+    ida = list[rbase + (e < nrt ? e : nrt - 1)];   // entries past nrt: query_at rejects them
   };
   auto fetch_rows = [&](int step) {
     int64_t qrow = 0, qhi = 0;
-    const bool ok = query_at(step, ida, qrow, qhi);
+    row_ok = query_at(step, ida, qrow, qhi);
+    if (!row_ok) qrow = qhi = 0;
     const bf16_t* qp = q + qrow + 8 * w;
     const bf16_t* dp = dout + qrow + 8 * w;
 #pragma unroll
     for (int i = 0; i < T::CH; ++i) {
-      qr[i] = ok ? *reinterpret_cast<const u32x4*>(qp + 8 * NW * i) : u32x4{0u, 0u, 0u, 0u};
-      dr[i] = ok ? *reinterpret_cast<const u32x4*>(dp + 8 * NW * i) : u32x4{0u, 0u, 0u, 0u};
+      qr[i] = *reinterpret_cast<const u32x4*>(qp + 8 * NW * i);
+      dr[i] = *reinterpret_cast<const u32x4*>(dp + 8 * NW * i);
     }
     if (w == 0) {
-      // an invalid query gets lse2 = +inf, hence p = 0 (its rows are zero)
-      st_l = ok ? lse[qhi] * kLog2e : __builtin_inff();
-      st_d = ok ? dvec[qhi] : 0.f;
+      st_l = lse[qhi];
+      st_d = dvec[qhi];
     }
+  };
+  auto stage_chunk = [&](int buf, int i) {
+    const u32x4 z = u32x4{0u, 0u, 0u, 0u};
+    const int o = kv_off<D>(lane, w + NW * i);
+    *reinterpret_cast<u32x4*>(lds + buf * T::BUF + o) = row_ok ? qr[i] : z;
+    *reinterpret_cast<u32x4*>(lds + buf * T::BUF + T::QE + o) = row_ok ? dr[i] : z;
   };
   auto stage_store = [&](int buf) {
-    bf16_t* b = lds + buf * T::BUF;
 #pragma unroll
-    for (int i = 0; i < T::CH; ++i) {
-      const int o = kv_off<D>(lane, w + NW * i);
-      *reinterpret_cast<u32x4*>(b + o) = qr[i];
-      *reinterpret_cast<u32x4*>(b + T::QE + o) = dr[i];
-    }
+    for (int i = 0; i < T::CH; ++i) stage_chunk(buf, i);
   };
+  // an invalid query gets lse2 = +inf, hence p = 0 (its rows are zero too)
   auto stage_stats = [&](int buf) {
     if (w == 0) {
-      stat[buf][0][lane] = st_l;
-      stat[buf][1][lane] = st_d;
+      stat[buf][0][lane] = row_ok ? st_l * kLog2e : __builtin_inff();
+      stat[buf][1][lane] = row_ok ? st_d : 0.f;
     }
   };
 
@@ -790,11 +797,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_bwd_dkdv(
         else dva[dt] = mfma32(fr[k], pb1[c], dva[dt]);
         if constexpr (ks >= NS - 8) {
           constexpr int i = ks - (NS - 8);   // tile chunk stores of the next step
-          if constexpr (i < T::CH) {
-            const int o = kv_off<D>(lane, w + NW * i);
-            *reinterpret_cast<u32x4*>(lds + (CB ^ 1) * T::BUF + o) = qr[i];
-            *reinterpret_cast<u32x4*>(lds + (CB ^ 1) * T::BUF + T::QE + o) = dr[i];
-          }
+          if constexpr (i < T::CH) stage_chunk(CB ^ 1, i);
         }
       }
       if constexpr (k + kPre < 4 * NS) fr[k + kPre] = frag(b, k + kPre);
