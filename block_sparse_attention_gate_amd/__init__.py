@@ -720,5 +720,5 @@ KERNEL_NAMES = ("block_mean", "transpose_v", "gate_topk", "route_count", "route_
                 "route_scan_buckets", "route_scatter", "attn_routed", "attn_own_merge",
                 "attn_full", "decode_plan", "decode_attn", "decode_merge", "merge_partials",
                 "pool_transpose", "block_mean_finalize", "route_scan_small", "bwd_dot",
-                "bwd_transform", "bwd_dq_routed", "bwd_dq_own", "bwd_dkdv", "naive_scores",
+                "bwd_tail", "bwd_dq_routed", "bwd_dq_own", "bwd_dkdv", "naive_scores",
                 "naive_softmax", "naive_pv")

@@ -57,7 +57,7 @@ moba_status fail(moba_status s, const char* fmt, ...) {
 enum KernelId {
   K_BLOCK_MEAN, K_TRANSPOSE_V, K_GATE, K_RCOUNT, K_RSCAN_ROWS, K_RSCAN_BUCKETS, K_RSCATTER,
   K_ATTN_ROUTED, K_ATTN_OWN, K_ATTN_FULL, K_DEC_PLAN, K_DEC_ATTN, K_DEC_MERGE, K_MERGE,
-  K_POOL_TRANSPOSE, K_MEAN_FINALIZE, K_RSCAN_SMALL, K_BWD_DOT, K_BWD_TRANSFORM,
+  K_POOL_TRANSPOSE, K_MEAN_FINALIZE, K_RSCAN_SMALL, K_BWD_DOT, K_BWD_TAIL,
   K_BWD_DQ_ROUTED, K_BWD_DQ_OWN, K_BWD_DKDV, K_NAIVE_SCORES, K_NAIVE_SOFTMAX, K_NAIVE_PV,
   K_COUNT
 };
@@ -65,7 +65,7 @@ const char* const kKernelNames[K_COUNT] = {
     "block_mean", "transpose_v", "gate_topk", "route_count", "route_scan_rows",
     "route_scan_buckets", "route_scatter", "attn_routed", "attn_own_merge", "attn_full",
     "decode_plan", "decode_attn", "decode_merge", "merge_partials", "pool_transpose",
-    "block_mean_finalize", "route_scan_small", "bwd_dot", "bwd_transform", "bwd_dq_routed",
+    "block_mean_finalize", "route_scan_small", "bwd_dot", "bwd_tail", "bwd_dq_routed",
     "bwd_dq_own", "bwd_dkdv", "naive_scores", "naive_softmax", "naive_pv"};
 
 struct ProfRecord {
@@ -759,7 +759,7 @@ moba_status full_impl(const moba_args* a) {
 struct BwdPlan {
   Plan f;                  // dims (forward_dims) and the routing-table offsets
   bool routed = false, need_tail = false;
-  size_t off_dvec = 0, off_kt = 0, off_ktail = 0, off_vtail = 0, off_dqp = 0, off_kvpart = 0,
+  size_t off_dvec = 0, off_ktail = 0, off_vtail = 0, off_dqp = 0, off_kvpart = 0,
          total = 0;
   bool need_kvpart = false;
 };
@@ -785,7 +785,9 @@ moba_status plan_backward(const moba_bwd_args* b, BwdPlan* bp) {
   moba_status st = forward_dims(&a, &bp->f);
   if (st != MOBA_OK) return st;
   Dims& d = bp->f.d;
-  d.tile_m = 128;  // four-wave routed dq tiles (eight waves would spill)
+  // routed dq tiles: eight waves (two per SIMD) in bf16, 128 queries per
+  // fp32 workgroup
+  d.tile_m = d.bf16 ? 256 : 128;
   if (d.bf16 && d.Lv * d.D >= ((int64_t)1 << 31))
     return fail(MOBA_ERR_UNSUPPORTED, "kv_len * head_dim >= 2^31");
   size_t off = 0;
@@ -796,8 +798,7 @@ moba_status plan_backward(const moba_bwd_args* b, BwdPlan* bp) {
   };
   Plan& p = bp->f;
   bp->off_dvec = take((size_t)d.S * d.H * d.Lq * 4);
-  // fp32 reads K and V as given (no K^T, no tail tiles)
-  if (d.bf16) bp->off_kt = take((size_t)d.S * d.Hkv * d.D * d.Lv * 2);
+  // fp32 reads K and V as given (no tail tiles)
   bp->need_tail = d.bf16 && d.L % 64 != 0;
   if (bp->need_tail) {
     bp->off_ktail = take((size_t)d.S * 64 * d.Hkv * d.D * 2);
@@ -846,7 +847,6 @@ moba_status backward_impl(const moba_bwd_args* b) {
   }
   char* w = ws.base;
   float* dvec = (float*)(w + bp.off_dvec);
-  void* kt = (void*)(w + bp.off_kt);
   void* ktail = bp.need_tail ? (void*)(w + bp.off_ktail) : nullptr;
   void* vtail = bp.need_tail ? (void*)(w + bp.off_vtail) : nullptr;
   const Plan& p = bp.f;
@@ -862,9 +862,8 @@ moba_status backward_impl(const moba_bwd_args* b) {
     return d.bf16 ? moba::launch_bwd_dot(b->out, b->dout, dvec, d, l.st)
                   : moba::launch_bwd_dot_f32(b->out, b->dout, dvec, d, l.st);
   });
-  if (d.bf16)
-    l.run(K_BWD_TRANSFORM,
-          [&] { return moba::launch_bwd_transform(b->k, b->v, kt, ktail, vtail, d, l.st); });
+  if (bp.need_tail)
+    l.run(K_BWD_TAIL, [&] { return moba::launch_bwd_tail(b->k, b->v, ktail, vtail, d, l.st); });
   if (bp.routed) {
     l.run(K_RCOUNT, [&] { return moba::launch_route_count(b->sel, counts, d, l.st); });
     const bool small_scan = moba::route_scan_small_fits(d);
@@ -880,14 +879,14 @@ moba_status backward_impl(const moba_bwd_args* b) {
       return moba::launch_route_scatter(b->sel, counts, boff, list, d, l.st, small_scan);
     });
     l.run(K_BWD_DQ_ROUTED, [&] {
-      return d.bf16 ? moba::launch_bwd_dq_routed(b->q, b->dout, b->k, b->v, kt, b->lse, dvec,
+      return d.bf16 ? moba::launch_bwd_dq_routed(b->q, b->dout, b->k, b->v, b->lse, dvec,
                                                  list, boff, toff, dqp, d, l.st)
                     : moba::launch_bwd_dq_routed_f32(b->q, b->dout, b->k, b->v, b->lse, dvec,
                                                      list, boff, toff, (float*)dqp, d, l.st);
     });
   }
   l.run(K_BWD_DQ_OWN, [&] {
-    return d.bf16 ? moba::launch_bwd_dq_own(b->q, b->dout, b->k, b->v, kt, ktail, vtail, b->lse,
+    return d.bf16 ? moba::launch_bwd_dq_own(b->q, b->dout, b->k, b->v, ktail, vtail, b->lse,
                                             dvec, dqp, b->dq, d, l.st)
                   : moba::launch_bwd_dq_own_f32(b->q, b->dout, b->k, b->v, b->lse, dvec,
                                                 (const float*)dqp, b->dq, d, l.st);

@@ -9,12 +9,13 @@
 //   dk_t += c ds_t q.
 // Kernels:
 //   k_bwd_dot        Dv per query-head.
-//   k_bwd_transform  K^T [S, Hkv, D, Lv] (zero past L) and, for a length that
-//                    is not a multiple of 64, the last K and V tiles [S, 64,
-//                    Hkv, D] zero padded (so that no tile load passes the end).
+//   k_bwd_tail       for a length that is not a multiple of 64, the last K
+//                    and V tiles [S, 64, Hkv, D] zero padded (so that no tile
+//                    load passes the end).
 //   k_bwd_dq_routed  per routed tile (the forward's tile list): S^T = K Q^T
 //                    and dP^T = V dO^T on MFMA, dS^T in registers, then
-//                    dQ^T += K^T dS^T; one bf16 dq partial per routed slot.
+//                    dQ^T += K^T dS^T with K^T read transposed from the K
+//                    tile; one bf16 dq partial per routed slot.
 //   k_bwd_dq_own     per query: the own block (causal mask) the same way, plus
 //                    the query's routed dq partials -> dq.
 //   k_bwd_dkdv       per 32 * NW keys of one block (key-stationary, no
@@ -63,46 +64,30 @@ __global__ __launch_bounds__(256) void k_bwd_dot(const bf16_t* __restrict__ o,
   }
 }
 
-// --------------------------------------------------- K^T and the last tiles
-// grid (Lv / 64, Hkv, S), 256 threads.
+// ------------------------------------------------------------ the last tiles
+// For a length that is not a multiple of 64: the last K and V tiles of every
+// (sequence, KV head), [S, 64, Hkv, D], zero past the end (so that no tile
+// load passes the end).  grid (Hkv, S), 256 threads.
 template <int D>
-__global__ __launch_bounds__(256) void k_bwd_transform(const bf16_t* __restrict__ k,
-                                                       const bf16_t* __restrict__ v,
-                                                       bf16_t* __restrict__ kt,
-                                                       bf16_t* __restrict__ ktail,
-                                                       bf16_t* __restrict__ vtail, int Hkv,
-                                                       int64_t L, int64_t Lv) {
-  constexpr int LD = D + 8, CPR = D / 8;
-  __shared__ bf16_t tile[64 * LD];
-  const int g = blockIdx.y, s = blockIdx.z;
-  const int64_t key0 = (int64_t)blockIdx.x * 64;
-  const int64_t nkey = L - key0;  // >= 1
+__global__ __launch_bounds__(256) void k_bwd_tail(const bf16_t* __restrict__ k,
+                                                  const bf16_t* __restrict__ v,
+                                                  bf16_t* __restrict__ ktail,
+                                                  bf16_t* __restrict__ vtail, int Hkv, int64_t L) {
+  constexpr int CPR = D / 8;
+  const int g = blockIdx.x, s = blockIdx.y;
+  const int64_t key0 = L / 64 * 64;
+  const int64_t nkey = L - key0;  // 1..63
   for (int c = threadIdx.x; c < 64 * CPR; c += 256) {
     const int row = c / CPR, cc = c % CPR;
     const int64_t src = (((int64_t)s * L + key0 + row) * Hkv + g) * D + cc * 8;
-    u32x4 kv = u32x4{0u, 0u, 0u, 0u};
-    if (row < nkey) kv = *reinterpret_cast<const u32x4*>(k + src);
-    *reinterpret_cast<u32x4*>(&tile[row * LD + cc * 8]) = kv;
-    if (nkey < 64) {
-      const int64_t dst = (((int64_t)s * 64 + row) * Hkv + g) * D + cc * 8;
-      u32x4 vv = u32x4{0u, 0u, 0u, 0u};
-      if (row < nkey) vv = *reinterpret_cast<const u32x4*>(v + src);
-      *reinterpret_cast<u32x4*>(ktail + dst) = kv;
-      *reinterpret_cast<u32x4*>(vtail + dst) = vv;
+    const int64_t dst = (((int64_t)s * 64 + row) * Hkv + g) * D + cc * 8;
+    u32x4 kv = u32x4{0u, 0u, 0u, 0u}, vv = u32x4{0u, 0u, 0u, 0u};
+    if (row < nkey) {
+      kv = *reinterpret_cast<const u32x4*>(k + src);
+      vv = *reinterpret_cast<const u32x4*>(v + src);
     }
-  }
-  __syncthreads();
-  for (int c = threadIdx.x; c < D * 8; c += 256) {
-    const int dd = c / 8, kc = c % 8;
-    uint32_t w[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t lo = tile[(kc * 8 + 2 * e) * LD + dd];
-      const uint32_t hi = tile[(kc * 8 + 2 * e + 1) * LD + dd];
-      w[e] = lo | (hi << 16);
-    }
-    *reinterpret_cast<u32x4*>(kt + (((int64_t)s * Hkv + g) * D + dd) * Lv + key0 + kc * 8) =
-        u32x4{w[0], w[1], w[2], w[3]};
+    *reinterpret_cast<u32x4*>(ktail + dst) = kv;
+    *reinterpret_cast<u32x4*>(vtail + dst) = vv;
   }
 }
 
@@ -129,6 +114,47 @@ __device__ __forceinline__ uint32_t fdiv(uint32_t x, const FastDiv& f) {
   return (t + ((x - t) >> f.s1)) >> f.s2;
 }
 
+// LDS tiles of 64 rows (keys or queries) of D bf16, unpadded, with the
+// 16-byte chunks of row r permuted by XOR with kv_swz(r).  The pattern makes
+// both reads of the tiles free of LDS bank conflicts: 16 consecutive rows at
+// one chunk (MFMA A rows with the contraction over d), and 4 consecutive rows
+// x 4 consecutive chunks (a 32-lane half of a transpose read, A rows d with
+// the contraction over the tile's rows).
+template <int D>
+__device__ __forceinline__ int kv_swz(int r) {
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
+template <int D>
+__device__ __forceinline__ int kv_off(int r, int chunk) {
+  return r * D + ((chunk ^ kv_swz<D>(r)) << 3);
+}
+
+// A operand of a product over the tile's rows (rows d = 32 dt + lane % 32,
+// k-slots = tile rows 16 c2 + 8 (lane / 32) + [0, 8)) from a row-major
+// [row][d] tile.
+// The LDS transpose read (16-bit elements, 64 bits per lane) hands lane i of
+// each 16-lane group element i % 4 of the values read by lanes i / 4 + 4e of
+// its group, e = 0..3; so lane 4e + f of a group reads dims 4f.. of row e,
+// and lane i receives dim i of four consecutive rows.  Two reads give the
+// eight rows.
+template <int D>
+__device__ __forceinline__ bf16x8 tr_frag(const bf16_t* tile, int dt, int c2, int lane) {
+  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+  const int grp = lane >> 4, e = (lane >> 2) & 3, f = lane & 3;
+  const int col = 32 * dt + 16 * (grp & 1) + 4 * f;
+  bf16x4 part[2];
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int r = 16 * c2 + 8 * (grp >> 1) + 4 * half + e;
+    const bf16_t* p = tile + kv_off<D>(r, col >> 3) + (col & 7);
+    part[half] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)const_cast<bf16_t*>(p));
+  }
+  return bf16x8{part[0][0], part[0][1], part[0][2], part[0][3],
+                part[1][0], part[1][1], part[1][2], part[1][3]};
+}
+
 // 8 bf16 of a query-like row for lane half hh: fragments of the B operand
 // (lane = query) of S^T = K Q^T and dP^T = V dO^T.
 template <int D>
@@ -142,124 +168,88 @@ __device__ __forceinline__ void bwd_row_frags(const bf16_t* row, bool valid, int
 }
 
 // ============================================================== dq kernels
+// K and V tiles of 64 keys, swizzled rows (kv_off); K^T for dQ^T += K^T dS^T
+// is read from the K tile with transpose reads.
 template <int D, int NW>
 struct DqTiles {
   static constexpr int NT = 64 * NW;
-  static constexpr int KS = D + 8;              // K and V tile row stride
-  static constexpr int TS = 64 + 8;             // K^T tile row stride
-  static constexpr int KE = 64 * KS;
-  static constexpr int BUF = 2 * KE + D * TS;   // K [64][KS], V [64][KS], K^T [D][TS]
+  static constexpr int KE = 64 * D;
+  static constexpr int BUF = 2 * KE;             // K, V (bf16 elements)
   static constexpr int RCH = 64 * (D / 8) / NT;  // 16-byte chunks per thread of K (and V)
-  static constexpr int TCH = D * 8 / NT;         // of K^T
 };
 
-// Global -> register staging of one 64-key tile of K, V (row-major, row
-// stride Hkv*D) and K^T (row stride Lv); fixed per-thread offsets.
+// Global -> register staging of one 64-key tile of K and V (row stride
+// Hkv*D); fixed per-thread offsets.
 template <int D, int NW>
 struct DqRegs {
   using T = DqTiles<D, NW>;
-  u32x4 kr[T::RCH], vr[T::RCH], tr[T::TCH];
-  int roff[T::RCH], rls[T::RCH], toff[T::TCH], tls[T::TCH];
-  __device__ __forceinline__ void setup(int krow_stride, int Lv, int tid) {
+  u32x4 kr[T::RCH], vr[T::RCH];
+  int roff[T::RCH], rls[T::RCH];
+  __device__ __forceinline__ void setup(int krow_stride, int tid) {
 #pragma unroll
     for (int i = 0; i < T::RCH; ++i) {
       const int c = tid + T::NT * i;
       const int row = c / (D / 8), cc = c % (D / 8);
       roff[i] = row * krow_stride + cc * 8;
-      rls[i] = row * T::KS + cc * 8;
-    }
-#pragma unroll
-    for (int i = 0; i < T::TCH; ++i) {
-      const int c = tid + T::NT * i;
-      const int dd = c / 8, kc = c % 8;
-      toff[i] = dd * Lv + kc * 8;
-      tls[i] = 2 * T::KE + dd * T::TS + kc * 8;
+      rls[i] = kv_off<D>(row, cc);
     }
   }
-  __device__ __forceinline__ void load(const bf16_t* kt, const bf16_t* vt, const bf16_t* ktt) {
+  __device__ __forceinline__ void load(const bf16_t* ksrc, const bf16_t* vsrc) {
 #pragma unroll
-    for (int i = 0; i < T::RCH; ++i) kr[i] = *reinterpret_cast<const u32x4*>(kt + roff[i]);
+    for (int i = 0; i < T::RCH; ++i) kr[i] = *reinterpret_cast<const u32x4*>(ksrc + roff[i]);
 #pragma unroll
-    for (int i = 0; i < T::RCH; ++i) vr[i] = *reinterpret_cast<const u32x4*>(vt + roff[i]);
-#pragma unroll
-    for (int i = 0; i < T::TCH; ++i) tr[i] = *reinterpret_cast<const u32x4*>(ktt + toff[i]);
+    for (int i = 0; i < T::RCH; ++i) vr[i] = *reinterpret_cast<const u32x4*>(vsrc + roff[i]);
   }
   __device__ __forceinline__ void store(bf16_t* buf) const {
 #pragma unroll
     for (int i = 0; i < T::RCH; ++i) *reinterpret_cast<u32x4*>(buf + rls[i]) = kr[i];
 #pragma unroll
     for (int i = 0; i < T::RCH; ++i) *reinterpret_cast<u32x4*>(buf + T::KE + rls[i]) = vr[i];
-#pragma unroll
-    for (int i = 0; i < T::TCH; ++i) *reinterpret_cast<u32x4*>(buf + tls[i]) = tr[i];
   }
 };
 
-// One 64-key step of one wave (32 queries, lane n = query).  MASK: drop keys
-// outside [klo, qpos].
+// One 64-key step of one wave (32 queries, lane n = query), as two 32-key
+// halves: S^T = K Q^T and dP^T = V dO^T (K / V rows in the kperm order),
+// dS^T in registers, then dQ^T += K^T dS^T.  MASK: drop keys outside
+// [klo, qpos].
 template <int D, bool MASK>
 __device__ __forceinline__ void dq_step(const bf16_t* buf, const bf16x8 (&qf)[D / 16],
                                         const bf16x8 (&df)[D / 16], f32x16 (&dq)[D / 32],
-                                        int n, int hh, float sl2, float lse2, float dv,
-                                        int key0, int klo, int qpos) {
-  using T = DqTiles<D, 4>;
-  f32x16 s[2] = {f32x16{}, f32x16{}};
-  f32x16 dp[2] = {f32x16{}, f32x16{}};
-  {
-    const bf16_t* r0 = buf + kperm(n) * T::KS + 8 * hh;
-    const bf16_t* r1 = r0 + 32 * T::KS;
-    bf16x8 a0[D / 16], a1[D / 16];
+                                        int lane, float sl2, float lse2, float dv, int key0,
+                                        int klo, int qpos) {
+  constexpr int KE = 64 * D;
+  const int n = lane & 31, hh = lane >> 5;
+  const int ar = kperm(n);
 #pragma unroll
-    for (int t = 0; t < D / 16; ++t) a0[t] = ld_bf16x8(r0 + 16 * t);
-#pragma unroll
-    for (int t = 0; t < D / 16; ++t) a1[t] = ld_bf16x8(r1 + 16 * t);
+  for (int kt = 0; kt < 2; ++kt) {
+    f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int t = 0; t < D / 16; ++t) {
-      s[0] = mfma32(a0[t], qf[t], s[0]);
-      s[1] = mfma32(a1[t], qf[t], s[1]);
+      const bf16_t* kr = buf + kv_off<D>(32 * kt + ar, 2 * t + hh);
+      s = mfma32(ld_bf16x8(kr), qf[t], s);
+      dp = mfma32(ld_bf16x8(kr + KE), df[t], dp);
     }
-  }
-  {
-    const bf16_t* r0 = buf + T::KE + kperm(n) * T::KS + 8 * hh;
-    const bf16_t* r1 = r0 + 32 * T::KS;
-    bf16x8 a0[D / 16], a1[D / 16];
-#pragma unroll
-    for (int t = 0; t < D / 16; ++t) a0[t] = ld_bf16x8(r0 + 16 * t);
-#pragma unroll
-    for (int t = 0; t < D / 16; ++t) a1[t] = ld_bf16x8(r1 + 16 * t);
-#pragma unroll
-    for (int t = 0; t < D / 16; ++t) {
-      dp[0] = mfma32(a0[t], df[t], dp[0]);
-      dp[1] = mfma32(a1[t], df[t], dp[1]);
-    }
-  }
-  // dS^T = P^T (dP^T - Dv), P^T = 2^(S^T sl2 - lse2); registers [8c, 8c+8) of
-  // subtile kt hold keys 32 kt + 16 c + 8 hh + [0, 8): the B operand layout.
-  bf16x8 dsb[2][2];
-#pragma unroll
-  for (int kt = 0; kt < 2; ++kt)
+    // dS^T = P^T (dP^T - Dv), P^T = 2^(S^T sl2 - lse2); registers [8c, 8c+8)
+    // hold keys 32 kt + 16 c + 8 hh + [0, 8): the B operand layout
+    bf16x8 dsb[2];
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
         const int reg = 8 * c + r;
-        float p = __builtin_amdgcn_exp2f(fmaf(s[kt][reg], sl2, -lse2));
+        float p = __builtin_amdgcn_exp2f(fmaf(s[reg], sl2, -lse2));
         if (MASK) {
           const int key = key0 + 32 * kt + acc_key(reg, hh);
           if (key > qpos || key < klo) p = 0.f;
         }
-        dsb[kt][c][r] = static_cast<__bf16>(p * (dp[kt][reg] - dv));
+        dsb[c][r] = static_cast<__bf16>(p * (dp[reg] - dv));
       }
-  // dQ^T += K^T dS^T
-  const bf16_t* tbase = buf + 2 * T::KE + 8 * hh + n * T::TS;
-  bf16x8 ta[D / 32][4];
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt)
+    for (int c = 0; c < 2; ++c)
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) ta[dt][kc] = ld_bf16x8(tbase + 32 * dt * T::TS + 16 * kc);
-#pragma unroll
-  for (int kc = 0; kc < 4; ++kc)
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) dq[dt] = mfma32(ta[dt][kc], dsb[kc >> 1][kc & 1], dq[dt]);
+      for (int dt = 0; dt < D / 32; ++dt)
+        dq[dt] = mfma32(tr_frag<D>(buf, dt, 2 * kt + c, lane), dsb[c], dq[dt]);
+  }
 }
 
 // dq^T accumulator (lane = query, rows d) -> a bf16 row, scaled.
@@ -284,11 +274,11 @@ __device__ __forceinline__ void store_dq_row(bf16_t* row, const f32x16 (&dq)[D /
 template <int D, int NW>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void k_bwd_dq_routed(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ dout,
-    const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, const bf16_t* __restrict__ kt,
+    const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const float* __restrict__ lse, const float* __restrict__ dvec,
     const uint32_t* __restrict__ list, const uint32_t* __restrict__ bucket_off,
     const uint32_t* __restrict__ tile_off, bf16_t* __restrict__ dqp, int64_t Lq, int64_t L,
-    int64_t Lv, int H, int Hkv, int kp, int B, int nb, int nrows, float sl2, float scale,
+    int H, int Hkv, int kp, int B, int nb, int nrows, float sl2, float scale,
     uint32_t nslots) {
   using T = DqTiles<D, NW>;
   constexpr int TM = 32 * NW;
@@ -331,24 +321,22 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_bwd_dq_routed(
   const int64_t krs = (int64_t)Hkv * D;
   const bf16_t* ktile = k + ((int64_t)s * L * Hkv + g) * D + (int64_t)j * B * krs;
   const bf16_t* vtile = v + ((int64_t)s * L * Hkv + g) * D + (int64_t)j * B * krs;
-  const bf16_t* tt = kt + ((int64_t)s * Hkv + g) * D * Lv + (int64_t)j * B;
   const int nsteps = B / 64;  // a selected past block is always whole
   f32x16 acc[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
   DqRegs<D, NW> tr;
-  tr.setup((int)krs, (int)Lv, tid);
-  tr.load(ktile, vtile, tt);
+  tr.setup((int)krs, tid);
+  tr.load(ktile, vtile);
   tr.store(lds);
   __syncthreads();
   for (int it = 0; it < nsteps; ++it) {
     const bool more = it + 1 < nsteps;
     ktile += 64 * krs;
     vtile += 64 * krs;
-    tt += 64;
-    if (more) tr.load(ktile, vtile, tt);
+    if (more) tr.load(ktile, vtile);
     if (wave_on)
-      dq_step<D, false>(lds + (it & 1) * T::BUF, qf, df, acc, n, hh, sl2, lse2, dv, 0, 0, 0);
+      dq_step<D, false>(lds + (it & 1) * T::BUF, qf, df, acc, lane, sl2, lse2, dv, 0, 0, 0);
     if (more) tr.store(lds + ((it + 1) & 1) * T::BUF);
     __syncthreads();
   }
@@ -363,10 +351,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_bwd_dq_routed(
 template <int D, int NW>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void k_bwd_dq_own(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ dout,
-    const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, const bf16_t* __restrict__ kt,
+    const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const bf16_t* __restrict__ ktail, const bf16_t* __restrict__ vtail,
     const float* __restrict__ lse, const float* __restrict__ dvec,
-    const bf16_t* __restrict__ dqp, bf16_t* __restrict__ dq, int Lq, int L, int Lv, int q_off,
+    const bf16_t* __restrict__ dqp, bf16_t* __restrict__ dq, int Lq, int L, int q_off,
     int H, int Hkv, int kp, int B, int HW, float sl2, float scale) {
   using T = DqTiles<D, NW>;
   __shared__ __attribute__((aligned(16))) bf16_t lds[2 * T::BUF];
@@ -405,7 +393,6 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_bwd_dq_own(
   const int64_t krs = (int64_t)Hkv * D;
   const bf16_t* kbase = k + ((int64_t)s * L * Hkv + g) * D;
   const bf16_t* vbase = v + ((int64_t)s * L * Hkv + g) * D;
-  const bf16_t* tbase = kt + ((int64_t)s * Hkv + g) * D * Lv;
   // the tile holding the end of a length that is not a multiple of 64 reads
   // K and V from the zero-padded copies (uniform pointer choice)
   const int ttail = (L % 64) ? L / 64 : -1;
@@ -415,11 +402,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_bwd_dq_own(
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
   DqRegs<D, NW> tr;
-  tr.setup((int)krs, Lv, tid);
+  tr.setup((int)krs, tid);
   auto load_tile = [&](int ti) {
     const int64_t off = (int64_t)ti * 64 * krs;
-    if (ti == ttail) tr.load(ktail_sg, vtail_sg, tbase + (int64_t)ti * 64);
-    else tr.load(kbase + off, vbase + off, tbase + (int64_t)ti * 64);
+    if (ti == ttail) tr.load(ktail_sg, vtail_sg);
+    else tr.load(kbase + off, vbase + off);
   };
   load_tile(t0);
   tr.store(lds);
@@ -442,9 +429,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_bwd_dq_own(
     if (more) load_tile(it + 1);
     bf16_t* cur = lds + ((it - t0) & 1) * T::BUF;
     if (it >= ws_ && it < wd_)
-      dq_step<D, false>(cur, qf, df, acc, n, hh, sl2, lse2, dv, 0, 0, 0);
+      dq_step<D, false>(cur, qf, df, acc, lane, sl2, lse2, dv, 0, 0, 0);
     else if (it >= wd_ && it < we_)
-      dq_step<D, true>(cur, qf, df, acc, n, hh, sl2, lse2, dv, it * 64, klo_l, pos);
+      dq_step<D, true>(cur, qf, df, acc, lane, sl2, lse2, dv, it * 64, klo_l, pos);
     if (more) tr.store(lds + ((it + 1 - t0) & 1) * T::BUF);
     __syncthreads();
   }
@@ -484,45 +471,6 @@ struct KvTiles {
   static constexpr int BUF = 2 * QE;            // Q, dO (bf16 elements)
   static constexpr int CH = D / 8 / NW;         // 16-byte chunks of a row per thread per tensor
 };
-
-// Q / dO tiles: QN rows of D bf16, unpadded, with the 16-byte chunks of row r
-// permuted by XOR with kv_swz(r).  The pattern makes both reads of the tiles
-// free of LDS bank conflicts: 16 consecutive rows at one chunk (the MFMA A
-// rows of S and dP), and 4 consecutive rows x 4 consecutive chunks (a
-// 32-lane half of a transpose read).
-template <int D>
-__device__ __forceinline__ int kv_swz(int r) {
-  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
-  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
-}
-
-template <int D>
-__device__ __forceinline__ int kv_off(int r, int chunk) {
-  return r * D + ((chunk ^ kv_swz<D>(r)) << 3);
-}
-
-// A operand of a product over queries (rows d = 32 dt + lane % 32, k-slots =
-// queries 16 c2 + 8 (lane / 32) + [0, 8)) from a row-major [query][d] tile.
-// The LDS transpose read (16-bit elements, 64 bits per lane) hands lane i of
-// each 16-lane group element i % 4 of the values read by lanes i / 4 + 4e of
-// its group, e = 0..3; so lane 4e + f of a group reads dims 4f.. of query e,
-// and lane i receives dim i of four consecutive queries.  Two reads give the
-// eight queries.
-template <int D>
-__device__ __forceinline__ bf16x8 tr_frag(const bf16_t* tile, int dt, int c2, int lane) {
-  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-  const int grp = lane >> 4, e = (lane >> 2) & 3, f = lane & 3;
-  const int col = 32 * dt + 16 * (grp & 1) + 4 * f;
-  bf16x4 part[2];
-#pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    const int r = 16 * c2 + 8 * (grp >> 1) + 4 * half + e;
-    const bf16_t* p = tile + kv_off<D>(r, col >> 3) + (col & 7);
-    part[half] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)const_cast<bf16_t*>(p));
-  }
-  return bf16x8{part[0][0], part[0][1], part[0][2], part[0][3],
-                part[1][0], part[1][1], part[1][2], part[1][3]};
-}
 
 // Calls f(std::integral_constant<int, K>) for K = B .. E-1 in order (a loop
 // whose index is a compile-time constant in the body).
@@ -894,21 +842,22 @@ hipError_t launch_bwd_dot(const void* out, const void* dout, float* dvec, const 
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_transform(const void* k, const void* v, void* kt, void* ktail, void* vtail,
-                                const Dims& d, hipStream_t st) {
-  if (d.L % 64 != 0 && (ktail == nullptr || vtail == nullptr)) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)(d.Lv / 64), d.Hkv, d.S);
-#define MOBA_BT(DV)                                                                             \
-  hipLaunchKernelGGL(k_bwd_transform<DV>, grid, dim3(256), 0, st, static_cast<const bf16_t*>(k), \
-                     static_cast<const bf16_t*>(v), static_cast<bf16_t*>(kt),                   \
-                     static_cast<bf16_t*>(ktail), static_cast<bf16_t*>(vtail), d.Hkv, d.L, d.Lv)
+hipError_t launch_bwd_tail(const void* k, const void* v, void* ktail, void* vtail, const Dims& d,
+                          hipStream_t st) {
+  if (d.L % 64 == 0) return hipSuccess;
+  if (ktail == nullptr || vtail == nullptr) return hipErrorInvalidValue;
+  const dim3 grid(d.Hkv, d.S);
+#define MOBA_BT(DV)                                                                          \
+  hipLaunchKernelGGL(k_bwd_tail<DV>, grid, dim3(256), 0, st, static_cast<const bf16_t*>(k), \
+                     static_cast<const bf16_t*>(v), static_cast<bf16_t*>(ktail),            \
+                     static_cast<bf16_t*>(vtail), d.Hkv, d.L)
   if (d.D == 128) MOBA_BT(128); else MOBA_BT(64);
 #undef MOBA_BT
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_dq_routed(const void* q, const void* dout, const void* k, const void* v,
-                                const void* kt, const float* lse, const float* dvec,
+                                const float* lse, const float* dvec,
                                 const uint32_t* list, const uint32_t* bucket_off,
                                 const uint32_t* tile_off, void* dqp, const Dims& d,
                                 hipStream_t st) {
@@ -919,25 +868,24 @@ hipError_t launch_bwd_dq_routed(const void* q, const void* dout, const void* k, 
   hipLaunchKernelGGL((k_bwd_dq_routed<DV, NWV>), dim3((unsigned)grid), dim3(64 * NWV), 0, st,  \
                      static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(dout),          \
                      static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v),             \
-                     static_cast<const bf16_t*>(kt), lse, dvec, list, bucket_off, tile_off,    \
-                     static_cast<bf16_t*>(dqp), d.Lq, d.L, d.Lv, d.H, d.Hkv, d.kp, d.B, d.nb,  \
+                     lse, dvec, list, bucket_off, tile_off,                                    \
+                     static_cast<bf16_t*>(dqp), d.Lq, d.L, d.H, d.Hkv, d.kp, d.B, d.nb,        \
                      d.nrows, sl2, scale, (uint32_t)d.slots)
-  if (d.tile_m == 256) {
-    if (d.D == 128) MOBA_BQR(128, 8); else MOBA_BQR(64, 8);
-  } else {
-    if (d.D == 128) MOBA_BQR(128, 4); else MOBA_BQR(64, 4);
-  }
+  // eight-wave tiles of 256 routed entries only (the four-wave form does not
+  // fit two waves per SIMD)
+  if (d.tile_m != 256) return hipErrorInvalidValue;
+  if (d.D == 128) MOBA_BQR(128, 8); else MOBA_BQR(64, 8);
 #undef MOBA_BQR
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_dq_own(const void* q, const void* dout, const void* k, const void* v,
-                             const void* kt, const void* ktail, const void* vtail,
+                             const void* ktail, const void* vtail,
                              const float* lse, const float* dvec, const void* dqp, void* dq,
                              const Dims& d, hipStream_t st) {
   if (d.L % 64 != 0 && (ktail == nullptr || vtail == nullptr)) return hipErrorInvalidValue;
   const int HW = gcd_i(d.G, 4);
-  constexpr int NW = 4;
+  constexpr int NW = 8;
   const int RW = 32 * NW / HW;
   const dim3 grid((unsigned)((d.Lq + RW - 1) / RW), d.S * d.H / HW);
   const float sl2 = kLog2e / sqrtf((float)d.D);
@@ -946,10 +894,9 @@ hipError_t launch_bwd_dq_own(const void* q, const void* dout, const void* k, con
   hipLaunchKernelGGL((k_bwd_dq_own<DV, NW>), grid, dim3(64 * NW), 0, st,                        \
                      static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(dout),           \
                      static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v),              \
-                     static_cast<const bf16_t*>(kt), static_cast<const bf16_t*>(ktail),         \
-                     static_cast<const bf16_t*>(vtail), lse, dvec,                              \
-                     static_cast<const bf16_t*>(dqp), static_cast<bf16_t*>(dq), (int)d.Lq,      \
-                     (int)d.L, (int)d.Lv, (int)d.q_off, d.H, d.Hkv, d.kp, d.B, HW, sl2, scale)
+                     static_cast<const bf16_t*>(ktail), static_cast<const bf16_t*>(vtail),      \
+                     lse, dvec, static_cast<const bf16_t*>(dqp), static_cast<bf16_t*>(dq),      \
+                     (int)d.Lq, (int)d.L, (int)d.q_off, d.H, d.Hkv, d.kp, d.B, HW, sl2, scale)
   if (d.D == 128) MOBA_BQO(128); else MOBA_BQO(64);
 #undef MOBA_BQO
   return hipGetLastError();

@@ -177,19 +177,20 @@ hipError_t launch_decode_merge(const float* part, const int32_t* ublk, const uin
                                float* lse_out = nullptr);
 
 // Backward (bf16), see attn_bwd.hip.  dvec [S*H*Lq] fp32 in query-head order;
-// kt [S, Hkv, D, Lv]; ktail / vtail [S, 64, Hkv, D] when L % 64 != 0; dqp one
-// bf16 row per routed slot; lse is the forward's natural log-sum-exp.
+// ktail / vtail [S, 64, Hkv, D] when L % 64 != 0 (launch_bwd_tail does nothing
+// otherwise); dqp one bf16 row per routed slot; lse is the forward's natural
+// log-sum-exp.
 hipError_t launch_bwd_dot(const void* out, const void* dout, float* dvec, const Dims& d,
                           hipStream_t st);
-hipError_t launch_bwd_transform(const void* k, const void* v, void* kt, void* ktail, void* vtail,
-                                const Dims& d, hipStream_t st);
+hipError_t launch_bwd_tail(const void* k, const void* v, void* ktail, void* vtail, const Dims& d,
+                          hipStream_t st);
 hipError_t launch_bwd_dq_routed(const void* q, const void* dout, const void* k, const void* v,
-                                const void* kt, const float* lse, const float* dvec,
+                                const float* lse, const float* dvec,
                                 const uint32_t* list, const uint32_t* bucket_off,
                                 const uint32_t* tile_off, void* dqp, const Dims& d,
                                 hipStream_t st);
 hipError_t launch_bwd_dq_own(const void* q, const void* dout, const void* k, const void* v,
-                             const void* kt, const void* ktail, const void* vtail,
+                             const void* ktail, const void* vtail,
                              const float* lse, const float* dvec, const void* dqp, void* dq,
                              const Dims& d, hipStream_t st);
 // list / bucket_off NULL: no routed entries (top-k 1 or a single block).

@@ -361,12 +361,11 @@ hipError_t launch_bwd_dot(const void* out, const void* dout, float* dvec, const 
   return hipSuccess;
 }
 
-hipError_t launch_bwd_transform(const void* k, const void* v, void* kt, void* ktail, void* vtail, const Dims& d, hipStream_t st) {
+hipError_t launch_bwd_tail(const void* k, const void* v, void* ktail, void* vtail, const Dims& d, hipStream_t st) {
   Call c;
-  c.name = "bwd_transform";
+  c.name = "bwd_tail";
   c.ptrs.push_back(reinterpret_cast<uintptr_t>(k));
   c.ptrs.push_back(reinterpret_cast<uintptr_t>(v));
-  c.ptrs.push_back(reinterpret_cast<uintptr_t>(kt));
   c.ptrs.push_back(reinterpret_cast<uintptr_t>(ktail));
   c.ptrs.push_back(reinterpret_cast<uintptr_t>(vtail));
   c.d = d; c.has_d = true;
@@ -375,14 +374,13 @@ hipError_t launch_bwd_transform(const void* k, const void* v, void* kt, void* kt
   return hipSuccess;
 }
 
-hipError_t launch_bwd_dq_routed(const void* q, const void* dout, const void* k, const void* v, const void* kt, const float* lse, const float* dvec, const uint32_t* list, const uint32_t* bucket_off, const uint32_t* tile_off, void* dqp, const Dims& d, hipStream_t st) {
+hipError_t launch_bwd_dq_routed(const void* q, const void* dout, const void* k, const void* v, const float* lse, const float* dvec, const uint32_t* list, const uint32_t* bucket_off, const uint32_t* tile_off, void* dqp, const Dims& d, hipStream_t st) {
   Call c;
   c.name = "bwd_dq_routed";
   c.ptrs.push_back(reinterpret_cast<uintptr_t>(q));
   c.ptrs.push_back(reinterpret_cast<uintptr_t>(dout));
   c.ptrs.push_back(reinterpret_cast<uintptr_t>(k));
   c.ptrs.push_back(reinterpret_cast<uintptr_t>(v));
-  c.ptrs.push_back(reinterpret_cast<uintptr_t>(kt));
   c.ptrs.push_back(reinterpret_cast<uintptr_t>(lse));
   c.ptrs.push_back(reinterpret_cast<uintptr_t>(dvec));
   c.ptrs.push_back(reinterpret_cast<uintptr_t>(list));
@@ -395,14 +393,13 @@ hipError_t launch_bwd_dq_routed(const void* q, const void* dout, const void* k, 
   return hipSuccess;
 }
 
-hipError_t launch_bwd_dq_own(const void* q, const void* dout, const void* k, const void* v, const void* kt, const void* ktail, const void* vtail, const float* lse, const float* dvec, const void* dqp, void* dq, const Dims& d, hipStream_t st) {
+hipError_t launch_bwd_dq_own(const void* q, const void* dout, const void* k, const void* v, const void* ktail, const void* vtail, const float* lse, const float* dvec, const void* dqp, void* dq, const Dims& d, hipStream_t st) {
   Call c;
   c.name = "bwd_dq_own";
   c.ptrs.push_back(reinterpret_cast<uintptr_t>(q));
   c.ptrs.push_back(reinterpret_cast<uintptr_t>(dout));
   c.ptrs.push_back(reinterpret_cast<uintptr_t>(k));
   c.ptrs.push_back(reinterpret_cast<uintptr_t>(v));
-  c.ptrs.push_back(reinterpret_cast<uintptr_t>(kt));
   c.ptrs.push_back(reinterpret_cast<uintptr_t>(ktail));
   c.ptrs.push_back(reinterpret_cast<uintptr_t>(vtail));
   c.ptrs.push_back(reinterpret_cast<uintptr_t>(lse));
