@@ -721,4 +721,4 @@ KERNEL_NAMES = ("block_mean", "transpose_v", "gate_topk", "route_count", "route_
                 "attn_full", "decode_plan", "decode_attn", "decode_merge", "merge_partials",
                 "pool_transpose", "block_mean_finalize", "route_scan_small", "bwd_dot",
                 "bwd_tail", "bwd_dq_routed", "bwd_dq_own", "bwd_dkdv", "naive_scores",
-                "naive_softmax", "naive_pv")
+                "naive_softmax", "naive_pv", "bwd_entries")

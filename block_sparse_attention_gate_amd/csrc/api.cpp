@@ -59,14 +59,14 @@ enum KernelId {
   K_ATTN_ROUTED, K_ATTN_OWN, K_ATTN_FULL, K_DEC_PLAN, K_DEC_ATTN, K_DEC_MERGE, K_MERGE,
   K_POOL_TRANSPOSE, K_MEAN_FINALIZE, K_RSCAN_SMALL, K_BWD_DOT, K_BWD_TAIL,
   K_BWD_DQ_ROUTED, K_BWD_DQ_OWN, K_BWD_DKDV, K_NAIVE_SCORES, K_NAIVE_SOFTMAX, K_NAIVE_PV,
-  K_COUNT
+  K_BWD_ENTRIES, K_COUNT
 };
 const char* const kKernelNames[K_COUNT] = {
     "block_mean", "transpose_v", "gate_topk", "route_count", "route_scan_rows",
     "route_scan_buckets", "route_scatter", "attn_routed", "attn_own_merge", "attn_full",
     "decode_plan", "decode_attn", "decode_merge", "merge_partials", "pool_transpose",
     "block_mean_finalize", "route_scan_small", "bwd_dot", "bwd_tail", "bwd_dq_routed",
-    "bwd_dq_own", "bwd_dkdv", "naive_scores", "naive_softmax", "naive_pv"};
+    "bwd_dq_own", "bwd_dkdv", "naive_scores", "naive_softmax", "naive_pv", "bwd_entries"};
 
 struct ProfRecord {
   int id;
@@ -759,7 +759,8 @@ moba_status full_impl(const moba_args* a) {
 struct BwdPlan {
   Plan f;                  // dims (forward_dims) and the routing-table offsets
   bool routed = false, need_tail = false;
-  size_t off_dvec = 0, off_ktail = 0, off_vtail = 0, off_dqp = 0, off_kvpart = 0,
+  size_t off_dvec = 0, off_rowstat = 0, off_ktail = 0, off_vtail = 0, off_dqp = 0, off_ent = 0,
+         off_kvpart = 0,
          total = 0;
   bool need_kvpart = false;
 };
@@ -798,6 +799,7 @@ moba_status plan_backward(const moba_bwd_args* b, BwdPlan* bp) {
   };
   Plan& p = bp->f;
   bp->off_dvec = take((size_t)d.S * d.H * d.Lq * 4);
+  if (d.bf16) bp->off_rowstat = take((size_t)d.S * d.H * d.Lq * 8);
   // fp32 reads K and V as given (no tail tiles)
   bp->need_tail = d.bf16 && d.L % 64 != 0;
   if (bp->need_tail) {
@@ -812,6 +814,8 @@ moba_status plan_backward(const moba_bwd_args* b, BwdPlan* bp) {
     p.off_toff = take((size_t)(d.nrows + 1) * 4);
     p.off_list = take((size_t)d.slots * 4);
     bp->off_dqp = take((size_t)d.slots * d.D * (d.bf16 ? 2 : 4));
+    // bf16 dk/dv reads every entry's Q / dO row index
+    if (d.bf16) bp->off_ent = take((size_t)d.slots * 4);
   }
   const size_t kvp = d.bf16 ? moba::bwd_dkdv_partial_floats(d) : 0;
   bp->need_kvpart = kvp > 0;
@@ -847,6 +851,7 @@ moba_status backward_impl(const moba_bwd_args* b) {
   }
   char* w = ws.base;
   float* dvec = (float*)(w + bp.off_dvec);
+  void* rowstat = d.bf16 ? (void*)(w + bp.off_rowstat) : nullptr;
   void* ktail = bp.need_tail ? (void*)(w + bp.off_ktail) : nullptr;
   void* vtail = bp.need_tail ? (void*)(w + bp.off_vtail) : nullptr;
   const Plan& p = bp.f;
@@ -859,7 +864,7 @@ moba_status backward_impl(const moba_bwd_args* b) {
 
   Launch l{ws.st};
   l.run(K_BWD_DOT, [&] {
-    return d.bf16 ? moba::launch_bwd_dot(b->out, b->dout, dvec, d, l.st)
+    return d.bf16 ? moba::launch_bwd_dot(b->out, b->dout, b->lse, dvec, rowstat, d, l.st)
                   : moba::launch_bwd_dot_f32(b->out, b->dout, dvec, d, l.st);
   });
   if (bp.need_tail)
@@ -891,12 +896,16 @@ moba_status backward_impl(const moba_bwd_args* b) {
                   : moba::launch_bwd_dq_own_f32(b->q, b->dout, b->k, b->v, b->lse, dvec,
                                                 (const float*)dqp, b->dq, d, l.st);
   });
+  void* ent = (bp.routed && d.bf16) ? (void*)(w + bp.off_ent) : nullptr;
+  if (ent)
+    l.run(K_BWD_ENTRIES,
+          [&] { return moba::launch_bwd_entry_rows(list, boff, ent, d, l.st); });
   l.run(K_BWD_DKDV, [&] {
     if (!d.bf16)
       return moba::launch_bwd_dkdv_f32(b->q, b->dout, b->k, b->v, b->lse, dvec, list, boff,
                                        b->dk, b->dv, d, l.st);
     float* kvpart = bp.need_kvpart ? (float*)(w + bp.off_kvpart) : nullptr;
-    return moba::launch_bwd_dkdv(b->q, b->dout, b->k, b->v, b->lse, dvec, list, boff, b->dk,
+    return moba::launch_bwd_dkdv(b->q, b->dout, b->k, b->v, rowstat, ent, boff, b->dk,
                                  b->dv, kvpart, d, l.st);
   });
   if (l.err != hipSuccess) return hip_fail(l);

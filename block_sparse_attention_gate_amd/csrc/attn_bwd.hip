@@ -37,11 +37,14 @@ namespace moba {
 
 // ------------------------------------------------------------ Dv = dO . o
 // One row per LPR = D/8 lanes (16 bytes of o and dO each); the row index is
-// in memory order (s, r, h) and Dv is written in query-head order.
+// in memory order (s, r, h).  Dv is written in query-head order; with
+// rowstat (bf16 dk/dv) also (lse log2(e), Dv) per row in memory order.
 template <int D>
 __global__ __launch_bounds__(256) void k_bwd_dot(const bf16_t* __restrict__ o,
                                                  const bf16_t* __restrict__ dout,
-                                                 float* __restrict__ dvec, int64_t nrows,
+                                                 const float* __restrict__ lse,
+                                                 float* __restrict__ dvec,
+                                                 float2* __restrict__ rowstat, int64_t nrows,
                                                  int64_t Lq, int H) {
   constexpr int LPR = D / 8;
   const int64_t row = (int64_t)blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
@@ -60,7 +63,9 @@ __global__ __launch_bounds__(256) void k_bwd_dot(const bf16_t* __restrict__ o,
   for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
   if (row < nrows && sub == 0) {
     const int64_t h = row % H, sr = row / H, r = sr % Lq, s = sr / Lq;
-    dvec[(s * H + h) * Lq + r] = acc;
+    const int64_t qh = (s * H + h) * Lq + r;
+    dvec[qh] = acc;
+    if (rowstat) rowstat[row] = make_float2(lse[qh] * kLog2e, acc);
   }
 }
 
@@ -89,29 +94,6 @@ __global__ __launch_bounds__(256) void k_bwd_tail(const bf16_t* __restrict__ k,
     *reinterpret_cast<u32x4*>(ktail + dst) = kv;
     *reinterpret_cast<u32x4*>(vtail + dst) = vv;
   }
-}
-
-// Unsigned 32-bit division by a divisor fixed for the launch, with a multiply
-// and shifts (Granlund and Montgomery, "Division by invariant integers using
-// multiplication", 1994: the round-up multiplier of ceil(log2 d) + 32 bits).
-struct FastDiv {
-  uint32_t d, m, s1, s2;
-};
-
-static FastDiv make_fastdiv(uint32_t d) {
-  uint32_t l = 0;
-  while (l < 32 && (uint64_t(1) << l) < d) ++l;
-  FastDiv f;
-  f.d = d;
-  f.m = (uint32_t)(((uint64_t(1) << 32) * ((uint64_t(1) << l) - d)) / d + 1);
-  f.s1 = l < 1 ? l : 1;
-  f.s2 = l > 1 ? l - 1 : 0;
-  return f;
-}
-
-__device__ __forceinline__ uint32_t fdiv(uint32_t x, const FastDiv& f) {
-  const uint32_t t = __umulhi(f.m, x);
-  return (t + ((x - t) >> f.s1)) >> f.s2;
 }
 
 // LDS tiles of 64 rows (keys or queries) of D bf16, unpadded, with the
@@ -459,6 +441,25 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_bwd_dq_own(
   store_dq_row<D>(dq + qrow, acc, hh, 1.0f);
 }
 
+// ============================================== routed entries -> query rows
+// For the dk/dv kernel, which reads every routed entry of a bucket once per
+// key chunk: per entry e (a slot id ((s*H + h)*Lq + r)*kp + t in routing
+// order) the row index (s*Lq + r)*H + h of its Q / dO rows and of rowstat,
+// so that the kernel's per-step gather needs no division.  grid
+// ceil(slots / 256) (an upper bound of the entry count), 256 threads.
+__global__ __launch_bounds__(256) void k_bwd_entry_rows(const uint32_t* __restrict__ list,
+                                                        const uint32_t* __restrict__ total,
+                                                        uint32_t* __restrict__ ent, int kp,
+                                                        int Lq, int H) {
+  const uint32_t e = blockIdx.x * 256u + threadIdx.x;
+  if (e >= *total) return;
+  const uint32_t qhh = list[e] / (uint32_t)kp;      // (s*H + h)*Lq + r
+  const uint32_t sh = qhh / (uint32_t)Lq;
+  const uint32_t r = qhh - sh * (uint32_t)Lq;
+  const uint32_t sq = sh / (uint32_t)H, h = sh - sq * (uint32_t)H;
+  ent[e] = (sq * (uint32_t)Lq + r) * (uint32_t)H + h;
+}
+
 // ============================================================ dk, dv kernel
 // Q and dO tiles of QN = 64 queries, row-major in LDS.  The A operands of
 // dV^T += dO^T P and dK^T += Q^T dS (rows d, contraction over queries) are
@@ -493,11 +494,11 @@ __device__ __forceinline__ void static_for(F&& f) {
 template <int D, int NW>
 __global__ __launch_bounds__(64 * NW, 1) void k_bwd_dkdv(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ dout,
-    const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, const float* __restrict__ lse,
-    const float* __restrict__ dvec, const uint32_t* __restrict__ list,
+    const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+    const float2* __restrict__ rowstat, const uint32_t* __restrict__ ent,
     const uint32_t* __restrict__ bucket_off, bf16_t* __restrict__ dk, bf16_t* __restrict__ dv,
-    float* __restrict__ kvpart, int Lq, int L, int q_off, int H, int Hkv, int kp, int B, int nb,
-    int nchunk, int nseg, FastDiv fd_kp, FastDiv fd_lq, float sl2, float scale) {
+    float* __restrict__ kvpart, int Lq, int L, int q_off, int H, int Hkv, int B, int nb,
+    int nchunk, int nseg, float sl2, float scale) {
   using T = KvTiles<D, NW>;
   constexpr int QN = T::QN;
   __shared__ __attribute__((aligned(16))) bf16_t lds[2 * T::BUF];
@@ -564,54 +565,44 @@ __global__ __launch_bounds__(64 * NW, 1) void k_bwd_dkdv(
   // chunks w, w + NW, ... of the row.
   u32x4 qr[T::CH], dr[T::CH];
   bool row_ok = false;               // query `lane` of step it+1 exists
-  float st_l = 0.f, st_d = 0.f;      // wave 0: lse, Dv of query `lane` (step it+1)
-  uint32_t ida = 0u;                 // entry id of query `lane` of step it+1, then it+2
-  // query `lane` of a step: row offset and query-head index, or false
-  auto query_at = [&](int step, uint32_t id, int64_t& qrow, int64_t& qhi) -> bool {
-    int r, h;
+  float2 st_ld = make_float2(0.f, 0.f);   // wave 0: lse2, Dv of query `lane` (step it+1)
+  uint32_t ida = 0u;                 // row index of query `lane` of step it+1, then it+2
+  // query `lane` of a step: its row index (s*Lq + r)*H + h, or false
+  auto query_at = [&](int step, uint32_t id, int64_t& qr_idx) -> bool {
     if (step < rsteps) {
       if (step * QN + lane >= nrt) return false;
-      const uint32_t qhh = fdiv(id, fd_kp);             // (s*H + h)*Lq + r
-      const uint32_t sh = fdiv(qhh, fd_lq);             // s*H + h
-      r = (int)(qhh - sh * fd_lq.d);
-      h = (int)(sh - (uint32_t)s * H);
-      if (r < 0 || r >= Lq || h < 0 || h >= H) return false;  // never for a routed slot
-    } else {
-      const int st = step - rsteps + olo;
-      const int hl = st / psteps_h, pc = st - hl * psteps_h;
-      const int p = p0 + pc * QN + lane;
-      if (p >= pend) return false;
-      r = p - q_off;
-      h = g * G + hl;
+      qr_idx = id;
+      return true;
     }
-    qrow = (((int64_t)s * Lq + r) * H + h) * D;
-    qhi = ((int64_t)s * H + h) * Lq + r;
+    const int st = step - rsteps + olo;
+    const int hl = st / psteps_h, pc = st - hl * psteps_h;
+    const int p = p0 + pc * QN + lane;
+    if (p >= pend) return false;
+    qr_idx = ((int64_t)s * Lq + (p - q_off)) * H + g * G + hl;
     return true;
   };
   // The loads below go to valid addresses whatever the query (row 0 and
-  // entry rbase stand in for invalid ones) and are not selected on right
-  // away: a select on a loaded value would wait for the load there, at the
-  // start of the step.  Invalid rows are zeroed when the tiles are stored.
+  // the bucket's last entry stand in for invalid ones) and are not selected
+  // on right away: a select on a loaded value would wait for the load there,
+  // at the start of the step.  Invalid rows are zeroed when the tiles are
+  // stored.
   auto fetch_id = [&](int step) {
     if (step >= rsteps) return;  // own steps need no ids (and rsteps > 0 means nrt > 0)
     const int e = step * QN + lane;
-    ida = list[rbase + (e < nrt ? e : nrt - 1)];   // entries past nrt: query_at rejects them
+    ida = ent[rbase + (e < nrt ? e : nrt - 1)];   // entries past nrt: query_at rejects them
   };
   auto fetch_rows = [&](int step) {
-    int64_t qrow = 0, qhi = 0;
-    row_ok = query_at(step, ida, qrow, qhi);
-    if (!row_ok) qrow = qhi = 0;
-    const bf16_t* qp = q + qrow + 8 * w;
-    const bf16_t* dp = dout + qrow + 8 * w;
+    int64_t qr_idx = 0;
+    row_ok = query_at(step, ida, qr_idx);
+    if (!row_ok) qr_idx = 0;
+    const bf16_t* qp = q + qr_idx * D + 8 * w;
+    const bf16_t* dp = dout + qr_idx * D + 8 * w;
 #pragma unroll
     for (int i = 0; i < T::CH; ++i) {
       qr[i] = *reinterpret_cast<const u32x4*>(qp + 8 * NW * i);
       dr[i] = *reinterpret_cast<const u32x4*>(dp + 8 * NW * i);
     }
-    if (w == 0) {
-      st_l = lse[qhi];
-      st_d = dvec[qhi];
-    }
+    if (w == 0) st_ld = rowstat[qr_idx];
   };
   auto stage_chunk = [&](int buf, int i) {
     const u32x4 z = u32x4{0u, 0u, 0u, 0u};
@@ -626,8 +617,8 @@ __global__ __launch_bounds__(64 * NW, 1) void k_bwd_dkdv(
   // an invalid query gets lse2 = +inf, hence p = 0 (its rows are zero too)
   auto stage_stats = [&](int buf) {
     if (w == 0) {
-      stat[buf][0][lane] = row_ok ? st_l * kLog2e : __builtin_inff();
-      stat[buf][1][lane] = row_ok ? st_d : 0.f;
+      stat[buf][0][lane] = row_ok ? st_ld.x : __builtin_inff();
+      stat[buf][1][lane] = row_ok ? st_ld.y : 0.f;
     }
   };
 
@@ -826,19 +817,19 @@ static int gcd_i(int a, int b) {
   return a;
 }
 
-hipError_t launch_bwd_dot(const void* out, const void* dout, float* dvec, const Dims& d,
-                          hipStream_t st) {
+hipError_t launch_bwd_dot(const void* out, const void* dout, const float* lse, float* dvec,
+                          void* rowstat, const Dims& d, hipStream_t st) {
   const int64_t nrows = (int64_t)d.S * d.Lq * d.H;
   const int rpb = 256 / (d.D / 8);
   const unsigned grid = (unsigned)((nrows + rpb - 1) / rpb);
   if (d.D == 128)
     hipLaunchKernelGGL(k_bwd_dot<128>, dim3(grid), dim3(256), 0, st,
-                       static_cast<const bf16_t*>(out), static_cast<const bf16_t*>(dout), dvec,
-                       nrows, d.Lq, d.H);
+                       static_cast<const bf16_t*>(out), static_cast<const bf16_t*>(dout), lse,
+                       dvec, static_cast<float2*>(rowstat), nrows, d.Lq, d.H);
   else
     hipLaunchKernelGGL(k_bwd_dot<64>, dim3(grid), dim3(256), 0, st,
-                       static_cast<const bf16_t*>(out), static_cast<const bf16_t*>(dout), dvec,
-                       nrows, d.Lq, d.H);
+                       static_cast<const bf16_t*>(out), static_cast<const bf16_t*>(dout), lse,
+                       dvec, static_cast<float2*>(rowstat), nrows, d.Lq, d.H);
   return hipGetLastError();
 }
 
@@ -902,8 +893,16 @@ hipError_t launch_bwd_dq_own(const void* q, const void* dout, const void* k, con
   return hipGetLastError();
 }
 
+hipError_t launch_bwd_entry_rows(const uint32_t* list, const uint32_t* bucket_off, void* ent,
+                                const Dims& d, hipStream_t st) {
+  if (d.slots <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_bwd_entry_rows, dim3((unsigned)((d.slots + 255) / 256)), dim3(256), 0, st,
+                     list, bucket_off + d.nrows, static_cast<uint32_t*>(ent), d.kp, (int)d.Lq, d.H);
+  return hipGetLastError();
+}
+
 hipError_t launch_bwd_dkdv(const void* q, const void* dout, const void* k, const void* v,
-                           const float* lse, const float* dvec, const uint32_t* list,
+                           const void* rowstat, const void* ent,
                            const uint32_t* bucket_off, void* dk, void* dv, float* kvpart,
                            const Dims& d, hipStream_t st) {
   const int NWv = bwd_dkdv_waves(d);
@@ -914,15 +913,14 @@ hipError_t launch_bwd_dkdv(const void* q, const void* dout, const void* k, const
   const int64_t grid = (int64_t)d.S * d.Hkv * d.nb * nchunk * nseg;
   const float sl2 = kLog2e / sqrtf((float)d.D);
   const float scale = 1.0f / sqrtf((float)d.D);
-  const FastDiv fkp = make_fastdiv((uint32_t)(d.kp > 0 ? d.kp : 1));
-  const FastDiv flq = make_fastdiv((uint32_t)d.Lq);
 #define MOBA_BKV(DV, NWV)                                                                       \
   hipLaunchKernelGGL((k_bwd_dkdv<DV, NWV>), dim3((unsigned)grid), dim3(64 * NWV), 0, st, \
                      static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(dout),           \
-                     static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v), lse, dvec,   \
-                     list, bucket_off, static_cast<bf16_t*>(dk), static_cast<bf16_t*>(dv),      \
-                     kvpart, (int)d.Lq, (int)d.L, (int)d.q_off, d.H, d.Hkv, d.kp, d.B, d.nb,    \
-                     nchunk, nseg, fkp, flq, sl2, scale)
+                     static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v),              \
+                     static_cast<const float2*>(rowstat), static_cast<const uint32_t*>(ent),    \
+                     bucket_off, static_cast<bf16_t*>(dk),                                      \
+                     static_cast<bf16_t*>(dv), kvpart, (int)d.Lq, (int)d.L, (int)d.q_off, d.H,  \
+                     d.Hkv, d.B, d.nb, nchunk, nseg, sl2, scale)
   if (NWv == 4) {
     if (d.D == 128) MOBA_BKV(128, 4); else MOBA_BKV(64, 4);
   } else {

@@ -180,8 +180,8 @@ hipError_t launch_decode_merge(const float* part, const int32_t* ublk, const uin
 // ktail / vtail [S, 64, Hkv, D] when L % 64 != 0 (launch_bwd_tail does nothing
 // otherwise); dqp one bf16 row per routed slot; lse is the forward's natural
 // log-sum-exp.
-hipError_t launch_bwd_dot(const void* out, const void* dout, float* dvec, const Dims& d,
-                          hipStream_t st);
+hipError_t launch_bwd_dot(const void* out, const void* dout, const float* lse, float* dvec,
+                          void* rowstat, const Dims& d, hipStream_t st);
 hipError_t launch_bwd_tail(const void* k, const void* v, void* ktail, void* vtail, const Dims& d,
                           hipStream_t st);
 hipError_t launch_bwd_dq_routed(const void* q, const void* dout, const void* k, const void* v,
@@ -199,8 +199,14 @@ hipError_t launch_bwd_dq_own(const void* q, const void* dout, const void* k, con
 int bwd_dkdv_waves(const Dims& d);
 int bwd_dkdv_segments(const Dims& d);
 size_t bwd_dkdv_partial_floats(const Dims& d);
+// rowstat (bf16 dk/dv): float2 (lse log2(e), Dv) per query-head row in
+// memory order [S, Lq, H], written by launch_bwd_dot when non-null.  ent: the
+// row index (s*Lq + r)*H + h of every routed entry (uint32, routing order),
+// written by launch_bwd_entry_rows from the routing list.
+hipError_t launch_bwd_entry_rows(const uint32_t* list, const uint32_t* bucket_off, void* ent,
+                                const Dims& d, hipStream_t st);
 hipError_t launch_bwd_dkdv(const void* q, const void* dout, const void* k, const void* v,
-                           const float* lse, const float* dvec, const uint32_t* list,
+                           const void* rowstat, const void* ent,
                            const uint32_t* bucket_off, void* dk, void* dv, float* kvpart,
                            const Dims& d, hipStream_t st);
 

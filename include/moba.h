@@ -365,7 +365,7 @@ int32_t moba_abi_version(void);
  * "attn_own_merge", "attn_full", "decode_plan", "decode_attn",
  * "decode_merge", "merge_partials", "pool_transpose", "block_mean_finalize",
  * "route_scan_small", and for the backward "bwd_dot", "bwd_tail",
- * "bwd_dq_routed", "bwd_dq_own", "bwd_dkdv", and for moba_naive_ex
+ * "bwd_dq_routed", "bwd_dq_own", "bwd_dkdv", "bwd_entries", and for moba_naive_ex
  * "naive_scores", "naive_softmax", "naive_pv".  Unknown names give
  * MOBA_ERR_INVALID_ARGUMENT.  (bf16 prefill runs the own-block attention,
  * "attn_own_merge", on an internal stream of the same device, forked from

@@ -246,6 +246,18 @@ static void check_route_and_backward() {
   hoststub::reset();
   expect(moba_backward_ex(&b) == MOBA_OK && count("bwd_dkdv") == 1 && count("bwd_dq_own") == 1,
          "backward: dq and dk/dv launched");
+  // bf16 dk/dv reads the entry rows written from the routing list
+  expect(count("bwd_entries") == 1 && first("route_scatter") < first("bwd_entries") &&
+             first("bwd_entries") < first("bwd_dkdv") && count("bwd_tail") == 0,
+         "backward: entry rows after the scatter and before dk/dv; no tail copy at 4096 keys");
+  b.kv_len = 4100; b.q_len = 4100;
+  hoststub::reset();
+  expect(moba_backward_ex(&b) == MOBA_OK && count("bwd_tail") == 1,
+         "backward: the last partial K/V tile copied when kv_len % 64 != 0");
+  b.dtype = MOBA_DTYPE_F32;
+  hoststub::reset();
+  expect(moba_backward_ex(&b) == MOBA_OK && count("bwd_entries") == 0 && count("bwd_tail") == 0,
+         "backward fp32: no entry rows, no tail copy");
 }
 
 int main() {

@@ -349,12 +349,14 @@ hipError_t launch_decode_merge(const float* part, const int32_t* ublk, const uin
   return hipSuccess;
 }
 
-hipError_t launch_bwd_dot(const void* out, const void* dout, float* dvec, const Dims& d, hipStream_t st) {
+hipError_t launch_bwd_dot(const void* out, const void* dout, const float* lse, float* dvec, void* rowstat, const Dims& d, hipStream_t st) {
   Call c;
   c.name = "bwd_dot";
   c.ptrs.push_back(reinterpret_cast<uintptr_t>(out));
   c.ptrs.push_back(reinterpret_cast<uintptr_t>(dout));
+  c.ptrs.push_back(reinterpret_cast<uintptr_t>(lse));
   c.ptrs.push_back(reinterpret_cast<uintptr_t>(dvec));
+  c.ptrs.push_back(reinterpret_cast<uintptr_t>(rowstat));
   c.d = d; c.has_d = true;
   c.stream = reinterpret_cast<uintptr_t>(st);
   record(c);
@@ -412,16 +414,27 @@ hipError_t launch_bwd_dq_own(const void* q, const void* dout, const void* k, con
   return hipSuccess;
 }
 
-hipError_t launch_bwd_dkdv(const void* q, const void* dout, const void* k, const void* v, const float* lse, const float* dvec, const uint32_t* list, const uint32_t* bucket_off, void* dk, void* dv, float* kvpart, const Dims& d, hipStream_t st) {
+hipError_t launch_bwd_entry_rows(const uint32_t* list, const uint32_t* bucket_off, void* ent, const Dims& d, hipStream_t st) {
+  Call c;
+  c.name = "bwd_entries";
+  c.ptrs.push_back(reinterpret_cast<uintptr_t>(list));
+  c.ptrs.push_back(reinterpret_cast<uintptr_t>(bucket_off));
+  c.ptrs.push_back(reinterpret_cast<uintptr_t>(ent));
+  c.d = d; c.has_d = true;
+  c.stream = reinterpret_cast<uintptr_t>(st);
+  record(c);
+  return hipSuccess;
+}
+
+hipError_t launch_bwd_dkdv(const void* q, const void* dout, const void* k, const void* v, const void* rowstat, const void* ent, const uint32_t* bucket_off, void* dk, void* dv, float* kvpart, const Dims& d, hipStream_t st) {
   Call c;
   c.name = "bwd_dkdv";
   c.ptrs.push_back(reinterpret_cast<uintptr_t>(q));
   c.ptrs.push_back(reinterpret_cast<uintptr_t>(dout));
   c.ptrs.push_back(reinterpret_cast<uintptr_t>(k));
   c.ptrs.push_back(reinterpret_cast<uintptr_t>(v));
-  c.ptrs.push_back(reinterpret_cast<uintptr_t>(lse));
-  c.ptrs.push_back(reinterpret_cast<uintptr_t>(dvec));
-  c.ptrs.push_back(reinterpret_cast<uintptr_t>(list));
+  c.ptrs.push_back(reinterpret_cast<uintptr_t>(rowstat));
+  c.ptrs.push_back(reinterpret_cast<uintptr_t>(ent));
   c.ptrs.push_back(reinterpret_cast<uintptr_t>(bucket_off));
   c.ptrs.push_back(reinterpret_cast<uintptr_t>(dk));
   c.ptrs.push_back(reinterpret_cast<uintptr_t>(dv));
