@@ -271,7 +271,8 @@ def run_backward(moba, w, steps, warmup):
         a = 2.0 * eff / t / 1e12
         res["roofline"] = {"bound": "mfma", "kernel": "bwd_dkdv", "achieved": a,
                            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                           "frac": a / PEAK_BF16_TFLOPS, "traffic": None,
+                           "frac": a / PEAK_BF16_TFLOPS,
+                           "traffic": measured_traffic(f"bwd_dkdv_{w.name}_backward_bytes"),
                            "avg_launch_ms": kern["bwd_dkdv"]["avg_ms"]}
     del q, k, v, out, sel, lse, dout, dq, dk, dv, ws
     torch.cuda.empty_cache()

@@ -331,7 +331,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_bwd_dq_routed(
 // group x RW = 32*NW/HW query rows; wave w: head h0 + w % HW, rows
 // [r0, r0 + 32).  grid (ceil(Lq / RW), S * H / HW).
 template <int D, int NW>
-__global__ __launch_bounds__(64 * NW, 8 / NW) void k_bwd_dq_own(
+__global__ __launch_bounds__(64 * NW, 1) void k_bwd_dq_own(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ dout,
     const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const bf16_t* __restrict__ ktail, const bf16_t* __restrict__ vtail,
@@ -879,19 +879,27 @@ hipError_t launch_bwd_dq_own(const void* q, const void* dout, const void* k, con
                              const Dims& d, hipStream_t st) {
   if (d.L % 64 != 0 && (ktail == nullptr || vtail == nullptr)) return hipErrorInvalidValue;
   const int HW = gcd_i(d.G, 4);
-  constexpr int NW = 8;
+  // eight-wave workgroups (two waves per SIMD) unless that leaves fewer than
+  // two workgroups per CU; four-wave ones then (one wave per SIMD, more
+  // workgroups)
+  const int64_t hg = (int64_t)d.S * d.H / HW;
+  const int NW = ((d.Lq + 256 / HW - 1) / (256 / HW)) * hg >= 512 ? 8 : 4;
   const int RW = 32 * NW / HW;
-  const dim3 grid((unsigned)((d.Lq + RW - 1) / RW), d.S * d.H / HW);
+  const dim3 grid((unsigned)((d.Lq + RW - 1) / RW), (unsigned)hg);
   const float sl2 = kLog2e / sqrtf((float)d.D);
   const float scale = 1.0f / sqrtf((float)d.D);
-#define MOBA_BQO(DV)                                                                            \
-  hipLaunchKernelGGL((k_bwd_dq_own<DV, NW>), grid, dim3(64 * NW), 0, st,                        \
+#define MOBA_BQO(DV, NWV)                                                                       \
+  hipLaunchKernelGGL((k_bwd_dq_own<DV, NWV>), grid, dim3(64 * NWV), 0, st,                      \
                      static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(dout),           \
                      static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v),              \
                      static_cast<const bf16_t*>(ktail), static_cast<const bf16_t*>(vtail),      \
                      lse, dvec, static_cast<const bf16_t*>(dqp), static_cast<bf16_t*>(dq),      \
                      (int)d.Lq, (int)d.L, (int)d.q_off, d.H, d.Hkv, d.kp, d.B, HW, sl2, scale)
-  if (d.D == 128) MOBA_BQO(128); else MOBA_BQO(64);
+  if (NW == 8) {
+    if (d.D == 128) MOBA_BQO(128, 8); else MOBA_BQO(64, 8);
+  } else {
+    if (d.D == 128) MOBA_BQO(128, 4); else MOBA_BQO(64, 4);
+  }
 #undef MOBA_BQO
   return hipGetLastError();
 }
