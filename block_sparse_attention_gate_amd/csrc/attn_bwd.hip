@@ -663,26 +663,26 @@ __global__ __launch_bounds__(64 * NW, 1) void k_bwd_dkdv(
   // queries 32 qb + 16 c + 8 hh + [0, 8) in order, the B operand layout of P
   // and dS for the products over queries.  Queries at positions before the
   // key (own steps) get p = 0.
-  auto soft = [&](int qb, int reg, int pos0, float s, float dp, const f32x4& l4,
+  auto soft = [&](int qb, int reg, bool mask, int pos0, float s, float dp, const f32x4& l4,
                   const f32x4& d4, bf16x8 (&pb)[2], bf16x8 (&dsb)[2]) {
     const int jj = reg & 3;
     const int qi = 32 * qb + acc_key(reg, hh);
     float p = __builtin_amdgcn_exp2f(fmaf(s, sl2, -l4[jj]));
-    p = pos0 + qi < key ? 0.f : p;
+    if (mask && pos0 + qi < key) p = 0.f;
     const float ds = p * (dp - d4[jj]);
     pb[reg >> 3][reg & 7] = static_cast<__bf16>(p);
     dsb[reg >> 3][reg & 7] = static_cast<__bf16>(ds);
   };
 
   f32x16 s0, d0, s1, d1;   // S and dP of the two query halves of a step
-  for (int it = 0; it < nsteps; ++it) {
+  // step `it`; MASK (own steps): the causal mask inside the block
+  auto step = [&](int it, auto maskc) {
+    constexpr bool MASK = decltype(maskc)::value;
     const int CB = it & 1;
     const bf16_t* b = lds + CB * T::BUF;
     const float* st = &stat[CB][0][0];
-    // position of the step's first query (own steps); routed steps mask
-    // nothing
-    int pos0 = 0x3fffffff;
-    if (it >= rsteps) {
+    int pos0 = 0;   // position of the step's first query (own steps)
+    if constexpr (MASK) {
       const int sidx = it - rsteps + olo;
       pos0 = p0 + (sidx - (sidx / psteps_h) * psteps_h) * QN;
     }
@@ -721,7 +721,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_bwd_dkdv(
         else s1 = mfma32(fr[k], kb[t], s1);
         static_for<0, EPS>([&](auto ec) {
           constexpr int reg = ks * EPS + decltype(ec)::value, g = reg >> 2;
-          soft(0, reg, pos0, s0[reg], d0[reg], l4[g & 1], d4[g & 1], pb0, dsb0);
+          soft(0, reg, MASK, pos0, s0[reg], d0[reg], l4[g & 1], d4[g & 1], pb0, dsb0);
         });
       } else if constexpr (ph == 2) {
         constexpr int dt = ks >> 2, c = (ks >> 1) & 1;
@@ -729,7 +729,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_bwd_dkdv(
         else dva[dt] = mfma32(fr[k], pb0[c], dva[dt]);
         static_for<0, EPS>([&](auto ec) {
           constexpr int reg = ks * EPS + decltype(ec)::value, g = 4 + (reg >> 2);
-          soft(1, reg, pos0, s1[reg], d1[reg], l4[g & 1], d4[g & 1], pb1, dsb1);
+          soft(1, reg, MASK, pos0, s1[reg], d1[reg], l4[g & 1], d4[g & 1], pb1, dsb1);
         });
       } else {
         constexpr int dt = ks >> 2, c = (ks >> 1) & 1;
@@ -751,7 +751,10 @@ __global__ __launch_bounds__(64 * NW, 1) void k_bwd_dkdv(
     for (int dt = 0; dt < D / 32; ++dt) asm volatile("" : "+a"(dka[dt]), "+a"(dva[dt]));
     asm volatile("" : "+a"(s0), "+a"(d0), "+a"(s1), "+a"(d1));
     __syncthreads();
-  }
+  };
+  // routed steps first (no mask), then the own steps
+  for (int it = 0; it < rsteps; ++it) step(it, std::false_type{});
+  for (int it = rsteps; it < nsteps; ++it) step(it, std::true_type{});
   if (!key_ok) return;
   // dK^T / dV^T accumulators: lane = key, register 4i + jj = dim
   // 32 dt + 8 i + 4 hh + jj
