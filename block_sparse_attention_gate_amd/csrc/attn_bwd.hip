@@ -559,11 +559,19 @@ __global__ __launch_bounds__(64 * NW, 1) void k_bwd_dkdv(
   const int nsteps = rsteps + (int)((int64_t)nown_all * (seg + 1) / nseg) - olo;
 
   // Staging, three steps in flight: the entry id of step it+2 (routed steps
-  // read it from the list), the Q / dO row and the two statistics of step
+  // read it from the list), the Q / dO rows and the two statistics of step
   // it+1 (requested once step it's first products are issued), and the LDS
-  // tiles of step it.  Lane l stages query l of a step; wave w its 16-byte
-  // chunks w, w + NW, ... of the row.
+  // tiles of step it.  Lane l finds query l of a step; wave w loads the rows
+  // of queries RPW w .. RPW (w + 1) - 1, RPI whole rows per load (CPR lanes
+  // per row, the row index passed between lanes), so that a load touches RPI
+  // rows rather than 64: the gather's cost is the number of rows a load
+  // instruction touches, not its bytes.
+  constexpr int CPR = D / 8;          // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;       // rows per load instruction
+  constexpr int RPW = QN / NW;        // rows per wave
+  static_assert(RPW == RPI * T::CH, "one load per chunk slot");
   u32x4 qr[T::CH], dr[T::CH];
+  int rok[T::CH];                     // the row of load i exists
   bool row_ok = false;               // query `lane` of step it+1 exists
   float2 st_ld = make_float2(0.f, 0.f);   // wave 0: lse2, Dv of query `lane` (step it+1)
   uint32_t ida = 0u;                 // row index of query `lane` of step it+1, then it+2
@@ -595,20 +603,26 @@ __global__ __launch_bounds__(64 * NW, 1) void k_bwd_dkdv(
     int64_t qr_idx = 0;
     row_ok = query_at(step, ida, qr_idx);
     if (!row_ok) qr_idx = 0;
-    const bf16_t* qp = q + qr_idx * D + 8 * w;
-    const bf16_t* dp = dout + qr_idx * D + 8 * w;
+    // row index < S*Lq*H, which is below 2^32 for any input that fits in
+    // device memory
+    const int myrow = (int)(uint32_t)qr_idx;
+    const int myok = row_ok ? 1 : 0;
 #pragma unroll
     for (int i = 0; i < T::CH; ++i) {
-      qr[i] = *reinterpret_cast<const u32x4*>(qp + 8 * NW * i);
-      dr[i] = *reinterpret_cast<const u32x4*>(dp + 8 * NW * i);
+      const int src = RPW * w + RPI * i + lane / CPR;   // query of this lane's row
+      const uint32_t ri = (uint32_t)__shfl(myrow, src);
+      rok[i] = __shfl(myok, src);
+      const int64_t off = (int64_t)ri * D + 8 * (lane % CPR);
+      qr[i] = *reinterpret_cast<const u32x4*>(q + off);
+      dr[i] = *reinterpret_cast<const u32x4*>(dout + off);
     }
     if (w == 0) st_ld = rowstat[qr_idx];
   };
   auto stage_chunk = [&](int buf, int i) {
     const u32x4 z = u32x4{0u, 0u, 0u, 0u};
-    const int o = kv_off<D>(lane, w + NW * i);
-    *reinterpret_cast<u32x4*>(lds + buf * T::BUF + o) = row_ok ? qr[i] : z;
-    *reinterpret_cast<u32x4*>(lds + buf * T::BUF + T::QE + o) = row_ok ? dr[i] : z;
+    const int o = kv_off<D>(RPW * w + RPI * i + lane / CPR, lane % CPR);
+    *reinterpret_cast<u32x4*>(lds + buf * T::BUF + o) = rok[i] ? qr[i] : z;
+    *reinterpret_cast<u32x4*>(lds + buf * T::BUF + T::QE + o) = rok[i] ? dr[i] : z;
   };
   auto stage_store = [&](int buf) {
 #pragma unroll
