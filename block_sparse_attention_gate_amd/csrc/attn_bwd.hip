@@ -558,10 +558,10 @@ __global__ __launch_bounds__(64 * NW, 1) void k_bwd_dkdv(
   const int olo = (int)((int64_t)nown_all * seg / nseg);   // this segment's own steps
   const int nsteps = rsteps + (int)((int64_t)nown_all * (seg + 1) / nseg) - olo;
 
-  // Staging, three steps in flight: the entry id of step it+2 (routed steps
-  // read it from the list), the Q / dO rows and the two statistics of step
-  // it+1 (requested once step it's first products are issued), and the LDS
-  // tiles of step it.  Lane l finds query l of a step; wave w loads the rows
+  // Staging, three steps in flight: the row index of the entries of step
+  // it+2 (routed steps read it from `ent`), the Q / dO rows and the two
+  // statistics of step it+1 (requested at the start of step it), and the
+  // LDS tiles of step it.  Lane l finds query l of a step; wave w loads the rows
   // of queries RPW w .. RPW (w + 1) - 1, RPI whole rows per load (CPR lanes
   // per row, the row index passed between lanes), so that a load touches RPI
   // rows rather than 64: the gather's cost is the number of rows a load
