@@ -8,7 +8,9 @@
 //   dv_t += p_t dO,   ds_t = p_t (dO.v_t - Dv),   dq = c sum_t ds_t k_t,
 //   dk_t += c ds_t q.
 // Kernels:
-//   k_bwd_dot        Dv per query-head.
+//   k_bwd_dot        Dv per query-head (and, for dk/dv, lse and Dv per row
+//                    in memory order).
+//   k_bwd_entry_rows the Q / dO row index of every routed entry.
 //   k_bwd_tail       for a length that is not a multiple of 64, the last K
 //                    and V tiles [S, 64, Hkv, D] zero padded (so that no tile
 //                    load passes the end).
