@@ -93,11 +93,12 @@ struct TileRegs {
 // before the accumulators are rescaled (probabilities stay <= 2^8, far from
 // fp32 or bf16 overflow).
 constexpr float kRescaleSlack = 8.0f;
+constexpr float kProbBound = 256.0f;  // 2^kRescaleSlack
 
 template <int D>
 struct FlashAcc {
   f32x16 o[D / 32];
-  float m;  // reference max of the scaled logits (base 2), within kRescaleSlack of the max
+  float m;  // reference max of the scaled logits (base 2)
   float l;  // running sum of this lane half's probabilities
   __device__ __forceinline__ void init() {
 #pragma unroll
@@ -106,6 +107,25 @@ struct FlashAcc {
     l = 0.f;
   }
 };
+
+// The 32 probabilities of one lane for one 64-key step against the reference
+// -mneg (base 2), rounded to bf16 for the P.V product; returns their fp32 sum
+// (two interleaved partial sums).
+__device__ __forceinline__ float step_probs(const f32x16 (&s)[2], float sl2, float mneg,
+                                            bf16x8 (&pb)[2][2]) {
+  float sum[2] = {0.f, 0.f};
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][8 * c + r], sl2, mneg));
+        sum[kt] += p;
+        pb[kt][c][r] = static_cast<__bf16>(p);
+      }
+  return sum[0] + sum[1];
+}
 
 // One 64-key step of one wave.  MASK: drop keys outside [klo, qpos].
 template <int D, bool MASK>
@@ -137,42 +157,35 @@ __device__ __forceinline__ void flash_step(const bf16_t* buf, const bf16x8 (&qf)
         if (key > qpos || key < klo) s[kt][reg] = -__builtin_inff();
       }
   }
-  float mx = s[0][0];
+  // Lazy rescale, checked through the probabilities: they are first taken
+  // against the current reference max acc.m.  A lane sum <= 2^kRescaleSlack
+  // bounds each of them, and the step needs no max.  Otherwise (a logit well
+  // above the reference, or the first step, where the reference is -inf and
+  // the sum is not finite) the wave computes the step max, moves the
+  // reference of every row whose max passed it, rescales O and l, and takes
+  // the probabilities again.  Exact up to rounding: l sums the same
+  // probabilities against the same reference, and the output is divided by
+  // it at the end.
+  bf16x8 pb[2][2];
+  float psum = step_probs(s, sl2, -acc.m, pb);
+  if (__any(!(psum <= kProbBound))) {
+    float mx = s[0][0];
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-    for (int reg = 0; reg < 16; ++reg) mx = fmaxf(mx, s[kt][reg]);
-  mx = fmaxf(mx, half_swap(mx));
-  // Lazy rescale: the reference max acc.m moves only when some row's tile
-  // max passes it by more than kRescaleSlack (base-2 units); otherwise the
-  // tile's probabilities are taken against the old reference and stay below
-  // 2^kRescaleSlack.  Exact up to rounding: the normaliser acc.l uses the
-  // same reference, and the output is divided by it at the end.
-  const float mt = mx * sl2;
-  if (__any(mt > acc.m + kRescaleSlack)) {
-    const float mnew = fmaxf(acc.m, mt);
-    const float alpha =
-        __builtin_amdgcn_exp2f(acc.m - ((mnew == -__builtin_inff()) ? 0.f : mnew));
+      for (int reg = 0; reg < 16; ++reg) mx = fmaxf(mx, s[kt][reg]);
+    mx = fmaxf(mx, half_swap(mx));
+    const float mnew = fmaxf(acc.m, mx * sl2);
+    const float mref = (mnew == -__builtin_inff()) ? 0.f : mnew;
+    const float alpha = __builtin_amdgcn_exp2f(acc.m - mref);
     acc.l *= alpha;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
       for (int reg = 0; reg < 16; ++reg) acc.o[dt][reg] *= alpha;
     acc.m = mnew;
+    psum = step_probs(s, sl2, -mref, pb);
   }
-  const float mref = (acc.m == -__builtin_inff()) ? 0.f : acc.m;
-  float psum = 0.f;
-  bf16x8 pb[2][2];
-#pragma unroll
-  for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][8 * c + r], sl2, -mref));
-        psum += p;
-        pb[kt][c][r] = static_cast<__bf16>(p);
-      }
   acc.l += psum;
   // O^T += V^T P^T: the D/32 accumulators are independent; interleave them.
   const bf16_t* vbase = buf + T::KE + 8 * hh + n * T::VS;
