@@ -128,7 +128,10 @@ __device__ __forceinline__ float step_probs(const f32x16 (&s)[2], float sl2, flo
 }
 
 // One 64-key step of one wave.  MASK: drop keys outside [klo, qpos].
-template <int D, bool MASK>
+// VPRE (0..4): 16-key groups of V^T fragments read from LDS before the
+// softmax, so that their latency passes under it (bounded by the kernel's
+// register budget); the rest are read after it.
+template <int D, bool MASK, int VPRE>
 __device__ __forceinline__ void flash_step(const bf16_t* buf, const bf16x8 (&qf)[D / 16],
                                            FlashAcc<D>& acc, int n, int hh, float sl2,
                                            int key0, int klo, int qpos) {
@@ -147,6 +150,15 @@ __device__ __forceinline__ void flash_step(const bf16_t* buf, const bf16x8 (&qf)
   for (int t = 0; t < D / 16; ++t) {
     s[0] = mfma32(ka[t], qf[t], s[0]);
     s[1] = mfma32(kb[t], qf[t], s[1]);
+  }
+  const bf16_t* vbase = buf + T::KE + 8 * hh + n * T::VS;
+  bf16x8 va[D / 32][4];
+  if (VPRE > 0) {
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int kc = 0; kc < VPRE; ++kc) va[dt][kc] = ld_bf16x8(vbase + 32 * dt * T::VS + 16 * kc);
+    __builtin_amdgcn_sched_barrier(0);
   }
   if (MASK) {
 #pragma unroll
@@ -188,17 +200,25 @@ __device__ __forceinline__ void flash_step(const bf16_t* buf, const bf16x8 (&qf)
   }
   acc.l += psum;
   // O^T += V^T P^T: the D/32 accumulators are independent; interleave them.
-  const bf16_t* vbase = buf + T::KE + 8 * hh + n * T::VS;
-  bf16x8 va[D / 32][4];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) va[dt][kc] = ld_bf16x8(vbase + 32 * dt * T::VS + 16 * kc);
+    for (int kc = VPRE; kc < 4; ++kc) va[dt][kc] = ld_bf16x8(vbase + 32 * dt * T::VS + 16 * kc);
 #pragma unroll
   for (int kc = 0; kc < 4; ++kc)
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
       acc.o[dt] = mfma32(va[dt][kc], pb[kc >> 1][kc & 1], acc.o[dt]);
+}
+
+// V^T fragment groups read before the softmax (flash_step's VPRE) per kernel
+// shape: as many as the register budget holds without spilling (two waves
+// per SIMD: 256 registers).
+template <int D, int NW, bool ROUTED>
+constexpr int vpre_groups() {
+  if (D == 64) return 4;
+  if (NW == 8) return 2;
+  return 0;
 }
 
 template <int D>
@@ -225,6 +245,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_routed(
     int64_t Lq, int64_t L, int64_t Lv, int H, int Hkv, int kp, int B, int nb, int nrows,
     float sl2, uint32_t nslots, int64_t prow0, int ph0, int pH) {
   using T = Tiles<D, NW>;
+  constexpr int VPRE = vpre_groups<D, NW, true>();
   constexpr int TM = 32 * NW;  // routed entries per tile
   // Eight-wave tiles (one workgroup per CU) copy the tile and bucket offsets
   // into LDS with parallel loads and search them there, instead of a chain of
@@ -299,7 +320,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_routed(
       ktile += ktile_step;
       vttile += 64;
       if (more) tr.load(ktile, vttile);
-      flash_step<D, false>(lds + (it & 1) * T::BUF, qf, acc, n, hh, sl2, 0, 0, 0);
+      flash_step<D, false, VPRE>(lds + (it & 1) * T::BUF, qf, acc, n, hh, sl2, 0, 0, 0);
       if (more) tr.store(lds + ((it + 1) & 1) * T::BUF);
       __syncthreads();
     }
@@ -347,6 +368,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_query(
     int q_off, int H, int Hkv, int kp, int B, int HW, float sl2, int nparts, int chunk_tiles,
     int ps0, int ph0, int pH) {
   using T = Tiles<D, NW>;
+  constexpr int VPRE = vpre_groups<D, NW, false>();
   __shared__ __attribute__((aligned(16))) bf16_t lds[2 * T::BUF];
   const int RW = 32 * NW / HW;
   // Modes 2 and 3: blockIdx.x = P * item + part (P key-range parts per item).
@@ -470,13 +492,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_query(
   }
   for (; it < wd_; ++it) {
     const bool more = advance(it);
-    flash_step<D, false>(lds + ((it - t0) & 1) * T::BUF, qf, acc, n, hh, sl2, 0, 0, 0);
+    flash_step<D, false, VPRE>(lds + ((it - t0) & 1) * T::BUF, qf, acc, n, hh, sl2, 0, 0, 0);
     if (more) tr.store(lds + ((it + 1 - t0) & 1) * T::BUF);
     __syncthreads();
   }
   for (; it < we_; ++it) {
     const bool more = advance(it);
-    flash_step<D, true>(lds + ((it - t0) & 1) * T::BUF, qf, acc, n, hh, sl2, it * 64, klo_l,
+    flash_step<D, true, VPRE>(lds + ((it - t0) & 1) * T::BUF, qf, acc, n, hh, sl2, it * 64, klo_l,
                         pos);
     if (more) tr.store(lds + ((it + 1 - t0) & 1) * T::BUF);
     __syncthreads();
