@@ -213,6 +213,13 @@ __device__ __forceinline__ void dq_step(const bf16_t* buf, const bf16x8 (&qf)[D 
       s = mfma32(ld_bf16x8(kr), qf[t], s);
       dp = mfma32(ld_bf16x8(kr + KE), df[t], dp);
     }
+    // The first two K^T fragments of the dQ product are read before dS, so
+    // that their LDS latency passes under it (more would not fit the register
+    // budget of two waves per SIMD).
+    bf16x8 kf0[D / 32];
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt) kf0[dt] = tr_frag<D>(buf, dt, 2 * kt, lane);
+    __builtin_amdgcn_sched_barrier(0);
     // dS^T = P^T (dP^T - Dv), P^T = 2^(S^T sl2 - lse2); registers [8c, 8c+8)
     // hold keys 32 kt + 16 c + 8 hh + [0, 8): the B operand layout
     bf16x8 dsb[2];
@@ -229,10 +236,12 @@ __device__ __forceinline__ void dq_step(const bf16_t* buf, const bf16x8 (&qf)[D 
         dsb[c][r] = static_cast<__bf16>(p * (dp[reg] - dv));
       }
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+    for (int dt = 2; dt < D / 32; ++dt) kf0[dt] = tr_frag<D>(buf, dt, 2 * kt, lane);
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-        dq[dt] = mfma32(tr_frag<D>(buf, dt, 2 * kt + c, lane), dsb[c], dq[dt]);
+    for (int dt = 0; dt < D / 32; ++dt) dq[dt] = mfma32(kf0[dt], dsb[0], dq[dt]);
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+      dq[dt] = mfma32(tr_frag<D>(buf, dt, 2 * kt + 1, lane), dsb[1], dq[dt]);
   }
 }
 
