@@ -534,7 +534,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_query(
     float M = lse_own;
     const int64_t sbase = (((int64_t)(s - ps0) * pH + (h - ph0)) * Lq + r) * kp;
     // all routed log-sum-exps first (independent loads), then the partial
-    // rows four at a time (four loads in flight per lane instead of one)
+    // rows four at a time (four rows in flight per lane instead of one).  A
+    // lane loads 16 bytes of a row, the half hh of each 32-byte group; the
+    // two lanes of a query then exchange the middle 8 bytes
+    // (v_permlane32_swap), which leaves each with its 4-element pieces of the
+    // accumulator layout (elements 8i + 4hh + [0, 4) of each 32-row group).
     float lsv[kMaxTopk - 1];
 #pragma unroll
     for (int t = 0; t < kMaxTopk - 1; ++t)
@@ -551,15 +555,15 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_query(
 #pragma unroll
     for (int t0 = 0; t0 < kMaxTopk - 1; t0 += 4) {
       if (t0 < npast) {
-        uint2 raw[4][D / 32][4];
+        u32x4 raw[4][D / 32][2];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const bf16_t* prow = po + (sbase + (t0 + u < npast ? t0 + u : t0)) * D;
 #pragma unroll
           for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              raw[u][dt][i] = *reinterpret_cast<const uint2*>(prow + 32 * dt + 8 * i + 4 * hh);
+            for (int m = 0; m < 2; ++m)
+              raw[u][dt][m] = *reinterpret_cast<const u32x4*>(prow + 32 * dt + 16 * m + 8 * hh);
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -569,12 +573,20 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_query(
 #pragma unroll
           for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const uint2 x = raw[u][dt][i];
-              acc.o[dt][4 * i] = fmaf(wt, __uint_as_float(x.x << 16), acc.o[dt][4 * i]);
-              acc.o[dt][4 * i + 1] = fmaf(wt, __uint_as_float(x.x & 0xffff0000u), acc.o[dt][4 * i + 1]);
-              acc.o[dt][4 * i + 2] = fmaf(wt, __uint_as_float(x.y << 16), acc.o[dt][4 * i + 2]);
-              acc.o[dt][4 * i + 3] = fmaf(wt, __uint_as_float(x.y & 0xffff0000u), acc.o[dt][4 * i + 3]);
+            for (int m = 0; m < 2; ++m) {
+              const u32x4 x = raw[u][dt][m];
+              // [0]: pieces i = 2m, [1]: i = 2m + 1 (first and second dwords)
+              const auto w0 = __builtin_amdgcn_permlane32_swap(x[0], x[2], false, false);
+              const auto w1 = __builtin_amdgcn_permlane32_swap(x[1], x[3], false, false);
+#pragma unroll
+              for (int e = 0; e < 2; ++e) {
+                const int i = 2 * m + e;
+                const uint32_t a = w0[e], b = w1[e];
+                acc.o[dt][4 * i] = fmaf(wt, __uint_as_float(a << 16), acc.o[dt][4 * i]);
+                acc.o[dt][4 * i + 1] = fmaf(wt, __uint_as_float(a & 0xffff0000u), acc.o[dt][4 * i + 1]);
+                acc.o[dt][4 * i + 2] = fmaf(wt, __uint_as_float(b << 16), acc.o[dt][4 * i + 2]);
+                acc.o[dt][4 * i + 3] = fmaf(wt, __uint_as_float(b & 0xffff0000u), acc.o[dt][4 * i + 3]);
+              }
             }
         }
       }
