@@ -19,13 +19,16 @@ def _moba():
     return moba
 
 
-def _run_case(w, n_uniform=None, seed=0, entry="moba_forward_ex"):
+def _run_case(w, n_uniform=None, seed=0, entry="moba_forward_ex", transform=None):
     """Parity run of one workload: every row when n_uniform is None, else a
     sample of rows (block edges + n_uniform uniform rows) for outputs.
-    `entry` names the forward under test (moba_forward_ex or moba_naive_ex)."""
+    `entry` names the forward under test (moba_forward_ex or moba_naive_ex);
+    `transform(q, k, v)` reshapes the seeded inputs first."""
     moba = _moba()
     print(f"case {w} via {entry}", flush=True)
     q, k, v = moba_inputs.make_inputs(w, device=DEV)
+    if transform is not None:
+        q, k, v = transform(q, k, v)
     out, sel = getattr(moba, entry)(q, k, v, w.block_size, w.topk, return_selection=True)
     torch.cuda.synchronize()
     batched = q.dim() == 4
@@ -122,6 +125,58 @@ SMALL = [
 @pytest.mark.parametrize("w", SMALL, ids=[w.name for w in SMALL])
 def test_small_parity(w):
     _run_case(w)
+
+
+def _growing_logits(B, qscale=2.0, kgrow=6.0):
+    """Inputs whose scaled logits grow along every block: q scaled by qscale
+    and key i of a block by 1 + kgrow * (i % B) / B, so that a block's later
+    64-key tiles pass the running reference max of the online softmax by far
+    more than its rescale slack (8 in base 2): the attention kernels take the
+    step max, rescale O and l and recompute the probabilities in the middle
+    of a block, which logits of the seeded N(0, 1) inputs never make them do.
+    V is scaled by 1/4 (exact in bf16): such peaked softmaxes give outputs of
+    the size of single V rows, and the bf16 roundings of P, of the partials
+    and of the output (2^-9 relative each) would otherwise reach the absolute
+    bound the parity check derives for outputs of O(1)."""
+    def f(q, k, v):
+        L = k.shape[-3]
+        pos = torch.arange(L, device=k.device, dtype=torch.float32)
+        sc = (1.0 + kgrow * torch.remainder(pos, B) / B).view(-1, 1, 1)
+        return ((q.float() * qscale).to(q.dtype), (k.float() * sc).to(k.dtype),
+                (v.float() * 0.25).to(v.dtype))
+    return f
+
+
+RESCALE = [
+    # small-problem path: routed tiles and the own block on the side stream
+    (moba_inputs.custom("rescale_d128", "bf16", 1, 2048, None, 2, 1, 128, 256, 3, 71), None),
+    (moba_inputs.custom("rescale_d64_ragged", "bf16", 1, 1500, None, 4, 2, 64, 128, 4, 72), None),
+    # more than 2^20 query-heads: the fused own-block attention and merge
+    (moba_inputs.custom("rescale_fused_own", "bf16", 1, 32768, None, 40, 8, 128, 512, 4, 73), 48),
+    (moba_inputs.custom("rescale_f32", "f32", 1, 1024, None, 2, 1, 64, 256, 3, 74), None),
+]
+
+
+@pytest.mark.parametrize("w,n_uniform", RESCALE, ids=[w.name for w, _ in RESCALE])
+def test_rescale_path_with_growing_logits(w, n_uniform):
+    """The online softmax's rescale of O and l in the middle of a block
+    (routed tiles and own block), against the oracle's exact softmax."""
+    tf = _growing_logits(w.block_size)
+    q, k, v, _, _ = _run_case(w, n_uniform=n_uniform, transform=tf)
+    # the inputs do force rescales: for most rows, the largest scaled logit
+    # (base 2) over the last 64 keys of its first block passes the one over
+    # the first 64 keys by more than the slack
+    qh, kh = to64(q), to64(k)
+    if qh.ndim == 4:
+        qh, kh = qh[0], kh[0]
+    B, D = w.block_size, qh.shape[-1]
+    rows = np.arange(B, qh.shape[0], 97)
+    l2s = np.log2(np.e) / np.sqrt(D)
+    first = np.einsum("rd,kd->rk", qh[rows, 0], kh[:64, 0]).max(axis=1) * l2s
+    last = np.einsum("rd,kd->rk", qh[rows, 0], kh[B - 64:B, 0]).max(axis=1) * l2s
+    frac = float(np.mean(last - first > 8.0))
+    print(f"  rows whose block-0 reference moves by > 8 (base 2): {frac:.2f}")
+    assert frac > 0.5
 
 
 EDGE = [
