@@ -672,7 +672,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_bwd_dkdv(
   constexpr int NS = D / 8;          // slots per phase
   constexpr int EPS = 16 / NS;       // softmax elements per slot
   constexpr int GS = 4 / EPS;        // slots per group of four elements
-  constexpr int kPre = 4;
+  constexpr int kPre = 6;
   const int arow = kperm(n);
   auto frag = [&](const bf16_t* b, int k) -> bf16x8 {
     if (k < 2 * NS) {
