@@ -6,8 +6,10 @@ import torch
 
 import moba_inputs
 from oracle import moba_oracle as O
-from tests.parity import (check_outputs, check_selection, check_selection_all_rows,
-                          device_fetch, host_fetch, sample_rows, to64)
+from tests.all_rows import compare_all_rows, reference_all_rows
+from tests.parity import (RELRMS, TOL, check_outputs, check_selection,
+                          check_selection_all_rows, device_fetch, host_fetch, sample_rows,
+                          to64)
 
 pytestmark = pytest.mark.gpu
 
@@ -99,6 +101,30 @@ def _run_large(w, n_sel_rows, n_out_rows, heads_out, n_edge_rows=32, seed=0, all
     emax, emean = check_outputs(out_rows, q_rows, rows, sel_rows, w.block_size, L, w.dtype,
                                 pairs, device_fetch(k, v), k.shape[1])
     print(f"  outputs ok on {len(pairs)} pairs: max|err| {emax:.2e} mean|err| {emean:.2e}")
+    if all_rows:
+        # every output row against the float32 PyTorch reference, which is
+        # first checked against the oracle on sampled pairs
+        ref = reference_all_rows(q, k, v, sel, w.block_size)
+        torch.cuda.synchronize()
+        fetch = device_fetch(k, v)
+        G = q.shape[1] // k.shape[1]
+        scale = 1.0 / np.sqrt(q.shape[2])
+        worst = 0.0
+        for h, n in pairs[:16]:
+            pos = int(rows[n])
+            keys = O.key_set(sel_rows[h, n], pos, w.block_size, L)
+            kk, vv = fetch(h // G, keys)
+            want = O.attend(q_rows[n, h], kk, vv, np.arange(keys.size), scale)
+            got = ref[h, pos].double().cpu().numpy()
+            worst = max(worst, float(np.abs(got - want).max() / max(np.abs(want).max(), 1e-30)))
+        assert worst <= 1e-4, f"float32 reference off the oracle by {worst:.2e} (relative)"
+        tmax, tmean = TOL[w.dtype]
+        amax, amean, rmax = compare_all_rows(out, ref, tmax, tmean, RELRMS[w.dtype])
+        del ref
+        print(f"  every output row ({L} rows x {q.shape[1]} heads) against the float32 "
+              f"reference (within {worst:.1e} of the oracle on {min(16, len(pairs))} pairs): "
+              f"max|err| {amax:.2e} mean|err| {amean:.2e} worst relative RMS {rmax:.2e}",
+              flush=True)
 
 
 SMALL = [
@@ -409,7 +435,8 @@ def test_error_paths_enqueue_nothing():
 
 def test_llama8b_128k_parity():
     """Llama-3.1-8B layer shape at 128K (32/8 heads, block 4096, top-k 12):
-    the selection of every query row of every head, outputs sampled."""
+    the selection of every query row of every head; outputs sampled against
+    the oracle and every row against the float32 reference."""
     _run_large(moba_inputs.WORKLOADS["llama8b_128k"], n_sel_rows=8192, n_out_rows=32,
                heads_out=(0, 5, 31), n_edge_rows=32, all_rows=True)
 
@@ -489,16 +516,18 @@ def test_routing_table_equals_the_oracle(w):
 
 def test_prefill_1m_parity():
     """The 1M-token prefill (32/8 heads, block 4096, top-k 12): the selection
-    of every query row of every head (33.6M query-heads), outputs sampled."""
+    of every query row of every head (33.6M query-heads); outputs sampled
+    against the oracle and every row against the float32 reference."""
     _run_large(moba_inputs.WORKLOADS["prefill_1m"], n_sel_rows=4096, n_out_rows=24,
                heads_out=(0, 17), n_edge_rows=24, all_rows=True)
 
 
-def test_prefill_10m_parity_sampled():
+def test_prefill_10m_parity():
     """10M tokens, one head (block 4096 -> 2560 blocks, top-k 12; 115M routed
-    entries), sampled like the 1M case."""
+    entries), checked like the 1M case: the selection of every row, outputs
+    sampled against the oracle and every row against the float32 reference."""
     _run_large(moba_inputs.WORKLOADS["prefill_10m"], n_sel_rows=4096, n_out_rows=24,
-               heads_out=(0,), n_edge_rows=24)
+               heads_out=(0,), n_edge_rows=24, all_rows=True)
 
 
 def test_largest_block_count_sampled():

@@ -101,3 +101,33 @@ def test_all_rows_check_rejects_a_planted_wrong_row(plant):
     sel[r] = row
     with pytest.raises(AssertionError):
         parity.check_selection_all_rows(q, kbar, sel, B, topk)
+
+
+def test_float32_every_row_reference_matches_the_oracle():
+    """The float32 reference that checks every output row of the 128K and 1M
+    GPU runs (tests/all_rows.py) against the oracle's forward on a small GQA
+    case with a ragged last block; a selection with one past block swapped
+    must move that row, so the reference attends the set it is given."""
+    import torch
+    from oracle import moba_oracle as O
+    from tests.all_rows import reference_all_rows
+    rng = np.random.default_rng(7)
+    L, H, Hkv, D, B, topk = 300, 4, 2, 64, 64, 3
+    q = rng.standard_normal((L, H, D))
+    k = rng.standard_normal((L, Hkv, D))
+    v = rng.standard_normal((L, Hkv, D))
+    out, sel, _ = O.moba_reference(q, k, v, B, topk)
+    t = lambda x: torch.tensor(x, dtype=torch.float32)
+    ref = reference_all_rows(t(q), t(k), t(v), torch.tensor(sel, dtype=torch.int32), B)
+    got = ref.permute(1, 0, 2).double().numpy()
+    assert np.abs(got - out).max() < 1e-5
+    # row 290 of head 1 (own block 4) keeps two of the past blocks 0..3;
+    # give it the one it dropped instead of its first
+    row = sel[1, 290].copy()
+    dropped = [j for j in range(4) if j not in row][0]
+    bad = sel.copy()
+    bad[1, 290, 0] = dropped
+    bad[1, 290] = np.sort(bad[1, 290])
+    ref2 = reference_all_rows(t(q), t(k), t(v), torch.tensor(bad, dtype=torch.int32), B)
+    assert np.abs(ref2[1, 290].double().numpy() - out[290, 1]).max() > 1e-3
+    assert torch.equal(ref2[0], ref[0])
