@@ -6,7 +6,8 @@ import torch
 
 import moba_inputs
 from oracle import moba_oracle as O
-from tests.all_rows import compare_all_rows, reference_all_rows
+from tests.all_rows import (compare_all_rows, compare_grad_rows, reference_all_rows,
+                            reference_backward_all)
 from tests.parity import (RELRMS, TOL, check_outputs, check_selection,
                           check_selection_all_rows, device_fetch, host_fetch, sample_rows,
                           to64)
@@ -936,12 +937,13 @@ def test_backward_is_deterministic(dtype):
         assert torch.equal(x.view(bits), y.view(bits))
 
 
-def test_backward_128k_sampled():
+def test_backward_128k_parity():
     """The Llama-layer shape at 128K (32/8 heads, block 4096, top-k 12): dq of
     sampled rows of four heads against the oracle (per row with dO.o from the
-    same bf16 output; over the sample against the exact gradient), and for dk
+    same bf16 output; over the sample against the exact gradient), for dk
     and dv the sums over all keys of every KV head, which the softmax fixes in
-    closed form (dK sums to zero, dV to the group's dO summed over queries)."""
+    closed form (dK sums to zero, dV to the group's dO summed over queries),
+    and every row of dq, dk and dv against the float32 gradient reference."""
     moba = _moba()
     w = moba_inputs.WORKLOADS["llama8b_128k"]
     print(f"case {w}", flush=True)
@@ -988,6 +990,19 @@ def test_backward_128k_sampled():
         exe.append(np.linalg.norm(got - exact) / np.linalg.norm(exact))
     print(f"  dq worst row rel RMS {max(errs):.2e}; vs exact over the sample {max(exe):.2e}")
     assert max(errs) <= BWD_RELRMS and max(exe) <= BWD_EXACT_REL
+    # every element of dq, dk and dv against the float32 gradient reference
+    # (pinned to the oracle's backward on the CPU), per row as above
+    refs = reference_backward_all(q, k, v, out, dout, sel, w.block_size)
+    torch.cuda.synchronize()
+    # the reference's dq rows agree with the oracle's on the sampled rows
+    ridx = torch.as_tensor(rows, device=DEV)
+    off = float(np.abs(refs[0][ridx, 31].double().cpu().numpy() - ref).max()
+                / np.abs(ref).max())
+    assert off <= 1e-4, f"float32 gradient reference off the oracle by {off:.2e}"
+    for name, got, r_ in zip(("dq", "dk", "dv"), (dq, dk, dv), refs):
+        worst, med, nbig, small = compare_grad_rows(name, got, r_, BWD_RELRMS)
+        print(f"  every {name} row ({nbig} rows): worst rel RMS {worst:.2e} (median {med:.2e}), "
+              f"near-zero rows off by {small:.1e}", flush=True)
 
 
 def test_plain_c_consumer_on_the_gpu():

@@ -131,3 +131,27 @@ def test_float32_every_row_reference_matches_the_oracle():
     ref2 = reference_all_rows(t(q), t(k), t(v), torch.tensor(bad, dtype=torch.int32), B)
     assert np.abs(ref2[1, 290].double().numpy() - out[290, 1]).max() > 1e-3
     assert torch.equal(ref2[0], ref[0])
+
+
+def test_float32_every_element_backward_reference_matches_the_oracle():
+    """The float32 gradient reference of the 128K GPU backward run
+    (tests/all_rows.py) against the oracle's backward on the same selection
+    and forward output (GQA, ragged last block): dq, dk and dv within 1e-4 of
+    the largest gradient."""
+    import torch
+    from oracle import moba_oracle as O
+    from tests.all_rows import reference_backward_all
+    rng = np.random.default_rng(11)
+    L, H, Hkv, D, B, topk = 300, 4, 2, 64, 64, 3
+    q = rng.standard_normal((L, H, D))
+    k = rng.standard_normal((L, Hkv, D))
+    v = rng.standard_normal((L, Hkv, D))
+    dout = rng.standard_normal((L, H, D))
+    out, sel, _ = O.moba_reference(q, k, v, B, topk)
+    out = out + 1e-3 * rng.standard_normal(out.shape)  # a stored output, rounded
+    ref = O.moba_backward_reference(q, k, v, dout, B, sel, out=out)
+    t = lambda x: torch.tensor(x, dtype=torch.float32)
+    got = reference_backward_all(t(q), t(k), t(v), t(out), t(dout),
+                                 torch.tensor(sel, dtype=torch.int32), B)
+    for g_, r_ in zip(got, ref):
+        assert np.abs(g_.double().numpy() - r_).max() <= 1e-4 * np.abs(r_).max()
