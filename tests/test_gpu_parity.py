@@ -381,9 +381,15 @@ def test_precomputed_block_means_prefill():
 
 
 def test_micro_32k_parity():
-    """The 32K single-head shape (block 2048, top-k 3): every selection, and
-    outputs for block-edge and uniform rows."""
-    _run_case(moba_inputs.WORKLOADS["micro_32k"], n_uniform=2048)
+    """The 32K single-head shape (block 2048, top-k 3): every selection,
+    outputs for block-edge and uniform rows against the oracle, and every
+    output row against the float32 reference of tests/all_rows.py."""
+    w = moba_inputs.WORKLOADS["micro_32k"]
+    q, k, v, out, sel = _run_case(w, n_uniform=2048)
+    ref = reference_all_rows(q, k, v, sel, w.block_size)
+    amax, amean, rmax = compare_all_rows(out, ref, *TOL[w.dtype], RELRMS[w.dtype])
+    print(f"  every output row against the float32 reference: max|err| {amax:.2e} "
+          f"mean|err| {amean:.2e} worst relative RMS {rmax:.2e}", flush=True)
 
 
 NAIVE = [
